@@ -1,0 +1,200 @@
+"""CPU oracle of the speculative-decoding verify-and-commit step.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU-baseline
+leg of the benchmark may import this package.  It wraps ``liboracle.so``, a
+plain single-threaded double-precision C restatement of the step (see
+``specdec_oracle.c`` for the passages it follows), and shares no code with the
+HIP path.  Its inputs come from the seeded generator; its outputs are never fed
+back into the device path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "specdec_oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+FLAG_RESIDUAL_FALLBACK = 0x2
+FLAG_NONFINITE = 0x4
+FLAG_TOKEN_RANGE = 0x8
+
+
+def _compile(src: str, out: str) -> None:
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared",
+           "-fno-fast-math", "-ffp-contract=off", "-I", HERE, "-o", out + ".tmp", src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+
+
+def build() -> str:
+    """Compile liboracle.so with gcc (-O2, no fast-math: IEEE double)."""
+    _compile(SRC, LIB)
+    return LIB
+
+
+def build_copy(source_text: str, workdir: str) -> "Oracle":
+    """Compile a (test-modified) copy of the oracle source and load it.
+
+    Used only by tests that plant a mistake in the oracle to show that its
+    pins catch it."""
+    os.makedirs(workdir, exist_ok=True)
+    src = os.path.join(workdir, "oracle_copy.c")
+    with open(src, "w") as f:
+        f.write(source_text)
+    out = os.path.join(workdir, "liboracle_copy.so")
+    _compile(src, out)
+    return Oracle(out)
+
+
+class _Args(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("gamma_max", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("is_bf16", ctypes.c_int32),
+                ("greedy", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("temperature", ctypes.c_double), ("top_p", ctypes.c_double),
+                ("seed", ctypes.c_uint64), ("round", ctypes.c_uint32),
+                ("pad_", ctypes.c_int32)]
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+class Oracle:
+    """A loaded oracle library (the default one, or a test build of a copy)."""
+
+    def __init__(self, path: str):
+        L = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        L.oracle_verify.argtypes = [ctypes.POINTER(_Args), P, P, P, P, P, ctypes.c_int32,
+                                    P, P, P, P, P, P, P, P, P]
+        L.oracle_verify.restype = ctypes.c_int
+        L.oracle_row_distribution.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
+                                              ctypes.c_int32, ctypes.c_double, P, P]
+        L.oracle_row_distribution.restype = ctypes.c_int
+        L.oracle_philox4x32_10.argtypes = [P, P, P]
+        L.oracle_philox4x32_10.restype = None
+        L.oracle_commit_kv.argtypes = [ctypes.c_int32] * 7 + [ctypes.c_int64, P, P, P, P, P, P]
+        L.oracle_commit_kv.restype = ctypes.c_int
+        self.lib = L
+        self.path = path
+
+    def philox4x32_10(self, ctr, key) -> np.ndarray:
+        c = np.ascontiguousarray(ctr, dtype=np.uint32)
+        k = np.ascontiguousarray(key, dtype=np.uint32)
+        out = np.zeros(4, dtype=np.uint32)
+        self.lib.oracle_philox4x32_10(_ptr(c), _ptr(k), _ptr(out))
+        return out
+
+    def row_distribution(self, row: np.ndarray, temperature: float = 1.0, top_k: int = 0,
+                         top_p: float = 1.0):
+        """Dense sampling distribution of one row; returns (prob, kept, near_cut)."""
+        row = np.ascontiguousarray(row)
+        is_bf16 = row.dtype == np.uint16
+        if not is_bf16:
+            row = row.astype(np.float32)
+        prob = np.zeros(row.shape[0], dtype=np.float64)
+        near = np.zeros(1, dtype=np.int32)
+        kept = self.lib.oracle_row_distribution(_ptr(row), int(is_bf16), row.shape[0],
+                                             float(temperature), int(top_k), float(top_p),
+                                             _ptr(prob), _ptr(near))
+        return prob, kept, bool(near[0])
+
+    def verify(self, target: np.ndarray, draft: Optional[np.ndarray], draft_tokens: np.ndarray,
+               gamma: Optional[np.ndarray] = None, *, greedy: bool = False,
+               temperature: float = 1.0, top_k: int = 0, top_p: float = 1.0,
+               seed: int = 0, round: int = 0, requests=None,
+               u_accept: Optional[np.ndarray] = None, u_sample: Optional[np.ndarray] = None):
+        """Run the oracle on (a subset of) a padded batch.  Returns a dict of arrays."""
+        target = np.ascontiguousarray(target)
+        B, G1, V = target.shape
+        G = G1 - 1
+        is_bf16 = target.dtype == np.uint16
+        if draft is not None:
+            draft = np.ascontiguousarray(draft)
+            assert draft.dtype == target.dtype and draft.shape == (B, G, V)
+        tokens = np.ascontiguousarray(draft_tokens, dtype=np.int32)
+        assert tokens.shape == (B, G)
+        if gamma is not None:
+            gamma = np.ascontiguousarray(gamma, dtype=np.int32)
+        ids = None
+        n = B
+        if requests is not None:
+            ids = np.ascontiguousarray(requests, dtype=np.int32)
+            n = ids.shape[0]
+        if u_accept is not None:
+            u_accept = np.ascontiguousarray(u_accept, dtype=np.float64)
+            u_sample = np.ascontiguousarray(u_sample, dtype=np.float64)
+            assert u_accept.shape == (n, G + 1) and u_sample.shape == (n, G + 1)
+        a = _Args(B, G, V, int(is_bf16), int(greedy), int(top_k), float(temperature),
+                  float(top_p), int(seed) & (2**64 - 1), int(round) & 0xFFFFFFFF, 0)
+        out = {
+            "accept_count": np.zeros(n, np.int32),
+            "out_tokens": np.zeros((n, G + 1), np.int32),
+            "p_draft": np.zeros((n, G), np.float64),
+            "q_draft": np.zeros((n, G), np.float64),
+            "residual_mass": np.zeros(n, np.float64),
+            "flags": np.zeros(n, np.uint32),
+            "near_pos": np.zeros(n, np.int32),
+        }
+        rc = self.lib.oracle_verify(ctypes.byref(a), _ptr(target), _ptr(draft), _ptr(tokens),
+                                 _ptr(gamma), _ptr(ids), n, _ptr(u_accept), _ptr(u_sample),
+                                 _ptr(out["accept_count"]), _ptr(out["out_tokens"]),
+                                 _ptr(out["p_draft"]), _ptr(out["q_draft"]),
+                                 _ptr(out["residual_mass"]), _ptr(out["flags"]),
+                                 _ptr(out["near_pos"]))
+        if rc != 0:
+            raise ValueError(f"oracle_verify rejected its arguments (code {rc})")
+        return out
+
+    def commit_kv(self, scratch: np.ndarray, pool: np.ndarray, block_table: np.ndarray,
+                  accept_count: np.ndarray, seq_lens: np.ndarray, gamma=None):
+        """Apply the commit to ``pool`` and ``seq_lens`` in place (numpy uint16/int32)."""
+        B, G1, L, two, H, D = scratch.shape
+        assert two == 2 and pool.dtype == np.uint16 and scratch.dtype == np.uint16
+        Lp, two2, NB, BS, Hp, Dp = pool.shape
+        assert (Lp, two2, Hp, Dp) == (L, 2, H, D)
+        assert pool.flags.c_contiguous and seq_lens.flags.c_contiguous
+        bt = np.ascontiguousarray(block_table, dtype=np.int32)
+        acc = np.ascontiguousarray(accept_count, dtype=np.int32)
+        gam = None if gamma is None else np.ascontiguousarray(gamma, dtype=np.int32)
+        assert seq_lens.dtype == np.int32
+        rc = self.lib.oracle_commit_kv(B, G1 - 1, L, H, D, BS, bt.shape[1], NB,
+                                    _ptr(np.ascontiguousarray(scratch)), _ptr(pool), _ptr(bt),
+                                    _ptr(acc), _ptr(gam), _ptr(seq_lens))
+        if rc != 0:
+            raise ValueError(f"oracle_commit_kv rejected its arguments (code {rc})")
+
+
+_default: Optional[Oracle] = None
+
+
+def default() -> Oracle:
+    """The oracle built from this directory's source (built on first use)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+            build()
+        _default = Oracle(LIB)
+    return _default
+
+
+def philox4x32_10(ctr, key):
+    return default().philox4x32_10(ctr, key)
+
+
+def row_distribution(row, temperature=1.0, top_k=0, top_p=1.0):
+    return default().row_distribution(row, temperature, top_k, top_p)
+
+
+def verify(*args, **kw):
+    return default().verify(*args, **kw)
+
+
+def commit_kv(*args, **kw):
+    return default().commit_kv(*args, **kw)

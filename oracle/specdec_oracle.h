@@ -1,0 +1,84 @@
+/* CPU oracle of the speculative-decoding verify-and-commit step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link,
+ * load or call this code: it exists so that tests, the smoke check and the CPU
+ * baseline of the benchmark can compare the HIP path against a plain,
+ * single-threaded, double-precision restatement of what the step computes.
+ * It shares no code with the HIP path.
+ *
+ * Layouts match the device layouts so the same host buffers feed both sides:
+ *   target  [B][G+1][V]  float32 or bfloat16 bit patterns (uint16)
+ *   draft   [B][G][V]    same type (unused in greedy mode, may be NULL)
+ *   tokens  [B][G] int32, gamma [B] int32 (NULL: every request uses G)
+ */
+#ifndef SPECDEC_ORACLE_H
+#define SPECDEC_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+    int32_t batch;        /* B */
+    int32_t gamma_max;    /* G */
+    int32_t vocab;        /* V */
+    int32_t is_bf16;      /* 1: logits are bfloat16 bit patterns, 0: float32 */
+    int32_t greedy;       /* 1: argmax-equality verification */
+    int32_t top_k;        /* 0: off */
+    double temperature;   /* > 0, sampling only */
+    double top_p;         /* 1.0: off */
+    uint64_t seed;        /* Philox key */
+    uint32_t round;       /* Philox counter word 2 */
+    int32_t pad_;
+} oracle_verify_args;
+
+/* Flag bits (per request), same meaning as on the device side. */
+#define ORACLE_FLAG_RESIDUAL_FALLBACK 0x2u  /* rejected but sum of [p-q]+ <= 0 */
+#define ORACLE_FLAG_NONFINITE         0x4u  /* NaN or +inf in a used row */
+#define ORACLE_FLAG_TOKEN_RANGE       0x8u  /* a draft token outside [0,V) */
+
+/* Verify selected requests.  req_ids[n] picks the requests (NULL: 0..B-1 and
+ * n must equal B); every output is indexed by the position in that list:
+ *   accept_count [n], out_tokens [n][G+1] (-1 padded), p_draft/q_draft [n][G]
+ *   (0 past gamma_i; untouched in greedy mode), residual_mass [n], flags [n],
+ *   near_pos [n]: smallest position whose output-determining decision lies
+ *   within 1e-6 of its threshold (accept test, inverse-CDF edge or top-p cut),
+ *   -1 if none.
+ * u_accept / u_sample [n][G+1] (may be NULL) replace the Philox uniforms.
+ * Returns 0, or a negative value on a malformed argument. */
+int oracle_verify(const oracle_verify_args* a, const void* target, const void* draft,
+                  const int32_t* draft_tokens, const int32_t* gamma,
+                  const int32_t* req_ids, int32_t n,
+                  const double* u_accept, const double* u_sample,
+                  int32_t* accept_count, int32_t* out_tokens,
+                  double* p_draft, double* q_draft, double* residual_mass,
+                  uint32_t* flags, int32_t* near_pos);
+
+/* Dense sampling distribution of one logits row after temperature, top-k and
+ * top-p.  near_cut (may be NULL) is set to 1 if the top-p cumulative lies
+ * within 1e-6 of top_p at the cut.  Returns the number of kept tokens. */
+int oracle_row_distribution(const void* row, int32_t is_bf16, int32_t vocab,
+                            double temperature, int32_t top_k, double top_p,
+                            double* prob, int32_t* near_cut);
+
+/* Philox4x32-10 block: out = philox(ctr, key). */
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
+
+/* Commit the verified K/V slots of every request into the paged pool.
+ *   scratch  [B][G+1][L][2][H][D] bf16 bits; slot j holds position t_i + j
+ *   pool     [L][2][num_blocks][block][H][D] bf16 bits
+ *   block_table [B][max_blocks], accept_count [B], gamma [B] (NULL: G)
+ *   seq_lens [B] in: t_i, out: t_i + m_i + 1
+ * Returns 0, or a negative value if a needed block-table entry is invalid. */
+int oracle_commit_kv(int32_t batch, int32_t gamma_max, int32_t layers, int32_t kv_heads,
+                     int32_t head_dim, int32_t block_size, int32_t max_blocks,
+                     int64_t num_blocks, const uint16_t* scratch, uint16_t* pool,
+                     const int32_t* block_table, const int32_t* accept_count,
+                     const int32_t* gamma, int32_t* seq_lens);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,70 @@
+"""The pins have teeth: a plausible mistake planted in a copy of the oracle
+source makes at least one of the named pins fail.
+
+Every mistake is planted in the oracle, on the CPU (a temporary copy of the C
+source, compiled with gcc); nothing here touches the HIP path.
+"""
+import os
+
+import pytest
+
+import oracle
+import pins
+
+# (name, source snippet, replacement, pins expected to catch it)
+MUTANTS = [
+    ("naive_resample_from_p", "r[v] = diff > 0.0 ? diff : 0.0;", "r[v] = pm[v];",
+     ["three_option_grid", "chisq_v8_g4"]),
+    ("non_strict_accept", "if (!(ua[i] < acc_p)) break;", "if (!(ua[i] <= acc_p)) break;",
+     ["strict_comparisons"]),
+    ("greedy_rows_shifted",
+     "g = row_argmax(row_ptr(target, a->is_bf16, (int64_t)b * (G + 1) + i, V), a->is_bf16, V);",
+     "g = row_argmax(row_ptr(target, a->is_bf16, (int64_t)b * (G + 1) + (i < gb ? i + 1 : i), V),"
+     " a->is_bf16, V);",
+     ["greedy_walkthrough", "greedy_matches_numpy"]),
+    ("sampling_rows_shifted",
+     "oracle_row_distribution(row_ptr(target, a->is_bf16, (int64_t)b * (G + 1) + i, V),",
+     "oracle_row_distribution(row_ptr(target, a->is_bf16, (int64_t)b * (G + 1)"
+     " + (i < gb ? i + 1 : i), V),",
+     ["chisq_v8_g4", "chisq_v16_g4"]),
+    ("temperature_dropped", "/ T", "/ 1.0", ["probabilities_logsumexp"]),
+    ("philox_multiplier", "0xD2511F53u", "0xD2511F55u", ["philox_kat"]),
+    ("philox_key_bump", "k1 += 0xBB67AE85u;", "k1 += 0xBB67AE86u;", ["philox_kat"]),
+    ("greedy_tie_highest_index", "if (z > best_z)", "if (z >= best_z)",
+     ["greedy_walkthrough", "greedy_matches_numpy"]),
+    ("residual_next_draft_row", "const double* qm = Q + (size_t)m * V;",
+     "const double* qm = Q + (size_t)(m + 1 < gb ? m + 1 : m) * V;",
+     ["chisq_v8_g4", "chisq_v16_g4"]),
+    ("bonus_from_draft",
+     "for (int64_t v = 0; v < V; ++v) { r[v] = pm[v]; R += r[v]; }\n"
+     "                if (residual_mass) residual_mass[k] = 0.0;",
+     "for (int64_t v = 0; v < V; ++v) { r[v] = Q[(size_t)(gb > 0 ? gb - 1 : 0) * V + v];"
+     " R += r[v]; }\n                if (residual_mass) residual_mass[k] = 0.0;",
+     ["expected_advance"]),
+    ("cdf_non_strict", "if (C > target_mass)", "if (C >= target_mass)",
+     ["strict_comparisons"]),
+    ("same_uniform_for_sampling", "*u_sample = (double)(w[1] >> 8)", "*u_sample = (double)(w[0] >> 8)",
+     ["chisq_v8_g4", "chisq_v16_g4", "chisq_v3_g1"]),
+    ("topk_drops_ties", "keep[v] = logit_at(row, is_bf16, v) >= tau;",
+     "keep[v] = logit_at(row, is_bf16, v) > tau;", ["truncation"]),
+    ("topp_cut_one_short", "if (cum >= top_p) { cut = j; break; }",
+     "if (cum >= top_p) { cut = j > 0 ? j - 1 : 0; break; }", ["truncation"]),
+    ("topp_not_renormalized", "if (keep[v]) S2 += exp(", "if (1) S2 += exp(", ["truncation"]),
+    ("commit_drops_last_accepted", "if (j <= m) {", "if (j < m) {", ["commit_numpy"]),
+    ("commit_length_t_plus_m", "seq_lens[b] = seq_lens[b] + accept_count[b] + 1;",
+     "seq_lens[b] = seq_lens[b] + accept_count[b];", ["commit_numpy"]),
+    ("residual_sign_flipped", "double diff = pm[v] - qm[v];", "double diff = qm[v] - pm[v];",
+     ["three_option_grid", "invariants"]),
+]
+
+
+@pytest.mark.parametrize("name,old,new,catchers", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(name, old, new, catchers, tmp_path):
+    src = open(oracle.SRC).read()
+    count = src.count(old)
+    assert count >= 1, f"snippet for {name} not found in the oracle source"
+    if name != "temperature_dropped":
+        assert count == 1, f"snippet for {name} is ambiguous ({count} matches)"
+    mutant = oracle.build_copy(src.replace(old, new), str(tmp_path / name))
+    caught = {c: pins.ALL_PINS[c](mutant) for c in catchers}
+    assert any(caught.values()), f"no pin caught the planted mistake {name}: {caught}"
