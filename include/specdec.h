@@ -1,0 +1,205 @@
+/* specdec.h -- verify-and-commit step of speculative decoding on one AMD
+ * Instinct MI355X (gfx950).  C ABI of libspecdec.so.
+ *
+ * One speculative round proposes gamma draft tokens, runs the target once over
+ * the pending token plus the drafts, then (this library) decides how many
+ * drafts to keep, draws the next token, and commits the surviving K/V entries:
+ *
+ *   specdec_verify     temperature (+ optional top-k / top-p) on target and
+ *                      draft rows, the min(1, p/q) acceptance test (or argmax
+ *                      equality in greedy mode), the longest contiguous
+ *                      accepted prefix, then the correction token from
+ *                      normalize(max(p - q, 0)) or the bonus token from the
+ *                      last target row.
+ *   specdec_commit_kv  copies the K/V of the kept slots into a paged cache,
+ *                      invalidates the rejected slots and sets the new length.
+ *
+ * Passages defining these operations (page title, section):
+ *   - "Speculative decoding tutorial: from distribution preservation and
+ *     KV-cache rollback to break-even": s.2 (four stages, contiguous prefix),
+ *     s.3-4 (greedy verification, logits alignment table), s.5.2-5.3
+ *     (rollback to t+m then t+m+1; bonus token), s.7.1-7.3 (acceptance
+ *     probability, residual distribution, left-to-right over positions),
+ *     s.13.2 (keep decisions on the GPU; no per-token host sync).
+ *   - AI-infra knowledge base page M013: s.03 (greedy walk-through), s.04
+ *     (p and q are the distributions after temperature and truncation), s.05
+ *     (three-option example), s.06 (commit or roll back the caches).
+ *   - "The apprentice's draft" (engineering half): s.2 Steps 2-4; s.5.4 (the
+ *     gamma+1 K/V entries of the verify pass, accepted ones written back).
+ *
+ * Conventions shared by every entry point
+ *   - All array arguments are DEVICE pointers to caller-owned memory; the
+ *     descriptor structs are HOST pointers read during the call only.  The
+ *     library allocates nothing and holds no state between calls.
+ *   - Work is enqueued on `stream` (NULL = the default stream) and the call
+ *     returns without synchronising; outputs are valid once the stream has
+ *     reached that point.  Nothing is copied back to the host.
+ *   - A non-OK status means that NOTHING was enqueued (argument errors are
+ *     found on the host before any launch), except SPECDEC_ERR_DEVICE, which
+ *     reports a launch failure from the HIP runtime.
+ *   - Data anomalies (a draft token outside [0,V), a non-finite logit, an
+ *     empty residual, an unusable block-table entry) never change the status;
+ *     they are reported per request in the optional `flags` output.
+ *   - Calls that share a workspace must be ordered (same stream, or
+ *     synchronised streams): concurrent calls on one workspace race.
+ */
+#ifndef SPECDEC_H
+#define SPECDEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPECDEC_ABI_VERSION 1
+
+typedef enum specdec_status {
+    SPECDEC_OK = 0,
+    SPECDEC_ERR_INVALID_ARGUMENT = 1,   /* bad descriptor, NULL or misaligned pointer */
+    SPECDEC_ERR_WORKSPACE_TOO_SMALL = 2,
+    SPECDEC_ERR_UNSUPPORTED = 3,        /* valid request this build does not implement */
+    SPECDEC_ERR_DEVICE = 4              /* the HIP runtime refused a launch */
+} specdec_status_t;
+
+typedef enum specdec_dtype { SPECDEC_F32 = 0, SPECDEC_BF16 = 1 } specdec_dtype_t;
+typedef enum specdec_mode { SPECDEC_SAMPLE = 0, SPECDEC_GREEDY = 1 } specdec_mode_t;
+
+/* Per-request flag bits (the `flags` outputs). */
+#define SPECDEC_FLAG_RESIDUAL_FALLBACK 0x2u  /* rejected, but sum max(p-q,0) <= 0: sampled p */
+#define SPECDEC_FLAG_NONFINITE         0x4u  /* NaN or +inf in a used logits row */
+#define SPECDEC_FLAG_TOKEN_RANGE       0x8u  /* a draft token outside [0,V): rejected */
+#define SPECDEC_FLAG_BAD_BLOCK         0x10u /* commit: window not committable, slot(s) skipped */
+#define SPECDEC_FLAG_BAD_GAMMA         0x20u /* verify: gamma_b outside [0,G], clamped into it */
+
+/* ------------------------------------------------------------------ verify */
+
+typedef struct specdec_verify_desc {
+    int32_t batch;        /* B >= 0 requests */
+    int32_t gamma_max;    /* G in [0, 63]: padded draft length */
+    int32_t vocab;        /* V >= 1 */
+    int32_t dtype;        /* specdec_dtype_t of both logits tensors */
+    int32_t mode;         /* specdec_mode_t */
+    int32_t top_k;        /* SAMPLE only: 0 = off, else keep logits >= k-th largest */
+    float temperature;    /* SAMPLE only: > 0 */
+    float top_p;          /* SAMPLE only: (0, 1]; 1 = off */
+    uint64_t seed;        /* Philox4x32-10 key (low word, high word) */
+    uint32_t round;       /* Philox counter word 2 (make it differ per round) */
+    uint32_t reserved;    /* must be 0 */
+} specdec_verify_desc_t;
+
+/* Bytes of device workspace specdec_verify needs for `desc` (0 on a bad
+ * descriptor).  The workspace holds per-chunk partial statistics and
+ * per-request arrival counters.  Its counter words must be zero before the
+ * first call that uses it (allocate it zero-filled, or run
+ * specdec_workspace_clear once); every completed call leaves them zero again,
+ * so one workspace serves any number of ordered calls.  Rounded to 256 B. */
+size_t specdec_verify_workspace_bytes(const specdec_verify_desc_t* desc);
+
+/* Verify one round for B requests.
+ *
+ * Inputs (device, row-major, 16-byte aligned for full speed):
+ *   target_logits [B][G+1][V] dtype: row i of request b is the target's
+ *       distribution that judges draft token i (row 0 is produced by the
+ *       pending token, i.e. the last committed token whose K/V is not yet in
+ *       the cache); row gamma_b yields the bonus token.
+ *   draft_logits  [B][G][V] dtype: row i is the draft distribution that
+ *       proposed draft token i.  Not read in GREEDY mode (may be NULL).
+ *   draft_tokens  [B][G] int32: the proposed tokens d_0..d_{gamma_b - 1}.
+ *   gamma         [B] int32 in [0, G], or NULL (every request uses G).  Rows
+ *       and tokens past gamma_b are never read.  A value outside [0, G] is
+ *       clamped into it and flagged (SPECDEC_FLAG_BAD_GAMMA).
+ * Outputs (device):
+ *   accept_count  [B] int32: m_b, the number of leading drafts kept.
+ *   out_tokens    [B][G+1] int32: d_0..d_{m-1}, then the correction (m <
+ *       gamma_b) or bonus (m = gamma_b) token at index m, then -1.
+ *   p_draft, q_draft [B][G] float, or NULL: p_i(d_i), q_i(d_i) after
+ *       temperature and truncation (0 past gamma_b).  Not written in GREEDY.
+ *   residual_mass [B] float, or NULL: sum_v max(p_m - q_m, 0) at the rejected
+ *       position, 0 when every draft was accepted.  Not written in GREEDY.
+ *   flags         [B] uint32, or NULL: SPECDEC_FLAG_* bits.
+ * Randomness: two uniforms per (request b, position i) from Philox4x32-10
+ *   with key = seed and counter = (i, b, round, 0); word 0 drives the accept
+ *   test (accept iff u < min(1, p/q)), word 1 the inverse-CDF draw at the
+ *   position where the round ends (token = min{v : cumsum(r)(v) > u R});
+ *   u = (word >> 8) * 2^-24.
+ * Greedy: draft i is kept iff it equals the argmax of target row i (raw
+ *   logits, lowest index on ties); the token at m is the argmax of row m.
+ * Errors: INVALID_ARGUMENT for a bad descriptor or a NULL required pointer;
+ *   WORKSPACE_TOO_SMALL if workspace_bytes < specdec_verify_workspace_bytes;
+ *   UNSUPPORTED for top_k != 0 or top_p < 1 (truncation is not built yet).
+ *   In each case nothing is enqueued. */
+specdec_status_t specdec_verify(const specdec_verify_desc_t* desc,
+                                const void* target_logits, const void* draft_logits,
+                                const int32_t* draft_tokens, const int32_t* gamma,
+                                int32_t* accept_count, int32_t* out_tokens,
+                                float* p_draft, float* q_draft, float* residual_mass,
+                                uint32_t* flags,
+                                void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/* ------------------------------------------------------------- commit K/V */
+
+typedef struct specdec_kv_desc {
+    int32_t batch;              /* B */
+    int32_t gamma_max;          /* G in [0, 63] */
+    int32_t num_layers;         /* L >= 1 */
+    int32_t num_kv_heads;       /* H >= 1 */
+    int32_t head_dim;           /* D >= 1 */
+    int32_t block_size;         /* tokens per physical block, >= 1 */
+    int32_t max_blocks_per_req; /* columns of the block table */
+    int32_t reserved;           /* must be 0 */
+    int64_t num_blocks;         /* physical blocks in the pool */
+} specdec_kv_desc_t;
+
+/* Bytes of device workspace specdec_commit_kv needs (per-request arrival
+ * counters; same zero-at-first-use rule as the verify workspace). */
+size_t specdec_commit_kv_workspace_bytes(const specdec_kv_desc_t* desc);
+
+/* Commit the verified slots of one round into a paged K/V cache.
+ *   scratch_kv  [B][G+1][L][2][H][D] bf16: the K (index 0) and V (index 1)
+ *       the verify forward produced; slot j of request b belongs to position
+ *       seq_lens[b] + j (slot 0 = the pending token).
+ *   kv_pool     [L][2][num_blocks][block_size][H][D] bf16, updated in place.
+ *   block_table [B][max_blocks_per_req] int32: physical block of each logical
+ *       block; entries covering positions t_b .. t_b + gamma_b must be valid.
+ *   accept_count [B] int32 (m_b, e.g. specdec_verify's output), gamma [B]
+ *       int32 or NULL (= G), both device-resident.
+ *   seq_lens    [B] int32, in place: in t_b (valid cache entries before the
+ *       round), out t_b + m_b + 1 (written after every slot of b was placed).
+ *   flags       [B] uint32 or NULL: SPECDEC_FLAG_BAD_BLOCK is OR-ed in when a
+ *       block-table entry needed by the window is outside [0, num_blocks) or
+ *       past the table (that slot is skipped), or when gamma_b, m_b or t_b is
+ *       out of range (nothing of that request is touched, its length kept).
+ * For j = 0..m_b the slot is copied to position t_b + j; for j = m_b+1 ..
+ * gamma_b the position is zero-filled (bf16 +0.0) so no rejected entry stays
+ * readable; positions outside [t_b, t_b + gamma_b] are not touched.
+ * Errors: INVALID_ARGUMENT for a bad descriptor or NULL pointer;
+ * WORKSPACE_TOO_SMALL; nothing is enqueued in either case. */
+specdec_status_t specdec_commit_kv(const specdec_kv_desc_t* desc,
+                                   const void* scratch_kv, void* kv_pool,
+                                   const int32_t* block_table, const int32_t* accept_count,
+                                   const int32_t* gamma, int32_t* seq_lens, uint32_t* flags,
+                                   void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
+/* ------------------------------------------------------------------ misc */
+
+/* Zero `bytes` of device memory at `workspace` with a fill kernel on
+ * `stream` (no hipMemset, so it may sit inside a captured graph).  bytes must
+ * be a multiple of 4 and workspace 4-byte aligned. */
+specdec_status_t specdec_workspace_clear(void* workspace, size_t bytes, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* specdec_status_string(specdec_status_t status);
+
+/* SPECDEC_ABI_VERSION of the loaded library. */
+int32_t specdec_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPECDEC_H */

@@ -1,0 +1,208 @@
+"""Speculative-decoding verify-and-commit on one MI355X (gfx950).
+
+Thin Python binding of ``libspecdec.so`` (C ABI declared in
+``include/specdec.h``).  The functions keep the C names and only marshal
+arguments: torch tensors become device pointers, the current torch stream
+becomes the HIP stream.  Every step of the computation runs in the HIP
+kernels; there is no CPU fallback, and the functions raise if the library is
+missing or refuses a call.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libspecdec.so")
+
+SPECDEC_OK = 0
+SPECDEC_ERR_INVALID_ARGUMENT = 1
+SPECDEC_ERR_WORKSPACE_TOO_SMALL = 2
+SPECDEC_ERR_UNSUPPORTED = 3
+SPECDEC_ERR_DEVICE = 4
+
+SPECDEC_F32, SPECDEC_BF16 = 0, 1
+SPECDEC_SAMPLE, SPECDEC_GREEDY = 0, 1
+
+FLAG_RESIDUAL_FALLBACK = 0x2
+FLAG_NONFINITE = 0x4
+FLAG_TOKEN_RANGE = 0x8
+FLAG_BAD_BLOCK = 0x10
+FLAG_BAD_GAMMA = 0x20
+
+# exported symbols of include/specdec.h
+EXPORTS = ("specdec_verify_workspace_bytes", "specdec_verify",
+           "specdec_commit_kv_workspace_bytes", "specdec_commit_kv",
+           "specdec_workspace_clear", "specdec_status_string", "specdec_abi_version")
+
+
+class VerifyDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("gamma_max", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("mode", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("temperature", ctypes.c_float), ("top_p", ctypes.c_float),
+                ("seed", ctypes.c_uint64), ("round", ctypes.c_uint32),
+                ("reserved", ctypes.c_uint32)]
+
+
+class KVDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("gamma_max", ctypes.c_int32),
+                ("num_layers", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("max_blocks_per_req", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int64)]
+
+
+class SpecdecError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)}")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libspecdec.so (build it with ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libspecdec.so is not built ({LIB_PATH}); run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, S = ctypes.c_void_p, ctypes.c_size_t
+        L.specdec_verify_workspace_bytes.argtypes = [ctypes.POINTER(VerifyDesc)]
+        L.specdec_verify_workspace_bytes.restype = S
+        L.specdec_verify.argtypes = [ctypes.POINTER(VerifyDesc)] + [P] * 11 + [S, P]
+        L.specdec_verify.restype = ctypes.c_int
+        L.specdec_commit_kv_workspace_bytes.argtypes = [ctypes.POINTER(KVDesc)]
+        L.specdec_commit_kv_workspace_bytes.restype = S
+        L.specdec_commit_kv.argtypes = [ctypes.POINTER(KVDesc)] + [P] * 8 + [S, P]
+        L.specdec_commit_kv.restype = ctypes.c_int
+        L.specdec_workspace_clear.argtypes = [P, S, P]
+        L.specdec_workspace_clear.restype = ctypes.c_int
+        L.specdec_status_string.argtypes = [ctypes.c_int]
+        L.specdec_status_string.restype = ctypes.c_char_p
+        L.specdec_abi_version.argtypes = []
+        L.specdec_abi_version.restype = ctypes.c_int32
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().specdec_status_string(int(status)).decode()
+
+
+def _ptr(x) -> Optional[int]:
+    """Device address of a tensor (or an int address); None stays NULL."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if not x.is_cuda:
+        raise ValueError("specdec arguments must be device tensors")
+    if not x.is_contiguous():
+        raise ValueError("specdec arguments must be contiguous")
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_verify_desc(batch, gamma_max, vocab, *, bf16=True, greedy=False, temperature=1.0,
+                     top_k=0, top_p=1.0, seed=0, round=0) -> VerifyDesc:
+    return VerifyDesc(int(batch), int(gamma_max), int(vocab),
+                      SPECDEC_BF16 if bf16 else SPECDEC_F32,
+                      SPECDEC_GREEDY if greedy else SPECDEC_SAMPLE, int(top_k),
+                      float(temperature), float(top_p), int(seed) & (2 ** 64 - 1),
+                      int(round) & 0xFFFFFFFF, 0)
+
+
+def make_kv_desc(batch, gamma_max, num_layers, num_kv_heads, head_dim, block_size,
+                 max_blocks_per_req, num_blocks) -> KVDesc:
+    return KVDesc(int(batch), int(gamma_max), int(num_layers), int(num_kv_heads),
+                  int(head_dim), int(block_size), int(max_blocks_per_req), 0, int(num_blocks))
+
+
+def specdec_verify_workspace_bytes(desc: VerifyDesc) -> int:
+    return int(lib().specdec_verify_workspace_bytes(ctypes.byref(desc)))
+
+
+def specdec_commit_kv_workspace_bytes(desc: KVDesc) -> int:
+    return int(lib().specdec_commit_kv_workspace_bytes(ctypes.byref(desc)))
+
+
+def specdec_verify(desc: VerifyDesc, target_logits, draft_logits, draft_tokens, gamma,
+                   accept_count, out_tokens, p_draft, q_draft, residual_mass, flags,
+                   workspace, workspace_bytes: Optional[int] = None, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = lib().specdec_verify(ctypes.byref(desc), _ptr(target_logits), _ptr(draft_logits),
+                              _ptr(draft_tokens), _ptr(gamma), _ptr(accept_count),
+                              _ptr(out_tokens), _ptr(p_draft), _ptr(q_draft),
+                              _ptr(residual_mass), _ptr(flags), _ptr(workspace),
+                              int(workspace_bytes), _stream(stream))
+    if st != SPECDEC_OK:
+        raise SpecdecError(st, "specdec_verify")
+
+
+def specdec_commit_kv(desc: KVDesc, scratch_kv, kv_pool, block_table, accept_count, gamma,
+                      seq_lens, flags, workspace, workspace_bytes: Optional[int] = None,
+                      stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = lib().specdec_commit_kv(ctypes.byref(desc), _ptr(scratch_kv), _ptr(kv_pool),
+                                 _ptr(block_table), _ptr(accept_count), _ptr(gamma),
+                                 _ptr(seq_lens), _ptr(flags), _ptr(workspace),
+                                 int(workspace_bytes), _stream(stream))
+    if st != SPECDEC_OK:
+        raise SpecdecError(st, "specdec_commit_kv")
+
+
+def specdec_workspace_clear(workspace, nbytes: Optional[int] = None, stream=None) -> None:
+    if nbytes is None:
+        nbytes = workspace.numel() * workspace.element_size()
+    st = lib().specdec_workspace_clear(_ptr(workspace), int(nbytes), _stream(stream))
+    if st != SPECDEC_OK:
+        raise SpecdecError(st, "specdec_workspace_clear")
+
+
+def specdec_abi_version() -> int:
+    return int(lib().specdec_abi_version())
+
+
+class Verifier:
+    """Owns the outputs and the zero-initialised workspace of one verify shape.
+
+    ``verifier(target, draft, draft_tokens, gamma)`` enqueues specdec_verify
+    on the current stream and returns the output tensors (still on device).
+    """
+
+    def __init__(self, desc: VerifyDesc, device="cuda"):
+        import torch
+        self.desc = desc
+        B, G = desc.batch, desc.gamma_max
+        nbytes = specdec_verify_workspace_bytes(desc)
+        if nbytes == 0:
+            raise SpecdecError(SPECDEC_ERR_INVALID_ARGUMENT, "specdec_verify_workspace_bytes")
+        self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        i32, f32 = torch.int32, torch.float32
+        self.accept_count = torch.empty(B, dtype=i32, device=device)
+        self.out_tokens = torch.empty(B, G + 1, dtype=i32, device=device)
+        self.p_draft = torch.empty(B, G, dtype=f32, device=device)
+        self.q_draft = torch.empty(B, G, dtype=f32, device=device)
+        self.residual_mass = torch.empty(B, dtype=f32, device=device)
+        self.flags = torch.empty(B, dtype=torch.int32, device=device)
+
+    def __call__(self, target, draft, draft_tokens, gamma=None, stream=None):
+        specdec_verify(self.desc, target, draft, draft_tokens, gamma, self.accept_count,
+                       self.out_tokens, self.p_draft, self.q_draft, self.residual_mass,
+                       self.flags, self.workspace, stream=stream)
+        return {"accept_count": self.accept_count, "out_tokens": self.out_tokens,
+                "p_draft": self.p_draft, "q_draft": self.q_draft,
+                "residual_mass": self.residual_mass, "flags": self.flags}

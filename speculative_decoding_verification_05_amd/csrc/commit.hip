@@ -1,0 +1,185 @@
+// specdec_commit_kv: the commit half of a speculative-decoding round.
+//
+// After verification keeps m drafts, the K/V of the pending token and of the
+// m accepted drafts become cache history and the rejected entries must not
+// stay readable; the cache length becomes t + m + 1 (AI-infra KB M013 s.06;
+// "Speculative decoding tutorial" s.5.2: trim to t+m, the replacement then
+// makes t+m+1; "The apprentice's draft" s.5.4: of the gamma+1 entries the
+// verify pass produced, the accepted ones are written into the cache, on a
+// paged (block-table) cache).
+//
+// One workgroup per (slot j, request b) moves that slot's L x 2 runs of
+// H x D bf16 with 16-byte vector loads and stores: the scratch side is one
+// contiguous span, the pool side one contiguous run per (layer, K|V) inside a
+// physical block.  Pure copy/zero-fill traffic, bound by HBM bandwidth.
+// The last workgroup of a request (arrival counter) writes the new length, so
+// no workgroup can read a length that was already advanced.
+#include "specdec.h"
+#include "specdec_device.h"
+
+#include <stdint.h>
+
+namespace specdec {
+namespace {
+
+struct CommitParams {
+    const uint16_t* scratch;   // [B][G+1][L][2][H][D]
+    uint16_t* pool;            // [L][2][NB][BS][H][D]
+    const int32_t* table;      // [B][maxb]
+    const int32_t* accept;
+    const int32_t* gamma;
+    int32_t* seq_lens;
+    uint32_t* flags;
+    uint32_t* cnt;             // [B]
+    int B, G, L, H, D, BS, maxb;
+    int64_t NB;
+    int hd;                    // H * D elements per run
+};
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void k_commit(CommitParams P) {
+    const int j = blockIdx.x, b = blockIdx.y;
+    const int g = P.gamma ? P.gamma[b] : P.G;
+    const int m = P.accept[b];
+    const int t = P.seq_lens[b];
+    bool bad = false;
+    if (g < 0 || g > P.G) {
+        bad = true;
+    } else if (j <= g) {
+        if (m < 0 || m > g || t < 0) {
+            bad = true;
+        } else {
+            const int64_t pos = static_cast<int64_t>(t) + j;
+            const int64_t lb = pos / P.BS;
+            const int off = static_cast<int>(pos % P.BS);
+            const int32_t phys = lb < P.maxb ? P.table[static_cast<size_t>(b) * P.maxb + lb] : -1;
+            if (phys < 0 || phys >= P.NB) {
+                bad = true;
+            } else {
+                const bool keep = j <= m;
+                const size_t runs = static_cast<size_t>(P.L) * 2;
+                const uint16_t* src = P.scratch + (static_cast<size_t>(b) * (P.G + 1) + j) * runs * P.hd;
+                if (VEC) {
+                    const int nv = P.hd / 8;  // 16-byte vectors per run
+                    const size_t total = runs * nv;
+                    for (size_t e = threadIdx.x; e < total; e += kThreads) {
+                        const size_t run = e / nv, w = e % nv;  // run = layer * 2 + (K|V)
+                        uint16_t* dst = P.pool + ((run * P.NB + phys) * P.BS + off) * P.hd + w * 8;
+                        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+                        if (keep) v = *reinterpret_cast<const uint4*>(src + run * P.hd + w * 8);
+                        *reinterpret_cast<uint4*>(dst) = v;
+                    }
+                } else {
+                    const size_t total = runs * P.hd;
+                    for (size_t e = threadIdx.x; e < total; e += kThreads) {
+                        const size_t run = e / P.hd, w = e % P.hd;
+                        uint16_t* dst = P.pool + ((run * P.NB + phys) * P.BS + off) * P.hd + w;
+                        *dst = keep ? src[run * P.hd + w] : static_cast<uint16_t>(0);
+                    }
+                }
+            }
+        }
+    }
+    if (bad && threadIdx.x == 0 && P.flags) atomicOr(P.flags + b, SPECDEC_FLAG_BAD_BLOCK);
+    __shared__ int s_last;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __threadfence();
+        const uint32_t old = atomicAdd(P.cnt + b, 1u);
+        s_last = (old == static_cast<uint32_t>(P.G));  // G+1 slots per request
+        if (s_last) P.cnt[b] = 0;
+    }
+    __syncthreads();
+    if (s_last && threadIdx.x == 0 && g >= 0 && g <= P.G && m >= 0 && m <= g && t >= 0)
+        P.seq_lens[b] = t + m + 1;
+}
+
+__global__ void k_fill_zero(uint32_t* p, size_t n) {
+    for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
+         i += static_cast<size_t>(gridDim.x) * blockDim.x)
+        p[i] = 0u;
+}
+
+bool valid_kv(const specdec_kv_desc_t* d) {
+    if (!d) return false;
+    if (d->batch < 0 || d->batch > 65535 || d->gamma_max < 0 || d->gamma_max > 63) return false;
+    if (d->num_layers < 1 || d->num_kv_heads < 1 || d->head_dim < 1 || d->block_size < 1)
+        return false;
+    if (d->max_blocks_per_req < 1 || d->num_blocks < 1 || d->reserved != 0) return false;
+    if (static_cast<int64_t>(d->num_kv_heads) * d->head_dim > (1 << 24)) return false;
+    return true;
+}
+
+}  // namespace
+}  // namespace specdec
+
+using namespace specdec;
+
+extern "C" size_t specdec_commit_kv_workspace_bytes(const specdec_kv_desc_t* d) {
+    if (!valid_kv(d)) return 0;
+    return (static_cast<size_t>(d->batch) * 4 + 255) & ~static_cast<size_t>(255);
+}
+
+extern "C" specdec_status_t specdec_commit_kv(const specdec_kv_desc_t* d, const void* scratch_kv,
+                                              void* kv_pool, const int32_t* block_table,
+                                              const int32_t* accept_count, const int32_t* gamma,
+                                              int32_t* seq_lens, uint32_t* flags, void* workspace,
+                                              size_t workspace_bytes, hipStream_t stream) {
+    if (!valid_kv(d)) return SPECDEC_ERR_INVALID_ARGUMENT;
+    if (!scratch_kv || !kv_pool || !block_table || !accept_count || !seq_lens || !workspace)
+        return SPECDEC_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < specdec_commit_kv_workspace_bytes(d)) return SPECDEC_ERR_WORKSPACE_TOO_SMALL;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 3u) != 0) return SPECDEC_ERR_INVALID_ARGUMENT;
+    if (d->batch == 0) return SPECDEC_OK;
+    CommitParams P{};
+    P.scratch = static_cast<const uint16_t*>(scratch_kv);
+    P.pool = static_cast<uint16_t*>(kv_pool);
+    P.table = block_table;
+    P.accept = accept_count;
+    P.gamma = gamma;
+    P.seq_lens = seq_lens;
+    P.flags = flags;
+    P.cnt = static_cast<uint32_t*>(workspace);
+    P.B = d->batch;
+    P.G = d->gamma_max;
+    P.L = d->num_layers;
+    P.H = d->num_kv_heads;
+    P.D = d->head_dim;
+    P.BS = d->block_size;
+    P.maxb = d->max_blocks_per_req;
+    P.NB = d->num_blocks;
+    P.hd = d->num_kv_heads * d->head_dim;
+    const bool vec = (P.hd % 8 == 0) && (reinterpret_cast<uintptr_t>(scratch_kv) & 15u) == 0 &&
+                     (reinterpret_cast<uintptr_t>(kv_pool) & 15u) == 0;
+    const dim3 grid(d->gamma_max + 1, d->batch);
+    if (vec)
+        hipLaunchKernelGGL(k_commit<true>, grid, dim3(kThreads), 0, stream, P);
+    else
+        hipLaunchKernelGGL(k_commit<false>, grid, dim3(kThreads), 0, stream, P);
+    return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_DEVICE;
+}
+
+extern "C" specdec_status_t specdec_workspace_clear(void* workspace, size_t bytes, hipStream_t stream) {
+    if (!workspace || (bytes & 3u) != 0 || (reinterpret_cast<uintptr_t>(workspace) & 3u) != 0)
+        return SPECDEC_ERR_INVALID_ARGUMENT;
+    if (bytes == 0) return SPECDEC_OK;
+    const size_t n = bytes / 4;
+    const size_t blocks = (n + kThreads - 1) / kThreads;
+    const unsigned grid = static_cast<unsigned>(blocks < 4096 ? blocks : 4096);
+    hipLaunchKernelGGL(k_fill_zero, dim3(grid), dim3(kThreads), 0, stream,
+                       static_cast<uint32_t*>(workspace), n);
+    return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_DEVICE;
+}
+
+extern "C" const char* specdec_status_string(specdec_status_t s) {
+    switch (s) {
+        case SPECDEC_OK: return "SPECDEC_OK";
+        case SPECDEC_ERR_INVALID_ARGUMENT: return "SPECDEC_ERR_INVALID_ARGUMENT: bad descriptor or pointer";
+        case SPECDEC_ERR_WORKSPACE_TOO_SMALL: return "SPECDEC_ERR_WORKSPACE_TOO_SMALL";
+        case SPECDEC_ERR_UNSUPPORTED: return "SPECDEC_ERR_UNSUPPORTED: request not implemented";
+        case SPECDEC_ERR_DEVICE: return "SPECDEC_ERR_DEVICE: HIP launch failed";
+    }
+    return "unknown specdec status";
+}
+
+extern "C" int32_t specdec_abi_version(void) { return SPECDEC_ABI_VERSION; }

@@ -1,0 +1,174 @@
+// Device helpers of the verify-and-commit kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace specdec {
+
+constexpr int kThreads = 256;  // 4 waves of 64 lanes per workgroup
+constexpr int kWave = 64;
+constexpr int kWaves = kThreads / kWave;
+
+__device__ __forceinline__ float neg_inf() { return __uint_as_float(0xff800000u); }
+__device__ __forceinline__ float pos_inf() { return __uint_as_float(0x7f800000u); }
+
+// ---------------------------------------------------------------- Philox
+// Philox4x32-10 of Salmon, Moraes, Dror and Shaw (SC'11): ten rounds, each
+// two 32x32->64-bit products with the published multipliers; the key is
+// bumped by the published Weyl increments before every round but the first.
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
+        const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
+        c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    }
+    return c;
+}
+
+// A uniform in [0, 1) from the 24 high bits of a word (exact in fp32).
+__device__ __forceinline__ float uniform24(uint32_t w) {
+    return (float)(w >> 8) * 5.9604644775390625e-08f;  // 2^-24
+}
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <bool BF16>
+__device__ __forceinline__ float load_logit(const void* row, int64_t v) {
+    if constexpr (BF16) {
+        const uint16_t h = static_cast<const uint16_t*>(row)[v];
+        return __uint_as_float(static_cast<uint32_t>(h) << 16);
+    } else {
+        return static_cast<const float*>(row)[v];
+    }
+}
+
+// Values of one 16-byte vector: 8 bf16 or 4 fp32 logits.
+template <bool BF16>
+struct Vec {
+    static constexpr int N = BF16 ? 8 : 4;
+    float x[N];
+};
+
+template <bool BF16>
+__device__ __forceinline__ Vec<BF16> widen(uint4 w) {
+    Vec<BF16> r;
+    if constexpr (BF16) {
+        r.x[0] = bf16_lo(w.x); r.x[1] = bf16_hi(w.x);
+        r.x[2] = bf16_lo(w.y); r.x[3] = bf16_hi(w.y);
+        r.x[4] = bf16_lo(w.z); r.x[5] = bf16_hi(w.z);
+        r.x[6] = bf16_lo(w.w); r.x[7] = bf16_hi(w.w);
+    } else {
+        r.x[0] = __uint_as_float(w.x); r.x[1] = __uint_as_float(w.y);
+        r.x[2] = __uint_as_float(w.z); r.x[3] = __uint_as_float(w.w);
+    }
+    return r;
+}
+
+// One 16-byte vector of a row (no bounds handling: the caller guarantees it).
+template <bool BF16>
+__device__ __forceinline__ uint4 load16(const void* row, int e) {
+    return *reinterpret_cast<const uint4*>(static_cast<const char*>(row) +
+                                           static_cast<size_t>(e) * (BF16 ? 2 : 4));
+}
+
+// Elements [e, e+N) of a row clipped to [.., hi), `fill` past hi.  Loads are
+// never skipped: the address is clamped into the row and the value replaced,
+// so a lane issues all its loads without branching and they stay in flight
+// together.  VEC: the row is 16-byte aligned and hi is a multiple of N, so a
+// 16-byte vector lies wholly inside [.., hi) or wholly past it (hi >= N).
+template <bool BF16, bool VEC>
+__device__ __forceinline__ Vec<BF16> load_vec(const void* row, int e, int hi, float fill) {
+    constexpr int N = Vec<BF16>::N;
+    Vec<BF16> r;
+    if constexpr (VEC) {
+        const int ec = min(e, hi - N);
+        const uint4 w = *reinterpret_cast<const uint4*>(
+            static_cast<const char*>(row) + static_cast<size_t>(ec) * (BF16 ? 2 : 4));
+        r = widen<BF16>(w);
+        if (e >= hi) {
+#pragma unroll
+            for (int k = 0; k < N; ++k) r.x[k] = fill;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+            const float x = load_logit<BF16>(row, min(e + k, hi - 1));
+            r.x[k] = (e + k < hi) ? x : fill;
+        }
+    }
+    return r;
+}
+
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v |= __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// Online-softmax pair (running maximum of the raw logits, sum of
+// 2^((x - max) * c)); combining rescales the sum of the smaller maximum.
+struct MaxSum {
+    float m;
+    float s;
+};
+
+__device__ __forceinline__ MaxSum combine(MaxSum a, MaxSum b, float c) {
+    const float m = fmaxf(a.m, b.m);
+    if (m == neg_inf()) return {m, 0.0f};
+    const float sa = a.m == neg_inf() ? 0.0f : a.s * exp2f((a.m - m) * c);
+    const float sb = b.m == neg_inf() ? 0.0f : b.s * exp2f((b.m - m) * c);
+    return {m, sa + sb};
+}
+
+__device__ __forceinline__ MaxSum wave_combine(MaxSum v, float c) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        MaxSum w{__shfl_xor(v.m, o, kWave), __shfl_xor(v.s, o, kWave)};
+        v = combine(v, w, c);
+    }
+    return v;
+}
+
+// (value, index) of a maximum: larger value wins, the lower index on ties.
+struct ArgMax {
+    float v;
+    int i;
+};
+
+__device__ __forceinline__ ArgMax better(ArgMax a, ArgMax b) {
+    if (a.v > b.v) return a;
+    if (b.v > a.v) return b;
+    return a.i <= b.i ? a : b;
+}
+
+__device__ __forceinline__ ArgMax wave_argmax(ArgMax v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        ArgMax w{__shfl_xor(v.v, o, kWave), __shfl_xor(v.i, o, kWave)};
+        v = better(v, w);
+    }
+    return v;
+}
+
+}  // namespace specdec
