@@ -1,0 +1,276 @@
+#!/usr/bin/env python3
+"""Throughput of the speculative-decoding verify step on one MI355X.
+
+Default workload: B=64 requests, gamma=4 drafts, V=128256, bf16 logits,
+T=0.8 sampling with a bonus token on full acceptance (the headline case).
+A step is one specdec_verify call over one batch: the statistics pass over
+every used logits row, the acceptance tests and ballot, and the correction /
+bonus draw.  Inputs are synthetic (seeded generator), resident in HBM before
+timing, and rotate over several independent input sets whose total exceeds the
+256 MB Infinity Cache, so every step reads its logits from HBM.
+
+Timing: W warmup steps, then exactly K steps replayed from a HIP graph,
+bracketed by torch.cuda.synchronize(); value = verified positions / second.
+The roofline entry is the statistics kernel (the dominant one): its
+algorithmic bytes per launch (every used logits row read once, plus draft
+tokens and outputs) over its average duration, timed live with start/stop
+events that bracket the kernel itself (specdec_verify_profiled).
+cpu_baseline: the CPU oracle (single-threaded C, double precision) run on the
+same input set for a bounded time.
+
+Other workloads (--workload) print the same JSON line for that recipe; the
+ones with a paged KV cache time verify + commit (seq_lens restored from a
+copy before every commit so that each step commits the same window).
+"""
+from __future__ import annotations
+
+import argparse
+import dataclasses
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E
+METRIC = "verified positions/sec + achieved HBM GB/s (% of peak), B=64 γ=4 V=128256"
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default=None, help="generator workload name")
+    ap.add_argument("--sets", type=int, default=0, help="rotating input sets (0: auto)")
+    ap.add_argument("--profile-steps", type=int, default=200)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time eager launches, no graph")
+    return ap.parse_args()
+
+
+def main() -> int:
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        log("bench.py measures the verify-and-commit step on one GPU; there is no multi-GPU "
+            "path in this build (requests would shard across GPUs with no exchange). "
+            "Run it with --gpus 1.")
+        return 2
+
+    import torch
+    import speculative_decoding_verification_05_amd as sd
+    from speculative_decoding_verification_05_amd import synth
+
+    dev = torch.device("cuda:0")
+    sd.lib()
+    wl0 = synth.WORKLOADS[args.workload or synth.HEADLINE]
+    greedy = wl0.mode == "greedy"
+    bf16 = wl0.dtype == "bf16"
+    per_set = synth.logits_bytes(wl0)
+    sets = args.sets or max(1, min(8, int(np.ceil(2 * 256e6 / per_set)) + (1 if per_set < 512e6 else 0)))
+    log(f"workload {wl0.name}: {per_set / 1e6:.2f} MB of logits per set, {sets} rotating sets")
+
+    # ---- inputs, resident in HBM
+    host, dev_in = [], []
+    for k in range(sets):
+        wl = dataclasses.replace(wl0, data_seed=wl0.data_seed + 100 * k)
+        x = synth.make_verify_inputs(wl)
+        host.append(x)
+        d = {"target": torch.from_numpy(x["target"].view(np.int16) if bf16 else x["target"]).to(dev),
+             "draft": None if greedy else torch.from_numpy(
+                 x["draft"].view(np.int16) if bf16 else x["draft"]).to(dev),
+             "tokens": torch.from_numpy(x["draft_tokens"]).to(dev),
+             "gamma": torch.from_numpy(x["gamma"]).to(dev)}
+        dev_in.append(d)
+        log(f"  input set {k} uploaded")
+    kv = None
+    if wl0.kv is not None:
+        kvin = synth.make_kv_inputs(wl0)
+        K = wl0.kv
+        kdesc = sd.make_kv_desc(wl0.batch, wl0.gamma_max, K.layers, K.kv_heads, K.head_dim,
+                                K.block_size, kvin.block_table.shape[1], kvin.num_blocks)
+        kv = {"desc": kdesc, "in": kvin,
+              "scratch": torch.from_numpy(kvin.scratch.view(np.int16)).to(dev),
+              "pool": torch.from_numpy(kvin.pool.view(np.int16)).to(dev),
+              "table": torch.from_numpy(kvin.block_table).to(dev),
+              "seq0": torch.from_numpy(kvin.seq_lens).to(dev),
+              "seq": torch.from_numpy(kvin.seq_lens.copy()).to(dev),
+              "ws": torch.zeros(sd.specdec_commit_kv_workspace_bytes(kdesc), dtype=torch.uint8,
+                                device=dev)}
+        log(f"  paged KV pool {kvin.pool.nbytes / 1e6:.1f} MB uploaded")
+
+    desc = sd.make_verify_desc(wl0.batch, wl0.gamma_max, wl0.vocab, bf16=bf16, greedy=greedy,
+                               temperature=wl0.temperature, top_k=wl0.top_k, top_p=wl0.top_p,
+                               seed=wl0.verify_seed)
+    ver = sd.Verifier(desc, dev)
+
+    def step(k: int) -> None:
+        d = dev_in[k]
+        ver(d["target"], d["draft"], d["tokens"], d["gamma"])
+        if kv is not None:
+            kv["seq"].copy_(kv["seq0"])
+            sd.specdec_commit_kv(kv["desc"], kv["scratch"], kv["pool"], kv["table"],
+                                 ver.accept_count, d["gamma"], kv["seq"], None, kv["ws"])
+
+    # ---- eager reference outputs, then the graph of one pass over the sets
+    eager = []
+    names = ("accept_count", "out_tokens", "p_draft", "q_draft", "residual_mass", "flags")
+    for k in range(sets):
+        step(k)
+        torch.cuda.synchronize()
+        eager.append({n: getattr(ver, n).clone() for n in names})
+    torch.cuda.synchronize()
+
+    graph = None
+    if not args.eager:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step(0)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for k in range(sets):
+                step(k)
+        # every replay must reproduce the eager outputs of the last set
+        for _ in range(3):
+            graph.replay()
+            torch.cuda.synchronize()
+            for n in ("accept_count", "out_tokens"):
+                if not torch.equal(getattr(ver, n), eager[-1][n]):
+                    log(f"graph replay differs from eager launches in {n}; timing eager launches")
+                    graph = None
+                    break
+            if graph is None:
+                break
+
+    reps = max(1, args.steps // sets)
+    steps = reps * sets
+    wreps = max(1, args.warmup // sets)
+
+    def run(n_reps: int) -> None:
+        for _ in range(n_reps):
+            if graph is not None:
+                graph.replay()
+            else:
+                for k in range(sets):
+                    step(k)
+
+    run(wreps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(reps)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    sec_per_step = (t1 - t0) / steps
+
+    gam_sets = [h["gamma"] for h in host]
+    positions = float(np.mean([g.sum() for g in gam_sets]))
+    value = positions / sec_per_step
+    acc = [e["accept_count"].cpu().numpy() for e in eager]
+    committed = float(np.mean([(a + 1).sum() for a in acc]))
+
+    # ---- live per-kernel timing with events around the kernels themselves
+    n_prof = max(sets, (args.profile_steps // sets) * sets)
+    ev = sd.HipEvents(4 * n_prof)
+    for j in range(n_prof):
+        d = dev_in[j % sets]
+        h = ev.handles[4 * j:4 * j + 4]
+        e = h
+        sd.specdec_verify_profiled(desc, d["target"], d["draft"], d["tokens"], d["gamma"],
+                                   ver.accept_count, ver.out_tokens, ver.p_draft, ver.q_draft,
+                                   ver.residual_mass, ver.flags, ver.workspace, e)
+    torch.cuda.synchronize()
+    k1 = np.array([ev.elapsed_ms(4 * j, 4 * j + 1) for j in range(n_prof)]) * 1e-3  # seconds
+    k2 = np.array([ev.elapsed_ms(4 * j + 2, 4 * j + 3) for j in range(n_prof)]) * 1e-3
+    ev.close()
+    k1_avg = float(k1.mean())
+
+    # algorithmic bytes of one statistics launch: used rows read once, draft
+    # tokens read, per-request outputs written
+    B, G = wl0.batch, wl0.gamma_max
+    out_bytes = B * 4 + B * (G + 1) * 4 + (0 if greedy else B * G * 8 + B * 4) + B * 4
+    alg_k1 = float(np.mean([synth.logits_bytes(wl0, g) for g in gam_sets])) + B * G * 4 + out_bytes
+    achieved = alg_k1 / k1_avg / 1e9
+    log(f"step {sec_per_step * 1e6:.2f} us ({'graph' if graph is not None else 'eager'}); "
+        f"stats kernel avg {k1_avg * 1e6:.2f} us (p10 {np.percentile(k1, 10) * 1e6:.2f}, "
+        f"p90 {np.percentile(k1, 90) * 1e6:.2f}); decision kernel avg {k2.mean() * 1e6:.2f} us")
+    log(f"stats kernel {achieved:.1f} GB/s = {100 * achieved / HBM_PEAK_GBPS:.1f}% of "
+        f"{HBM_PEAK_GBPS:.0f} GB/s; whole step {alg_k1 / sec_per_step / 1e9:.1f} GB/s")
+    log(f"mean accepted {np.mean([a.mean() for a in acc]):.3f} of {G}; histogram of m: "
+        f"{np.bincount(np.concatenate(acc), minlength=G + 1).tolist()}; "
+        f"committed tokens/s {committed / sec_per_step:.3e}")
+
+    # ---- CPU baseline: the oracle on the host copy of input set 0
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        x = host[0]
+        ref = None
+        reps_c, t_c = 0, 0.0
+        n_req = B
+        # bounded sample: whole batches while under the time budget, else fewer requests
+        t_s = time.perf_counter()
+        while True:
+            r = oracle.verify(x["target"], None if greedy else x["draft"], x["draft_tokens"],
+                              x["gamma"], greedy=greedy, temperature=wl0.temperature,
+                              top_k=wl0.top_k, top_p=wl0.top_p, seed=wl0.verify_seed,
+                              requests=np.arange(n_req))
+            ref = ref or r
+            reps_c += 1
+            t_c = time.perf_counter() - t_s
+            if t_c >= args.cpu_seconds or reps_c >= 50:
+                break
+        cpu_pos = reps_c * float(x["gamma"][:n_req].sum()) / t_c
+        m_ok = np.array_equal(ref["accept_count"][ref["near_pos"] < 0],
+                              eager[0]["accept_count"].cpu().numpy()[ref["near_pos"] < 0])
+        log(f"oracle: {reps_c} x {n_req} requests in {t_c:.2f} s on 1 core; GPU accept counts "
+            f"{'match' if m_ok else 'DIFFER FROM'} the oracle's on set 0")
+        cpu = {"value": cpu_pos, "unit": "positions/s", "cores": 1, "kind": "oracle",
+               "sample": f"{reps_c} pass(es) over all {n_req} requests of input set 0 "
+                         f"({t_c:.1f} s, single-threaded C, double precision)"}
+
+    res = {
+        "metric": METRIC if wl0.name == synth.HEADLINE else f"verified positions/sec ({wl0.name})",
+        "value": value,
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": wreps * sets,
+        "ms_per_step": sec_per_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl0.name, "batch": B, "gamma_max": G, "vocab": wl0.vocab,
+                   "logits": wl0.dtype, "mode": wl0.mode, "temperature": wl0.temperature,
+                   "top_k": wl0.top_k, "top_p": wl0.top_p, "kv_commit": wl0.kv is not None,
+                   "rotating_input_sets": sets,
+                   "launch": "hipgraph" if graph is not None else "eager",
+                   "committed_tokens_per_s": committed / sec_per_step,
+                   "step_GBps": alg_k1 / sec_per_step / 1e9},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "k_stats_greedy" if greedy else "k_stats_sample",
+                     "kernel_avg_us": k1_avg * 1e6, "bytes_per_launch": alg_k1},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -80,7 +80,7 @@ typedef enum specdec_mode { SPECDEC_SAMPLE = 0, SPECDEC_GREEDY = 1 } specdec_mod
 typedef struct specdec_verify_desc {
     int32_t batch;        /* B >= 0 requests */
     int32_t gamma_max;    /* G in [0, 63]: padded draft length */
-    int32_t vocab;        /* V >= 1 */
+    int32_t vocab;        /* V >= 1; at most 4194304 (bf16) / 2097152 (fp32) */
     int32_t dtype;        /* specdec_dtype_t of both logits tensors */
     int32_t mode;         /* specdec_mode_t */
     int32_t top_k;        /* SAMPLE only: 0 = off, else keep logits >= k-th largest */
@@ -140,6 +140,23 @@ specdec_status_t specdec_verify(const specdec_verify_desc_t* desc,
                                 uint32_t* flags,
                                 void* workspace, size_t workspace_bytes,
                                 hipStream_t stream);
+
+/* specdec_verify with per-pass timing for profilers and benchmarks.
+ * stage_events: NULL, or a host array of 4 hipEvent_t created by the caller
+ * (any entry may be NULL): [0]/[1] are recorded at the start/end of the
+ * statistics pass kernel (the one full read of the logits), [2]/[3] at the
+ * start/end of the decision kernel (acceptance tests and, when sampling, the
+ * correction/bonus draw).  The events bracket the kernels' execution
+ * (hipExtLaunchKernel), not the enqueue.
+ * Everything else, including every error, is as for specdec_verify. */
+specdec_status_t specdec_verify_profiled(const specdec_verify_desc_t* desc,
+                                         const void* target_logits, const void* draft_logits,
+                                         const int32_t* draft_tokens, const int32_t* gamma,
+                                         int32_t* accept_count, int32_t* out_tokens,
+                                         float* p_draft, float* q_draft, float* residual_mass,
+                                         uint32_t* flags,
+                                         void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream, hipEvent_t* stage_events);
 
 /* ------------------------------------------------------------- commit K/V */
 

@@ -31,7 +31,7 @@ FLAG_BAD_BLOCK = 0x10
 FLAG_BAD_GAMMA = 0x20
 
 # exported symbols of include/specdec.h
-EXPORTS = ("specdec_verify_workspace_bytes", "specdec_verify",
+EXPORTS = ("specdec_verify_workspace_bytes", "specdec_verify", "specdec_verify_profiled",
            "specdec_commit_kv_workspace_bytes", "specdec_commit_kv",
            "specdec_workspace_clear", "specdec_status_string", "specdec_abi_version")
 
@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.specdec_verify_workspace_bytes.restype = S
         L.specdec_verify.argtypes = [ctypes.POINTER(VerifyDesc)] + [P] * 11 + [S, P]
         L.specdec_verify.restype = ctypes.c_int
+        L.specdec_verify_profiled.argtypes = [ctypes.POINTER(VerifyDesc)] + [P] * 11 + [S, P, P]
+        L.specdec_verify_profiled.restype = ctypes.c_int
         L.specdec_commit_kv_workspace_bytes.argtypes = [ctypes.POINTER(KVDesc)]
         L.specdec_commit_kv_workspace_bytes.restype = S
         L.specdec_commit_kv.argtypes = [ctypes.POINTER(KVDesc)] + [P] * 8 + [S, P]
@@ -151,6 +153,23 @@ def specdec_verify(desc: VerifyDesc, target_logits, draft_logits, draft_tokens, 
         raise SpecdecError(st, "specdec_verify")
 
 
+def specdec_verify_profiled(desc: VerifyDesc, target_logits, draft_logits, draft_tokens, gamma,
+                            accept_count, out_tokens, p_draft, q_draft, residual_mass, flags,
+                            workspace, stage_events, workspace_bytes: Optional[int] = None,
+                            stream=None) -> None:
+    """stage_events: four raw hipEvent_t handles (ints; None entries allowed)."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    handles = (ctypes.c_void_p * 4)(*[None if e is None else int(e) for e in stage_events])
+    st = lib().specdec_verify_profiled(ctypes.byref(desc), _ptr(target_logits), _ptr(draft_logits),
+                                       _ptr(draft_tokens), _ptr(gamma), _ptr(accept_count),
+                                       _ptr(out_tokens), _ptr(p_draft), _ptr(q_draft),
+                                       _ptr(residual_mass), _ptr(flags), _ptr(workspace),
+                                       int(workspace_bytes), _stream(stream), handles)
+    if st != SPECDEC_OK:
+        raise SpecdecError(st, "specdec_verify_profiled")
+
+
 def specdec_commit_kv(desc: KVDesc, scratch_kv, kv_pool, block_table, accept_count, gamma,
                       seq_lens, flags, workspace, workspace_bytes: Optional[int] = None,
                       stream=None) -> None:
@@ -174,6 +193,34 @@ def specdec_workspace_clear(workspace, nbytes: Optional[int] = None, stream=None
 
 def specdec_abi_version() -> int:
     return int(lib().specdec_abi_version())
+
+
+class HipEvents:
+    """Raw timing events of the HIP runtime (for specdec_verify_profiled)."""
+
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.handles = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.handles.append(h.value)
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.handles[a], self.handles[b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def close(self) -> None:
+        for h in self.handles:
+            self.hip.hipEventDestroy(h)
+        self.handles = []
 
 
 class Verifier:

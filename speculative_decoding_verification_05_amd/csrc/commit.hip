@@ -81,13 +81,15 @@ __global__ __launch_bounds__(kThreads) void k_commit(CommitParams P) {
         }
     }
     if (bad && threadIdx.x == 0 && P.flags) atomicOr(P.flags + b, SPECDEC_FLAG_BAD_BLOCK);
+    // Every lane read t before this point (its copies used it), so once all
+    // G+1 workgroups of the request have arrived nobody reads the old length
+    // any more: no fence is needed, only the device-scope counter.
     __shared__ int s_last;
     __syncthreads();
     if (threadIdx.x == 0) {
-        __threadfence();
         const uint32_t old = atomicAdd(P.cnt + b, 1u);
         s_last = (old == static_cast<uint32_t>(P.G));  // G+1 slots per request
-        if (s_last) P.cnt[b] = 0;
+        if (s_last) atomicExch(P.cnt + b, 0u);
     }
     __syncthreads();
     if (s_last && threadIdx.x == 0 && g >= 0 && g <= P.G && m >= 0 && m <= g && t >= 0)

@@ -79,6 +79,17 @@ __device__ __forceinline__ uint4 load16(const void* row, int e) {
                                            static_cast<size_t>(e) * (BF16 ? 2 : 4));
 }
 
+// The same with the nontemporal (streaming) hint: for data read exactly once,
+// it keeps the read stream from displacing useful lines and measurably raises
+// the achieved HBM read bandwidth on gfx950.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+template <bool BF16>
+__device__ __forceinline__ uint4 load16_stream(const void* row, int e) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+        static_cast<const char*>(row) + static_cast<size_t>(e) * (BF16 ? 2 : 4)));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Elements [e, e+N) of a row clipped to [.., hi), `fill` past hi.  Loads are
 // never skipped: the address is clamped into the row and the value replaced,
 // so a lane issues all its loads without branching and they stay in flight

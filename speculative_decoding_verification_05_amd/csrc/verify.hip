@@ -13,35 +13,39 @@
 //     the argmax at the first mismatch (tutorial s.3-4; KB M013 s.03).
 //
 // Kernels (all HBM-bandwidth bound, no matrix cores: nothing is a contraction):
-//   k_stats_sample  one pass over every used logits row, split in chunks of
-//                   32 KB.  Each workgroup streams its chunk with 16-byte loads,
-//                   four in flight per lane, and reduces it to an online
-//                   (max, sum 2^((z-max)c)) pair; the chunk that holds the
-//                   drafted token also records that logit.  The last workgroup
-//                   of a request to finish (arrival counter) combines the
-//                   request's pairs, runs the acceptance tests on one wave and
-//                   finds m with a ballot: m = count of trailing ones.
-//   k_stats_greedy  the same pass computing (max, lowest index) per chunk;
-//                   its last workgroup per request compares drafts with the
-//                   row argmaxes and writes every output.
-//   k_sample        the draw at position m.  Workgroup (chunk, request)
-//                   computes the chunk's residual (or p_gamma) mass with a
-//                   block prefix scan; the request's last workgroup finds the
-//                   chunk where the running mass passes u*R, re-scans it and
-//                   takes the first token whose prefix exceeds u*R.
-// Cross-workgroup hand-off uses device-scope release/acquire fences around a
-// per-request atomic counter; nothing ever waits on another workgroup, so
-// every workgroup finishes regardless of scheduling order.
+//   k_stats          the one full pass over every used logits row, split in
+//                    chunks.  Each workgroup streams its chunk with branch-free
+//                    16-byte loads (four per lane per tile, the next tile in
+//                    flight while the current one is reduced) and stores one
+//                    partial: the online (max, sum 2^((z - max) c)) pair in
+//                    sampling mode, (max, lowest index) in greedy mode.  No
+//                    atomics and no cross-workgroup traffic: the kernel
+//                    boundary publishes the partials.
+//   k_decide_sample  workgroup (chunk, request).  Every workgroup of a request
+//                    combines the request's partials, runs the acceptance tests
+//                    on one wave and takes m from a ballot (identical results in
+//                    all of them); each then computes its chunk's sampling mass
+//                    (max(p_m - q_m, 0), or p_gamma on a full accept).  The
+//                    request's last workgroup to finish finds the chunk where
+//                    the running mass passes u*R, re-scans it with a block
+//                    prefix sum, and writes every output of the request.
+//   k_decide_greedy  one workgroup per request: row argmaxes from the
+//                    partials, the argmax-equality prefix and every output.
+// The only cross-workgroup hand-off (chunk masses inside k_decide_sample)
+// uses device-scope atomics; nothing ever waits on another workgroup.
 #include "specdec.h"
 #include "specdec_device.h"
 
+#include <hip/hip_ext.h>
 #include <stdint.h>
 #include <stdlib.h>
 
 namespace specdec {
 namespace {
 
-constexpr int kUnroll = 4;   // 16-byte loads in flight per lane in the stats pass
+constexpr int kUnroll = 4;    // 16-byte vectors per lane per tile, statistics pass
+constexpr int kUnroll2 = 2;   // per row per tile, sampling pass
+constexpr int kMaxPart = 512; // partials per request the decision kernels stage in LDS
 
 struct VerifyParams {
     const void* target;
@@ -55,15 +59,14 @@ struct VerifyParams {
     float* residual_mass;
     uint32_t* flags;
     // workspace
-    uint32_t* cnt1;     // [B] arrivals in the stats pass
-    uint32_t* cnt2;     // [B] arrivals in the sampling pass
-    float4* part;       // [B][R][nc] per-chunk partials, R = 2G+1 (sample) or G+1 (greedy)
-    float2* rowstat;    // [B][2G+1] (max, sum) of every used row
-    float* csum;        // [B][nc2] chunk masses of the sampling pass
+    float4* part;       // [B][R][nc] chunk partials, R = 2G+1 (sample) or G+1 (greedy)
+    uint32_t* cnt;      // [B] arrivals in the sampling pass
+    uint32_t* csum;     // [B][nc2] chunk masses of the sampling pass (float bits)
     int B, G, V;
     int rows;           // R
-    int nc, chunk;      // stats pass: chunks per row, elements per chunk
-    int nc2, chunk2;    // sampling pass
+    int nc, chunk;      // statistics pass: chunks per row, elements per chunk
+    int nc2, chunk2;    // sampling pass: chunks per row, elements per chunk (one tile)
+    int wpr, cpw;       // sampling pass: workgroups per request, chunks per workgroup
     float c;            // log2(e) / T
     uint32_t key0, key1, round;
 };
@@ -84,26 +87,100 @@ __device__ __forceinline__ const void* row_ptr(const void* base, size_t row, int
     return static_cast<const char*>(base) + row * static_cast<size_t>(V) * (bf16 ? 2 : 4);
 }
 
-// Arrival at a per-request counter after this workgroup's results are stored.
-// Returns true (to every lane) in the last workgroup to arrive; that
-// workgroup then reads what the others wrote.
-__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t total) {
+__device__ __forceinline__ const void* target_row(const VerifyParams& P, int b, int i, bool bf16) {
+    return row_ptr(P.target, static_cast<size_t>(b) * (P.G + 1) + i, P.V, bf16);
+}
+
+__device__ __forceinline__ const void* draft_row(const VerifyParams& P, int b, int i, bool bf16) {
+    return row_ptr(P.draft, static_cast<size_t>(b) * P.G + i, P.V, bf16);
+}
+
+// Cross-workgroup hand-off.  A device-scope fence costs an L2 write-back and
+// invalidate, and those serialise per XCD (measured: ~0.4 us each, which made
+// a fence per workgroup dominate a pass).  Instead, the words another
+// workgroup must read are published with device-scope atomic exchanges and
+// read back with atomic read-modify-writes; both are performed at the
+// device's coherence point, so no cache maintenance is needed.  The arrival
+// increment uses an address that depends on the exchanges' returned values
+// (through an empty asm statement the optimiser cannot see through), so it is
+// issued only once the published words have landed.
+__device__ __forceinline__ uint32_t publish(uint32_t* p, uint32_t v) { return atomicExch(p, v); }
+__device__ __forceinline__ uint32_t fetch(uint32_t* p) { return atomicOr(p, 0u); }
+
+// Arrival at a per-request counter; lane 0 passes the OR of its publish()
+// results as `dep`.  Returns true (to every lane) in the last workgroup to
+// arrive, which may then fetch() what the others published.
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t total, uint32_t dep) {
     __shared__ int s_last;
-    __syncthreads();
     if (threadIdx.x == 0) {
-        __threadfence();  // release this workgroup's partials device-wide
-        const uint32_t old = atomicAdd(counter, 1u);
+        uint32_t zero = 0u;
+        asm volatile("" : "+v"(zero) : "v"(dep));
+        const uint32_t old = atomicAdd(counter + zero, 1u);
         s_last = (old == total - 1);
-        if (s_last) *counter = 0;  // leave the workspace ready for the next call
+        if (s_last) atomicExch(counter, 0u);  // ready for the next call
     }
     __syncthreads();
-    if (s_last) __threadfence();  // acquire the other workgroups' partials
     return s_last;
 }
 
-// ------------------------------------------------------------------ sampling
+// ------------------------------------------------------------------ streaming
 
-// Block reduction of the per-lane online pairs.
+template <bool BF16, int U>
+__device__ __forceinline__ void load_tile(uint4 (&raw)[U], const void* rp, int t0) {
+    constexpr int N = Vec<BF16>::N;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        raw[u] = load16_stream<BF16>(rp, t0 + (u * kThreads + threadIdx.x) * N);
+}
+
+template <bool BF16, int U>
+__device__ __forceinline__ void widen_tile(Vec<BF16> (&v)[U], const uint4 (&raw)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = widen<BF16>(raw[u]);
+}
+
+// Streams elements [lo, hi) of one row through consume(v, t0) in tiles of
+// kThreads lanes x U 16-byte vectors (lane l holds vectors u*kThreads + l).
+// Whole tiles use branch-free loads, and the next tile's loads are issued
+// before the current tile is consumed; a ragged last tile takes the clipped
+// path.  keep() is asked once, after the first tile's loads are in flight;
+// false abandons the row (the function then returns false).
+template <bool BF16, bool VEC, int U, class F, class K>
+__device__ __forceinline__ bool stream_row(const void* rp, int lo, int hi, F&& consume, K&& keep) {
+    constexpr int N = Vec<BF16>::N;
+    constexpr int TILE = kThreads * N * U;
+    const int full_end = VEC ? lo + ((hi - lo) / TILE) * TILE : lo;
+    int t0 = lo;
+    if (t0 < full_end) {
+        uint4 cur[U];
+        load_tile<BF16, U>(cur, rp, t0);
+        if (!keep()) return false;
+        for (; t0 + TILE < full_end; t0 += TILE) {
+            uint4 nxt[U];
+            load_tile<BF16, U>(nxt, rp, t0 + TILE);
+            Vec<BF16> v[U];
+            widen_tile<BF16, U>(v, cur);
+            consume(v, t0);
+#pragma unroll
+            for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+        }
+        Vec<BF16> v[U];
+        widen_tile<BF16, U>(v, cur);
+        consume(v, t0);
+        t0 += TILE;
+    } else if (!keep()) {
+        return false;
+    }
+    for (; t0 < hi; t0 += TILE) {
+        Vec<BF16> v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[u] = load_vec<BF16, VEC>(rp, t0 + (u * kThreads + threadIdx.x) * N, hi, neg_inf());
+        consume(v, t0);
+    }
+    return true;
+}
+
 __device__ __forceinline__ MaxSum block_combine(MaxSum v, float c) {
     __shared__ float s_m[kWaves], s_s[kWaves];
     v = wave_combine(v, c);
@@ -115,152 +192,6 @@ __device__ __forceinline__ MaxSum block_combine(MaxSum v, float c) {
     for (int k = 1; k < kWaves; ++k) r = combine(r, MaxSum{s_m[k], s_s[k]}, c);
     return r;
 }
-
-// The per-request decision of sampling mode, run by the whole workgroup that
-// arrived last: (max, sum) of every used row, then the acceptance tests.
-__device__ void decide_sample(const VerifyParams& P, int b, int g) {
-    __shared__ float2 s_stat[127];
-    const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
-    const float c = P.c;
-    // rows 0..g are target rows, G+1 .. G+g draft rows
-    for (int s = w; s < P.rows; s += kWaves) {
-        const bool used = (s <= P.G) ? (s <= g) : (s - (P.G + 1) < g);
-        if (!used) continue;
-        const float4* pr = P.part + (static_cast<size_t>(b) * P.rows + s) * P.nc;
-        MaxSum acc{neg_inf(), 0.0f};
-        for (int k = l; k < P.nc; k += kWave) {
-            const float4 q = pr[k];
-            acc = combine(acc, MaxSum{q.x, q.y}, c);
-        }
-        acc = wave_combine(acc, c);
-        if (l == 0) {
-            s_stat[s] = make_float2(acc.m, acc.s);
-            P.rowstat[static_cast<size_t>(b) * P.rows + s] = make_float2(acc.m, acc.s);
-        }
-    }
-    __syncthreads();
-    if (w != 0) return;
-    // lane i: position i
-    const int i = l;
-    uint32_t fl = 0;
-    bool acc = false;
-    float pd = 0.0f, qd = 0.0f;
-    int d = -1;
-    if (i == 0) fl |= gamma_flag(P, b);
-    if (i <= g) {
-        const float2 t = s_stat[i];
-        if (!(t.x < pos_inf()) || !(t.y == t.y)) fl |= SPECDEC_FLAG_NONFINITE;
-    }
-    if (i < g) {
-        d = P.tokens[static_cast<size_t>(b) * P.G + i];
-        const float2 t = s_stat[i];
-        const float2 q = s_stat[P.G + 1 + i];
-        if (!(q.x < pos_inf()) || !(q.y == q.y)) fl |= SPECDEC_FLAG_NONFINITE;
-        float a = 0.0f;
-        if (d >= 0 && d < P.V) {
-            const int cd = d / P.chunk;
-            const float zt = P.part[(static_cast<size_t>(b) * P.rows + i) * P.nc + cd].z;
-            const float zq = P.part[(static_cast<size_t>(b) * P.rows + P.G + 1 + i) * P.nc + cd].z;
-            pd = exp2f((zt - t.x) * c) / t.y;
-            qd = exp2f((zq - q.x) * c) / q.y;
-            if (qd > 0.0f) a = fminf(1.0f, pd / qd);
-            else a = pd > 0.0f ? 1.0f : 0.0f;
-        } else {
-            fl |= SPECDEC_FLAG_TOKEN_RANGE;
-        }
-        const uint4 r = philox4x32_10(make_uint4(static_cast<uint32_t>(i), static_cast<uint32_t>(b),
-                                                 P.round, 0u), P.key0, P.key1);
-        acc = uniform24(r.x) < a;
-    }
-    const uint64_t mask = __ballot(acc);
-    // m = number of leading accepted positions (ones from bit 0), capped at g
-    const int m = min(g, static_cast<int>(__builtin_ctzll(~mask)));
-    fl = wave_or(fl);
-    int32_t* out = P.out_tokens + static_cast<size_t>(b) * (P.G + 1);
-    if (i <= P.G && i != m) out[i] = i < m ? d : -1;
-    if (i < P.G) {
-        if (P.p_draft) P.p_draft[static_cast<size_t>(b) * P.G + i] = pd;
-        if (P.q_draft) P.q_draft[static_cast<size_t>(b) * P.G + i] = qd;
-    }
-    if (i == 0) {
-        P.accept_count[b] = m;
-        if (P.flags) P.flags[b] = fl;
-    }
-}
-
-template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_stats_sample(VerifyParams P) {
-    const int ci = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
-    const int g = request_gamma(P, b);
-    const bool is_target = s <= P.G;
-    const int i = is_target ? s : s - (P.G + 1);
-    if (is_target ? (i > g) : (i >= g)) return;  // padding row: never read
-    const size_t row = is_target ? static_cast<size_t>(b) * (P.G + 1) + i
-                                 : static_cast<size_t>(b) * P.G + i;
-    const void* rp = row_ptr(is_target ? P.target : P.draft, row, P.V, BF16);
-    const int lo = ci * P.chunk;
-    const int hi = min(P.V, lo + P.chunk);
-    const float c = P.c;
-    constexpr int N = Vec<BF16>::N;
-    constexpr int TILE = kThreads * N * kUnroll;
-
-    // Tiles wholly inside the chunk stream with branch-free 16-byte loads (all
-    // kUnroll of a lane in flight together); only the last tile of a row's
-    // last chunk takes the clipped path.
-    float m = neg_inf(), sum = 0.0f;
-    auto consume = [&](const Vec<BF16> (&v)[kUnroll]) {
-        float tm = neg_inf();
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-            for (int k = 0; k < N; ++k) tm = fmaxf(tm, v[u].x[k]);
-        const float mn = fmaxf(m, tm);
-        if (mn == neg_inf()) return;
-        float part = 0.0f;
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            float q = 0.0f;
-#pragma unroll
-            for (int k = 0; k < N; ++k) q += __builtin_amdgcn_exp2f((v[u].x[k] - mn) * c);
-            part += q;
-        }
-        sum = (m == neg_inf() ? 0.0f : sum * exp2f((m - mn) * c)) + part;
-        m = mn;
-    };
-    const int full_end = VEC ? lo + ((hi - lo) / TILE) * TILE : lo;
-    for (int t0 = lo; t0 < full_end; t0 += TILE) {
-        uint4 raw[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) raw[u] = load16<BF16>(rp, t0 + (u * kThreads + threadIdx.x) * N);
-        Vec<BF16> v[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) v[u] = widen<BF16>(raw[u]);
-        consume(v);
-    }
-    for (int t0 = full_end; t0 < hi; t0 += TILE) {
-        Vec<BF16> v[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            v[u] = load_vec<BF16, VEC>(rp, t0 + (u * kThreads + threadIdx.x) * N, hi, neg_inf());
-        consume(v);
-    }
-    const MaxSum r = block_combine(MaxSum{m, sum}, c);
-
-    // the logit of the token this row judges (target) or proposed (draft)
-    if (threadIdx.x == 0) {
-        float zd = 0.0f;
-        if (i < g) {
-            const int d = P.tokens[static_cast<size_t>(b) * P.G + i];
-            if (d >= lo && d < hi) zd = load_logit<BF16>(rp, d);
-        }
-        P.part[(static_cast<size_t>(b) * P.rows + s) * P.nc + ci] = make_float4(r.m, r.s, zd, 0.0f);
-    }
-    const uint32_t total = static_cast<uint32_t>((2 * g + 1) * P.nc);
-    if (!arrive_last(P.cnt1 + b, total)) return;
-    decide_sample(P, b, g);
-}
-
-// ------------------------------------------------------------------ greedy
 
 __device__ __forceinline__ ArgMax block_argmax(ArgMax v) {
     __shared__ float s_v[kWaves];
@@ -275,154 +206,261 @@ __device__ __forceinline__ ArgMax block_argmax(ArgMax v) {
     return r;
 }
 
-__device__ void decide_greedy(const VerifyParams& P, int b, int g) {
-    __shared__ int s_arg[64];
-    __shared__ uint32_t s_nan[64];
+__device__ __forceinline__ float block_sum(float v) {
+    __shared__ float s_v[kWaves];
+    v = wave_sum(v);
     const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
-    for (int s = w; s <= g; s += kWaves) {
-        const float4* pr = P.part + (static_cast<size_t>(b) * P.rows + s) * P.nc;
-        ArgMax best{neg_inf(), 0x7fffffff};
-        uint32_t nan = 0;
-        for (int k = l; k < P.nc; k += kWave) {
-            const float4 q = pr[k];
-            const int idx = __float_as_int(q.y);
-            if (idx != 0x7fffffff) best = better(best, ArgMax{q.x, idx});
-            nan |= __float_as_uint(q.z);
-        }
-        best = wave_argmax(best);
-        nan = wave_or(nan);
-        if (l == 0) { s_arg[s] = best.i; s_nan[s] = nan; }
-    }
     __syncthreads();
-    if (w != 0) return;
-    const int i = l;
-    uint32_t fl = 0;
-    bool acc = false;
-    int d = -1;
-    if (i == 0) fl |= gamma_flag(P, b);
-    if (i <= g && s_nan[i]) fl |= SPECDEC_FLAG_NONFINITE;
-    if (i < g) {
-        d = P.tokens[static_cast<size_t>(b) * P.G + i];
-        if (d < 0 || d >= P.V) fl |= SPECDEC_FLAG_TOKEN_RANGE;
-        acc = (d == s_arg[i]);
-    }
-    const uint64_t mask = __ballot(acc);
-    const int m = min(g, static_cast<int>(__builtin_ctzll(~mask)));
-    fl = wave_or(fl);
-    int32_t* out = P.out_tokens + static_cast<size_t>(b) * (P.G + 1);
-    if (i <= P.G) out[i] = i < m ? d : (i == m ? s_arg[m] : -1);
-    if (i == 0) {
-        P.accept_count[b] = m;
-        if (P.flags) P.flags[b] = fl;
-    }
+    if (l == 0) s_v[w] = v;
+    __syncthreads();
+    float r = s_v[0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) r += s_v[k];
+    return r;
 }
 
-template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_stats_greedy(VerifyParams P) {
-    const int ci = blockIdx.x, i = blockIdx.y, b = blockIdx.z;
-    const int g = request_gamma(P, b);
-    if (i > g) return;
-    const void* rp = row_ptr(P.target, static_cast<size_t>(b) * (P.G + 1) + i, P.V, BF16);
+// ------------------------------------------------------------------ statistics pass
+
+// Workgroup (chunk ci, row slot s, request b).  Slots 0..G are target rows,
+// G+1..2G draft rows (sampling only).  Rows past gamma_b are abandoned after
+// their first loads are issued, so the gamma_b load never stalls the stream.
+template <bool BF16, bool VEC, bool GREEDY>
+__global__ __launch_bounds__(kThreads) void k_stats(VerifyParams P) {
+    const int ci = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
+    const bool is_target = s <= P.G;
+    const int i = is_target ? s : s - (P.G + 1);
+    const void* rp = is_target ? target_row(P, b, i, BF16) : draft_row(P, b, i, BF16);
     const int lo = ci * P.chunk;
     const int hi = min(P.V, lo + P.chunk);
-    constexpr int N = Vec<BF16>::N;
-    constexpr int TILE = kThreads * N * kUnroll;
-    // Each lane visits its elements in ascending index order, so a strict ">"
-    // keeps the lowest index among equal maxima.
-    ArgMax best{neg_inf(), 0x7fffffff};
-    bool nan = false;
-    auto consume = [&](const Vec<BF16> (&v)[kUnroll], int t0) {
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int e = t0 + (u * kThreads + threadIdx.x) * N;
-#pragma unroll
-            for (int k = 0; k < N; ++k) {
-                const float x = v[u].x[k];
-                nan |= (x != x);
-                const bool first = best.i == 0x7fffffff && e + k < hi;
-                if (x > best.v || first) { best.v = x; best.i = e + k; }
-            }
-        }
+    auto keep = [&]() {
+        if (!P.gamma) return true;
+        const int g = request_gamma(P, b);
+        return is_target ? i <= g : i < g;
     };
-    const int full_end = VEC ? lo + ((hi - lo) / TILE) * TILE : lo;
-    for (int t0 = lo; t0 < full_end; t0 += TILE) {
-        uint4 raw[kUnroll];
+    constexpr int N = Vec<BF16>::N;
+    float4* slot = P.part + (static_cast<size_t>(b) * P.rows + s) * P.nc + ci;
+    if constexpr (GREEDY) {
+        // Each lane visits its elements in ascending index order, so a strict
+        // ">" keeps the lowest index among equal maxima.
+        ArgMax best{neg_inf(), 0x7fffffff};
+        bool nan = false;
+        auto consume = [&](const Vec<BF16> (&v)[kUnroll], int t0) {
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) raw[u] = load16<BF16>(rp, t0 + (u * kThreads + threadIdx.x) * N);
-        Vec<BF16> v[kUnroll];
+            for (int u = 0; u < kUnroll; ++u) {
+                const int e = t0 + (u * kThreads + threadIdx.x) * N;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) v[u] = widen<BF16>(raw[u]);
-        consume(v, t0);
+                for (int k = 0; k < N; ++k) {
+                    const float x = v[u].x[k];
+                    nan |= (x != x);
+                    const bool first = best.i == 0x7fffffff && e + k < hi;
+                    if (x > best.v || first) { best.v = x; best.i = e + k; }
+                }
+            }
+        };
+        if (!stream_row<BF16, VEC, kUnroll>(rp, lo, hi, consume, keep)) return;
+        const ArgMax r = block_argmax(best);
+        const bool any_nan = __syncthreads_or(nan);
+        if (threadIdx.x == 0)
+            *slot = make_float4(r.v, __uint_as_float(static_cast<uint32_t>(r.i) |
+                                                     (any_nan ? 0x80000000u : 0u)), 0.0f, 0.0f);
+    } else {
+        // the token this row judges (target) or proposed (draft); its logit
+        // rides along with the partial of the chunk that holds it
+        const int d = i < P.G ? P.tokens[static_cast<size_t>(b) * P.G + i] : -1;
+        const float c = P.c;
+        float m = neg_inf(), sum = 0.0f;
+        auto consume = [&](const Vec<BF16> (&v)[kUnroll], int) {
+            float tm = neg_inf();
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+                for (int k = 0; k < N; ++k) tm = fmaxf(tm, v[u].x[k]);
+            const float mn = fmaxf(m, tm);
+            if (mn == neg_inf()) return;
+            float part = 0.0f;
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                float q = 0.0f;
+#pragma unroll
+                for (int k = 0; k < N; ++k) q += __builtin_amdgcn_exp2f((v[u].x[k] - mn) * c);
+                part += q;
+            }
+            sum = (m == neg_inf() ? 0.0f : sum * exp2f((m - mn) * c)) + part;
+            m = mn;
+        };
+        if (!stream_row<BF16, VEC, kUnroll>(rp, lo, hi, consume, keep)) return;
+        const MaxSum r = block_combine(MaxSum{m, sum}, c);
+        if (threadIdx.x == 0) {
+            const float zd = (d >= lo && d < hi) ? load_logit<BF16>(rp, d) : 0.0f;
+            *slot = make_float4(r.m, r.s, zd, 0.0f);
+        }
     }
-    for (int t0 = full_end; t0 < hi; t0 += TILE) {
-        Vec<BF16> v[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            v[u] = load_vec<BF16, VEC>(rp, t0 + (u * kThreads + threadIdx.x) * N, hi, neg_inf());
-        consume(v, t0);
-    }
-    const ArgMax r = block_argmax(best);
-    const bool any_nan = __syncthreads_or(nan);
-    if (threadIdx.x == 0)
-        P.part[(static_cast<size_t>(b) * P.rows + i) * P.nc + ci] =
-            make_float4(r.v, __int_as_float(r.i), __uint_as_float(any_nan ? 1u : 0u), 0.0f);
-    const uint32_t total = static_cast<uint32_t>((g + 1) * P.nc);
-    if (!arrive_last(P.cnt1 + b, total)) return;
-    decide_greedy(P, b, g);
 }
 
 // ------------------------------------------------------------------ sampling pass
 
-struct ScanRow {
-    const void* p;   // target row m (or gamma)
-    const void* q;   // draft row m, or nullptr when the mass is p itself
-    float mp, sp, mq, sq, c;
+// The mass the draw at position m samples from: max(p - q, 0) on a
+// rejection, p itself when q is absent (bonus, or the empty-residual
+// fallback).  p = 2^((z - max) c) / sum, q likewise.
+struct MassRows {
+    const void* p;
+    const void* q;
+    float mp, isp, mq, isq, c;
 };
 
-template <bool BF16>
-__device__ __forceinline__ float mass_at(const ScanRow& a, float zp, float zq) {
-    const float pv = exp2f((zp - a.mp) * a.c) / a.sp;
+__device__ __forceinline__ float mass_at(const MassRows& a, float zp, float zq) {
+    const float pv = __builtin_amdgcn_exp2f((zp - a.mp) * a.c) * a.isp;
     if (!a.q) return pv;
-    const float qv = exp2f((zq - a.mq) * a.c) / a.sq;
+    const float qv = __builtin_amdgcn_exp2f((zq - a.mq) * a.c) * a.isq;
     return fmaxf(pv - qv, 0.0f);
 }
 
-// Chunk [lo, hi) of the sampling mass r (max(p - q, 0), or p), scanned in
-// ascending token order in tiles of 256 lanes x 16 bytes.  Returns the
-// chunk's total, defined as the inclusive prefix at its last element.
-// With base + prefix(v) > target for some v in the chunk, *tok receives the
-// first such v.  *last_pos receives the largest v with r(v) > 0.
-// Kept out of line so that the chunk total of the mass pass and the prefix
-// values of the search pass come from the very same instructions.
+// One chunk of the sampling pass is one tile: lane l holds the 16-byte
+// vectors u*kThreads + l, u < kUnroll2, of each row.  Loads are clamped into
+// the row (a vector is wholly inside [lo, hi) or wholly past it) and the
+// values of out-of-range vectors are discarded after use, so no load sits
+// behind a branch.
 template <bool BF16, bool VEC>
-__device__ __noinline__ float scan_chunk(const ScanRow a, int lo, int hi, float base, float target,
-                                         int* tok, int* last_pos) {
+struct ChunkRegs {
+    uint4 p[kUnroll2], q[kUnroll2];
+};
+
+template <bool BF16, bool VEC>
+__device__ __forceinline__ void load_chunk(ChunkRegs<BF16, VEC>& r, const MassRows& a, int lo, int hi) {
     constexpr int N = Vec<BF16>::N;
-    constexpr int TILE = kThreads * N;
+#pragma unroll
+    for (int u = 0; u < kUnroll2; ++u) {
+        const int e = min(lo + (u * kThreads + threadIdx.x) * N, hi - N);
+        r.p[u] = load16<BF16>(a.p, e);
+        if (a.q) r.q[u] = load16<BF16>(a.q, e);
+    }
+}
+
+// Lane's share of the chunk's mass (VEC layout).
+template <bool BF16, bool VEC>
+__device__ __forceinline__ float lane_mass(const ChunkRegs<BF16, VEC>& r, const MassRows& a, int lo, int hi) {
+    constexpr int N = Vec<BF16>::N;
+    float acc = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kUnroll2; ++u) {
+        const Vec<BF16> vp = widen<BF16>(r.p[u]);
+        Vec<BF16> vq;
+        if (a.q) vq = widen<BF16>(r.q[u]);
+        float s = 0.0f;
+#pragma unroll
+        for (int k = 0; k < N; ++k) s += mass_at(a, vp.x[k], a.q ? vq.x[k] : 0.0f);
+        const int e = lo + (u * kThreads + threadIdx.x) * N;
+        acc += (e < hi) ? s : 0.0f;
+    }
+    return acc;
+}
+
+// Lane's share of the chunk's mass with element loads (rows not 16-byte
+// aligned): a slow path kept simple.
+template <bool BF16>
+__device__ float lane_mass_elements(const MassRows& a, int lo, int hi) {
+    constexpr int N = Vec<BF16>::N;
+    float acc = 0.0f;
+    for (int u = 0; u < kUnroll2; ++u) {
+        const int e = lo + (u * kThreads + threadIdx.x) * N;
+        for (int k = 0; k < N; ++k) {
+            if (e + k >= hi) break;
+            const float zp = load_logit<BF16>(a.p, e + k);
+            const float zq = a.q ? load_logit<BF16>(a.q, e + k) : 0.0f;
+            acc += mass_at(a, zp, zq);
+        }
+    }
+    return acc;
+}
+
+// Masses of chunks [k0, k1) published to csum[k]; the next chunk's loads are
+// in flight while the current one is reduced.  Returns the OR of the
+// publish() results (the dependency for arrive_last).
+template <bool BF16, bool VEC>
+__device__ uint32_t mass_chunks(const MassRows& a, int k0, int k1, int chunk2, int V, uint32_t* csum) {
+    uint32_t dep = 0;
+    if (k0 >= k1) return dep;
+    if constexpr (VEC) {
+        ChunkRegs<BF16, VEC> cur, nxt;
+        load_chunk<BF16, VEC>(cur, a, k0 * chunk2, min(V, (k0 + 1) * chunk2));
+        for (int k = k0; k < k1; ++k) {
+            const int kn = min(k + 1, k1 - 1);  // re-loads the last chunk once: no branch
+            load_chunk<BF16, VEC>(nxt, a, kn * chunk2, min(V, (kn + 1) * chunk2));
+            const int lo = k * chunk2, hi = min(V, lo + chunk2);
+            const float t = block_sum(lane_mass<BF16, VEC>(cur, a, lo, hi));
+            if (threadIdx.x == 0) dep |= publish(csum + k, __float_as_uint(t));
+            cur = nxt;
+        }
+    } else {
+        for (int k = k0; k < k1; ++k) {
+            const int lo = k * chunk2, hi = min(V, lo + chunk2);
+            const float t = block_sum(lane_mass_elements<BF16>(a, lo, hi));
+            if (threadIdx.x == 0) dep |= publish(csum + k, __float_as_uint(t));
+        }
+    }
+    return dep;
+}
+
+// Mass of one chunk (the empty-residual fallback path).
+template <bool BF16, bool VEC>
+__device__ float chunk_mass(const MassRows& a, int lo, int hi) {
+    if constexpr (VEC) {
+        ChunkRegs<BF16, VEC> r;
+        load_chunk<BF16, VEC>(r, a, lo, hi);
+        return block_sum(lane_mass<BF16, VEC>(r, a, lo, hi));
+    } else {
+        return block_sum(lane_mass_elements<BF16>(a, lo, hi));
+    }
+}
+
+// First v of the chunk [lo, hi) with base + prefix(v) > target, scanning the
+// mass in ascending token order: the chunk's vectors are all loaded first,
+// then each group of kThreads vectors gets a block prefix sum.  Returns
+// 0x7fffffff if none; *last_pos receives the chunk's largest v with mass > 0.
+template <bool BF16, bool VEC>
+__device__ int search_chunk(const MassRows& a, int lo, int hi, float base, float target,
+                            int* last_pos) {
+    constexpr int N = Vec<BF16>::N;
     __shared__ float s_wtot[kWaves];
     __shared__ float s_tile_end;
     __shared__ int s_found, s_last;
     const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
-    __syncthreads();  // a previous call's results have been read by every lane
+    // every load of the chunk in flight at once (clamped, no branches)
+    Vec<BF16> vp[kUnroll2], vq[kUnroll2];
+    if constexpr (VEC) {
+        ChunkRegs<BF16, VEC> raw;
+        load_chunk<BF16, VEC>(raw, a, lo, hi);
+#pragma unroll
+        for (int u = 0; u < kUnroll2; ++u) {
+            vp[u] = widen<BF16>(raw.p[u]);
+            if (a.q) vq[u] = widen<BF16>(raw.q[u]);
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < kUnroll2; ++u) {
+            const int e = lo + (u * kThreads + threadIdx.x) * N;
+            vp[u] = load_vec<BF16, VEC>(a.p, e, hi, neg_inf());
+            if (a.q) vq[u] = load_vec<BF16, VEC>(a.q, e, hi, neg_inf());
+        }
+    }
+    __syncthreads();
     if (threadIdx.x == 0) { s_found = 0x7fffffff; s_last = -1; }
-    float tile_base = 0.0f;
-    for (int t0 = lo; t0 < hi; t0 += TILE) {
-        const int e = t0 + threadIdx.x * N;
-        const Vec<BF16> vp = load_vec<BF16, VEC>(a.p, e, hi, neg_inf());
-        Vec<BF16> vq;
-        if (a.q) vq = load_vec<BF16, VEC>(a.q, e, hi, neg_inf());
-        float r[N], inc[N];
+    float tile_base = base;
+#pragma unroll
+    for (int u = 0; u < kUnroll2; ++u) {
+        const int e = lo + (u * kThreads + threadIdx.x) * N;
+        float inc[N];
         int lastp = -1;
+        float run = 0.0f;
 #pragma unroll
         for (int k = 0; k < N; ++k) {
-            r[k] = (e + k < hi) ? mass_at<BF16>(a, vp.x[k], a.q ? vq.x[k] : 0.0f) : 0.0f;
-            if (r[k] > 0.0f) lastp = e + k;
+            const float r = (e + k < hi) ? mass_at(a, vp[u].x[k], a.q ? vq[u].x[k] : 0.0f) : 0.0f;
+            if (r > 0.0f) lastp = e + k;
+            run += r;
+            inc[k] = run;
         }
-        inc[0] = r[0];
-#pragma unroll
-        for (int k = 1; k < N; ++k) inc[k] = inc[k - 1] + r[k];
         // exclusive scan of lane totals: inclusive within the wave, shifted
-        float x = inc[N - 1];
+        float x = run;
 #pragma unroll
         for (int o = 1; o < kWave; o <<= 1) {
             const float y = __shfl_up(x, o, kWave);
@@ -438,58 +476,134 @@ __device__ __noinline__ float scan_chunk(const ScanRow a, int lo, int hi, float 
         const float lane_base = tile_base + (woff + ex);
         int first = 0x7fffffff;
 #pragma unroll
-        for (int k = N - 1; k >= 0; --k) {
-            const float pre = lane_base + inc[k];
-            if (base + pre > target) first = e + k;
-        }
-        if (first != 0x7fffffff) atomicMin(&s_found, first);
-        if (lastp >= 0) atomicMax(&s_last, lastp);
+        for (int k = N - 1; k >= 0; --k)
+            if (lane_base + inc[k] > target) first = e + k;
+        // lanes hold ascending token ranges: the lowest crossing lane has the
+        // wave's first crossing, the highest lane with mass its last token
+        // with mass; one LDS atomic per wave
+        const uint64_t cross = __ballot(first != 0x7fffffff);
+        const uint64_t pos = __ballot(lastp >= 0);
+        const int f = __shfl(first, cross ? __builtin_ctzll(cross) : 0, kWave);
+        const int lp = __shfl(lastp, pos ? 63 - __builtin_clzll(pos) : 0, kWave);
+        if (l == 0 && cross) atomicMin(&s_found, f);
+        if (l == 0 && pos) atomicMax(&s_last, lp);
         if (threadIdx.x == kThreads - 1) s_tile_end = lane_base + inc[N - 1];
         __syncthreads();
         tile_base = s_tile_end;
-        if (s_found != 0x7fffffff) break;
     }
     __syncthreads();
-    *tok = s_found;
     *last_pos = s_last;
-    return tile_base;
+    return s_found;
+}
+
+// Stage the request's chunk partials in LDS with one batch of independent
+// loads (rows x chunks <= kMaxPart).
+__device__ __forceinline__ void stage_partials(const VerifyParams& P, int b, float4* s_part) {
+    const int n = P.rows * P.nc;
+    const float4* src = P.part + static_cast<size_t>(b) * n;
+    for (int t = threadIdx.x; t < n; t += kThreads) s_part[t] = src[t];
 }
 
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_sample(VerifyParams P) {
+__global__ __launch_bounds__(kThreads) void k_decide_sample(VerifyParams P) {
+    __shared__ float4 s_part[kMaxPart];
+    __shared__ float2 s_stat[127];
     __shared__ float s_csum[1024];
+    __shared__ int s_m;
+    __shared__ uint32_t s_fl;
     __shared__ float s_R;
-    const int ci = blockIdx.x, b = blockIdx.y;
+    const int wg = blockIdx.x, b = blockIdx.y;
+    const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+    const int i = l;
+    const float c = P.c;
+
+    // (0) independent loads first: partials, the drafted tokens, gamma_b
+    stage_partials(P, b, s_part);
+    int d = -1;
+    if (w == 0 && i < P.G) d = P.tokens[static_cast<size_t>(b) * P.G + i];
     const int g = request_gamma(P, b);
-    const int m = min(max(P.accept_count[b], 0), g);  // written by the stats pass
+    __syncthreads();
+
+    // (1) (max, sum) of every used row from its chunk partials
+    for (int s = w; s < P.rows; s += kWaves) {
+        const bool used = (s <= P.G) ? (s <= g) : (s - (P.G + 1) < g);
+        if (!used) continue;
+        MaxSum acc{neg_inf(), 0.0f};
+        for (int k = l; k < P.nc; k += kWave) {
+            const float4 q = s_part[s * P.nc + k];
+            acc = combine(acc, MaxSum{q.x, q.y}, c);
+        }
+        acc = wave_combine(acc, c);
+        if (l == 0) s_stat[s] = make_float2(acc.m, acc.s);
+    }
+    __syncthreads();
+
+    // (2) acceptance tests, lane i = position i of wave 0; m from a ballot
+    float pd = 0.0f, qd = 0.0f;
+    if (w == 0) {
+        uint32_t fl = (i == 0) ? gamma_flag(P, b) : 0u;
+        bool acc = false;
+        if (i <= g) {
+            const float2 t = s_stat[i];
+            if (!(t.x < pos_inf()) || !(t.y == t.y)) fl |= SPECDEC_FLAG_NONFINITE;
+        }
+        if (i < g) {
+            const float2 t = s_stat[i];
+            const float2 q = s_stat[P.G + 1 + i];
+            if (!(q.x < pos_inf()) || !(q.y == q.y)) fl |= SPECDEC_FLAG_NONFINITE;
+            float a = 0.0f;
+            if (d >= 0 && d < P.V) {
+                const int cd = d / P.chunk;
+                const float zt = s_part[i * P.nc + cd].z;
+                const float zq = s_part[(P.G + 1 + i) * P.nc + cd].z;
+                pd = exp2f((zt - t.x) * c) / t.y;
+                qd = exp2f((zq - q.x) * c) / q.y;
+                if (qd > 0.0f) a = fminf(1.0f, pd / qd);
+                else a = pd > 0.0f ? 1.0f : 0.0f;
+            } else {
+                fl |= SPECDEC_FLAG_TOKEN_RANGE;
+            }
+            const uint4 r = philox4x32_10(make_uint4(static_cast<uint32_t>(i), static_cast<uint32_t>(b),
+                                                     P.round, 0u), P.key0, P.key1);
+            acc = uniform24(r.x) < a;
+        } else {
+            d = -1;
+        }
+        const uint64_t mask = __ballot(acc);
+        const int m = min(g, static_cast<int>(__builtin_ctzll(~mask)));
+        fl = wave_or(fl);
+        if (l == 0) { s_m = m; s_fl = fl; }
+    }
+    __syncthreads();
+    const int m = s_m;
+
+    // (3) this workgroup's chunks of the sampling mass at position m
     const bool resid = m < g;
-    const float2 st = P.rowstat[static_cast<size_t>(b) * P.rows + m];
-    ScanRow a;
-    a.p = row_ptr(P.target, static_cast<size_t>(b) * (P.G + 1) + m, P.V, BF16);
-    a.mp = st.x;
-    a.sp = st.y;
-    a.c = P.c;
+    MassRows a;
+    const float2 tp = s_stat[m];
+    a.p = target_row(P, b, m, BF16);
+    a.mp = tp.x;
+    a.isp = 1.0f / tp.y;
+    a.c = c;
     a.q = nullptr;
     a.mq = 0.0f;
-    a.sq = 1.0f;
+    a.isq = 0.0f;
     if (resid) {
-        const float2 sq = P.rowstat[static_cast<size_t>(b) * P.rows + P.G + 1 + m];
-        a.q = row_ptr(P.draft, static_cast<size_t>(b) * P.G + m, P.V, BF16);
-        a.mq = sq.x;
-        a.sq = sq.y;
+        const float2 tq = s_stat[P.G + 1 + m];
+        a.q = draft_row(P, b, m, BF16);
+        a.mq = tq.x;
+        a.isq = 1.0f / tq.y;
     }
-    int tok, lastp;
-    const int lo = ci * P.chunk2, hi = min(P.V, lo + P.chunk2);
-    const float cs = scan_chunk<BF16, VEC>(a, lo, hi, 0.0f, pos_inf(), &tok, &lastp);
-    if (threadIdx.x == 0) P.csum[static_cast<size_t>(b) * P.nc2 + ci] = cs;
-    if (!arrive_last(P.cnt2 + b, static_cast<uint32_t>(P.nc2))) return;
+    uint32_t* csum = P.csum + static_cast<size_t>(b) * P.nc2;
+    const int k0 = wg * P.cpw, k1 = min(P.nc2, k0 + P.cpw);
+    const uint32_t dep = mass_chunks<BF16, VEC>(a, k0, k1, P.chunk2, P.V, csum);
+    if (!arrive_last(P.cnt + b, static_cast<uint32_t>(P.wpr), dep)) return;
 
-    // Last workgroup of request b: R, the chunk where the mass passes u*R,
-    // then the token inside it.
-    for (int k = threadIdx.x; k < P.nc2; k += kThreads)
-        s_csum[k] = P.csum[static_cast<size_t>(b) * P.nc2 + k];
+    // (4) last workgroup of the request: R, the chunk where the running mass
+    // passes u*R, the token inside it, then every output of the request.
+    for (int k = threadIdx.x; k < P.nc2; k += kThreads) s_csum[k] = __uint_as_float(fetch(csum + k));
     __syncthreads();
-    uint32_t fl = 0;
+    uint32_t fl2 = 0;
     float R_report = 0.0f;
     if (threadIdx.x == 0) {
         float R = 0.0f;
@@ -501,12 +615,10 @@ __global__ __launch_bounds__(kThreads) void k_sample(VerifyParams P) {
         R_report = s_R;
         if (!(s_R > 0.0f)) {
             // empty residual: draw from p_m instead (never divide by zero)
-            fl |= SPECDEC_FLAG_RESIDUAL_FALLBACK;
+            fl2 |= SPECDEC_FLAG_RESIDUAL_FALLBACK;
             a.q = nullptr;
             for (int k = 0; k < P.nc2; ++k) {
-                const int l2 = k * P.chunk2, h2 = min(P.V, l2 + P.chunk2);
-                int t2, lp2;
-                const float v = scan_chunk<BF16, VEC>(a, l2, h2, 0.0f, pos_inf(), &t2, &lp2);
+                const float v = chunk_mass<BF16, VEC>(a, k * P.chunk2, min(P.V, (k + 1) * P.chunk2));
                 if (threadIdx.x == 0) s_csum[k] = v;
             }
             __syncthreads();
@@ -532,41 +644,94 @@ __global__ __launch_bounds__(kThreads) void k_sample(VerifyParams P) {
             if (next > target) { cstar = k; before = C; break; }
             C = next;
         }
+        if (cstar < 0) {
+            // rounding left u*R at or above the total: the last chunk with mass
+            cstar = P.nc2 - 1;
+            while (cstar > 0 && !(s_csum[cstar] > 0.0f)) --cstar;
+            before = pos_inf();  // no crossing: take its last token with mass
+        }
         s_chunk = cstar;
         s_before = before;
     }
     __syncthreads();
-    int token = -1;
-    if (s_chunk >= 0) {
-        const int l2 = s_chunk * P.chunk2, h2 = min(P.V, l2 + P.chunk2);
-        int t2, lp2;
-        scan_chunk<BF16, VEC>(a, l2, h2, s_before, target, &t2, &lp2);
-        // The chunk total ends a partial last tile with a differently
-        // associated sum than its last element's prefix; if that rounding
-        // leaves no element above u*R, the crossing is the chunk's last token
-        // with mass.
-        token = t2 != 0x7fffffff ? t2 : lp2;
-    } else {
-        // rounding left u*R at or above the total: the last token with mass
-        int k = P.nc2 - 1;
-        while (k > 0 && !(s_csum[k] > 0.0f)) --k;
-        const int l2 = k * P.chunk2, h2 = min(P.V, l2 + P.chunk2);
-        int t2, lp2;
-        scan_chunk<BF16, VEC>(a, l2, h2, 0.0f, pos_inf(), &t2, &lp2);
-        token = lp2;
+    int lastp;
+    const int l2 = s_chunk * P.chunk2, h2 = min(P.V, l2 + P.chunk2);
+    int token = search_chunk<BF16, VEC>(a, l2, h2, s_before, target, &lastp);
+    // The chunk sums and the in-chunk prefixes associate the additions
+    // differently; if that rounding leaves no element above u*R in the chosen
+    // chunk, the crossing is its last token with mass.
+    if (token == 0x7fffffff) token = lastp;
+
+    if (w == 0) {
+        int32_t* out = P.out_tokens + static_cast<size_t>(b) * (P.G + 1);
+        if (i <= P.G) out[i] = i < m ? d : (i == m ? token : -1);
+        if (i < P.G) {
+            if (P.p_draft) P.p_draft[static_cast<size_t>(b) * P.G + i] = pd;
+            if (P.q_draft) P.q_draft[static_cast<size_t>(b) * P.G + i] = qd;
+        }
+        if (i == 0) {
+            P.accept_count[b] = m;
+            if (P.residual_mass) P.residual_mass[b] = R_report;
+            if (P.flags) P.flags[b] = s_fl | fl2;
+        }
     }
-    if (threadIdx.x == 0) {
-        P.out_tokens[static_cast<size_t>(b) * (P.G + 1) + m] = token;
-        if (P.residual_mass) P.residual_mass[b] = R_report;
-        if (P.flags && fl) P.flags[b] |= fl;
+}
+
+// ------------------------------------------------------------------ greedy decision
+
+__global__ __launch_bounds__(kThreads) void k_decide_greedy(VerifyParams P) {
+    __shared__ float4 s_part[kMaxPart];
+    __shared__ int s_arg[64];
+    __shared__ uint32_t s_nan[64];
+    const int b = blockIdx.x;
+    const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+    stage_partials(P, b, s_part);
+    const int i = l;
+    int d = -1;
+    if (w == 0 && i < P.G) d = P.tokens[static_cast<size_t>(b) * P.G + i];
+    const int g = request_gamma(P, b);
+    __syncthreads();
+    for (int s = w; s <= g; s += kWaves) {
+        ArgMax best{neg_inf(), 0x7fffffff};
+        uint32_t nan = 0;
+        for (int k = l; k < P.nc; k += kWave) {
+            const float4 q = s_part[s * P.nc + k];
+            const uint32_t word = __float_as_uint(q.y);  // index, bit 31: a NaN was seen
+            const int idx = static_cast<int>(word & 0x7fffffffu);
+            if (idx != 0x7fffffff) best = better(best, ArgMax{q.x, idx});
+            nan |= word >> 31;
+        }
+        best = wave_argmax(best);
+        nan = wave_or(nan);
+        if (l == 0) { s_arg[s] = best.i; s_nan[s] = nan; }
+    }
+    __syncthreads();
+    if (w != 0) return;
+    uint32_t fl = (i == 0) ? gamma_flag(P, b) : 0u;
+    bool acc = false;
+    if (i <= g && s_nan[i]) fl |= SPECDEC_FLAG_NONFINITE;
+    if (i < g) {
+        if (d < 0 || d >= P.V) fl |= SPECDEC_FLAG_TOKEN_RANGE;
+        acc = (d == s_arg[i]);
+    } else {
+        d = -1;
+    }
+    const uint64_t mask = __ballot(acc);
+    const int m = min(g, static_cast<int>(__builtin_ctzll(~mask)));
+    fl = wave_or(fl);
+    int32_t* out = P.out_tokens + static_cast<size_t>(b) * (P.G + 1);
+    if (i <= P.G) out[i] = i < m ? d : (i == m ? s_arg[m] : -1);
+    if (i == 0) {
+        P.accept_count[b] = m;
+        if (P.flags) P.flags[b] = fl;
     }
 }
 
 // ------------------------------------------------------------------ host side
 
 struct Layout {
-    int rows, nc, chunk, nc2, chunk2;
-    size_t off_cnt1, off_cnt2, off_part, off_rowstat, off_csum, total;
+    int rows, nc, chunk, nc2, chunk2, wpr, cpw;
+    size_t off_cnt, off_part, off_csum, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -580,8 +745,11 @@ int env_int(const char* name, int dflt) {
 
 bool valid_desc(const specdec_verify_desc_t* d) {
     if (!d) return false;
-    if (d->batch < 0 || d->batch > 65535 || d->gamma_max < 0 || d->gamma_max > 63 || d->vocab < 1) return false;
+    if (d->batch < 0 || d->batch > 65535 || d->gamma_max < 0 || d->gamma_max > 63 || d->vocab < 1)
+        return false;
     if (d->dtype != SPECDEC_F32 && d->dtype != SPECDEC_BF16) return false;
+    // at most 1024 sampling chunks of 256 lanes x 2 x 16 bytes per row
+    if (d->vocab > 1024 * kThreads * kUnroll2 * (d->dtype == SPECDEC_BF16 ? 8 : 4)) return false;
     if (d->mode != SPECDEC_SAMPLE && d->mode != SPECDEC_GREEDY) return false;
     if (d->reserved != 0) return false;
     if (d->mode == SPECDEC_SAMPLE) {
@@ -593,67 +761,79 @@ bool valid_desc(const specdec_verify_desc_t* d) {
     return true;
 }
 
+// Chunking.  Statistics pass: about one round of workgroups resident at once
+// (8 per CU x 256 CUs), so that every workgroup streams from the start and
+// none waits for a slot; whole tiles per chunk.  Sampling pass: one tile of
+// 256 lanes x 2 vectors per chunk (at most 1024 per row), and about 512
+// workgroups in all, each taking a run of consecutive chunks of one request.
 Layout make_layout(const specdec_verify_desc_t* d) {
     Layout L{};
     const bool bf16 = d->dtype == SPECDEC_BF16;
     const int n = bf16 ? 8 : 4;
     const int tile = kThreads * n * kUnroll;
-    const int tiles = env_int("SPECDEC_STATS_TILES", 2);
+    const int vt = (d->vocab + tile - 1) / tile;
     L.rows = d->mode == SPECDEC_SAMPLE ? 2 * d->gamma_max + 1 : d->gamma_max + 1;
+    const double rows_total = static_cast<double>(d->batch > 0 ? d->batch : 1) * L.rows;
+    int nc_want = static_cast<int>(2048.0 / rows_total);
+    nc_want = nc_want < 1 ? 1 : nc_want;
+    int tiles = (vt + nc_want - 1) / nc_want;
+    tiles = env_int("SPECDEC_STATS_TILES", tiles < 1 ? 1 : tiles);
+    // the decision kernels stage rows x chunks partials in LDS
+    while (static_cast<long>(L.rows) * ((vt + tiles - 1) / tiles) > kMaxPart) ++tiles;
     L.chunk = tile * tiles;
     L.nc = (d->vocab + L.chunk - 1) / L.chunk;
-    // sampling pass: chunks of 2 tiles of 256 x 16 B, at most 1024 of them
-    const int tile2 = kThreads * n;
-    L.chunk2 = tile2 * env_int("SPECDEC_SAMPLE_TILES", 2);
-    while ((d->vocab + L.chunk2 - 1) / L.chunk2 > 1024) L.chunk2 *= 2;
+    L.chunk2 = kThreads * n * kUnroll2;
     L.nc2 = (d->vocab + L.chunk2 - 1) / L.chunk2;
+    // sampling pass: about two workgroups per CU, all resident from the start
+    const int bb = d->batch > 0 ? d->batch : 1;
+    int wpr = static_cast<int>(512.0 / bb + 0.5);
+    wpr = env_int("SPECDEC_SAMPLE_WPR", wpr < 1 ? 1 : (wpr > L.nc2 ? L.nc2 : wpr));
+    L.cpw = (L.nc2 + wpr - 1) / wpr;
+    L.wpr = (L.nc2 + L.cpw - 1) / L.cpw;
     const size_t B = static_cast<size_t>(d->batch);
     size_t off = 0;
-    L.off_cnt1 = off; off = align256(off + B * 4);
-    L.off_cnt2 = off; off = align256(off + B * 4);
+    L.off_cnt = off; off = align256(off + B * 4);
     L.off_part = off; off = align256(off + B * L.rows * L.nc * sizeof(float4));
-    L.off_rowstat = off; off = align256(off + B * L.rows * sizeof(float2));
-    L.off_csum = off; off = align256(off + B * L.nc2 * sizeof(float));
+    L.off_csum = off; off = align256(off + B * L.nc2 * sizeof(uint32_t));
     L.total = off;
     return L;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Launch the passes of one call.  ev (may be null) holds start/stop events of
+// the statistics pass and of the sampling pass; they bracket the kernels
+// themselves (hipExtLaunchKernel), not the host-side enqueue.
 template <bool BF16, bool VEC>
 specdec_status_t launch_all(const specdec_verify_desc_t* d, const VerifyParams& P, const Layout& L,
-                            hipStream_t stream) {
+                            hipStream_t stream, hipEvent_t* ev) {
     const dim3 block(kThreads);
+    hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
+    hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
+    auto launch = [&](auto kernel, dim3 grid, hipEvent_t start, hipEvent_t stop) {
+        if (ev)
+            hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, start, stop, 0, P);
+        else
+            hipLaunchKernelGGL(kernel, grid, block, 0, stream, P);
+    };
     if (d->mode == SPECDEC_GREEDY) {
-        const dim3 grid(L.nc, d->gamma_max + 1, d->batch);
-        hipLaunchKernelGGL((k_stats_greedy<BF16, VEC>), grid, block, 0, stream, P);
-    } else {
-        const dim3 grid(L.nc, 2 * d->gamma_max + 1, d->batch);
-        hipLaunchKernelGGL((k_stats_sample<BF16, VEC>), grid, block, 0, stream, P);
+        launch(k_stats<BF16, VEC, true>, dim3(L.nc, L.rows, d->batch), e0, e1);
         if (hipGetLastError() != hipSuccess) return SPECDEC_ERR_DEVICE;
-        const dim3 grid2(L.nc2, d->batch);
-        hipLaunchKernelGGL((k_sample<BF16, VEC>), grid2, block, 0, stream, P);
+        launch(k_decide_greedy, dim3(d->batch), e2, e3);
+    } else {
+        launch(k_stats<BF16, VEC, false>, dim3(L.nc, L.rows, d->batch), e0, e1);
+        if (hipGetLastError() != hipSuccess) return SPECDEC_ERR_DEVICE;
+        launch(k_decide_sample<BF16, VEC>, dim3(L.wpr, d->batch), e2, e3);
     }
     return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_DEVICE;
 }
 
-}  // namespace
-}  // namespace specdec
-
-using namespace specdec;
-
-extern "C" size_t specdec_verify_workspace_bytes(const specdec_verify_desc_t* desc) {
-    if (!valid_desc(desc)) return 0;
-    return make_layout(desc).total;
-}
-
-extern "C" specdec_status_t specdec_verify(const specdec_verify_desc_t* d,
-                                           const void* target_logits, const void* draft_logits,
-                                           const int32_t* draft_tokens, const int32_t* gamma,
-                                           int32_t* accept_count, int32_t* out_tokens,
-                                           float* p_draft, float* q_draft, float* residual_mass,
-                                           uint32_t* flags, void* workspace,
-                                           size_t workspace_bytes, hipStream_t stream) {
+specdec_status_t verify_impl(const specdec_verify_desc_t* d, const void* target_logits,
+                             const void* draft_logits, const int32_t* draft_tokens,
+                             const int32_t* gamma, int32_t* accept_count, int32_t* out_tokens,
+                             float* p_draft, float* q_draft, float* residual_mass, uint32_t* flags,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream,
+                             hipEvent_t* ev) {
     if (!valid_desc(d)) return SPECDEC_ERR_INVALID_ARGUMENT;
     const bool sample = d->mode == SPECDEC_SAMPLE;
     if (!target_logits || !accept_count || !out_tokens || !workspace)
@@ -678,11 +858,9 @@ extern "C" specdec_status_t specdec_verify(const specdec_verify_desc_t* d,
     P.residual_mass = residual_mass;
     P.flags = flags;
     char* ws = static_cast<char*>(workspace);
-    P.cnt1 = reinterpret_cast<uint32_t*>(ws + L.off_cnt1);
-    P.cnt2 = reinterpret_cast<uint32_t*>(ws + L.off_cnt2);
+    P.cnt = reinterpret_cast<uint32_t*>(ws + L.off_cnt);
     P.part = reinterpret_cast<float4*>(ws + L.off_part);
-    P.rowstat = reinterpret_cast<float2*>(ws + L.off_rowstat);
-    P.csum = reinterpret_cast<float*>(ws + L.off_csum);
+    P.csum = reinterpret_cast<uint32_t*>(ws + L.off_csum);
     P.B = d->batch;
     P.G = d->gamma_max;
     P.V = d->vocab;
@@ -691,6 +869,8 @@ extern "C" specdec_status_t specdec_verify(const specdec_verify_desc_t* d,
     P.chunk = L.chunk;
     P.nc2 = L.nc2;
     P.chunk2 = L.chunk2;
+    P.wpr = L.wpr;
+    P.cpw = L.cpw;
     P.c = sample ? static_cast<float>(1.4426950408889634 / static_cast<double>(d->temperature)) : 1.0f;
     P.key0 = static_cast<uint32_t>(d->seed & 0xffffffffu);
     P.key1 = static_cast<uint32_t>(d->seed >> 32);
@@ -700,6 +880,41 @@ extern "C" specdec_status_t specdec_verify(const specdec_verify_desc_t* d,
     const size_t es = bf16 ? 2 : 4;
     const bool vec = aligned16(target_logits) && (!sample || aligned16(draft_logits)) &&
                      (static_cast<size_t>(d->vocab) * es) % 16 == 0;
-    if (bf16) return vec ? launch_all<true, true>(d, P, L, stream) : launch_all<true, false>(d, P, L, stream);
-    return vec ? launch_all<false, true>(d, P, L, stream) : launch_all<false, false>(d, P, L, stream);
+    if (bf16)
+        return vec ? launch_all<true, true>(d, P, L, stream, ev)
+                   : launch_all<true, false>(d, P, L, stream, ev);
+    return vec ? launch_all<false, true>(d, P, L, stream, ev)
+               : launch_all<false, false>(d, P, L, stream, ev);
+}
+
+}  // namespace
+}  // namespace specdec
+
+using namespace specdec;
+
+extern "C" size_t specdec_verify_workspace_bytes(const specdec_verify_desc_t* desc) {
+    if (!valid_desc(desc)) return 0;
+    return make_layout(desc).total;
+}
+
+extern "C" specdec_status_t specdec_verify(const specdec_verify_desc_t* d,
+                                           const void* target_logits, const void* draft_logits,
+                                           const int32_t* draft_tokens, const int32_t* gamma,
+                                           int32_t* accept_count, int32_t* out_tokens,
+                                           float* p_draft, float* q_draft, float* residual_mass,
+                                           uint32_t* flags, void* workspace,
+                                           size_t workspace_bytes, hipStream_t stream) {
+    return verify_impl(d, target_logits, draft_logits, draft_tokens, gamma, accept_count,
+                       out_tokens, p_draft, q_draft, residual_mass, flags, workspace,
+                       workspace_bytes, stream, nullptr);
+}
+
+extern "C" specdec_status_t specdec_verify_profiled(
+    const specdec_verify_desc_t* d, const void* target_logits, const void* draft_logits,
+    const int32_t* draft_tokens, const int32_t* gamma, int32_t* accept_count,
+    int32_t* out_tokens, float* p_draft, float* q_draft, float* residual_mass, uint32_t* flags,
+    void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* stage_events) {
+    return verify_impl(d, target_logits, draft_logits, draft_tokens, gamma, accept_count,
+                       out_tokens, p_draft, q_draft, residual_mass, flags, workspace,
+                       workspace_bytes, stream, stage_events);
 }

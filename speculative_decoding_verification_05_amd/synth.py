@@ -316,5 +316,6 @@ def logits_bytes(wl: Workload, gamma: Optional[Sequence[int]] = None) -> int:
         gamma = [wl.gamma_max] * wl.batch
     rows = 0
     for g in gamma:
+        g = int(g)
         rows += (g + 1) + (g if wl.mode == "sample" else 0)
-    return rows * wl.vocab * wl.elem_bytes
+    return int(rows) * int(wl.vocab) * int(wl.elem_bytes)
