@@ -74,6 +74,7 @@ typedef enum specdec_mode { SPECDEC_SAMPLE = 0, SPECDEC_GREEDY = 1 } specdec_mod
 #define SPECDEC_FLAG_TOKEN_RANGE       0x8u  /* a draft token outside [0,V): rejected */
 #define SPECDEC_FLAG_BAD_BLOCK         0x10u /* commit: window not committable, slot(s) skipped */
 #define SPECDEC_FLAG_BAD_GAMMA         0x20u /* verify: gamma_b outside [0,G], clamped into it */
+#define SPECDEC_FLAG_TRUNC_OVERFLOW    0x40u /* verify: a kept set exceeded 1024 tokens (ties): clipped */
 
 /* ------------------------------------------------------------------ verify */
 
@@ -130,8 +131,16 @@ size_t specdec_verify_workspace_bytes(const specdec_verify_desc_t* desc);
  *   logits, lowest index on ties); the token at m is the argmax of row m.
  * Errors: INVALID_ARGUMENT for a bad descriptor or a NULL required pointer;
  *   WORKSPACE_TOO_SMALL if workspace_bytes < specdec_verify_workspace_bytes;
- *   UNSUPPORTED for top_k != 0 or top_p < 1 (truncation is not built yet).
- *   In each case nothing is enqueued. */
+ *   UNSUPPORTED, in SAMPLE mode with truncation (0 < top_k < V, or
+ *   top_p < 1), when V exceeds 16384 16-byte vectors (131072 bf16 / 65536
+ *   fp32 logits), when top_k > 1024, or for top_p < 1 without an effective
+ *   top_k on a vocabulary above 2048.  In each case nothing is enqueued.
+ * Truncation: top-k keeps every token whose raw logit is >= the k-th largest
+ *   raw logit (ties kept); top-p then keeps the shortest prefix, in order of
+ *   raw logit descending and token index ascending, whose cumulative
+ *   probability under softmax(z/T) over the top-k set reaches top_p.  p and q
+ *   are softmax(z/T) renormalised over their own kept sets, and both the
+ *   acceptance test and the residual use them. */
 specdec_status_t specdec_verify(const specdec_verify_desc_t* desc,
                                 const void* target_logits, const void* draft_logits,
                                 const int32_t* draft_tokens, const int32_t* gamma,

@@ -29,6 +29,7 @@ FLAG_NONFINITE = 0x4
 FLAG_TOKEN_RANGE = 0x8
 FLAG_BAD_BLOCK = 0x10
 FLAG_BAD_GAMMA = 0x20
+FLAG_TRUNC_OVERFLOW = 0x40
 
 # exported symbols of include/specdec.h
 EXPORTS = ("specdec_verify_workspace_bytes", "specdec_verify", "specdec_verify_profiled",

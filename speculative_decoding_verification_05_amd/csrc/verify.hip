@@ -33,8 +33,7 @@
 //                    partials, the argmax-equality prefix and every output.
 // The only cross-workgroup hand-off (chunk masses inside k_decide_sample)
 // uses device-scope atomics; nothing ever waits on another workgroup.
-#include "specdec.h"
-#include "specdec_device.h"
+#include "verify_internal.h"
 
 #include <hip/hip_ext.h>
 #include <stdint.h>
@@ -42,86 +41,6 @@
 
 namespace specdec {
 namespace {
-
-constexpr int kUnroll = 4;    // 16-byte vectors per lane per tile, statistics pass
-constexpr int kUnroll2 = 2;   // per row per tile, sampling pass
-constexpr int kMaxPart = 512; // partials per request the decision kernels stage in LDS
-
-struct VerifyParams {
-    const void* target;
-    const void* draft;
-    const int32_t* tokens;
-    const int32_t* gamma;
-    int32_t* accept_count;
-    int32_t* out_tokens;
-    float* p_draft;
-    float* q_draft;
-    float* residual_mass;
-    uint32_t* flags;
-    // workspace
-    float4* part;       // [B][R][nc] chunk partials, R = 2G+1 (sample) or G+1 (greedy)
-    uint32_t* cnt;      // [B] arrivals in the sampling pass
-    uint32_t* csum;     // [B][nc2] chunk masses of the sampling pass (float bits)
-    int B, G, V;
-    int rows;           // R
-    int nc, chunk;      // statistics pass: chunks per row, elements per chunk
-    int nc2, chunk2;    // sampling pass: chunks per row, elements per chunk (one tile)
-    int wpr, cpw;       // sampling pass: workgroups per request, chunks per workgroup
-    float c;            // log2(e) / T
-    uint32_t key0, key1, round;
-};
-
-// gamma_b clamped into [0, G] (an out-of-range value is flagged by the
-// decision step), so no row past the padded layout is ever addressed.
-__device__ __forceinline__ int request_gamma(const VerifyParams& P, int b) {
-    const int g = P.gamma ? P.gamma[b] : P.G;
-    return min(max(g, 0), P.G);
-}
-
-__device__ __forceinline__ uint32_t gamma_flag(const VerifyParams& P, int b) {
-    const int g = P.gamma ? P.gamma[b] : P.G;
-    return (g < 0 || g > P.G) ? SPECDEC_FLAG_BAD_GAMMA : 0u;
-}
-
-__device__ __forceinline__ const void* row_ptr(const void* base, size_t row, int V, bool bf16) {
-    return static_cast<const char*>(base) + row * static_cast<size_t>(V) * (bf16 ? 2 : 4);
-}
-
-__device__ __forceinline__ const void* target_row(const VerifyParams& P, int b, int i, bool bf16) {
-    return row_ptr(P.target, static_cast<size_t>(b) * (P.G + 1) + i, P.V, bf16);
-}
-
-__device__ __forceinline__ const void* draft_row(const VerifyParams& P, int b, int i, bool bf16) {
-    return row_ptr(P.draft, static_cast<size_t>(b) * P.G + i, P.V, bf16);
-}
-
-// Cross-workgroup hand-off.  A device-scope fence costs an L2 write-back and
-// invalidate, and those serialise per XCD (measured: ~0.4 us each, which made
-// a fence per workgroup dominate a pass).  Instead, the words another
-// workgroup must read are published with device-scope atomic exchanges and
-// read back with atomic read-modify-writes; both are performed at the
-// device's coherence point, so no cache maintenance is needed.  The arrival
-// increment uses an address that depends on the exchanges' returned values
-// (through an empty asm statement the optimiser cannot see through), so it is
-// issued only once the published words have landed.
-__device__ __forceinline__ uint32_t publish(uint32_t* p, uint32_t v) { return atomicExch(p, v); }
-__device__ __forceinline__ uint32_t fetch(uint32_t* p) { return atomicOr(p, 0u); }
-
-// Arrival at a per-request counter; lane 0 passes the OR of its publish()
-// results as `dep`.  Returns true (to every lane) in the last workgroup to
-// arrive, which may then fetch() what the others published.
-__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t total, uint32_t dep) {
-    __shared__ int s_last;
-    if (threadIdx.x == 0) {
-        uint32_t zero = 0u;
-        asm volatile("" : "+v"(zero) : "v"(dep));
-        const uint32_t old = atomicAdd(counter + zero, 1u);
-        s_last = (old == total - 1);
-        if (s_last) atomicExch(counter, 0u);  // ready for the next call
-    }
-    __syncthreads();
-    return s_last;
-}
 
 // ------------------------------------------------------------------ streaming
 
@@ -203,19 +122,6 @@ __device__ __forceinline__ ArgMax block_argmax(ArgMax v) {
     ArgMax r{s_v[0], s_i[0]};
 #pragma unroll
     for (int k = 1; k < kWaves; ++k) r = better(r, ArgMax{s_v[k], s_i[k]});
-    return r;
-}
-
-__device__ __forceinline__ float block_sum(float v) {
-    __shared__ float s_v[kWaves];
-    v = wave_sum(v);
-    const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
-    __syncthreads();
-    if (l == 0) s_v[w] = v;
-    __syncthreads();
-    float r = s_v[0];
-#pragma unroll
-    for (int k = 1; k < kWaves; ++k) r += s_v[k];
     return r;
 }
 
@@ -731,8 +637,25 @@ __global__ __launch_bounds__(kThreads) void k_decide_greedy(VerifyParams P) {
 
 struct Layout {
     int rows, nc, chunk, nc2, chunk2, wpr, cpw;
-    size_t off_cnt, off_part, off_csum, total;
+    bool trunc;
+    size_t off_cnt, off_part, off_csum, off_nuc, total;
 };
+
+// Truncation mode: sampling with an effective top-k or with top-p.
+bool truncation_mode(const specdec_verify_desc_t* d) {
+    return d->mode == SPECDEC_SAMPLE &&
+           ((d->top_k > 0 && d->top_k < d->vocab) || d->top_p < 1.0f);
+}
+
+// Truncation requests this build cannot serve (see specdec.h).
+bool truncation_supported(const specdec_verify_desc_t* d) {
+    const int n = d->dtype == SPECDEC_BF16 ? 8 : 4;
+    const bool use_k = d->top_k > 0 && d->top_k < d->vocab;
+    if (d->vocab > kTruncVecs * kTruncThreads * n) return false;
+    if (use_k && d->top_k > 1024) return false;
+    if (!use_k && d->vocab > kTruncCap) return false;
+    return true;
+}
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -795,6 +718,9 @@ Layout make_layout(const specdec_verify_desc_t* d) {
     L.off_cnt = off; off = align256(off + B * 4);
     L.off_part = off; off = align256(off + B * L.rows * L.nc * sizeof(float4));
     L.off_csum = off; off = align256(off + B * L.nc2 * sizeof(uint32_t));
+    L.trunc = truncation_mode(d);
+    L.off_nuc = off;
+    if (L.trunc) off = align256(off + B * L.rows * (1 + kNucCap) * sizeof(uint2));
     L.total = off;
     return L;
 }
@@ -840,7 +766,7 @@ specdec_status_t verify_impl(const specdec_verify_desc_t* d, const void* target_
         return SPECDEC_ERR_INVALID_ARGUMENT;
     if (d->gamma_max > 0 && !draft_tokens) return SPECDEC_ERR_INVALID_ARGUMENT;
     if (sample && d->gamma_max > 0 && !draft_logits) return SPECDEC_ERR_INVALID_ARGUMENT;
-    if (sample && (d->top_k != 0 || d->top_p < 1.0f)) return SPECDEC_ERR_UNSUPPORTED;
+    if (truncation_mode(d) && !truncation_supported(d)) return SPECDEC_ERR_UNSUPPORTED;
     const Layout L = make_layout(d);
     if (workspace_bytes < L.total) return SPECDEC_ERR_WORKSPACE_TOO_SMALL;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return SPECDEC_ERR_INVALID_ARGUMENT;
@@ -861,6 +787,9 @@ specdec_status_t verify_impl(const specdec_verify_desc_t* d, const void* target_
     P.cnt = reinterpret_cast<uint32_t*>(ws + L.off_cnt);
     P.part = reinterpret_cast<float4*>(ws + L.off_part);
     P.csum = reinterpret_cast<uint32_t*>(ws + L.off_csum);
+    P.nuc = reinterpret_cast<uint2*>(ws + L.off_nuc);
+    P.top_k = d->top_k;
+    P.top_p = d->top_p;
     P.B = d->batch;
     P.G = d->gamma_max;
     P.V = d->vocab;
@@ -880,6 +809,7 @@ specdec_status_t verify_impl(const specdec_verify_desc_t* d, const void* target_
     const size_t es = bf16 ? 2 : 4;
     const bool vec = aligned16(target_logits) && (!sample || aligned16(draft_logits)) &&
                      (static_cast<size_t>(d->vocab) * es) % 16 == 0;
+    if (L.trunc) return launch_truncated(P, bf16, vec, stream, ev);
     if (bf16)
         return vec ? launch_all<true, true>(d, P, L, stream, ev)
                    : launch_all<true, false>(d, P, L, stream, ev);

@@ -1,0 +1,123 @@
+// Internal interface shared by the verify kernels (verify.hip) and the
+// truncation kernels (truncate.hip): the per-call parameter block and small
+// device helpers.  Not part of the public ABI.
+#pragma once
+
+#include "specdec.h"
+#include "specdec_device.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace specdec {
+
+constexpr int kUnroll = 4;        // 16-byte vectors per lane per tile, statistics pass
+constexpr int kUnroll2 = 2;       // per row per tile, sampling pass
+constexpr int kMaxPart = 512;     // partials per request the decision kernels stage in LDS
+constexpr int kTruncThreads = 1024;  // truncation pass: one workgroup per row
+constexpr int kTruncVecs = 16;    // 16-byte vectors per lane: rows of up to 16 x 1024 vectors
+constexpr int kTruncCap = 2048;   // candidate slots (LDS) of the truncation pass
+constexpr int kNucCap = 1024;     // kept tokens recorded per row
+
+
+
+struct VerifyParams {
+    const void* target;
+    const void* draft;
+    const int32_t* tokens;
+    const int32_t* gamma;
+    int32_t* accept_count;
+    int32_t* out_tokens;
+    float* p_draft;
+    float* q_draft;
+    float* residual_mass;
+    uint32_t* flags;
+    // workspace
+    float4* part;       // [B][R][nc] chunk partials, R = 2G+1 (sample) or G+1 (greedy)
+    uint32_t* cnt;      // [B] arrivals in the sampling pass
+    uint32_t* csum;     // [B][nc2] chunk masses of the sampling pass (float bits)
+    int B, G, V;
+    int rows;           // R
+    int nc, chunk;      // statistics pass: chunks per row, elements per chunk
+    int nc2, chunk2;    // sampling pass: chunks per row, elements per chunk (one tile)
+    int wpr, cpw;       // sampling pass: workgroups per request, chunks per workgroup
+    float c;            // log2(e) / T
+    uint32_t key0, key1, round;
+    // truncation (top-k / top-p) mode
+    int top_k;          // 0 or >= V: no top-k
+    float top_p;        // 1: no top-p
+    uint2* nuc;         // [B][R][1 + kNucCap] kept-token records
+};
+
+// gamma_b clamped into [0, G] (an out-of-range value is flagged by the
+// decision step), so no row past the padded layout is ever addressed.
+__device__ __forceinline__ int request_gamma(const VerifyParams& P, int b) {
+    const int g = P.gamma ? P.gamma[b] : P.G;
+    return min(max(g, 0), P.G);
+}
+
+__device__ __forceinline__ uint32_t gamma_flag(const VerifyParams& P, int b) {
+    const int g = P.gamma ? P.gamma[b] : P.G;
+    return (g < 0 || g > P.G) ? SPECDEC_FLAG_BAD_GAMMA : 0u;
+}
+
+__device__ __forceinline__ const void* row_ptr(const void* base, size_t row, int V, bool bf16) {
+    return static_cast<const char*>(base) + row * static_cast<size_t>(V) * (bf16 ? 2 : 4);
+}
+
+__device__ __forceinline__ const void* target_row(const VerifyParams& P, int b, int i, bool bf16) {
+    return row_ptr(P.target, static_cast<size_t>(b) * (P.G + 1) + i, P.V, bf16);
+}
+
+__device__ __forceinline__ const void* draft_row(const VerifyParams& P, int b, int i, bool bf16) {
+    return row_ptr(P.draft, static_cast<size_t>(b) * P.G + i, P.V, bf16);
+}
+
+// Cross-workgroup hand-off.  A device-scope fence costs an L2 write-back and
+// invalidate, and those serialise per XCD (measured: ~0.4 us each, which made
+// a fence per workgroup dominate a pass).  Instead, the words another
+// workgroup must read are published with device-scope atomic exchanges and
+// read back with atomic read-modify-writes; both are performed at the
+// device's coherence point, so no cache maintenance is needed.  The arrival
+// increment uses an address that depends on the exchanges' returned values
+// (through an empty asm statement the optimiser cannot see through), so it is
+// issued only once the published words have landed.
+__device__ __forceinline__ uint32_t publish(uint32_t* p, uint32_t v) { return atomicExch(p, v); }
+__device__ __forceinline__ uint32_t fetch(uint32_t* p) { return atomicOr(p, 0u); }
+
+// Arrival at a per-request counter; lane 0 passes the OR of its publish()
+// results as `dep`.  Returns true (to every lane) in the last workgroup to
+// arrive, which may then fetch() what the others published.
+__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t total, uint32_t dep) {
+    __shared__ int s_last;
+    if (threadIdx.x == 0) {
+        uint32_t zero = 0u;
+        asm volatile("" : "+v"(zero) : "v"(dep));
+        const uint32_t old = atomicAdd(counter + zero, 1u);
+        s_last = (old == total - 1);
+        if (s_last) atomicExch(counter, 0u);  // ready for the next call
+    }
+    __syncthreads();
+    return s_last;
+}
+
+// Sum over the kThreads lanes of a workgroup (same value returned to all).
+__device__ __forceinline__ float block_sum(float v) {
+    __shared__ float s_v[kWaves];
+    v = wave_sum(v);
+    const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+    __syncthreads();
+    if (l == 0) s_v[w] = v;
+    __syncthreads();
+    float r = s_v[0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) r += s_v[k];
+    return r;
+}
+
+// Truncation mode (top-k and/or top-p): one pass that selects and records
+// every used row's kept tokens, then the per-request decision over them.
+specdec_status_t launch_truncated(const VerifyParams& P, bool bf16, bool vec, hipStream_t stream,
+                                  hipEvent_t* ev);
+
+}  // namespace specdec

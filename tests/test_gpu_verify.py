@@ -197,3 +197,61 @@ def test_greedy_ragged_and_gamma_zero():
     x = synth.make_verify_inputs(wl)
     x["gamma"][::5] = 0
     check_greedy(wl, x, label="greedy ragged")
+
+
+# ------------------------------------------------------------ top-k / top-p
+
+@pytest.mark.parametrize("batch,vocab", [(12, 128256), (6, 10007), (8, 1500)])
+def test_truncation_recipe_sizes(batch, vocab):
+    """T=0.7, top-k 50 then top-p 0.9, Zipf-biased logits: several vocabularies,
+    including unaligned rows and one that fits the candidate buffer whole."""
+    check_sample(W["b128_g4_v128256_topk50_topp09"].scaled(batch, vocab))
+
+
+def test_truncation_full_size_sampled_requests():
+    """B=128, gamma=4, V=128256: the whole batch on the GPU, 16 requests on the oracle."""
+    wl = W["b128_g4_v128256_topk50_topp09"]
+    x = synth.make_verify_inputs(wl)
+    req = np.random.default_rng(6).choice(wl.batch, 16, replace=False)
+    check_sample(wl, x, requests=req, label="top-k/top-p full (16 sampled requests)")
+
+
+@pytest.mark.parametrize("top_k,top_p", [(50, 1.0), (1, 1.0), (1024, 0.95), (0, 0.8), (3000, 0.5)])
+def test_truncation_parameter_edges(top_k, top_p):
+    """top-k only, k=1 (greedy-like), the largest k, top-p alone on a small
+    vocabulary, and k >= V (top-k off)."""
+    vocab = 2000 if top_k in (0, 3000) else 40000
+    wl = W["b128_g4_v128256_topk50_topp09"].scaled(10, vocab, top_k=top_k, top_p=top_p)
+    check_sample(wl)
+
+
+def test_truncation_ties_at_the_kth_value():
+    """Several logits equal to the k-th largest: all of them are kept."""
+    wl = W["b128_g4_v128256_topk50_topp09"].scaled(8, 30000, top_p=1.0)
+    x = synth.make_verify_inputs(wl)
+    for arr in (x["target"], x["draft"]):
+        for b in range(8):
+            for i in range(arr.shape[1]):
+                row = arr[b, i]
+                if row[0] == synth.BF16_QNAN:
+                    continue
+                v = synth.bf16_bits_to_f32(row)
+                order = np.argsort(-v, kind="stable")
+                row[order[50:56]] = row[order[49]]
+    check_sample(wl, x, label="ties at the k-th value")
+
+
+def test_truncation_unsupported_shapes_are_rejected():
+    import torch
+    B, G = 2, 2
+    for vocab, top_k, top_p in ((200000, 50, 0.9), (50000, 2000, 1.0), (5000, 0, 0.9)):
+        desc = sd.make_verify_desc(B, G, vocab, temperature=1.0, top_k=top_k, top_p=top_p)
+        ws = torch.zeros(sd.specdec_verify_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+        t = torch.zeros(B, G + 1, vocab, dtype=torch.int16, device="cuda")
+        d = torch.zeros(B, G, vocab, dtype=torch.int16, device="cuda")
+        tok = torch.zeros(B, G, dtype=torch.int32, device="cuda")
+        acc = torch.zeros(B, dtype=torch.int32, device="cuda")
+        out = torch.zeros(B, G + 1, dtype=torch.int32, device="cuda")
+        with pytest.raises(sd.SpecdecError) as e:
+            sd.specdec_verify(desc, t, d, tok, None, acc, out, None, None, None, None, ws)
+        assert e.value.status == sd.SPECDEC_ERR_UNSUPPORTED
