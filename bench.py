@@ -45,6 +45,29 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
+def measured_traffic(kernel_workload: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary, or None if there is none or the kernel sources have
+    changed since the counters were taken (sha256 recorded with them)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel_workload}__pmc_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if "kernel_source_sha256" not in fields or "traffic_bytes_per_launch" not in fields:
+        return None
+    h = hashlib.sha256()
+    for f in fields["kernel_sources"].split():
+        h.update(open(os.path.join(ROOT, "speculative_decoding_verification_05_amd", "csrc", f), "rb").read())
+    if h.hexdigest() != fields["kernel_source_sha256"]:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -56,6 +79,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches, no graph")
+    ap.add_argument("--pmc-copy-mib", type=int, default=0,
+                    help="first run one device-to-device copy of this many MiB (a dispatch of "
+                         "known size to calibrate FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -74,6 +100,14 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     sd.lib()
+    if args.pmc_copy_mib:
+        src = torch.ones(args.pmc_copy_mib << 18, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {args.pmc_copy_mib} MiB read + {args.pmc_copy_mib} MiB written")
+        del src, dst
     wl0 = synth.WORKLOADS[args.workload or synth.HEADLINE]
     greedy = wl0.mode == "greedy"
     bf16 = wl0.dtype == "bf16"
@@ -263,8 +297,10 @@ def main() -> int:
                    "committed_tokens_per_s": committed / sec_per_step,
                    "step_GBps": alg_k1 / sec_per_step / 1e9},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "kernel": "k_stats_greedy" if greedy else "k_stats_sample",
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(f"k_stats_sample__{wl0.name}") if not greedy else None,
+                     "kernel": ("k_stats_greedy" if greedy else
+                                "k_truncate" if (wl0.top_k or wl0.top_p < 1.0) else "k_stats_sample"),
                      "kernel_avg_us": k1_avg * 1e6, "bytes_per_launch": alg_k1},
         "cpu_baseline": cpu,
     }
