@@ -132,8 +132,7 @@ size_t specdec_verify_workspace_bytes(const specdec_verify_desc_t* desc);
  * Errors: INVALID_ARGUMENT for a bad descriptor or a NULL required pointer;
  *   WORKSPACE_TOO_SMALL if workspace_bytes < specdec_verify_workspace_bytes;
  *   UNSUPPORTED, in SAMPLE mode with truncation (0 < top_k < V, or
- *   top_p < 1), when V exceeds 16384 16-byte vectors (131072 bf16 / 65536
- *   fp32 logits), when top_k > 1024, or for top_p < 1 without an effective
+ *   top_p < 1), when top_k > 1024, or for top_p < 1 without an effective
  *   top_k on a vocabulary above 2048.  In each case nothing is enqueued.
  * Truncation: top-k keeps every token whose raw logit is >= the k-th largest
  *   raw logit (ties kept); top-p then keeps the shortest prefix, in order of

@@ -649,10 +649,8 @@ bool truncation_mode(const specdec_verify_desc_t* d) {
 
 // Truncation requests this build cannot serve (see specdec.h).
 bool truncation_supported(const specdec_verify_desc_t* d) {
-    const int n = d->dtype == SPECDEC_BF16 ? 8 : 4;
     const bool use_k = d->top_k > 0 && d->top_k < d->vocab;
-    if (d->vocab > kTruncVecs * kTruncThreads * n) return false;
-    if (use_k && d->top_k > 1024) return false;
+    if (use_k && d->top_k > kNucCap) return false;
     if (!use_k && d->vocab > kTruncCap) return false;
     return true;
 }

@@ -14,10 +14,8 @@ namespace specdec {
 constexpr int kUnroll = 4;        // 16-byte vectors per lane per tile, statistics pass
 constexpr int kUnroll2 = 2;       // per row per tile, sampling pass
 constexpr int kMaxPart = 512;     // partials per request the decision kernels stage in LDS
-constexpr int kTruncThreads = 1024;  // truncation pass: one workgroup per row
-constexpr int kTruncVecs = 16;    // 16-byte vectors per lane: rows of up to 16 x 1024 vectors
-constexpr int kTruncCap = 2048;   // candidate slots (LDS) of the truncation pass
-constexpr int kNucCap = 1024;     // kept tokens recorded per row
+constexpr int kTruncCap = 2048;   // vocabulary limit of top-p without an effective top-k
+constexpr int kNucCap = 1024;     // kept tokens recorded per row (and the top-k limit)
 
 
 

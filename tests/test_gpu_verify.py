@@ -225,6 +225,42 @@ def test_truncation_parameter_edges(top_k, top_p):
     check_sample(wl)
 
 
+def test_truncation_large_vocabulary():
+    """Truncation on a 262144-token vocabulary (the ragged recipe's rows)."""
+    wl = W["b512_ragged_v262144_kv"].scaled(6, top_k=50, top_p=0.9)
+    check_sample(wl)
+
+
+def test_truncation_loose_bound_takes_the_exact_search():
+    """A first tile far below the rest of the row makes the lower bound from
+    the first tile useless: the candidate buffer overflows and the k-th value
+    is found by the exact bitwise search instead."""
+    wl = W["b128_g4_v128256_topk50_topp09"].scaled(4, 40000)
+    x = synth.make_verify_inputs(wl)
+    for arr in (x["target"], x["draft"]):
+        vals = synth.bf16_bits_to_f32(arr)
+        keep = arr == synth.BF16_QNAN
+        vals[:, :, :8192] -= np.float32(40.0)
+        arr[:] = synth.f32_to_bf16_bits(vals)
+        arr[keep] = synth.BF16_QNAN
+    check_sample(wl, x, label="loose first-tile bound")
+
+
+def test_truncation_oversized_kept_set_is_flagged():
+    """Thousands of logits tied at the top: the kept set exceeds the 1024
+    recorded tokens; the request is flagged (documented limit)."""
+    wl = W["b128_g4_v128256_topk50_topp09"].scaled(2, 20000, top_p=1.0)
+    x = synth.make_verify_inputs(wl)
+    rng = np.random.default_rng(8)
+    for arr in (x["target"], x["draft"]):
+        keep = arr == synth.BF16_QNAN
+        arr[:] = synth.f32_to_bf16_bits(rng.integers(0, 3, arr.shape).astype(np.float32))
+        arr[keep] = synth.BF16_QNAN
+    got = gpu_verify(x, bf16=True, temperature=wl.temperature, top_k=wl.top_k, top_p=wl.top_p,
+                     seed=wl.verify_seed)
+    assert np.all(got["flags"] & sd.FLAG_TRUNC_OVERFLOW)
+
+
 def test_truncation_ties_at_the_kth_value():
     """Several logits equal to the k-th largest: all of them are kept."""
     wl = W["b128_g4_v128256_topk50_topp09"].scaled(8, 30000, top_p=1.0)
@@ -244,7 +280,7 @@ def test_truncation_ties_at_the_kth_value():
 def test_truncation_unsupported_shapes_are_rejected():
     import torch
     B, G = 2, 2
-    for vocab, top_k, top_p in ((200000, 50, 0.9), (50000, 2000, 1.0), (5000, 0, 0.9)):
+    for vocab, top_k, top_p in ((50000, 2000, 1.0), (5000, 0, 0.9)):
         desc = sd.make_verify_desc(B, G, vocab, temperature=1.0, top_k=top_k, top_p=top_p)
         ws = torch.zeros(sd.specdec_verify_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
         t = torch.zeros(B, G + 1, vocab, dtype=torch.int16, device="cuda")
