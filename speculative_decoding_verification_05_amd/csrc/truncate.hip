@@ -14,22 +14,23 @@
 //   then p (or q) is softmax(z/T) restricted to, and renormalised over, what
 //   is kept.  Target and draft rows are filtered independently.
 //
-// k_trunc_select  one 256-lane workgroup per used row.  One full streaming
-//                 read keeps, per lane, the maximum of each of 8 slots of
-//                 consecutive tiles; the k-th largest of the 256 lane maxima
-//                 is a lower bound on the row's k-th largest logit (they are
-//                 distinct elements of the row).  Only the lane-slots whose
-//                 maximum reaches the bound are read again (a few percent of
-//                 the row, from cache), their elements at or above the bound
-//                 are appended to an LDS buffer with wave ballots (a few dozen
-//                 of 128K for the tested shapes), and the buffer is
-//                 bitonic-sorted by (logit desc, index asc) and
-//                 cut to the exact top-k set (ties kept) and then to the top-p
-//                 prefix.  The kept tokens are recorded sorted by token index
-//                 with their weights 2^((z - max) c) and the kept total.  If
-//                 the buffer overflows (very flat rows, heavy ties) the k-th
-//                 value is found exactly by a bitwise search over re-reads of
-//                 the row instead.
+// k_trunc_select  one 256-lane workgroup per used row, one streaming read of
+//                 the row.  Each lane keeps the four largest of its per-tile
+//                 maxima (the maximum of its 32 elements of a tile) with
+//                 their tiles: distinct elements of the row, so the k-th
+//                 largest of these 1024 values bounds the row's k-th largest
+//                 logit from below, and every element at or above that bound
+//                 lies in one of its lane's top-three tiles (or the lane's
+//                 fourth maximum reaches the bound too, and its whole share
+//                 is read again).  Those tiles (a few percent of the row) are
+//                 read again and their elements at or above the bound go to
+//                 per-wave LDS regions: a few dozen of 128K tokens for the
+//                 tested shapes.  One wave then ranks them by (logit desc,
+//                 index asc), keeps the exact top-k set (ties kept) and the
+//                 top-p prefix, and records the kept tokens sorted by index
+//                 with their weights 2^((z - max) c) and the kept total
+//                 (longer lists go through LDS bitonic sorts; lists past the
+//                 LDS capacity through an exact bitwise search over re-reads).
 // k_decide_trunc  one workgroup per request: p(d_i), q(d_i) from the records,
 //                 the acceptance tests, m, then the inverse CDF of the
 //                 residual (or bonus) over the short kept list in ascending
@@ -38,12 +39,13 @@
 
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 namespace specdec {
 namespace {
 
 constexpr int kSelCap = 2048;                 // LDS candidate slots per row
-constexpr int kSlots = 8;                     // per-lane tile-slot maxima of the first read
-constexpr int kMaxTps = 2;                    // tiles re-read per batch
+constexpr int kWaveCap = kSelCap / kWaves;   // each wave's region of them
 constexpr uint32_t kRowOverflow = 1u << 16;   // record header: kept set clipped
 constexpr uint32_t kRowNonfinite = 1u << 17;  // record header: NaN or +inf in the row
 
@@ -134,10 +136,52 @@ __device__ __forceinline__ void append_hits(bool hit, float x, int e, float* bz,
     }
 }
 
+// Element q of a 16-byte vector of bf16 or fp32 logits, widened to float.
+template <bool BF16>
+__device__ __forceinline__ float elem(const uint4& r, int q) {
+    if constexpr (BF16) {
+        const uint32_t w = q < 2 ? r.x : q < 4 ? r.y : q < 6 ? r.z : r.w;
+        return (q & 1) ? bf16_hi(w) : bf16_lo(w);
+    } else {
+        return __uint_as_float(q == 0 ? r.x : q == 1 ? r.y : q == 2 ? r.z : r.w);
+    }
+}
+
+// The 16-byte vector holding the values of v (which came from such a vector,
+// or are -inf).
+template <bool BF16>
+__device__ __forceinline__ uint4 narrow(const Vec<BF16>& v) {
+    if constexpr (BF16) {
+        auto pair = [&](int k) {
+            return (__float_as_uint(v.x[k]) >> 16) | (__float_as_uint(v.x[k + 1]) & 0xffff0000u);
+        };
+        return make_uint4(pair(0), pair(2), pair(4), pair(6));
+    } else {
+        return make_uint4(__float_as_uint(v.x[0]), __float_as_uint(v.x[1]),
+                          __float_as_uint(v.x[2]), __float_as_uint(v.x[3]));
+    }
+}
+
+// The 16-byte vector of elements [e, e+N) of a row clipped to [.., V),
+// -inf past V (load_vec's clamping, without widening).
+template <bool BF16, bool VEC>
+__device__ __forceinline__ uint4 load_raw(const void* rp, int e, int V) {
+    if constexpr (VEC) {
+        constexpr int N = Vec<BF16>::N;
+        const uint4 w = *reinterpret_cast<const uint4*>(
+            static_cast<const char*>(rp) + static_cast<size_t>(min(e, V - N)) * (BF16 ? 2 : 4));
+        const uint32_t f = BF16 ? 0xff80ff80u : 0xff800000u;
+        return e < V ? w : make_uint4(f, f, f, f);
+    } else {
+        return narrow<BF16>(load_vec<BF16, false>(rp, e, V, neg_inf()));
+    }
+}
+
 // One pass over a whole row in tiles of 256 lanes x kUnroll 16-byte vectors
 // (the next tile's loads in flight while the current one is visited), then
-// a clipped tail; f(v, t0) sees a lane's kUnroll vectors of the tile at t0
-// (vector u holds tokens t0 + (u * 256 + lane) * N ...).
+// a clipped tail filled with -inf; f(r, t0, full) sees a lane's kUnroll raw
+// vectors of the tile at t0 (vector u holds tokens t0 + (u * 256 + lane) * N
+// ...); `full` is std::true_type for tiles wholly inside the row.
 template <bool BF16, bool VEC, class F>
 __device__ __forceinline__ void stream_tiles(const void* rp, int V, F&& f) {
     constexpr int N = Vec<BF16>::N;
@@ -154,102 +198,110 @@ __device__ __forceinline__ void stream_tiles(const void* rp, int V, F&& f) {
             uint4 nxt[kUnroll];
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) nxt[u] = load16_stream<BF16>(rp, tn + (u * kThreads + t) * N);
-            Vec<BF16> v[kUnroll];
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) v[u] = widen<BF16>(cur[u]);
-            f(v, t0);
+            f(cur, t0, std::true_type{});
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) cur[u] = nxt[u];
         }
     }
     for (; t0 < V; t0 += TILE) {
-        Vec<BF16> v[kUnroll];
+        uint4 r[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-            v[u] = load_vec<BF16, VEC>(rp, t0 + (u * kThreads + t) * N, V, neg_inf());
-        f(v, t0);
+            r[u] = narrow<BF16>(load_vec<BF16, VEC>(rp, t0 + (u * kThreads + t) * N, V, neg_inf()));
+        f(r, t0, std::false_type{});
     }
 }
 
-// Largest number of set bits of `hits` in the workgroup (the re-read rounds).
-__device__ __forceinline__ int __reduce_max_hits(uint32_t hits) {
-    __shared__ int s_r;
-    if (threadIdx.x == 0) s_r = 0;
-    __syncthreads();
-    int c = __popc(hits);
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) c = max(c, __shfl_xor(c, o, kWave));
-    if (threadIdx.x % kWave == 0) atomicMax(&s_r, c);
-    __syncthreads();
-    return s_r;
-}
-
-// Sorting network step of a wave-wide bitonic sort held one entry per lane:
-// exchange with lane l ^ j, keeping the entry that belongs at this lane.
-template <class Before>
-__device__ __forceinline__ void wave_bitonic_step(float& z, int& id, int k, int j, Before before) {
-    const int l = threadIdx.x % kWave;
-    const float zp = __shfl_xor(z, j, kWave);
-    const int ip = __shfl_xor(id, j, kWave);
-    const bool up = (l & k) == 0;
-    const bool low = (l & j) == 0;
-    // the lower lane of an ascending (up) pair keeps the entry that comes first
-    const bool partner_first = before(zp, ip, z, id);
-    const bool take = (low == up) ? partner_first : before(z, id, zp, ip);
-    if (take) { z = zp; id = ip; }
-}
-
-// Candidates s_z/s_i[0..C), C <= 64, to the kept-token record, by one wave.
+// Candidates s_z/s_i[0..C), C <= 64, to the kept-token record, by one wave:
+// each candidate's rank by (logit desc, index asc) and by index, counted
+// against every other candidate read by broadcast from LDS (no sorting
+// network), a prefix of the weights in rank order the same way, and the kept
+// tokens placed by index rank.  s_z/s_i[64..192) serve as scratch.
 __device__ void select_in_wave(const VerifyParams& P, int b, int s, int C, bool use_k,
-                               const float* s_z, const int* s_i, uint32_t rowflags) {
+                               float* s_z, int* s_i, uint32_t rowflags) {
     const int l = threadIdx.x % kWave;
-    float z = l < C ? s_z[l] : neg_inf();
-    int id = l < C ? s_i[l] : 0x7fffffff;
-    auto by_logit = [](float za, int ia, float zb, int ib) { return precedes(za, ia, zb, ib); };
-    for (int k = 2; k <= kWave; k <<= 1)
-        for (int j = k >> 1; j > 0; j >>= 1) wave_bitonic_step(z, id, k, j, by_logit);
-    // lane l now holds the l-th entry by (logit desc, index asc)
+    const bool in = l < C;
+    const float z = in ? s_z[l] : neg_inf();
+    const int id = in ? s_i[l] : 0x7fffffff;
+    // sentinels past C, which precede nothing: whole float4 reads, no checks
+    if (l < 4) {
+        s_z[C + l] = neg_inf();
+        s_i[C + l] = 0x7fffffff;
+    }
+    int rank = 0, lower = 0;
+    for (int j0 = 0; j0 < C; j0 += 4) {
+        const float4 zj = *reinterpret_cast<const float4*>(s_z + j0);
+        const int4 ij = *reinterpret_cast<const int4*>(s_i + j0);
+        const float zz[4] = {zj.x, zj.y, zj.z, zj.w};
+        const int ii[4] = {ij.x, ij.y, ij.z, ij.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            rank += static_cast<int>((zz[k] > z) | ((zz[k] == z) & (ii[k] < id)));
+            lower += static_cast<int>(ii[k] < id);
+        }
+    }
+    auto lane_of = [&](bool pred) { return __builtin_ctzll(__ballot(pred)); };
     int K = C;
     if (use_k && P.top_k <= C) {
-        const float tau = __shfl(z, P.top_k - 1, kWave);
-        K = __popcll(__ballot(l < C && z >= tau));
+        const float tau = __shfl(z, lane_of(in && rank == P.top_k - 1), kWave);
+        K = __popcll(__ballot(in && z >= tau));
     }
-    const float M = __shfl(z, 0, kWave);
-    const float e = l < K ? exp2f((z - M) * P.c) : 0.0f;
-    float pre = e;  // inclusive prefix in that order
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const float y = __shfl_up(pre, o, kWave);
-        if (l >= o) pre += y;
+    const float M = __shfl(z, lane_of(in && rank == 0), kWave);
+    const float e = in && rank < K ? exp2f((z - M) * P.c) : 0.0f;
+    // inclusive prefix of the weights in rank order, summed in candidate
+    // order (monotone in rank: every term is non-negative)
+    float* s_e = s_z + 2 * kWave;
+    int* s_r = s_i + 2 * kWave;
+    s_e[l] = e;
+    s_r[l] = in ? rank : 0x7fffffff;
+    float pre = 0.0f;
+    for (int j0 = 0; j0 < C; j0 += 4) {
+        const float4 ej = *reinterpret_cast<const float4*>(s_e + j0);
+        const int4 rj = *reinterpret_cast<const int4*>(s_r + j0);
+        pre += rj.x <= rank ? ej.x : 0.0f;
+        pre += rj.y <= rank ? ej.y : 0.0f;
+        pre += rj.z <= rank ? ej.z : 0.0f;
+        pre += rj.w <= rank ? ej.w : 0.0f;
     }
     int Nk = K;
     if (P.top_p < 1.0f) {
-        const float goal = P.top_p * __shfl(pre, K - 1, kWave);
-        const uint64_t hit = __ballot(l < K && pre >= goal);
-        Nk = hit ? __builtin_ctzll(hit) + 1 : K;
+        const float goal = P.top_p * __shfl(pre, lane_of(in && rank == K - 1), kWave);
+        Nk = min(K, __popcll(__ballot(in && rank < K && pre < goal)) + 1);
     }
-    const float Sn = __shfl(pre, Nk - 1, kWave);
-    // the kept tokens by ascending index
-    float ek = l < Nk ? e : 0.0f;
-    int ik = l < Nk ? id : 0x7fffffff;
-    auto by_index = [](float, int ia, float, int ib) { return ia < ib; };
-    for (int k = 2; k <= kWave; k <<= 1)
-        for (int j = k >> 1; j > 0; j >>= 1) wave_bitonic_step(ek, ik, k, j, by_index);
+    const float Sn = __shfl(pre, lane_of(in && rank == Nk - 1), kWave);
+    // the kept tokens by ascending index: every candidate at its index rank,
+    // then the kept ones compacted in that order
+    const bool kept = in && rank < Nk;
+    if (in) {
+        s_i[kWave + lower] = kept ? id : -1;
+        s_z[kWave + lower] = e;
+    }
+    const int id2 = in ? s_i[kWave + l] : -1;
+    const float e2 = in ? s_z[kWave + l] : 0.0f;
+    const uint64_t km = __ballot(id2 >= 0);
     uint2* rec = row_record(P, b, s);
-    if (l < Nk) rec[1 + l] = make_uint2(static_cast<uint32_t>(ik), __float_as_uint(ek));
+    if (id2 >= 0)
+        rec[1 + __popcll(km & ((1ull << l) - 1ull))] = make_uint2(static_cast<uint32_t>(id2), __float_as_uint(e2));
     if (l == 0) rec[0] = make_uint2(static_cast<uint32_t>(Nk) | rowflags, __float_as_uint(Sn));
 }
 
-// ------------------------------------------------------------------ selection
+// Inverse of ordered_key, clamped to -inf below the key of -inf (never a NaN).
+__device__ __forceinline__ float key_value(uint32_t key) {
+    if (key < 0x007fffffu) return neg_inf();
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
 
 template <bool BF16, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_trunc_select(VerifyParams P) {
-    __shared__ float s_z[kSelCap];
-    __shared__ int s_i[kSelCap];
-    __shared__ float s_tm[kSlots * kThreads];
+    __shared__ __align__(16) float s_z[kSelCap];
+    __shared__ __align__(16) int s_i[kSelCap];
     __shared__ float s_wt[kWaves];
     __shared__ int s_count, s_cut;
+    __shared__ int s_cw[kWaves];
     constexpr int N = Vec<BF16>::N;
+    constexpr int TILE = kThreads * N * kUnroll;
+    // widened bf16 values share the low 16 key bits: searching the top 16 is exact
+    constexpr int LO = BF16 ? 16 : 0;
     const int s = blockIdx.x, b = blockIdx.y;
     const bool is_target = s <= P.G;
     const int i = is_target ? s : s - (P.G + 1);
@@ -257,117 +309,185 @@ __global__ __launch_bounds__(kThreads) void k_trunc_select(VerifyParams P) {
     if (is_target ? (i > g) : (i >= g)) return;  // padding row
     const void* rp = is_target ? target_row(P, b, i, BF16) : draft_row(P, b, i, BF16);
     const int V = P.V;
-    const int t = threadIdx.x;
+    const int t = threadIdx.x, w = t / kWave, l = t % kWave;
+    const uint64_t below = (1ull << l) - 1ull;
     const bool use_k = P.top_k > 0 && P.top_k < V;
-    uint64_t bad = 0;  // wave-uniform: a NaN or +inf was seen
 
-    // (1) the one full read: per lane, the maximum of each slot of
-    // consecutive tiles (kSlots slots per row, in LDS) and non-finite values;
-    // then the bound, the k-th largest lane maximum (k distinct elements of
-    // the row, so a lower bound on its k-th largest logit)
-    constexpr int TILE = kThreads * N * kUnroll;
-    const int ntiles = (V + TILE - 1) / TILE;
-    const int tps = (ntiles + kSlots - 1) / kSlots;  // tiles per slot
-    float run = neg_inf(), lm = neg_inf();
-    int cur_slot = 0;
-    auto tile_max = [&](const Vec<BF16> (&v)[kUnroll], int t0) {
-        const int slot = (t0 / TILE) / tps;
-        if (slot != cur_slot) {  // uniform: tiles are visited in order
-            s_tm[cur_slot * kThreads + t] = run;
-            run = neg_inf();
-            cur_slot = slot;
-        }
-        float m = neg_inf();
+    // (1) the one read.  Per lane, the four largest of its per-tile maxima
+    // (the maximum of the lane's kUnroll vectors of a tile) with the tiles
+    // they come from; they are distinct elements of the row.
+    float v1 = neg_inf(), v2 = neg_inf(), v3 = neg_inf(), v4 = neg_inf();
+    int t1 = -1, t2 = -1, t3 = -1, t4 = -1;
+    uint64_t bad = 0;  // wave-uniform: a NaN was seen
+    auto visit = [&](const uint4 (&r)[kUnroll], int t0, auto) {
+        float m = neg_inf();  // the tail is filled with -inf; NaNs are skipped
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int e0 = t0 + (u * kThreads + t) * N;
+        for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
-            for (int k = 0; k < N; ++k) {
-                const float x = v[u].x[k];
-                const bool valid = e0 + k < V;
-                m = valid ? fmaxf(m, x) : m;
-                bad |= __ballot(valid && __builtin_isnan(x));
+            for (int q = 0; q < N; ++q) {
+                const float x = elem<BF16>(r[u], q);
+                m = fmaxf(m, x);
+                bad |= __ballot(__builtin_isnan(x));
             }
-        }
-        run = fmaxf(run, m);
-        lm = fmaxf(lm, m);
+        const int tile = t0 / TILE;
+        const bool c1 = m > v1, c2 = m > v2, c3 = m > v3, c4 = m > v4;
+        t4 = c3 ? t3 : (c4 ? tile : t4);
+        t3 = c2 ? t2 : (c3 ? tile : t3);
+        t2 = c1 ? t1 : (c2 ? tile : t2);
+        t1 = c1 ? tile : t1;
+        v4 = fmaxf(v4, fminf(m, v3));
+        v3 = fmaxf(v3, fminf(m, v2));
+        v2 = fmaxf(v2, fminf(m, v1));
+        v1 = fmaxf(v1, m);
     };
-    stream_tiles<BF16, VEC>(rp, V, tile_max);
-    s_tm[cur_slot * kThreads + t] = run;
-    for (int sl = cur_slot + 1; sl < kSlots; ++sl) s_tm[sl * kThreads + t] = neg_inf();
-    bad |= __ballot(lm == pos_inf());
-    float bound = neg_inf();
-    if (t == 0) s_count = 0;
-    if (use_k && V > kSelCap && P.top_k <= kThreads) {
-        // the k-th largest lane maximum: every wave runs the same bitwise
-        // search over the 256 staged values (ballot counts, no barriers)
-        s_z[t] = lm;
-        __syncthreads();
-        const int l = t % kWave;
-        uint32_t kq[kWaves];
-#pragma unroll
-        for (int q = 0; q < kWaves; ++q) kq[q] = ordered_key(s_z[q * kWave + l]);
+    stream_tiles<BF16, VEC>(rp, V, visit);
+    bad |= __ballot(v1 == pos_inf());
+
+    // k-th largest of the values zr[0..R) over the wave's lanes, by a
+    // bitwise search over keys compared as floats (key_value is monotone)
+    auto wave_kth = [&](const float* zr, auto R_t) {
+        constexpr int R = decltype(R_t)::value;
         uint32_t key = 0;
-        for (int bit = 31; bit >= 0; --bit) {
+        for (int bit = 31; bit >= LO; --bit) {
             const uint32_t trial = key | (1u << bit);
+            const float tf = key_value(trial);
             int cnt = 0;
 #pragma unroll
-            for (int q = 0; q < kWaves; ++q) cnt += __popcll(__ballot(kq[q] >= trial));
+            for (int j = 0; j < R; ++j) cnt += __popcll(__ballot(zr[j] >= tf));
             if (cnt >= P.top_k) key = trial;
         }
-        bound = __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+        return key_value(key);
+    };
+
+    // (2) the bound: the k-th largest of the 4 x 256 tracked maxima, a lower
+    // bound on the row's k-th largest logit (every wave runs the same search
+    // over the staged values)
+    float bound = neg_inf();
+    if (t == 0) s_count = 0;
+    if (use_k) {
+        s_z[t] = v1;
+        s_z[kThreads + t] = v2;
+        s_z[2 * kThreads + t] = v3;
+        s_z[3 * kThreads + t] = v4;
+        __syncthreads();
+        constexpr int R = 4 * kThreads / kWave;
+        float zr[R];
+#pragma unroll
+        for (int j = 0; j < R; ++j) zr[j] = s_z[j * kWave + l];
+        bound = wave_kth(zr, std::integral_constant<int, R>{});
     }
     __syncthreads();
 
-    // (2) re-read only the lane-slots whose maximum reaches the bound (a few
-    // percent of them), one batch of loads per round, and append every
-    // element >= bound
-    uint32_t hits = 0;
-    for (int sl = 0; sl < kSlots; ++sl)
-        if (s_tm[sl * kThreads + t] >= bound) hits |= 1u << sl;
-    const int rounds = __reduce_max_hits(hits);
-    for (int r = 0; r < rounds; ++r) {
-        const int sl = hits ? __builtin_ctz(hits) : -1;
-        hits &= hits - 1u;
-        // the slot's tiles in batches of kMaxTps, each batch's loads issued together
-        for (int tb = 0; tb < tps; tb += kMaxTps) {
-            Vec<BF16> v[kMaxTps][kUnroll];
+    // (3) every element at or above the bound lies in a tile whose lane
+    // maximum reaches it: read those tiles again (at most three per lane,
+    // one batch of loads) and append their elements >= bound to the wave's
+    // own LDS region (a wave-uniform count, no atomics).  A lane with a
+    // fourth such tile has its whole share re-read by its wave instead.
+    float* zw = s_z + w * kWaveCap;
+    int* iw = s_i + w * kWaveCap;
+    int c = 0;
+    auto append = [&](bool h, float x, int e) {
+        const uint64_t mask = __ballot(h);
+        if (!mask) return;
+        const int slot = c + __popcll(mask & below);
+        if (h && slot < kWaveCap) {
+            zw[slot] = x;
+            iw[slot] = e;
+        }
+        c += __popcll(mask);
+    };
+    const bool all = t4 >= 0 && v4 >= bound;
+    const int tl[3] = {t1 >= 0 && v1 >= bound && !all ? t1 : -1, t2 >= 0 && v2 >= bound && !all ? t2 : -1,
+                       t3 >= 0 && v3 >= bound && !all ? t3 : -1};
+    const bool any1 = __ballot(tl[0] >= 0) != 0, any2 = __ballot(tl[1] >= 0) != 0,
+               any3 = __ballot(tl[2] >= 0) != 0;
+    const int nt = any3 ? 3 : any2 ? 2 : any1 ? 1 : 0;
+    if (nt > 0) {
+        uint4 rv[3][kUnroll];
 #pragma unroll
-            for (int tt = 0; tt < kMaxTps; ++tt) {
-                const int tile = sl * tps + tb + tt;
-                const int t0 = (sl >= 0 && tb + tt < tps && tile < ntiles ? tile : 0) * TILE;
+        for (int j = 0; j < 3; ++j) {
+            if (j >= nt) break;
+            const int base = (tl[j] >= 0 ? tl[j] : 0) * TILE;
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) rv[j][u] = load_raw<BF16, VEC>(rp, base + (u * kThreads + t) * N, V);
+        }
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            if (j >= nt) break;
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+                for (int q = 0; q < N; ++q) {
+                    const int e = tl[j] * TILE + (u * kThreads + t) * N + q;
+                    const float x = elem<BF16>(rv[j][u], q);
+                    append(tl[j] >= 0 && e < V && x >= bound, x, e);
+                }
+        }
+    }
+    {
+        // whole-share re-reads, one lane at a time: lane l reads tiles l, l + 64, ...
+        uint64_t heavy = __ballot(all);
+        const int ntiles = (V + TILE - 1) / TILE;
+        while (heavy) {
+            const int L = __builtin_ctzll(heavy);
+            heavy &= heavy - 1ull;
+            const int lane = t - l + L;  // the heavy lane's thread index
+            for (int tile0 = 0; tile0 < ntiles; tile0 += kWave) {
+                const int tile = tile0 + l;
+                const int base = (tile < ntiles ? tile : 0) * TILE;
+                uint4 v[kUnroll];
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) v[u] = load_raw<BF16, VEC>(rp, base + (u * kThreads + lane) * N, V);
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u)
-                    v[tt][u] = load_vec<BF16, VEC>(rp, t0 + (u * kThreads + t) * N, V, neg_inf());
-            }
 #pragma unroll
-            for (int tt = 0; tt < kMaxTps; ++tt) {
-                const int tile = sl * tps + tb + tt;
-                const bool live = sl >= 0 && tb + tt < tps && tile < ntiles;
-                const int t0 = (live ? tile : 0) * TILE;
-#pragma unroll
-                for (int u = 0; u < kUnroll; ++u) {
-                    const int e0 = t0 + (u * kThreads + t) * N;
-#pragma unroll
-                    for (int k = 0; k < N; ++k) {
-                        const float x = v[tt][u].x[k];
-                        append_hits(live && e0 + k < V && x >= bound, x, e0 + k, s_z, s_i, &s_count);
+                    for (int q = 0; q < N; ++q) {
+                        const int e = base + (u * kThreads + lane) * N + q;
+                        const float x = elem<BF16>(v[u], q);
+                        append(tile < ntiles && e < V && x >= bound, x, e);
                     }
-                }
             }
         }
     }
-    __syncthreads();
-    int C = s_count;
-    uint32_t rowflags = bad ? kRowNonfinite : 0u;
-    const bool any_bad = __syncthreads_or(bad != 0);
-    if (any_bad) rowflags = kRowNonfinite;
+    if (l == 0) s_cw[w] = c;
+    uint32_t rowflags = 0;
+    if (__syncthreads_or(bad != 0)) rowflags = kRowNonfinite;
+    int C = 0;
+    bool spill = false;
+#pragma unroll
+    for (int q = 0; q < kWaves; ++q) {
+        const int cq = s_cw[q];
+        C += cq;
+        spill |= cq > kWaveCap;
+    }
+    if (spill) C = kSelCap + 1;
+    // wave 0 moves the wave regions' entries together into s_z/s_i[0..C)
+    // (every destination at or before its source, each chunk read before
+    // any of it is written)
+    auto gather = [&]() {
+        int dst = 0;
+        for (int q = 0; q < kWaves; ++q) {
+            const int cq = s_cw[q];
+            for (int j0 = 0; j0 < cq; j0 += kWave) {
+                const int p = j0 + l;
+                const bool in = p < cq;
+                const float zv = in ? s_z[q * kWaveCap + p] : 0.0f;
+                const int iv = in ? s_i[q * kWaveCap + p] : 0;
+                if (in) {
+                    s_z[dst + l] = zv;
+                    s_i[dst + l] = iv;
+                }
+                dst += min(kWave, cq - j0);
+            }
+        }
+    };
+    bool packed = false;
 
     if (C > kSelCap) {
-        // Overflow: the exact k-th largest value by a bitwise search on
-        // ordered keys (largest key t with count(key >= t) >= k), each step
-        // one read of the row, then the buffer is refilled with the elements
-        // at or above it.
+        // Overflow (heavy ties, or very flat rows with a large k): the exact
+        // k-th largest value by a bitwise search on ordered keys (largest key
+        // t with count(key >= t) >= k), each step one read of the row, then
+        // the buffer is refilled with the elements at or above it.
         uint32_t key = 0;
         for (int bit = 31; bit >= 0; --bit) {
             const uint32_t trial = key | (1u << bit);
@@ -394,13 +514,18 @@ __global__ __launch_bounds__(kThreads) void k_trunc_select(VerifyParams P) {
         __syncthreads();
         C = s_count;
         if (C > kSelCap) { rowflags |= kRowOverflow; C = kSelCap; }
+        packed = true;
     }
     if (C <= kWave) {
-        // The usual case: one wave finishes the row in registers (shuffle
-        // bitonic sorts, ballots and a wave prefix scan; no barriers).
+        // The usual case: one wave finishes the row (no barriers).
         if (t >= kWave) return;
+        if (!packed) gather();
         select_in_wave(P, b, s, C, use_k, s_z, s_i, rowflags);
         return;
+    }
+    if (!packed) {
+        if (t < kWave) gather();
+        __syncthreads();
     }
     const int n = pow2_at_least(C < 2 ? 2 : C);
     for (int p = C + t; p < n; p += kThreads) { s_z[p] = neg_inf(); s_i[p] = 0x7fffffff; }
