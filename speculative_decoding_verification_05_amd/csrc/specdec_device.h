@@ -119,22 +119,74 @@ __device__ __forceinline__ Vec<BF16> load_vec(const void* row, int e, int hi, fl
 }
 
 // ---------------------------------------------------------------- reductions
+// Wave-wide scans and reductions with DPP row moves (row_shr 1/2/4/8 inside
+// each 16-lane row, then row_bcast 15 and 31 across rows): a handful of
+// VALU-latency steps instead of LDS permutes.  Lanes whose source lies
+// outside the row (or in a masked row) read the operation's identity.  The
+// reduction result is the scan's lane 63, broadcast through an SGPR.
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t identity, uint32_t x) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(identity), static_cast<int>(x),
+                                                             CTRL, ROW_MASK, 0xf, false));
+}
+
+template <class T>
+__device__ __forceinline__ uint32_t to_bits(T v) { return __builtin_bit_cast(uint32_t, v); }
+template <class T>
+__device__ __forceinline__ T from_bits(uint32_t v) { return __builtin_bit_cast(T, v); }
+
+// Inclusive scan of a 32-bit value under an associative op with identity `id`.
+template <class T, class Op>
+__device__ __forceinline__ T wave_scan(T x, T id, Op op) {
+    const uint32_t i = to_bits(id);
+    x = op(x, from_bits<T>(dpp_move<kDppRowShr1>(i, to_bits(x))));
+    x = op(x, from_bits<T>(dpp_move<kDppRowShr2>(i, to_bits(x))));
+    x = op(x, from_bits<T>(dpp_move<kDppRowShr4>(i, to_bits(x))));
+    x = op(x, from_bits<T>(dpp_move<kDppRowShr8>(i, to_bits(x))));
+    x = op(x, from_bits<T>(dpp_move<kDppRowBcast15, 0xa>(i, to_bits(x))));
+    x = op(x, from_bits<T>(dpp_move<kDppRowBcast31, 0xc>(i, to_bits(x))));
+    return x;
+}
+
+// x of lane `lane` (wave-uniform) to every lane.
+template <class T>
+__device__ __forceinline__ T lane_value(T x, int lane) {
+    return from_bits<T>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(to_bits(x)), lane)));
+}
+
+template <class T>
+__device__ __forceinline__ T lane63(T x) {
+    return from_bits<T>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(to_bits(x)), 63)));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-    return v;
+    return lane63(wave_scan(v, neg_inf(), [](float a, float b) { return fmaxf(a, b); }));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+    return lane63(wave_scan(v, 0.0f, [](float a, float b) { return a + b; }));
+}
+
+// Inclusive prefix sum over the wave's lanes.
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+    return wave_scan(v, 0.0f, [](float a, float b) { return a + b; });
+}
+
+// Exclusive prefix sum (lane 0 gets 0) from an inclusive one: a whole-wave
+// shift right by one lane.
+__device__ __forceinline__ float wave_shift_right(float incl) {
+    return from_bits<float>(dpp_move<0x138>(0u, to_bits(incl)));
+}
+
+__device__ __forceinline__ int wave_isum(int v) {
+    return lane63(wave_scan(v, 0, [](int a, int b) { return a + b; }));
 }
 
 __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v |= __shfl_xor(v, o, kWave);
-    return v;
+    return lane63(wave_scan(v, 0u, [](uint32_t a, uint32_t b) { return a | b; }));
 }
 
 // Online-softmax pair (running maximum of the raw logits, sum of
@@ -152,13 +204,21 @@ __device__ __forceinline__ MaxSum combine(MaxSum a, MaxSum b, float c) {
     return {m, sa + sb};
 }
 
+// The pair scans below follow wave_scan's steps, moving both members.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ MaxSum dpp_pair(MaxSum v) {
+    return {from_bits<float>(dpp_move<CTRL, ROW_MASK>(to_bits(neg_inf()), to_bits(v.m))),
+            from_bits<float>(dpp_move<CTRL, ROW_MASK>(0u, to_bits(v.s)))};
+}
+
 __device__ __forceinline__ MaxSum wave_combine(MaxSum v, float c) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) {
-        MaxSum w{__shfl_xor(v.m, o, kWave), __shfl_xor(v.s, o, kWave)};
-        v = combine(v, w, c);
-    }
-    return v;
+    v = combine(v, dpp_pair<kDppRowShr1>(v), c);
+    v = combine(v, dpp_pair<kDppRowShr2>(v), c);
+    v = combine(v, dpp_pair<kDppRowShr4>(v), c);
+    v = combine(v, dpp_pair<kDppRowShr8>(v), c);
+    v = combine(v, dpp_pair<kDppRowBcast15, 0xa>(v), c);
+    v = combine(v, dpp_pair<kDppRowBcast31, 0xc>(v), c);
+    return {lane63(v.m), lane63(v.s)};
 }
 
 // (value, index) of a maximum: larger value wins, the lower index on ties.
@@ -173,13 +233,20 @@ __device__ __forceinline__ ArgMax better(ArgMax a, ArgMax b) {
     return a.i <= b.i ? a : b;
 }
 
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ ArgMax dpp_pair(ArgMax v) {
+    return {from_bits<float>(dpp_move<CTRL, ROW_MASK>(to_bits(neg_inf()), to_bits(v.v))),
+            static_cast<int>(dpp_move<CTRL, ROW_MASK>(0x7fffffffu, static_cast<uint32_t>(v.i)))};
+}
+
 __device__ __forceinline__ ArgMax wave_argmax(ArgMax v) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) {
-        ArgMax w{__shfl_xor(v.v, o, kWave), __shfl_xor(v.i, o, kWave)};
-        v = better(v, w);
-    }
-    return v;
+    v = better(v, dpp_pair<kDppRowShr1>(v));
+    v = better(v, dpp_pair<kDppRowShr2>(v));
+    v = better(v, dpp_pair<kDppRowShr4>(v));
+    v = better(v, dpp_pair<kDppRowShr8>(v));
+    v = better(v, dpp_pair<kDppRowBcast15, 0xa>(v));
+    v = better(v, dpp_pair<kDppRowBcast31, 0xc>(v));
+    return {lane63(v.v), lane63(v.i)};
 }
 
 }  // namespace specdec

@@ -63,8 +63,7 @@ __device__ __forceinline__ bool precedes(float z, int i, float z2, int i2) {
 __device__ __forceinline__ int block_count(int v) {
     __shared__ int s_w[kWaves];
     const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    v = wave_isum(v);
     __syncthreads();
     if (l == 0) s_w[w] = v;
     __syncthreads();
@@ -129,7 +128,7 @@ __device__ __forceinline__ void append_hits(bool hit, float x, int e, float* bz,
     const int l = threadIdx.x % kWave;
     int base = 0;
     if (l == __builtin_ctzll(mask)) base = atomicAdd(count, __popcll(mask));
-    base = __shfl(base, __builtin_ctzll(mask), kWave);
+    base = lane_value(base, __builtin_ctzll(mask));
     if (hit) {
         const int slot = base + __popcll(mask & ((1ull << l) - 1ull));
         if (slot < kSelCap) { bz[slot] = x; bi[slot] = e; }
@@ -243,10 +242,10 @@ __device__ void select_in_wave(const VerifyParams& P, int b, int s, int C, bool 
     auto lane_of = [&](bool pred) { return __builtin_ctzll(__ballot(pred)); };
     int K = C;
     if (use_k && P.top_k <= C) {
-        const float tau = __shfl(z, lane_of(in && rank == P.top_k - 1), kWave);
+        const float tau = lane_value(z, lane_of(in && rank == P.top_k - 1));
         K = __popcll(__ballot(in && z >= tau));
     }
-    const float M = __shfl(z, lane_of(in && rank == 0), kWave);
+    const float M = lane_value(z, lane_of(in && rank == 0));
     const float e = in && rank < K ? exp2f((z - M) * P.c) : 0.0f;
     // inclusive prefix of the weights in rank order, summed in candidate
     // order (monotone in rank: every term is non-negative)
@@ -265,10 +264,10 @@ __device__ void select_in_wave(const VerifyParams& P, int b, int s, int C, bool 
     }
     int Nk = K;
     if (P.top_p < 1.0f) {
-        const float goal = P.top_p * __shfl(pre, lane_of(in && rank == K - 1), kWave);
+        const float goal = P.top_p * lane_value(pre, lane_of(in && rank == K - 1));
         Nk = min(K, __popcll(__ballot(in && rank < K && pre < goal)) + 1);
     }
-    const float Sn = __shfl(pre, lane_of(in && rank == Nk - 1), kWave);
+    const float Sn = lane_value(pre, lane_of(in && rank == Nk - 1));
     // the kept tokens by ascending index: every candidate at its index rank,
     // then the kept ones compacted in that order
     const bool kept = in && rank < Nk;
@@ -557,11 +556,7 @@ __global__ __launch_bounds__(kThreads) void k_trunc_select(VerifyParams P) {
         for (int base = 0; base < K; base += kThreads) {
             const int p = base + t;
             float x = p < K ? exp2f((s_z[p] - M) * cc) : 0.0f;
-#pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                const float y = __shfl_up(x, o, kWave);
-                if (l >= o) x += y;
-            }
+            x = wave_prefix_sum(x);
             __syncthreads();
             if (l == kWave - 1) s_wt[w] = x;
             __syncthreads();
@@ -609,7 +604,7 @@ __device__ __forceinline__ float record_weight(const uint2* rec, int n, int d) {
         const bool hit = static_cast<int>(ent.x) == d;
         const uint64_t mask = __ballot(hit);
         if (mask) {
-            e = __shfl(__uint_as_float(ent.y), __builtin_ctzll(mask), kWave);
+            e = lane_value(__uint_as_float(ent.y), __builtin_ctzll(mask));
             break;
         }
     }
@@ -746,11 +741,7 @@ __global__ __launch_bounds__(kThreads) void k_decide_trunc(VerifyParams P) {
         const int p = base + t;
         const float r = p < np ? mass(p, with_q) : 0.0f;
         float x = r;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const float y = __shfl_up(x, o, kWave);
-            if (l >= o) x += y;
-        }
+        x = wave_prefix_sum(x);
         __syncthreads();
         if (l == kWave - 1) s_wt[w] = x;
         __syncthreads();

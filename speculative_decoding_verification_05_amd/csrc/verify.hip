@@ -279,23 +279,60 @@ __device__ float lane_mass_elements(const MassRows& a, int lo, int hi) {
     return acc;
 }
 
-// Masses of chunks [k0, k1) published to csum[k]; the next chunk's loads are
-// in flight while the current one is reduced.  Returns the OR of the
-// publish() results (the dependency for arrive_last).
+// Sums over the kThreads lanes of NV values at once (one LDS exchange).
+template <int NV>
+__device__ __forceinline__ void block_sums(float (&v)[NV]) {
+    __shared__ float s_v[NV][kWaves];
+    const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) v[j] = wave_sum(v[j]);
+    __syncthreads();
+    if (l == 0) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) s_v[j][w] = v[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        float r = s_v[j][0];
+#pragma unroll
+        for (int k = 1; k < kWaves; ++k) r += s_v[j][k];
+        v[j] = r;
+    }
+}
+
+// Masses of chunks [k0, k1) published to csum[k].  The loads of a group of
+// kMassGroup chunks are issued together (a workgroup's whole share of the
+// row pair is typically one group), then the group's sums are reduced at
+// once.  Returns the OR of the publish() results (the dependency for
+// arrive_last).
+constexpr int kMassGroup = 4;
+
 template <bool BF16, bool VEC>
 __device__ uint32_t mass_chunks(const MassRows& a, int k0, int k1, int chunk2, int V, uint32_t* csum) {
     uint32_t dep = 0;
     if (k0 >= k1) return dep;
     if constexpr (VEC) {
-        ChunkRegs<BF16, VEC> cur, nxt;
-        load_chunk<BF16, VEC>(cur, a, k0 * chunk2, min(V, (k0 + 1) * chunk2));
-        for (int k = k0; k < k1; ++k) {
-            const int kn = min(k + 1, k1 - 1);  // re-loads the last chunk once: no branch
-            load_chunk<BF16, VEC>(nxt, a, kn * chunk2, min(V, (kn + 1) * chunk2));
-            const int lo = k * chunk2, hi = min(V, lo + chunk2);
-            const float t = block_sum(lane_mass<BF16, VEC>(cur, a, lo, hi));
-            if (threadIdx.x == 0) dep |= publish(csum + k, __float_as_uint(t));
-            cur = nxt;
+        for (int kb = k0; kb < k1; kb += kMassGroup) {
+            ChunkRegs<BF16, VEC> r[kMassGroup];
+#pragma unroll
+            for (int j = 0; j < kMassGroup; ++j) {
+                const int k = min(kb + j, k1 - 1);  // past k1: the last chunk again, discarded
+                load_chunk<BF16, VEC>(r[j], a, k * chunk2, min(V, (k + 1) * chunk2));
+            }
+            float part[kMassGroup];
+#pragma unroll
+            for (int j = 0; j < kMassGroup; ++j) {
+                const int k = min(kb + j, k1 - 1);
+                const int lo = k * chunk2, hi = min(V, lo + chunk2);
+                part[j] = lane_mass<BF16, VEC>(r[j], a, lo, hi);
+            }
+            block_sums(part);
+            if (threadIdx.x == 0) {
+#pragma unroll
+                for (int j = 0; j < kMassGroup; ++j)
+                    if (kb + j < k1) dep |= publish(csum + kb + j, __float_as_uint(part[j]));
+            }
         }
     } else {
         for (int k = k0; k < k1; ++k) {
@@ -366,14 +403,8 @@ __device__ int search_chunk(const MassRows& a, int lo, int hi, float base, float
             inc[k] = run;
         }
         // exclusive scan of lane totals: inclusive within the wave, shifted
-        float x = run;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const float y = __shfl_up(x, o, kWave);
-            if (l >= o) x += y;
-        }
-        float ex = __shfl_up(x, 1, kWave);
-        if (l == 0) ex = 0.0f;
+        const float x = wave_prefix_sum(run);
+        const float ex = wave_shift_right(x);
         __syncthreads();
         if (l == kWave - 1) s_wtot[w] = x;
         __syncthreads();
@@ -389,8 +420,8 @@ __device__ int search_chunk(const MassRows& a, int lo, int hi, float base, float
         // with mass; one LDS atomic per wave
         const uint64_t cross = __ballot(first != 0x7fffffff);
         const uint64_t pos = __ballot(lastp >= 0);
-        const int f = __shfl(first, cross ? __builtin_ctzll(cross) : 0, kWave);
-        const int lp = __shfl(lastp, pos ? 63 - __builtin_clzll(pos) : 0, kWave);
+        const int f = lane_value(first, cross ? __builtin_ctzll(cross) : 0);
+        const int lp = lane_value(lastp, pos ? 63 - __builtin_clzll(pos) : 0);
         if (l == 0 && cross) atomicMin(&s_found, f);
         if (l == 0 && pos) atomicMax(&s_last, lp);
         if (threadIdx.x == kThreads - 1) s_tile_end = lane_base + inc[N - 1];
@@ -430,17 +461,31 @@ __global__ __launch_bounds__(kThreads) void k_decide_sample(VerifyParams P) {
     const int g = request_gamma(P, b);
     __syncthreads();
 
-    // (1) (max, sum) of every used row from its chunk partials
-    for (int s = w; s < P.rows; s += kWaves) {
-        const bool used = (s <= P.G) ? (s <= g) : (s - (P.G + 1) < g);
-        if (!used) continue;
-        MaxSum acc{neg_inf(), 0.0f};
-        for (int k = l; k < P.nc; k += kWave) {
-            const float4 q = s_part[s * P.nc + k];
-            acc = combine(acc, MaxSum{q.x, q.y}, c);
+    // (1) (max, sum) of every used row from its chunk partials: a lane per
+    // row over a few partials, else a wave per row
+    if (P.nc <= kSerialParts) {
+        for (int s = threadIdx.x; s < P.rows; s += kThreads) {
+            const bool used = (s <= P.G) ? (s <= g) : (s - (P.G + 1) < g);
+            if (!used) continue;
+            MaxSum acc{neg_inf(), 0.0f};
+            for (int k = 0; k < P.nc; ++k) {
+                const float4 q = s_part[s * P.nc + k];
+                acc = combine(acc, MaxSum{q.x, q.y}, c);
+            }
+            s_stat[s] = make_float2(acc.m, acc.s);
         }
-        acc = wave_combine(acc, c);
-        if (l == 0) s_stat[s] = make_float2(acc.m, acc.s);
+    } else {
+        for (int s = w; s < P.rows; s += kWaves) {
+            const bool used = (s <= P.G) ? (s <= g) : (s - (P.G + 1) < g);
+            if (!used) continue;
+            MaxSum acc{neg_inf(), 0.0f};
+            for (int k = l; k < P.nc; k += kWave) {
+                const float4 q = s_part[s * P.nc + k];
+                acc = combine(acc, MaxSum{q.x, q.y}, c);
+            }
+            acc = wave_combine(acc, c);
+            if (l == 0) s_stat[s] = make_float2(acc.m, acc.s);
+        }
     }
     __syncthreads();
 
@@ -509,14 +554,57 @@ __global__ __launch_bounds__(kThreads) void k_decide_sample(VerifyParams P) {
     // passes u*R, the token inside it, then every output of the request.
     for (int k = threadIdx.x; k < P.nc2; k += kThreads) s_csum[k] = __uint_as_float(fetch(csum + k));
     __syncthreads();
+    // Wave 0 walks the chunk sums in chunk order: lane l takes a run of
+    // consecutive chunks, and a wave prefix sum of the runs' totals gives
+    // each run its offset.  total() leaves R in s_R; pick() leaves the chunk
+    // where the running mass first passes `target` and the mass before it
+    // (or, if rounding leaves none, the last chunk with mass and +inf).
+    __shared__ int s_chunk;
+    __shared__ float s_before;
+    const int per = (P.nc2 + kWave - 1) / kWave;
+    const int r0 = l * per, r1 = min(P.nc2, r0 + per);
+    auto total = [&]() {
+        if (w == 0) {
+            float run = 0.0f;
+            for (int k = r0; k < r1; ++k) run += s_csum[k];
+            const float R = lane63(wave_prefix_sum(run));
+            if (l == 0) s_R = R;
+        }
+        __syncthreads();
+    };
+    auto pick = [&](float target) {
+        if (w == 0) {
+            float run = 0.0f;
+            for (int k = r0; k < r1; ++k) run += s_csum[k];
+            float before = wave_shift_right(wave_prefix_sum(run));
+            int found = -1, lastk = -1;
+            float fb = 0.0f;
+            for (int k = r0; k < r1; ++k) {
+                const float next = before + s_csum[k];
+                if (found < 0 && next > target) { found = k; fb = before; }
+                if (s_csum[k] > 0.0f) lastk = k;
+                before = next;
+            }
+            const uint64_t hit = __ballot(found >= 0);
+            const uint64_t pos = __ballot(lastk >= 0);
+            int cstar;
+            float bef;
+            if (hit) {
+                const int src = __builtin_ctzll(hit);
+                cstar = lane_value(found, src);
+                bef = lane_value(fb, src);
+            } else {
+                // rounding left u*R at or above the total: the last chunk with mass
+                cstar = pos ? lane_value(lastk, 63 - __builtin_clzll(pos)) : 0;
+                bef = pos_inf();  // no crossing: take its last token with mass
+            }
+            if (l == 0) { s_chunk = cstar; s_before = bef; }
+        }
+        __syncthreads();
+    };
     uint32_t fl2 = 0;
     float R_report = 0.0f;
-    if (threadIdx.x == 0) {
-        float R = 0.0f;
-        for (int k = 0; k < P.nc2; ++k) R += s_csum[k];
-        s_R = R;
-    }
-    __syncthreads();
+    total();
     if (resid) {
         R_report = s_R;
         if (!(s_R > 0.0f)) {
@@ -528,38 +616,13 @@ __global__ __launch_bounds__(kThreads) void k_decide_sample(VerifyParams P) {
                 if (threadIdx.x == 0) s_csum[k] = v;
             }
             __syncthreads();
-            if (threadIdx.x == 0) {
-                float R = 0.0f;
-                for (int k = 0; k < P.nc2; ++k) R += s_csum[k];
-                s_R = R;
-            }
-            __syncthreads();
+            total();
         }
     }
     const uint4 rnd = philox4x32_10(make_uint4(static_cast<uint32_t>(m), static_cast<uint32_t>(b),
                                                P.round, 0u), P.key0, P.key1);
     const float target = uniform24(rnd.y) * s_R;
-    __shared__ int s_chunk;
-    __shared__ float s_before;
-    if (threadIdx.x == 0) {
-        float C = 0.0f;
-        int cstar = -1;
-        float before = 0.0f;
-        for (int k = 0; k < P.nc2; ++k) {
-            const float next = C + s_csum[k];
-            if (next > target) { cstar = k; before = C; break; }
-            C = next;
-        }
-        if (cstar < 0) {
-            // rounding left u*R at or above the total: the last chunk with mass
-            cstar = P.nc2 - 1;
-            while (cstar > 0 && !(s_csum[cstar] > 0.0f)) --cstar;
-            before = pos_inf();  // no crossing: take its last token with mass
-        }
-        s_chunk = cstar;
-        s_before = before;
-    }
-    __syncthreads();
+    pick(target);
     int lastp;
     const int l2 = s_chunk * P.chunk2, h2 = min(P.V, l2 + P.chunk2);
     int token = search_chunk<BF16, VEC>(a, l2, h2, s_before, target, &lastp);
@@ -597,19 +660,33 @@ __global__ __launch_bounds__(kThreads) void k_decide_greedy(VerifyParams P) {
     if (w == 0 && i < P.G) d = P.tokens[static_cast<size_t>(b) * P.G + i];
     const int g = request_gamma(P, b);
     __syncthreads();
-    for (int s = w; s <= g; s += kWaves) {
-        ArgMax best{neg_inf(), 0x7fffffff};
-        uint32_t nan = 0;
-        for (int k = l; k < P.nc; k += kWave) {
+    // a lane per row over a few partials, else a wave per row
+    auto part_argmax = [&](int s, int k0, int step, ArgMax& best, uint32_t& nan) {
+        for (int k = k0; k < P.nc; k += step) {
             const float4 q = s_part[s * P.nc + k];
             const uint32_t word = __float_as_uint(q.y);  // index, bit 31: a NaN was seen
             const int idx = static_cast<int>(word & 0x7fffffffu);
             if (idx != 0x7fffffff) best = better(best, ArgMax{q.x, idx});
             nan |= word >> 31;
         }
-        best = wave_argmax(best);
-        nan = wave_or(nan);
-        if (l == 0) { s_arg[s] = best.i; s_nan[s] = nan; }
+    };
+    if (P.nc <= kSerialParts) {
+        for (int s = threadIdx.x; s <= g; s += kThreads) {
+            ArgMax best{neg_inf(), 0x7fffffff};
+            uint32_t nan = 0;
+            part_argmax(s, 0, 1, best, nan);
+            s_arg[s] = best.i;
+            s_nan[s] = nan;
+        }
+    } else {
+        for (int s = w; s <= g; s += kWaves) {
+            ArgMax best{neg_inf(), 0x7fffffff};
+            uint32_t nan = 0;
+            part_argmax(s, l, kWave, best, nan);
+            best = wave_argmax(best);
+            nan = wave_or(nan);
+            if (l == 0) { s_arg[s] = best.i; s_nan[s] = nan; }
+        }
     }
     __syncthreads();
     if (w != 0) return;
