@@ -302,27 +302,27 @@ __device__ __forceinline__ void block_sums(float (&v)[NV]) {
 }
 
 // Masses of chunks [k0, k1) published to csum[k].  The loads of a group of
-// kMassGroup chunks are issued together (a workgroup's whole share of the
-// row pair is typically one group), then the group's sums are reduced at
-// once.  Returns the OR of the publish() results (the dependency for
-// arrive_last).
-constexpr int kMassGroup = 4;
-
-template <bool BF16, bool VEC>
+// GROUP chunks are issued together and the group's sums reduced at once.
+// GROUP = kMassGroupWide: a workgroup's whole share (at most that many
+// chunks) in one group.  Smaller GROUP (long shares): the next group's loads
+// are in flight while the current one is reduced, in fewer registers.
+// Returns the OR of the publish() results (the dependency for arrive_last).
+template <bool BF16, bool VEC, int GROUP>
 __device__ uint32_t mass_chunks(const MassRows& a, int k0, int k1, int chunk2, int V, uint32_t* csum) {
     uint32_t dep = 0;
     if (k0 >= k1) return dep;
     if constexpr (VEC) {
-        for (int kb = k0; kb < k1; kb += kMassGroup) {
-            ChunkRegs<BF16, VEC> r[kMassGroup];
+        auto load_group = [&](ChunkRegs<BF16, VEC>(&r)[GROUP], int kb) {
 #pragma unroll
-            for (int j = 0; j < kMassGroup; ++j) {
+            for (int j = 0; j < GROUP; ++j) {
                 const int k = min(kb + j, k1 - 1);  // past k1: the last chunk again, discarded
                 load_chunk<BF16, VEC>(r[j], a, k * chunk2, min(V, (k + 1) * chunk2));
             }
-            float part[kMassGroup];
+        };
+        auto reduce_group = [&](ChunkRegs<BF16, VEC>(&r)[GROUP], int kb) {
+            float part[GROUP];
 #pragma unroll
-            for (int j = 0; j < kMassGroup; ++j) {
+            for (int j = 0; j < GROUP; ++j) {
                 const int k = min(kb + j, k1 - 1);
                 const int lo = k * chunk2, hi = min(V, lo + chunk2);
                 part[j] = lane_mass<BF16, VEC>(r[j], a, lo, hi);
@@ -330,8 +330,27 @@ __device__ uint32_t mass_chunks(const MassRows& a, int k0, int k1, int chunk2, i
             block_sums(part);
             if (threadIdx.x == 0) {
 #pragma unroll
-                for (int j = 0; j < kMassGroup; ++j)
+                for (int j = 0; j < GROUP; ++j)
                     if (kb + j < k1) dep |= publish(csum + kb + j, __float_as_uint(part[j]));
+            }
+        };
+        ChunkRegs<BF16, VEC> cur[GROUP];
+        if constexpr (GROUP == kMassGroupWide) {
+            for (int kb = k0; kb < k1; kb += GROUP) {
+                load_group(cur, kb);
+                reduce_group(cur, kb);
+            }
+        } else {
+            ChunkRegs<BF16, VEC> nxt[GROUP];
+            load_group(cur, k0);
+            for (int kb = k0; kb < k1; kb += GROUP) {
+                const bool more = kb + GROUP < k1;
+                if (more) load_group(nxt, kb + GROUP);
+                reduce_group(cur, kb);
+                if (more) {
+#pragma unroll
+                    for (int j = 0; j < GROUP; ++j) cur[j] = nxt[j];
+                }
             }
         }
     } else {
@@ -441,7 +460,7 @@ __device__ __forceinline__ void stage_partials(const VerifyParams& P, int b, flo
     for (int t = threadIdx.x; t < n; t += kThreads) s_part[t] = src[t];
 }
 
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, int GROUP>
 __global__ __launch_bounds__(kThreads) void k_decide_sample(VerifyParams P) {
     __shared__ float4 s_part[kMaxPart];
     __shared__ float2 s_stat[127];
@@ -547,7 +566,7 @@ __global__ __launch_bounds__(kThreads) void k_decide_sample(VerifyParams P) {
     }
     uint32_t* csum = P.csum + static_cast<size_t>(b) * P.nc2;
     const int k0 = wg * P.cpw, k1 = min(P.nc2, k0 + P.cpw);
-    const uint32_t dep = mass_chunks<BF16, VEC>(a, k0, k1, P.chunk2, P.V, csum);
+    const uint32_t dep = mass_chunks<BF16, VEC, GROUP>(a, k0, k1, P.chunk2, P.V, csum);
     if (!arrive_last(P.cnt + b, static_cast<uint32_t>(P.wpr), dep)) return;
 
     // (4) last workgroup of the request: R, the chunk where the running mass
@@ -714,7 +733,7 @@ __global__ __launch_bounds__(kThreads) void k_decide_greedy(VerifyParams P) {
 
 struct Layout {
     int rows, nc, chunk, nc2, chunk2, wpr, cpw;
-    bool trunc;
+    bool trunc, wide;
     size_t off_cnt, off_part, off_csum, off_nuc, total;
 };
 
@@ -762,8 +781,8 @@ bool valid_desc(const specdec_verify_desc_t* d) {
 // Chunking.  Statistics pass: about one round of workgroups resident at once
 // (8 per CU x 256 CUs), so that every workgroup streams from the start and
 // none waits for a slot; whole tiles per chunk.  Sampling pass: one tile of
-// 256 lanes x 2 vectors per chunk (at most 1024 per row), and about 512
-// workgroups in all, each taking a run of consecutive chunks of one request.
+// 256 lanes x 2 vectors per chunk (at most 1024 per row), each workgroup
+// taking a run of consecutive chunks of one request.
 Layout make_layout(const specdec_verify_desc_t* d) {
     Layout L{};
     const bool bf16 = d->dtype == SPECDEC_BF16;
@@ -782,10 +801,15 @@ Layout make_layout(const specdec_verify_desc_t* d) {
     L.nc = (d->vocab + L.chunk - 1) / L.chunk;
     L.chunk2 = kThreads * n * kUnroll2;
     L.nc2 = (d->vocab + L.chunk2 - 1) / L.chunk2;
-    // sampling pass: about two workgroups per CU, all resident from the start
+    // sampling pass, all workgroups resident from the start: about 512 (two
+    // per CU) when each then holds at most kMassGroupWide chunks, its whole
+    // share loaded at once; else about 1024 (four per CU) of the leaner
+    // double-buffered kind
     const int bb = d->batch > 0 ? d->batch : 1;
-    int wpr = static_cast<int>(512.0 / bb + 0.5);
-    wpr = env_int("SPECDEC_SAMPLE_WPR", wpr < 1 ? 1 : (wpr > L.nc2 ? L.nc2 : wpr));
+    const int w512 = max(1, static_cast<int>(512.0 / bb + 0.5));
+    L.wide = L.nc2 <= kMassGroupWide * w512;
+    int wpr = L.wide ? w512 : max(1, static_cast<int>(1024.0 / bb + 0.5));
+    wpr = env_int("SPECDEC_SAMPLE_WPR", wpr > L.nc2 ? L.nc2 : wpr);
     L.cpw = (L.nc2 + wpr - 1) / wpr;
     L.wpr = (L.nc2 + L.cpw - 1) / L.cpw;
     const size_t B = static_cast<size_t>(d->batch);
@@ -824,7 +848,10 @@ specdec_status_t launch_all(const specdec_verify_desc_t* d, const VerifyParams& 
     } else {
         launch(k_stats<BF16, VEC, false>, dim3(L.nc, L.rows, d->batch), e0, e1);
         if (hipGetLastError() != hipSuccess) return SPECDEC_ERR_DEVICE;
-        launch(k_decide_sample<BF16, VEC>, dim3(L.wpr, d->batch), e2, e3);
+        if (L.wide)
+            launch(k_decide_sample<BF16, VEC, kMassGroupWide>, dim3(L.wpr, d->batch), e2, e3);
+        else
+            launch(k_decide_sample<BF16, VEC, kMassGroupChunks>, dim3(L.wpr, d->batch), e2, e3);
     }
     return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_DEVICE;
 }

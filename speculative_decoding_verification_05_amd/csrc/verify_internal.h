@@ -15,6 +15,8 @@ constexpr int kUnroll = 4;        // 16-byte vectors per lane per tile, statisti
 constexpr int kUnroll2 = 2;       // per row per tile, sampling pass
 constexpr int kMaxPart = 512;     // partials per request the decision kernels stage in LDS
 constexpr int kTruncCap = 2048;   // vocabulary limit of top-p without an effective top-k
+constexpr int kMassGroupWide = 4;    // sampling-pass chunks loaded at once (short shares)
+constexpr int kMassGroupChunks = 2;  // ... and per double-buffered group (long shares)
 constexpr int kSerialParts = 16;  // at most this many partials per row: one lane combines them
 constexpr int kNucCap = 1024;     // kept tokens recorded per row (and the top-k limit)
 
