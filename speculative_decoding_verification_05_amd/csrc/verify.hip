@@ -13,14 +13,8 @@
 //     the argmax at the first mismatch (tutorial s.3-4; KB M013 s.03).
 //
 // Kernels (all HBM-bandwidth bound, no matrix cores: nothing is a contraction):
-//   k_stats          the one full pass over every used logits row, split in
-//                    chunks.  Each workgroup streams its chunk with branch-free
-//                    16-byte loads (four per lane per tile, the next tile in
-//                    flight while the current one is reduced) and stores one
-//                    partial: the online (max, sum 2^((z - max) c)) pair in
-//                    sampling mode, (max, lowest index) in greedy mode.  No
-//                    atomics and no cross-workgroup traffic: the kernel
-//                    boundary publishes the partials.
+//   k_stats          (stats.hip) the one full pass over every used row, one
+//                    partial per (chunk, row).
 //   k_decide_sample  workgroup (chunk, request).  Every workgroup of a request
 //                    combines the request's partials, runs the acceptance tests
 //                    on one wave and takes m from a ballot (identical results in
@@ -41,167 +35,6 @@
 
 namespace specdec {
 namespace {
-
-// ------------------------------------------------------------------ streaming
-
-template <bool BF16, int U>
-__device__ __forceinline__ void load_tile(uint4 (&raw)[U], const void* rp, int t0) {
-    constexpr int N = Vec<BF16>::N;
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-        raw[u] = load16_stream<BF16>(rp, t0 + (u * kThreads + threadIdx.x) * N);
-}
-
-template <bool BF16, int U>
-__device__ __forceinline__ void widen_tile(Vec<BF16> (&v)[U], const uint4 (&raw)[U]) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = widen<BF16>(raw[u]);
-}
-
-// Streams elements [lo, hi) of one row through consume(v, t0) in tiles of
-// kThreads lanes x U 16-byte vectors (lane l holds vectors u*kThreads + l).
-// Whole tiles use branch-free loads, and the next tile's loads are issued
-// before the current tile is consumed; a ragged last tile takes the clipped
-// path.  keep() is asked once, after the first tile's loads are in flight;
-// false abandons the row (the function then returns false).
-template <bool BF16, bool VEC, int U, class F, class K>
-__device__ __forceinline__ bool stream_row(const void* rp, int lo, int hi, F&& consume, K&& keep) {
-    constexpr int N = Vec<BF16>::N;
-    constexpr int TILE = kThreads * N * U;
-    const int full_end = VEC ? lo + ((hi - lo) / TILE) * TILE : lo;
-    int t0 = lo;
-    if (t0 < full_end) {
-        uint4 cur[U];
-        load_tile<BF16, U>(cur, rp, t0);
-        if (!keep()) return false;
-        for (; t0 + TILE < full_end; t0 += TILE) {
-            uint4 nxt[U];
-            load_tile<BF16, U>(nxt, rp, t0 + TILE);
-            Vec<BF16> v[U];
-            widen_tile<BF16, U>(v, cur);
-            consume(v, t0);
-#pragma unroll
-            for (int u = 0; u < U; ++u) cur[u] = nxt[u];
-        }
-        Vec<BF16> v[U];
-        widen_tile<BF16, U>(v, cur);
-        consume(v, t0);
-        t0 += TILE;
-    } else if (!keep()) {
-        return false;
-    }
-    for (; t0 < hi; t0 += TILE) {
-        Vec<BF16> v[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            v[u] = load_vec<BF16, VEC>(rp, t0 + (u * kThreads + threadIdx.x) * N, hi, neg_inf());
-        consume(v, t0);
-    }
-    return true;
-}
-
-__device__ __forceinline__ MaxSum block_combine(MaxSum v, float c) {
-    __shared__ float s_m[kWaves], s_s[kWaves];
-    v = wave_combine(v, c);
-    const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
-    if (l == 0) { s_m[w] = v.m; s_s[w] = v.s; }
-    __syncthreads();
-    MaxSum r{s_m[0], s_s[0]};
-#pragma unroll
-    for (int k = 1; k < kWaves; ++k) r = combine(r, MaxSum{s_m[k], s_s[k]}, c);
-    return r;
-}
-
-__device__ __forceinline__ ArgMax block_argmax(ArgMax v) {
-    __shared__ float s_v[kWaves];
-    __shared__ int s_i[kWaves];
-    v = wave_argmax(v);
-    const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
-    if (l == 0) { s_v[w] = v.v; s_i[w] = v.i; }
-    __syncthreads();
-    ArgMax r{s_v[0], s_i[0]};
-#pragma unroll
-    for (int k = 1; k < kWaves; ++k) r = better(r, ArgMax{s_v[k], s_i[k]});
-    return r;
-}
-
-// ------------------------------------------------------------------ statistics pass
-
-// Workgroup (chunk ci, row slot s, request b).  Slots 0..G are target rows,
-// G+1..2G draft rows (sampling only).  Rows past gamma_b are abandoned after
-// their first loads are issued, so the gamma_b load never stalls the stream.
-template <bool BF16, bool VEC, bool GREEDY>
-__global__ __launch_bounds__(kThreads) void k_stats(VerifyParams P) {
-    const int ci = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
-    const bool is_target = s <= P.G;
-    const int i = is_target ? s : s - (P.G + 1);
-    const void* rp = is_target ? target_row(P, b, i, BF16) : draft_row(P, b, i, BF16);
-    const int lo = ci * P.chunk;
-    const int hi = min(P.V, lo + P.chunk);
-    auto keep = [&]() {
-        if (!P.gamma) return true;
-        const int g = request_gamma(P, b);
-        return is_target ? i <= g : i < g;
-    };
-    constexpr int N = Vec<BF16>::N;
-    float4* slot = P.part + (static_cast<size_t>(b) * P.rows + s) * P.nc + ci;
-    if constexpr (GREEDY) {
-        // Each lane visits its elements in ascending index order, so a strict
-        // ">" keeps the lowest index among equal maxima.
-        ArgMax best{neg_inf(), 0x7fffffff};
-        bool nan = false;
-        auto consume = [&](const Vec<BF16> (&v)[kUnroll], int t0) {
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int e = t0 + (u * kThreads + threadIdx.x) * N;
-#pragma unroll
-                for (int k = 0; k < N; ++k) {
-                    const float x = v[u].x[k];
-                    nan |= (x != x);
-                    const bool first = best.i == 0x7fffffff && e + k < hi;
-                    if (x > best.v || first) { best.v = x; best.i = e + k; }
-                }
-            }
-        };
-        if (!stream_row<BF16, VEC, kUnroll>(rp, lo, hi, consume, keep)) return;
-        const ArgMax r = block_argmax(best);
-        const bool any_nan = __syncthreads_or(nan);
-        if (threadIdx.x == 0)
-            *slot = make_float4(r.v, __uint_as_float(static_cast<uint32_t>(r.i) |
-                                                     (any_nan ? 0x80000000u : 0u)), 0.0f, 0.0f);
-    } else {
-        // the token this row judges (target) or proposed (draft); its logit
-        // rides along with the partial of the chunk that holds it
-        const int d = i < P.G ? P.tokens[static_cast<size_t>(b) * P.G + i] : -1;
-        const float c = P.c;
-        float m = neg_inf(), sum = 0.0f;
-        auto consume = [&](const Vec<BF16> (&v)[kUnroll], int) {
-            float tm = neg_inf();
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-                for (int k = 0; k < N; ++k) tm = fmaxf(tm, v[u].x[k]);
-            const float mn = fmaxf(m, tm);
-            if (mn == neg_inf()) return;
-            float part = 0.0f;
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                float q = 0.0f;
-#pragma unroll
-                for (int k = 0; k < N; ++k) q += __builtin_amdgcn_exp2f((v[u].x[k] - mn) * c);
-                part += q;
-            }
-            sum = (m == neg_inf() ? 0.0f : sum * exp2f((m - mn) * c)) + part;
-            m = mn;
-        };
-        if (!stream_row<BF16, VEC, kUnroll>(rp, lo, hi, consume, keep)) return;
-        const MaxSum r = block_combine(MaxSum{m, sum}, c);
-        if (threadIdx.x == 0) {
-            const float zd = (d >= lo && d < hi) ? load_logit<BF16>(rp, d) : 0.0f;
-            *slot = make_float4(r.m, r.s, zd, 0.0f);
-        }
-    }
-}
 
 // ------------------------------------------------------------------ sampling pass
 
@@ -841,13 +674,12 @@ specdec_status_t launch_all(const specdec_verify_desc_t* d, const VerifyParams& 
         else
             hipLaunchKernelGGL(kernel, grid, block, 0, stream, P);
     };
-    if (d->mode == SPECDEC_GREEDY) {
-        launch(k_stats<BF16, VEC, true>, dim3(L.nc, L.rows, d->batch), e0, e1);
-        if (hipGetLastError() != hipSuccess) return SPECDEC_ERR_DEVICE;
+    const bool greedy = d->mode == SPECDEC_GREEDY;
+    if (launch_stats(P, BF16, VEC, greedy, dim3(L.nc, L.rows, d->batch), stream, e0, e1) != SPECDEC_OK)
+        return SPECDEC_ERR_DEVICE;
+    if (greedy) {
         launch(k_decide_greedy, dim3(d->batch), e2, e3);
     } else {
-        launch(k_stats<BF16, VEC, false>, dim3(L.nc, L.rows, d->batch), e0, e1);
-        if (hipGetLastError() != hipSuccess) return SPECDEC_ERR_DEVICE;
         if (L.wide)
             launch(k_decide_sample<BF16, VEC, kMassGroupWide>, dim3(L.wpr, d->batch), e2, e3);
         else

@@ -116,6 +116,11 @@ __device__ __forceinline__ float block_sum(float v) {
     return r;
 }
 
+// The statistics pass (one partial per chunk of every used row); start/stop
+// events (both null, or both set) bracket the kernel.
+specdec_status_t launch_stats(const VerifyParams& P, bool bf16, bool vec, bool greedy, dim3 grid,
+                              hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+
 // Truncation mode (top-k and/or top-p): one pass that selects and records
 // every used row's kept tokens, then the per-request decision over them.
 specdec_status_t launch_truncated(const VerifyParams& P, bool bf16, bool vec, hipStream_t stream,
