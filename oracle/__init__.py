@@ -23,6 +23,8 @@ LIB = os.path.join(HERE, "liboracle.so")
 FLAG_RESIDUAL_FALLBACK = 0x2
 FLAG_NONFINITE = 0x4
 FLAG_TOKEN_RANGE = 0x8
+FLAG_EOS = 0x80
+FLAG_LENGTH = 0x100
 
 
 def _compile(src: str, out: str) -> None:
@@ -58,7 +60,7 @@ class _Args(ctypes.Structure):
                 ("greedy", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("temperature", ctypes.c_double), ("top_p", ctypes.c_double),
                 ("seed", ctypes.c_uint64), ("round", ctypes.c_uint32),
-                ("pad_", ctypes.c_int32)]
+                ("eos_token", ctypes.c_int32)]
 
 
 def _ptr(a: Optional[np.ndarray]):
@@ -71,8 +73,8 @@ class Oracle:
     def __init__(self, path: str):
         L = ctypes.CDLL(path)
         P = ctypes.c_void_p
-        L.oracle_verify.argtypes = [ctypes.POINTER(_Args), P, P, P, P, P, ctypes.c_int32,
-                                    P, P, P, P, P, P, P, P, P]
+        L.oracle_verify.argtypes = [ctypes.POINTER(_Args), P, P, P, P, P, P, ctypes.c_int32,
+                                    P, P, P, P, P, P, P, P, P, P]
         L.oracle_verify.restype = ctypes.c_int
         L.oracle_row_distribution.argtypes = [P, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
                                               ctypes.c_int32, ctypes.c_double, P, P]
@@ -81,6 +83,8 @@ class Oracle:
         L.oracle_philox4x32_10.restype = None
         L.oracle_commit_kv.argtypes = [ctypes.c_int32] * 7 + [ctypes.c_int64, P, P, P, P, P, P]
         L.oracle_commit_kv.restype = ctypes.c_int
+        L.oracle_rollback_kv.argtypes = [ctypes.c_int32] * 7 + [ctypes.c_int64, P, P, P, P, P]
+        L.oracle_rollback_kv.restype = ctypes.c_int
         self.lib = L
         self.path = path
 
@@ -109,8 +113,13 @@ class Oracle:
                gamma: Optional[np.ndarray] = None, *, greedy: bool = False,
                temperature: float = 1.0, top_k: int = 0, top_p: float = 1.0,
                seed: int = 0, round: int = 0, requests=None,
-               u_accept: Optional[np.ndarray] = None, u_sample: Optional[np.ndarray] = None):
-        """Run the oracle on (a subset of) a padded batch.  Returns a dict of arrays."""
+               u_accept: Optional[np.ndarray] = None, u_sample: Optional[np.ndarray] = None,
+               eos_token: int = -1, max_tokens: Optional[np.ndarray] = None):
+        """Run the oracle on (a subset of) a padded batch.  Returns a dict of arrays.
+
+        eos_token (-1: none) and max_tokens ([B] per-request token budget, or
+        None) cut the committed list; accept_count is then the number of
+        drafts left in it and num_tokens its length."""
         target = np.ascontiguousarray(target)
         B, G1, V = target.shape
         G = G1 - 1
@@ -131,10 +140,14 @@ class Oracle:
             u_accept = np.ascontiguousarray(u_accept, dtype=np.float64)
             u_sample = np.ascontiguousarray(u_sample, dtype=np.float64)
             assert u_accept.shape == (n, G + 1) and u_sample.shape == (n, G + 1)
+        if max_tokens is not None:
+            max_tokens = np.ascontiguousarray(max_tokens, dtype=np.int32)
+            assert max_tokens.shape == (B,)
         a = _Args(B, G, V, int(is_bf16), int(greedy), int(top_k), float(temperature),
-                  float(top_p), int(seed) & (2**64 - 1), int(round) & 0xFFFFFFFF, 0)
+                  float(top_p), int(seed) & (2**64 - 1), int(round) & 0xFFFFFFFF, int(eos_token))
         out = {
             "accept_count": np.zeros(n, np.int32),
+            "num_tokens": np.zeros(n, np.int32),
             "out_tokens": np.zeros((n, G + 1), np.int32),
             "p_draft": np.zeros((n, G), np.float64),
             "q_draft": np.zeros((n, G), np.float64),
@@ -143,8 +156,9 @@ class Oracle:
             "near_pos": np.zeros(n, np.int32),
         }
         rc = self.lib.oracle_verify(ctypes.byref(a), _ptr(target), _ptr(draft), _ptr(tokens),
-                                 _ptr(gamma), _ptr(ids), n, _ptr(u_accept), _ptr(u_sample),
-                                 _ptr(out["accept_count"]), _ptr(out["out_tokens"]),
+                                 _ptr(gamma), _ptr(max_tokens), _ptr(ids), n, _ptr(u_accept),
+                                 _ptr(u_sample), _ptr(out["accept_count"]),
+                                 _ptr(out["num_tokens"]), _ptr(out["out_tokens"]),
                                  _ptr(out["p_draft"]), _ptr(out["q_draft"]),
                                  _ptr(out["residual_mass"]), _ptr(out["flags"]),
                                  _ptr(out["near_pos"]))
@@ -169,6 +183,22 @@ class Oracle:
                                     _ptr(acc), _ptr(gam), _ptr(seq_lens))
         if rc != 0:
             raise ValueError(f"oracle_commit_kv rejected its arguments (code {rc})")
+
+
+    def rollback_kv(self, pool: np.ndarray, block_table: np.ndarray, accept_count: np.ndarray,
+                    seq_lens: np.ndarray, gamma_max: int, gamma=None):
+        """Roll back a draft cache in place (``pool`` uint16, ``seq_lens`` int32)."""
+        Lp, two, NB, BS, H, D = pool.shape
+        assert two == 2 and pool.dtype == np.uint16 and pool.flags.c_contiguous
+        assert seq_lens.dtype == np.int32 and seq_lens.flags.c_contiguous
+        bt = np.ascontiguousarray(block_table, dtype=np.int32)
+        acc = np.ascontiguousarray(accept_count, dtype=np.int32)
+        gam = None if gamma is None else np.ascontiguousarray(gamma, dtype=np.int32)
+        rc = self.lib.oracle_rollback_kv(bt.shape[0], int(gamma_max), Lp, H, D, BS, bt.shape[1],
+                                      NB, _ptr(pool), _ptr(bt), _ptr(acc), _ptr(gam),
+                                      _ptr(seq_lens))
+        if rc != 0:
+            raise ValueError(f"oracle_rollback_kv rejected its arguments (code {rc})")
 
 
 _default: Optional[Oracle] = None
@@ -198,3 +228,7 @@ def verify(*args, **kw):
 
 def commit_kv(*args, **kw):
     return default().commit_kv(*args, **kw)
+
+
+def rollback_kv(*args, **kw):
+    return default().rollback_kv(*args, **kw)

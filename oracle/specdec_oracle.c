@@ -29,6 +29,9 @@
  *  - uniforms: Philox4x32-10, key = seed, counter = (position, request,
  *    round, 0); word 0 -> accept test, word 1 -> sampling; u = (w >> 8) 2^-24;
  *  - greedy ties go to the lowest token index, on raw logits;
+ *  - the committed list (accepted drafts, then the drawn token) is cut after
+ *    its first end-of-sequence token and after the request's token budget;
+ *    the accept count reported is the number of drafts left in it;
  *  - top-k keeps every token whose raw logit is >= the k-th largest raw
  *    logit; top-p then orders the kept tokens by probability (equivalently
  *    raw logit) descending, index ascending, keeps the shortest prefix whose
@@ -211,11 +214,40 @@ static void note_near(int32_t* near, int32_t pos)
     if (*near < 0 || pos < *near) *near = pos;
 }
 
+/* Round end.  The list the step would commit is out[0..m]: the m accepted
+ * drafts, then the correction or bonus token.  Decoding stops after an
+ * end-of-sequence token and once the output-length limit is reached ([KB]
+ * s.03: EOS and length limits can end a round early; [TUT] s.5.2: nothing
+ * after an EOS in the candidate block may reach the cache; [TUT] s.11: the
+ * loop runs while fewer than max_new_tokens were produced and stops after
+ * emitting EOS).  So the list is cut after its first EOS and after `budget`
+ * tokens (budget < 0: no limit).  Returns the number of tokens kept; *kept_m
+ * receives the drafts among them, and the rest of out[] becomes -1. */
+static int32_t round_end(int32_t m, int32_t G, int32_t* out, int32_t eos, int32_t budget,
+                         uint32_t* fl, int32_t* kept_m)
+{
+    int32_t n = m + 1;
+    int32_t e = -1;
+    if (eos >= 0)
+        for (int32_t j = 0; j <= m; ++j)
+            if (out[j] == eos) { e = j; break; }
+    if (e >= 0) n = e + 1;
+    if (budget >= 0 && budget <= n) {
+        n = budget;
+        *fl |= ORACLE_FLAG_LENGTH;
+    }
+    if (e >= 0 && e < n) *fl |= ORACLE_FLAG_EOS;
+    for (int32_t j = n; j <= G; ++j) out[j] = -1;
+    *kept_m = m < n ? m : n;
+    return n;
+}
+
 int oracle_verify(const oracle_verify_args* a, const void* target, const void* draft,
                   const int32_t* draft_tokens, const int32_t* gamma,
+                  const int32_t* max_tokens,
                   const int32_t* req_ids, int32_t n,
                   const double* u_accept_in, const double* u_sample_in,
-                  int32_t* accept_count, int32_t* out_tokens,
+                  int32_t* accept_count, int32_t* num_tokens, int32_t* out_tokens,
                   double* p_draft, double* q_draft, double* residual_mass,
                   uint32_t* flags, int32_t* near_pos)
 {
@@ -244,6 +276,7 @@ int oracle_verify(const oracle_verify_args* a, const void* target, const void* d
         int32_t* out = out_tokens + (size_t)k * (G + 1);
         uint32_t fl = 0;
         int32_t near = -1;
+        int32_t committed_m = 0;
         for (int32_t j = 0; j <= G; ++j) out[j] = -1;
         for (int32_t i = 0; i < gb; ++i)
             if (d[i] < 0 || d[i] >= V) fl |= ORACLE_FLAG_TOKEN_RANGE;
@@ -264,8 +297,8 @@ int oracle_verify(const oracle_verify_args* a, const void* target, const void* d
                 ++m;
             }
             out[m] = g;
-            accept_count[k] = m;
             if (residual_mass) residual_mass[k] = 0.0;
+            committed_m = m;
         } else {
             for (int32_t i = 0; i < gb; ++i)
                 if (row_nonfinite(row_ptr(draft, a->is_bf16, (int64_t)b * G + i, V), a->is_bf16, V))
@@ -364,7 +397,14 @@ int oracle_verify(const oracle_verify_args* a, const void* target, const void* d
             if (fabs(us[m] - C_prev / R) < NEAR_EPS || fabs(us[m] - C / R) < NEAR_EPS)
                 note_near(&near, m);
             out[m] = tok;
-            accept_count[k] = m;
+            committed_m = m;
+        }
+        {
+            const int32_t budget = max_tokens ? (max_tokens[b] < 0 ? 0 : max_tokens[b]) : -1;
+            int32_t kept_m = 0;
+            const int32_t nt = round_end(committed_m, G, out, a->eos_token, budget, &fl, &kept_m);
+            accept_count[k] = kept_m;
+            if (num_tokens) num_tokens[k] = nt;
         }
         if (flags) flags[k] = fl;
         if (near_pos) near_pos[k] = near;
@@ -414,5 +454,46 @@ int oracle_commit_kv(int32_t B, int32_t G, int32_t L, int32_t H, int32_t D, int3
         }
     }
     for (int32_t b = 0; b < B; ++b) seq_lens[b] = seq_lens[b] + accept_count[b] + 1;
+    return 0;
+}
+
+/* The draft's cache after verification ([KB] s.06: the target cache and the
+ * draft cache must both return to the committed context; [TUT] s.5.1: their
+ * lengths equal the committed length after every round; [TUT] s.5.2: trim to
+ * t+m, then the replacement token is fed to both; [TUT] s.5.3: on a full
+ * accept the draft still has to consume the last draft and the bonus).
+ * Proposing wrote the pending token and d_0..d_{gamma-2} at positions
+ * t..t+gamma-1, so the entries of the pending token and the m accepted drafts
+ * (as far as they were written) stay, the later ones are zero-filled, and the
+ * length becomes t + min(m + 1, gamma). */
+int oracle_rollback_kv(int32_t B, int32_t G, int32_t L, int32_t H, int32_t D, int32_t bs,
+                       int32_t max_blocks, int64_t num_blocks, uint16_t* pool,
+                       const int32_t* block_table, const int32_t* accept_count,
+                       const int32_t* gamma, int32_t* seq_lens)
+{
+    const size_t row = (size_t)H * (size_t)D;
+    for (int32_t b = 0; b < B; ++b) {
+        const int32_t gb = gamma ? gamma[b] : G;
+        const int32_t m = accept_count[b];
+        const int32_t t = seq_lens[b];
+        if (gb < 0 || gb > G || m < 0 || m > gb || t < 0) return -1;
+        for (int32_t j = m + 1; j < gb; ++j) {
+            const int64_t pos = (int64_t)t + j;
+            if (pos / bs >= max_blocks) return -2;
+            const int32_t blk = block_table[(size_t)b * max_blocks + pos / bs];
+            if (blk < 0 || blk >= num_blocks) return -3;
+            const int64_t off = pos % bs;
+            for (int32_t l = 0; l < L; ++l)
+                for (int32_t kv = 0; kv < 2; ++kv)
+                    memset(pool + ((((size_t)l * 2 + kv) * (size_t)num_blocks + (size_t)blk)
+                                   * (size_t)bs + (size_t)off) * row,
+                           0, row * sizeof(uint16_t));
+        }
+    }
+    for (int32_t b = 0; b < B; ++b) {
+        const int32_t gb = gamma ? gamma[b] : G;
+        const int32_t keep = accept_count[b] + 1 < gb ? accept_count[b] + 1 : gb;
+        seq_lens[b] = seq_lens[b] + keep;
+    }
     return 0;
 }

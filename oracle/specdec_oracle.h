@@ -31,28 +31,35 @@ typedef struct {
     double top_p;         /* 1.0: off */
     uint64_t seed;        /* Philox key */
     uint32_t round;       /* Philox counter word 2 */
-    int32_t pad_;
+    int32_t eos_token;    /* -1: none; else the end-of-sequence token id */
 } oracle_verify_args;
 
 /* Flag bits (per request), same meaning as on the device side. */
 #define ORACLE_FLAG_RESIDUAL_FALLBACK 0x2u  /* rejected but sum of [p-q]+ <= 0 */
 #define ORACLE_FLAG_NONFINITE         0x4u  /* NaN or +inf in a used row */
 #define ORACLE_FLAG_TOKEN_RANGE       0x8u  /* a draft token outside [0,V) */
+#define ORACLE_FLAG_EOS               0x80u /* the committed list ends with an EOS token */
+#define ORACLE_FLAG_LENGTH            0x100u /* the token budget ended the committed list */
 
 /* Verify selected requests.  req_ids[n] picks the requests (NULL: 0..B-1 and
  * n must equal B); every output is indexed by the position in that list:
- *   accept_count [n], out_tokens [n][G+1] (-1 padded), p_draft/q_draft [n][G]
+ *   accept_count [n]: drafts kept (after the EOS / budget cut),
+ *   num_tokens [n] (may be NULL): tokens committed this round,
+ *   out_tokens [n][G+1] (-1 padded), p_draft/q_draft [n][G]
  *   (0 past gamma_i; untouched in greedy mode), residual_mass [n], flags [n],
  *   near_pos [n]: smallest position whose output-determining decision lies
  *   within 1e-6 of its threshold (accept test, inverse-CDF edge or top-p cut),
  *   -1 if none.
  * u_accept / u_sample [n][G+1] (may be NULL) replace the Philox uniforms.
+ * max_tokens [B] (indexed by request, may be NULL): the most tokens request b
+ *   may commit this round (values below 0 count as 0).
  * Returns 0, or a negative value on a malformed argument. */
 int oracle_verify(const oracle_verify_args* a, const void* target, const void* draft,
                   const int32_t* draft_tokens, const int32_t* gamma,
+                  const int32_t* max_tokens,
                   const int32_t* req_ids, int32_t n,
                   const double* u_accept, const double* u_sample,
-                  int32_t* accept_count, int32_t* out_tokens,
+                  int32_t* accept_count, int32_t* num_tokens, int32_t* out_tokens,
                   double* p_draft, double* q_draft, double* residual_mass,
                   uint32_t* flags, int32_t* near_pos);
 
@@ -77,6 +84,18 @@ int oracle_commit_kv(int32_t batch, int32_t gamma_max, int32_t layers, int32_t k
                      int64_t num_blocks, const uint16_t* scratch, uint16_t* pool,
                      const int32_t* block_table, const int32_t* accept_count,
                      const int32_t* gamma, int32_t* seq_lens);
+
+/* Roll back the draft model's paged cache after verification.  While
+ * proposing, the draft wrote positions t_i .. t_i + gamma_i - 1 in place (the
+ * pending token, then d_0 .. d_{gamma_i - 2}).  Positions t_i + m_i + 1 ..
+ * t_i + gamma_i - 1 are zero-filled and seq_lens becomes
+ * t_i + min(m_i + 1, gamma_i).
+ *   pool [L][2][num_blocks][block][H][D] bf16 bits; the rest as for commit.
+ * Returns 0, or a negative value if a needed block-table entry is invalid. */
+int oracle_rollback_kv(int32_t batch, int32_t gamma_max, int32_t layers, int32_t kv_heads,
+                       int32_t head_dim, int32_t block_size, int32_t max_blocks,
+                       int64_t num_blocks, uint16_t* pool, const int32_t* block_table,
+                       const int32_t* accept_count, const int32_t* gamma, int32_t* seq_lens);
 
 #ifdef __cplusplus
 }

@@ -195,6 +195,155 @@ def pin_greedy_matches_numpy(orc, trials=40):
     return errs
 
 
+
+# ------------------------------------------------- round end: EOS and budget
+
+def pin_round_end_walkthrough(orc):
+    """The walk-through with an EOS token and a token budget (hand-derived
+    table in tests/golden/round_end_walkthrough.txt)."""
+    draft = [1, 2, 3, 4]
+    V, G = 8, len(draft)
+    rng = np.random.default_rng(17)
+    rows = {"W": _greedy_rows([1, 2, 5, 4, 6], V, rng)[None],
+            "A": _greedy_rows([1, 2, 3, 4, 6], V, rng)[None]}
+    errs = []
+    with open(os.path.join(GOLDEN, "round_end_walkthrough.txt")) as f:
+        lines = [ln.strip() for ln in f if ln.strip() and not ln.startswith("#")]
+    for ln in lines:
+        head, toks, kept, flags = [x.strip() for x in ln.split("|")]
+        scen, eos, budget = head.split()
+        eos, budget = int(eos), int(budget)
+        want = [int(x) for x in toks.split()]
+        mt = None if budget < 0 else np.array([budget], np.int32)
+        r = orc.verify(rows[scen], None, np.array([draft], np.int32), greedy=True,
+                       eos_token=eos, max_tokens=mt)
+        got = [int(x) for x in r["out_tokens"][0] if x >= 0]
+        fl = int(r["flags"][0])
+        got_flags = set()
+        if fl & 0x80:
+            got_flags.add("E")
+        if fl & 0x100:
+            got_flags.add("L")
+        want_flags = set(flags.split()) - {"-"}
+        if (got != want or int(r["accept_count"][0]) != int(kept)
+                or int(r["num_tokens"][0]) != len(want) or got_flags != want_flags
+                or np.any(r["out_tokens"][0][len(want):] != -1)):
+            errs.append(f"{ln}: got {got} kept={r['accept_count'][0]} n={r['num_tokens'][0]} "
+                        f"flags={sorted(got_flags)}")
+    return errs
+
+
+def _ar_greedy(rows_argmax, d, gb, eos, budget):
+    """Target-only greedy decoding of one round, a token at a time: emit the
+    target's choice, stop after EOS or at the budget, and continue to the next
+    row only while the draft agreed ("Speculative decoding tutorial" s.6: the
+    accepted drafts are exactly what the target alone would have produced)."""
+    out = []
+    i = 0
+    while True:
+        if budget is not None and len(out) >= budget:
+            break
+        tok = int(rows_argmax[i])
+        out.append(tok)
+        if tok == eos:
+            break
+        if i < gb and d[i] == tok:
+            i += 1
+            continue
+        break
+    return out
+
+
+def pin_round_end_autoregressive(orc, B=300):
+    """Greedy round end on random rows with planted EOS tokens == target-only
+    decoding of the same rows, token by token."""
+    rng = np.random.default_rng(19)
+    G, V, eos = 6, 12, 3
+    z = rng.standard_normal((B, G + 1, V)).astype(np.float32)
+    am = np.argmax(z, axis=2)
+    d = am[:, :G].copy().astype(np.int32)
+    flip = rng.random((B, G)) < 0.25
+    d[flip] = (d[flip] + 1 + rng.integers(0, V - 1, flip.sum())) % V
+    gam = rng.integers(0, G + 1, B).astype(np.int32)
+    budget = rng.integers(-1, G + 3, B).astype(np.int32)
+    r = orc.verify(z, None, d, gam, greedy=True, eos_token=eos, max_tokens=budget)
+    errs = []
+    for b in range(B):
+        want = _ar_greedy(am[b], d[b], int(gam[b]), eos, max(int(budget[b]), 0))
+        got = [int(x) for x in r["out_tokens"][b] if x >= 0]
+        kept = sum(1 for i in range(min(len(want), int(gam[b]))) if want[i] == d[b, i]
+                   and all(want[j] == d[b, j] for j in range(i)))
+        if got != want or int(r["num_tokens"][b]) != len(want) or int(r["accept_count"][b]) != kept:
+            errs.append(f"request {b}: got {got} (kept {r['accept_count'][b]}), "
+                        f"target-only decoding gives {want} (kept {kept})")
+    return errs
+
+
+def pin_round_end_prefix(orc, B=200):
+    """Sampling: with the same uniforms, the list cut by EOS / budget is the
+    uncut list up to its first EOS or the budget, whichever comes first."""
+    rng = np.random.default_rng(23)
+    G, V, T, eos = 5, 6, 1.0, 2
+    tgt = rng.standard_normal((B, G + 1, V)).astype(np.float32)
+    drf = (tgt[:, :G] + 0.5 * rng.standard_normal((B, G, V))).astype(np.float32)
+    d = rng.integers(0, V, (B, G)).astype(np.int32)
+    budget = rng.integers(0, G + 3, B).astype(np.int32)
+    full = orc.verify(tgt, drf, d, temperature=T, seed=41)
+    cut = orc.verify(tgt, drf, d, temperature=T, seed=41, eos_token=eos, max_tokens=budget)
+    errs = []
+    for b in range(B):
+        lst = [int(x) for x in full["out_tokens"][b] if x >= 0]
+        n = len(lst)
+        if eos in lst:
+            n = lst.index(eos) + 1
+        n = min(n, int(budget[b]))
+        got = [int(x) for x in cut["out_tokens"][b] if x >= 0]
+        m = int(full["accept_count"][b])
+        if got != lst[:n] or int(cut["accept_count"][b]) != min(m, n):
+            errs.append(f"request {b}: {got} vs {lst[:n]}")
+    return errs
+
+
+# ------------------------------------------------- draft-cache rollback
+
+def pin_rollback_invariants(orc, B=7):
+    """Draft cache after a round: the proposer wrote positions t..t+gamma-1;
+    the entries of the committed prefix stay, later ones are zero, nothing
+    else moves, and once the draft has consumed the tokens it is missing the
+    lengths of the two caches agree ("Speculative decoding tutorial" s.5.1
+    and s.5.3; AI-infra KB M013 s.06)."""
+    rng = np.random.default_rng(37)
+    G, L, H, D, bs = 5, 2, 2, 4, 4
+    t = rng.integers(0, 17, B).astype(np.int32)
+    gam = rng.integers(0, G + 1, B).astype(np.int32)
+    m = np.array([rng.integers(0, g + 1) for g in gam], np.int32)
+    max_blocks = (17 + G + bs) // bs
+    nb = B * max_blocks + 2
+    table = rng.permutation(nb)[:B * max_blocks].reshape(B, max_blocks).astype(np.int32)
+    pool = rng.integers(1, 2 ** 16, (L, 2, nb, bs, H, D)).astype(np.uint16)
+    before = pool.copy()
+    seq = t.copy()
+    orc.rollback_kv(pool, table, m, seq, G, gam)
+    errs = []
+    for b in range(B):
+        target_len = t[b] + m[b] + 1            # after the target's commit
+        missing = target_len - seq[b]           # tokens the draft still has to consume
+        if missing != (1 if m[b] == gam[b] else 0):
+            errs.append(f"request {b}: draft length {seq[b]}, target {target_len}, "
+                        f"m={m[b]} gamma={gam[b]}")
+        for pos in range(max_blocks * bs):
+            blk, off = table[b, pos // bs], pos % bs
+            now, old = pool[:, :, blk, off], before[:, :, blk, off]
+            rejected = t[b] + m[b] + 1 <= pos <= t[b] + gam[b] - 1
+            if rejected and np.any(now != 0):
+                errs.append(f"request {b}: rejected position {pos} still holds data")
+            if not rejected and not np.array_equal(now, old):
+                errs.append(f"request {b}: position {pos} changed")
+    untouched = np.setdiff1d(np.arange(nb), table.ravel())
+    if not np.array_equal(pool[:, :, untouched], before[:, :, untouched]):
+        errs.append("a block outside every table changed")
+    return errs
+
 # ------------------------------------------------- closed form at fixed alpha
 
 def _fixed_alpha_batch(alpha, gamma, B):
@@ -492,4 +641,8 @@ ALL_PINS = {
     "invariants": pin_invariants,
     "truncation": pin_truncation,
     "commit_numpy": pin_commit_numpy,
+    "round_end_walkthrough": pin_round_end_walkthrough,
+    "round_end_autoregressive": pin_round_end_autoregressive,
+    "round_end_prefix": pin_round_end_prefix,
+    "rollback_invariants": pin_rollback_invariants,
 }

@@ -55,6 +55,20 @@ MUTANTS = [
      "seq_lens[b] = seq_lens[b] + accept_count[b];", ["commit_numpy"]),
     ("residual_sign_flipped", "double diff = pm[v] - qm[v];", "double diff = qm[v] - pm[v];",
      ["three_option_grid", "invariants"]),
+    ("eos_itself_dropped", "if (e >= 0) n = e + 1;", "if (e >= 0) n = e;",
+     ["round_end_walkthrough", "round_end_autoregressive"]),
+    ("eos_search_skips_drawn_token", "for (int32_t j = 0; j <= m; ++j)\n            if (out[j] == eos)",
+     "for (int32_t j = 0; j < m; ++j)\n            if (out[j] == eos)",
+     ["round_end_walkthrough", "round_end_autoregressive"]),
+    ("budget_one_too_many", "n = budget;", "n = budget + 1 < m + 1 ? budget + 1 : m + 1;",
+     ["round_end_walkthrough", "round_end_prefix"]),
+    ("accept_count_not_cut", "*kept_m = m < n ? m : n;", "*kept_m = m;",
+     ["round_end_walkthrough", "round_end_autoregressive"]),
+    ("rollback_keeps_first_rejected", "for (int32_t j = m + 1; j < gb; ++j) {",
+     "for (int32_t j = m + 2; j < gb; ++j) {", ["rollback_invariants"]),
+    ("rollback_length_past_written",
+     "const int32_t keep = accept_count[b] + 1 < gb ? accept_count[b] + 1 : gb;",
+     "const int32_t keep = accept_count[b] + 1;", ["rollback_invariants"]),
 ]
 
 
