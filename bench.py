@@ -19,8 +19,10 @@ cpu_baseline: the CPU oracle (single-threaded C, double precision) run on the
 same input set for a bounded time.
 
 Other workloads (--workload) print the same JSON line for that recipe; the
-ones with a paged KV cache time verify + commit (seq_lens restored from a
-copy before every commit so that each step commits the same window).
+ones with a paged KV cache time a whole round: verify, the target's commit
+and the draft cache's rollback (seq_lens restored from a copy before every
+commit and rollback so that each step touches the same window).  Their JSON
+line also lists each kernel's average time and algorithmic bandwidth.
 """
 from __future__ import annotations
 
@@ -143,19 +145,38 @@ def main() -> int:
               "ws": torch.zeros(sd.specdec_commit_kv_workspace_bytes(kdesc), dtype=torch.uint8,
                                 device=dev)}
         log(f"  paged KV pool {kvin.pool.nbytes / 1e6:.1f} MB uploaded")
+        dpool, _, dseq, nb = synth.make_draft_kv_inputs(wl0, kvin)
+        DK = wl0.draft_kv
+        ddesc = sd.make_kv_desc(wl0.batch, wl0.gamma_max, DK.layers, DK.kv_heads, DK.head_dim,
+                                DK.block_size, kvin.block_table.shape[1], nb)
+        kv.update({"ddesc": ddesc, "dpool": torch.from_numpy(dpool.view(np.int16)).to(dev),
+                   "dseq0": torch.from_numpy(dseq).to(dev),
+                   "dseq": torch.from_numpy(dseq.copy()).to(dev),
+                   "dws": torch.zeros(sd.specdec_commit_kv_workspace_bytes(ddesc),
+                                      dtype=torch.uint8, device=dev)})
+        log(f"  draft KV pool {dpool.nbytes / 1e6:.1f} MB uploaded")
 
     desc = sd.make_verify_desc(wl0.batch, wl0.gamma_max, wl0.vocab, bf16=bf16, greedy=greedy,
                                temperature=wl0.temperature, top_k=wl0.top_k, top_p=wl0.top_p,
                                seed=wl0.verify_seed)
     ver = sd.Verifier(desc, dev)
 
+    def commit(k: int) -> None:
+        kv["seq"].copy_(kv["seq0"])
+        sd.specdec_commit_kv(kv["desc"], kv["scratch"], kv["pool"], kv["table"],
+                             ver.accept_count, dev_in[k]["gamma"], kv["seq"], None, kv["ws"])
+
+    def rollback(k: int) -> None:
+        kv["dseq"].copy_(kv["dseq0"])
+        sd.specdec_rollback_kv(kv["ddesc"], kv["dpool"], kv["table"], ver.accept_count,
+                               dev_in[k]["gamma"], kv["dseq"], None, kv["dws"])
+
     def step(k: int) -> None:
         d = dev_in[k]
         ver(d["target"], d["draft"], d["tokens"], d["gamma"])
         if kv is not None:
-            kv["seq"].copy_(kv["seq0"])
-            sd.specdec_commit_kv(kv["desc"], kv["scratch"], kv["pool"], kv["table"],
-                                 ver.accept_count, d["gamma"], kv["seq"], None, kv["ws"])
+            commit(k)
+            rollback(k)
 
     # ---- eager reference outputs, then the graph of one pass over the sets
     eager = []
@@ -223,14 +244,54 @@ def main() -> int:
         d = dev_in[j % sets]
         h = ev.handles[4 * j:4 * j + 4]
         e = h
-        sd.specdec_verify_profiled(desc, d["target"], d["draft"], d["tokens"], d["gamma"],
-                                   ver.accept_count, ver.out_tokens, ver.p_draft, ver.q_draft,
-                                   ver.residual_mass, ver.flags, ver.workspace, e)
+        sd.specdec_verify_profiled(desc, d["target"], d["draft"], d["tokens"], d["gamma"], None,
+                                   ver.accept_count, ver.num_tokens, ver.out_tokens, ver.p_draft,
+                                   ver.q_draft, ver.residual_mass, ver.flags, ver.workspace, e)
     torch.cuda.synchronize()
     k1 = np.array([ev.elapsed_ms(4 * j, 4 * j + 1) for j in range(n_prof)]) * 1e-3  # seconds
     k2 = np.array([ev.elapsed_ms(4 * j + 2, 4 * j + 3) for j in range(n_prof)]) * 1e-3
     ev.close()
     k1_avg = float(k1.mean())
+    kernels = {}
+    if kv is not None:
+        # commit and rollback run on torch's current stream: torch events bracket them
+        tc = []
+        for j in range(n_prof):
+            k = j % sets
+            d = dev_in[k]
+            ver(d["target"], d["draft"], d["tokens"], d["gamma"])
+            kv["seq"].copy_(kv["seq0"])
+            kv["dseq"].copy_(kv["dseq0"])
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record()
+            sd.specdec_commit_kv(kv["desc"], kv["scratch"], kv["pool"], kv["table"],
+                                 ver.accept_count, d["gamma"], kv["seq"], None, kv["ws"])
+            e[1].record()
+            e[2].record()
+            sd.specdec_rollback_kv(kv["ddesc"], kv["dpool"], kv["table"], ver.accept_count,
+                                   d["gamma"], kv["dseq"], None, kv["dws"])
+            e[3].record()
+            tc.append(e)
+        torch.cuda.synchronize()
+        t_commit = np.array([e[0].elapsed_time(e[1]) for e in tc]) * 1e-3
+        t_roll = np.array([e[2].elapsed_time(e[3]) for e in tc]) * 1e-3
+        K, DK = wl0.kv, wl0.draft_kv
+        slot_t = K.layers * 2 * K.kv_heads * K.head_dim * 2
+        slot_d = DK.layers * 2 * DK.kv_heads * DK.head_dim * 2
+        cb, rb = [], []
+        for k in range(sets):
+            m = eager[k]["accept_count"].cpu().numpy().astype(np.int64)
+            g = host[k]["gamma"].astype(np.int64)
+            # copy: read + write per kept slot; zero-fill: write per rejected slot
+            cb.append(float(((m + 1) * 2 + (g - m)).sum() * slot_t))
+            rb.append(float(np.maximum(g - 1 - m, 0).sum() * slot_d))
+        for name, t, by in (("k_commit", t_commit, cb), ("k_rollback", t_roll, rb)):
+            avg = float(t.mean())
+            b_avg = float(np.mean(by))
+            kernels[name] = {"avg_us": avg * 1e6, "bytes_per_launch": b_avg,
+                             "GBps": b_avg / avg / 1e9, "frac": b_avg / avg / 1e9 / HBM_PEAK_GBPS}
+            log(f"{name}: avg {avg * 1e6:.2f} us, {b_avg / 1e6:.2f} MB algorithmic, "
+                f"{b_avg / avg / 1e9:.1f} GB/s")
 
     # algorithmic bytes of one statistics launch: used rows read once, draft
     # tokens read, per-request outputs written
@@ -292,10 +353,14 @@ def main() -> int:
         "config": {"workload": wl0.name, "batch": B, "gamma_max": G, "vocab": wl0.vocab,
                    "logits": wl0.dtype, "mode": wl0.mode, "temperature": wl0.temperature,
                    "top_k": wl0.top_k, "top_p": wl0.top_p, "kv_commit": wl0.kv is not None,
+                   "draft_rollback": wl0.draft_kv is not None,
                    "rotating_input_sets": sets,
                    "launch": "hipgraph" if graph is not None else "eager",
                    "committed_tokens_per_s": committed / sec_per_step,
                    "step_GBps": alg_k1 / sec_per_step / 1e9},
+        "kernels": dict({"stats": {"avg_us": k1_avg * 1e6, "bytes_per_launch": alg_k1,
+                                   "GBps": achieved, "frac": achieved / HBM_PEAK_GBPS},
+                         "decision": {"avg_us": float(k2.mean()) * 1e6}}, **kernels),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(f"k_stats_sample__{wl0.name}") if not greedy else None,

@@ -13,6 +13,8 @@
  *                      last target row.
  *   specdec_commit_kv  copies the K/V of the kept slots into a paged cache,
  *                      invalidates the rejected slots and sets the new length.
+ *   specdec_rollback_kv  brings the draft model's paged cache back to the
+ *                      committed sequence.
  *
  * Passages defining these operations (page title, section):
  *   - "Speculative decoding tutorial: from distribution preservation and
@@ -55,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SPECDEC_ABI_VERSION 1
+#define SPECDEC_ABI_VERSION 2
 
 typedef enum specdec_status {
     SPECDEC_OK = 0,
@@ -75,6 +77,8 @@ typedef enum specdec_mode { SPECDEC_SAMPLE = 0, SPECDEC_GREEDY = 1 } specdec_mod
 #define SPECDEC_FLAG_BAD_BLOCK         0x10u /* commit: window not committable, slot(s) skipped */
 #define SPECDEC_FLAG_BAD_GAMMA         0x20u /* verify: gamma_b outside [0,G], clamped into it */
 #define SPECDEC_FLAG_TRUNC_OVERFLOW    0x40u /* verify: a kept set exceeded 1024 tokens (ties): clipped */
+#define SPECDEC_FLAG_EOS               0x80u /* verify: the committed list ends with the EOS token */
+#define SPECDEC_FLAG_LENGTH            0x100u /* verify: the token budget ended the committed list */
 
 /* ------------------------------------------------------------------ verify */
 
@@ -89,7 +93,8 @@ typedef struct specdec_verify_desc {
     float top_p;          /* SAMPLE only: (0, 1]; 1 = off */
     uint64_t seed;        /* Philox4x32-10 key (low word, high word) */
     uint32_t round;       /* Philox counter word 2 (make it differ per round) */
-    uint32_t reserved;    /* must be 0 */
+    int32_t eos_token;    /* -1: no end-of-sequence handling; else the EOS id in [0, V).
+                             NOTE: a zero-filled descriptor means EOS = token 0. */
 } specdec_verify_desc_t;
 
 /* Bytes of device workspace specdec_verify needs for `desc` (0 on a bad
@@ -102,6 +107,16 @@ size_t specdec_verify_workspace_bytes(const specdec_verify_desc_t* desc);
 
 /* Verify one round for B requests.
  *
+ * Round end (AI-infra KB M013 s.03: an end-of-sequence token or the output
+ * length limit can end a round early; "Speculative decoding tutorial" s.11:
+ * decoding continues while fewer than max_new_tokens were produced and stops
+ * right after emitting EOS; s.5.2: nothing after an EOS in the candidate
+ * block may reach the cache).  The list a round commits is d_0..d_{m-1} and
+ * then the correction or bonus token; it is cut after its first EOS token
+ * (desc->eos_token >= 0) and after max_tokens[b] tokens.  accept_count then
+ * counts the drafts left in the list, so specdec_commit_kv and
+ * specdec_rollback_kv keep exactly the committed tokens' K/V.
+ *
  * Inputs (device, row-major, 16-byte aligned for full speed):
  *   target_logits [B][G+1][V] dtype: row i of request b is the target's
  *       distribution that judges draft token i (row 0 is produced by the
@@ -113,10 +128,19 @@ size_t specdec_verify_workspace_bytes(const specdec_verify_desc_t* desc);
  *   gamma         [B] int32 in [0, G], or NULL (every request uses G).  Rows
  *       and tokens past gamma_b are never read.  A value outside [0, G] is
  *       clamped into it and flagged (SPECDEC_FLAG_BAD_GAMMA).
+ *   max_tokens    [B] int32, or NULL (no limit): the most tokens request b
+ *       may commit this round (its remaining output length); values below 0
+ *       count as 0.
  * Outputs (device):
- *   accept_count  [B] int32: m_b, the number of leading drafts kept.
+ *   accept_count  [B] int32: m_b, the number of leading drafts kept (after
+ *       the round-end cut; without EOS or budget, the accepted prefix).
+ *   num_tokens    [B] int32, or NULL: n_b, tokens committed this round
+ *       (m_b + 1 unless the cut removed the drawn token).  When it is m_b + 1
+ *       and neither EOS nor LENGTH is flagged, out_tokens[b][m_b] is the next
+ *       round's pending token; otherwise the request has finished.
  *   out_tokens    [B][G+1] int32: d_0..d_{m-1}, then the correction (m <
- *       gamma_b) or bonus (m = gamma_b) token at index m, then -1.
+ *       gamma_b) or bonus (m = gamma_b) token at index m, then -1; with a
+ *       round-end cut, -1 from index n_b on.
  *   p_draft, q_draft [B][G] float, or NULL: p_i(d_i), q_i(d_i) after
  *       temperature and truncation (0 past gamma_b).  Not written in GREEDY.
  *   residual_mass [B] float, or NULL: sum_v max(p_m - q_m, 0) at the rejected
@@ -143,7 +167,8 @@ size_t specdec_verify_workspace_bytes(const specdec_verify_desc_t* desc);
 specdec_status_t specdec_verify(const specdec_verify_desc_t* desc,
                                 const void* target_logits, const void* draft_logits,
                                 const int32_t* draft_tokens, const int32_t* gamma,
-                                int32_t* accept_count, int32_t* out_tokens,
+                                const int32_t* max_tokens,
+                                int32_t* accept_count, int32_t* num_tokens, int32_t* out_tokens,
                                 float* p_draft, float* q_draft, float* residual_mass,
                                 uint32_t* flags,
                                 void* workspace, size_t workspace_bytes,
@@ -160,7 +185,9 @@ specdec_status_t specdec_verify(const specdec_verify_desc_t* desc,
 specdec_status_t specdec_verify_profiled(const specdec_verify_desc_t* desc,
                                          const void* target_logits, const void* draft_logits,
                                          const int32_t* draft_tokens, const int32_t* gamma,
-                                         int32_t* accept_count, int32_t* out_tokens,
+                                         const int32_t* max_tokens,
+                                         int32_t* accept_count, int32_t* num_tokens,
+                                         int32_t* out_tokens,
                                          float* p_draft, float* q_draft, float* residual_mass,
                                          uint32_t* flags,
                                          void* workspace, size_t workspace_bytes,
@@ -210,6 +237,34 @@ specdec_status_t specdec_commit_kv(const specdec_kv_desc_t* desc,
                                    const int32_t* gamma, int32_t* seq_lens, uint32_t* flags,
                                    void* workspace, size_t workspace_bytes,
                                    hipStream_t stream);
+
+/* Bring the draft model's paged cache back to the committed sequence after
+ * specdec_verify (AI-infra KB M013 s.06: the target cache and the draft cache
+ * must both return to the correct context; "Speculative decoding tutorial"
+ * s.5.1: both lengths equal the committed length after a round, s.5.2: both
+ * are trimmed to the accepted prefix, s.5.3: on a full accept the draft
+ * still has to consume the last draft and the bonus token).
+ *   kv_pool     the draft's [L][2][num_blocks][block_size][H][D] bf16 pool
+ *       (desc describes the draft model), updated in place.
+ *   block_table [B][max_blocks_per_req] int32, accept_count [B] (m_b),
+ *       gamma [B] or NULL (= G): as for specdec_commit_kv.
+ *   seq_lens    [B] int32, in place: in t_b, the draft cache length before
+ *       the round (equal to the target's); out t_b + min(m_b + 1, gamma_b).
+ *   flags       [B] uint32 or NULL: SPECDEC_FLAG_BAD_BLOCK as for commit.
+ * While proposing, the draft wrote its own K/V in place for the pending token
+ * and d_0 .. d_{gamma_b - 2}, i.e. positions t_b .. t_b + gamma_b - 1.  The
+ * entries of the pending token and of the kept drafts stay; positions
+ * t_b + m_b + 1 .. t_b + gamma_b - 1 are zero-filled (bf16 +0.0); nothing
+ * else is touched.  After the call the draft cache holds the committed
+ * sequence except, when m_b = gamma_b, d_{gamma_b - 1}, which the draft has
+ * not consumed yet; the new pending token is consumed by the next round.
+ * Workspace: specdec_commit_kv_workspace_bytes(desc) bytes, same rules.
+ * Errors: as for specdec_commit_kv. */
+specdec_status_t specdec_rollback_kv(const specdec_kv_desc_t* desc, void* kv_pool,
+                                     const int32_t* block_table, const int32_t* accept_count,
+                                     const int32_t* gamma, int32_t* seq_lens, uint32_t* flags,
+                                     void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
 
 /* ------------------------------------------------------------------ misc */
 

@@ -30,10 +30,12 @@ FLAG_TOKEN_RANGE = 0x8
 FLAG_BAD_BLOCK = 0x10
 FLAG_BAD_GAMMA = 0x20
 FLAG_TRUNC_OVERFLOW = 0x40
+FLAG_EOS = 0x80
+FLAG_LENGTH = 0x100
 
 # exported symbols of include/specdec.h
 EXPORTS = ("specdec_verify_workspace_bytes", "specdec_verify", "specdec_verify_profiled",
-           "specdec_commit_kv_workspace_bytes", "specdec_commit_kv",
+           "specdec_commit_kv_workspace_bytes", "specdec_commit_kv", "specdec_rollback_kv",
            "specdec_workspace_clear", "specdec_status_string", "specdec_abi_version")
 
 
@@ -43,7 +45,7 @@ class VerifyDesc(ctypes.Structure):
                 ("mode", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("temperature", ctypes.c_float), ("top_p", ctypes.c_float),
                 ("seed", ctypes.c_uint64), ("round", ctypes.c_uint32),
-                ("reserved", ctypes.c_uint32)]
+                ("eos_token", ctypes.c_int32)]
 
 
 class KVDesc(ctypes.Structure):
@@ -73,14 +75,16 @@ def lib() -> ctypes.CDLL:
         P, S = ctypes.c_void_p, ctypes.c_size_t
         L.specdec_verify_workspace_bytes.argtypes = [ctypes.POINTER(VerifyDesc)]
         L.specdec_verify_workspace_bytes.restype = S
-        L.specdec_verify.argtypes = [ctypes.POINTER(VerifyDesc)] + [P] * 11 + [S, P]
+        L.specdec_verify.argtypes = [ctypes.POINTER(VerifyDesc)] + [P] * 13 + [S, P]
         L.specdec_verify.restype = ctypes.c_int
-        L.specdec_verify_profiled.argtypes = [ctypes.POINTER(VerifyDesc)] + [P] * 11 + [S, P, P]
+        L.specdec_verify_profiled.argtypes = [ctypes.POINTER(VerifyDesc)] + [P] * 13 + [S, P, P]
         L.specdec_verify_profiled.restype = ctypes.c_int
         L.specdec_commit_kv_workspace_bytes.argtypes = [ctypes.POINTER(KVDesc)]
         L.specdec_commit_kv_workspace_bytes.restype = S
         L.specdec_commit_kv.argtypes = [ctypes.POINTER(KVDesc)] + [P] * 8 + [S, P]
         L.specdec_commit_kv.restype = ctypes.c_int
+        L.specdec_rollback_kv.argtypes = [ctypes.POINTER(KVDesc)] + [P] * 7 + [S, P]
+        L.specdec_rollback_kv.restype = ctypes.c_int
         L.specdec_workspace_clear.argtypes = [P, S, P]
         L.specdec_workspace_clear.restype = ctypes.c_int
         L.specdec_status_string.argtypes = [ctypes.c_int]
@@ -118,12 +122,12 @@ def _stream(stream) -> Optional[int]:
 
 
 def make_verify_desc(batch, gamma_max, vocab, *, bf16=True, greedy=False, temperature=1.0,
-                     top_k=0, top_p=1.0, seed=0, round=0) -> VerifyDesc:
+                     top_k=0, top_p=1.0, seed=0, round=0, eos_token=-1) -> VerifyDesc:
     return VerifyDesc(int(batch), int(gamma_max), int(vocab),
                       SPECDEC_BF16 if bf16 else SPECDEC_F32,
                       SPECDEC_GREEDY if greedy else SPECDEC_SAMPLE, int(top_k),
                       float(temperature), float(top_p), int(seed) & (2 ** 64 - 1),
-                      int(round) & 0xFFFFFFFF, 0)
+                      int(round) & 0xFFFFFFFF, int(eos_token))
 
 
 def make_kv_desc(batch, gamma_max, num_layers, num_kv_heads, head_dim, block_size,
@@ -141,12 +145,14 @@ def specdec_commit_kv_workspace_bytes(desc: KVDesc) -> int:
 
 
 def specdec_verify(desc: VerifyDesc, target_logits, draft_logits, draft_tokens, gamma,
-                   accept_count, out_tokens, p_draft, q_draft, residual_mass, flags,
-                   workspace, workspace_bytes: Optional[int] = None, stream=None) -> None:
+                   max_tokens, accept_count, num_tokens, out_tokens, p_draft, q_draft,
+                   residual_mass, flags, workspace, workspace_bytes: Optional[int] = None,
+                   stream=None) -> None:
     if workspace_bytes is None:
         workspace_bytes = workspace.numel() * workspace.element_size()
     st = lib().specdec_verify(ctypes.byref(desc), _ptr(target_logits), _ptr(draft_logits),
-                              _ptr(draft_tokens), _ptr(gamma), _ptr(accept_count),
+                              _ptr(draft_tokens), _ptr(gamma), _ptr(max_tokens),
+                              _ptr(accept_count), _ptr(num_tokens),
                               _ptr(out_tokens), _ptr(p_draft), _ptr(q_draft),
                               _ptr(residual_mass), _ptr(flags), _ptr(workspace),
                               int(workspace_bytes), _stream(stream))
@@ -155,15 +161,16 @@ def specdec_verify(desc: VerifyDesc, target_logits, draft_logits, draft_tokens, 
 
 
 def specdec_verify_profiled(desc: VerifyDesc, target_logits, draft_logits, draft_tokens, gamma,
-                            accept_count, out_tokens, p_draft, q_draft, residual_mass, flags,
-                            workspace, stage_events, workspace_bytes: Optional[int] = None,
-                            stream=None) -> None:
+                            max_tokens, accept_count, num_tokens, out_tokens, p_draft, q_draft,
+                            residual_mass, flags, workspace, stage_events,
+                            workspace_bytes: Optional[int] = None, stream=None) -> None:
     """stage_events: four raw hipEvent_t handles (ints; None entries allowed)."""
     if workspace_bytes is None:
         workspace_bytes = workspace.numel() * workspace.element_size()
     handles = (ctypes.c_void_p * 4)(*[None if e is None else int(e) for e in stage_events])
     st = lib().specdec_verify_profiled(ctypes.byref(desc), _ptr(target_logits), _ptr(draft_logits),
-                                       _ptr(draft_tokens), _ptr(gamma), _ptr(accept_count),
+                                       _ptr(draft_tokens), _ptr(gamma), _ptr(max_tokens),
+                                       _ptr(accept_count), _ptr(num_tokens),
                                        _ptr(out_tokens), _ptr(p_draft), _ptr(q_draft),
                                        _ptr(residual_mass), _ptr(flags), _ptr(workspace),
                                        int(workspace_bytes), _stream(stream), handles)
@@ -182,6 +189,18 @@ def specdec_commit_kv(desc: KVDesc, scratch_kv, kv_pool, block_table, accept_cou
                                  int(workspace_bytes), _stream(stream))
     if st != SPECDEC_OK:
         raise SpecdecError(st, "specdec_commit_kv")
+
+
+def specdec_rollback_kv(desc: KVDesc, kv_pool, block_table, accept_count, gamma, seq_lens,
+                        flags, workspace, workspace_bytes: Optional[int] = None,
+                        stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = lib().specdec_rollback_kv(ctypes.byref(desc), _ptr(kv_pool), _ptr(block_table),
+                                   _ptr(accept_count), _ptr(gamma), _ptr(seq_lens), _ptr(flags),
+                                   _ptr(workspace), int(workspace_bytes), _stream(stream))
+    if st != SPECDEC_OK:
+        raise SpecdecError(st, "specdec_rollback_kv")
 
 
 def specdec_workspace_clear(workspace, nbytes: Optional[int] = None, stream=None) -> None:
@@ -241,16 +260,19 @@ class Verifier:
         self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=device)
         i32, f32 = torch.int32, torch.float32
         self.accept_count = torch.empty(B, dtype=i32, device=device)
+        self.num_tokens = torch.empty(B, dtype=i32, device=device)
         self.out_tokens = torch.empty(B, G + 1, dtype=i32, device=device)
         self.p_draft = torch.empty(B, G, dtype=f32, device=device)
         self.q_draft = torch.empty(B, G, dtype=f32, device=device)
         self.residual_mass = torch.empty(B, dtype=f32, device=device)
         self.flags = torch.empty(B, dtype=torch.int32, device=device)
 
-    def __call__(self, target, draft, draft_tokens, gamma=None, stream=None):
-        specdec_verify(self.desc, target, draft, draft_tokens, gamma, self.accept_count,
-                       self.out_tokens, self.p_draft, self.q_draft, self.residual_mass,
-                       self.flags, self.workspace, stream=stream)
-        return {"accept_count": self.accept_count, "out_tokens": self.out_tokens,
+    def __call__(self, target, draft, draft_tokens, gamma=None, max_tokens=None, stream=None):
+        specdec_verify(self.desc, target, draft, draft_tokens, gamma, max_tokens,
+                       self.accept_count, self.num_tokens, self.out_tokens, self.p_draft,
+                       self.q_draft, self.residual_mass, self.flags, self.workspace,
+                       stream=stream)
+        return {"accept_count": self.accept_count, "num_tokens": self.num_tokens,
+                "out_tokens": self.out_tokens,
                 "p_draft": self.p_draft, "q_draft": self.q_draft,
                 "residual_mass": self.residual_mass, "flags": self.flags}

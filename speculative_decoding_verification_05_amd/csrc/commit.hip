@@ -8,6 +8,14 @@
 // verify pass produced, the accepted ones are written into the cache, on a
 // paged (block-table) cache).
 //
+// specdec_rollback_kv runs the same kernel on the draft model's cache with
+// no scratch: the draft wrote its own entries for positions t..t+gamma-1
+// while proposing, so the kept ones stay where they are, positions
+// t+m+1..t+gamma-1 are zero-filled and the length becomes t+min(m+1, gamma)
+// (KB M013 s.06: both caches return to the committed context; tutorial
+// s.5.1-5.3: equal lengths, trim to the accepted prefix, and on a full accept
+// the draft still has to consume its last draft and the bonus).
+//
 // One workgroup per (slot j, request b) moves that slot's L x 2 runs of
 // H x D bf16 with 16-byte vector loads and stores: the scratch side is one
 // contiguous span, the pool side one contiguous run per (layer, K|V) inside a
@@ -23,7 +31,7 @@ namespace specdec {
 namespace {
 
 struct CommitParams {
-    const uint16_t* scratch;   // [B][G+1][L][2][H][D]
+    const uint16_t* scratch;   // [B][G+1][L][2][H][D]; null: draft-cache rollback
     uint16_t* pool;            // [L][2][NB][BS][H][D]
     const int32_t* table;      // [B][maxb]
     const int32_t* accept;
@@ -42,40 +50,40 @@ __global__ __launch_bounds__(kThreads) void k_commit(CommitParams P) {
     const int g = P.gamma ? P.gamma[b] : P.G;
     const int m = P.accept[b];
     const int t = P.seq_lens[b];
+    const bool rollback = P.scratch == nullptr;
     bool bad = false;
     if (g < 0 || g > P.G) {
         bad = true;
-    } else if (j <= g) {
-        if (m < 0 || m > g || t < 0) {
+    } else if (m < 0 || m > g || t < 0) {
+        bad = j == 0;  // flagged once; nothing of the request is touched
+    } else if (rollback ? (j > m && j < g) : j <= g) {
+        const int64_t pos = static_cast<int64_t>(t) + j;
+        const int64_t lb = pos / P.BS;
+        const int off = static_cast<int>(pos % P.BS);
+        const int32_t phys = lb < P.maxb ? P.table[static_cast<size_t>(b) * P.maxb + lb] : -1;
+        if (phys < 0 || phys >= P.NB) {
             bad = true;
         } else {
-            const int64_t pos = static_cast<int64_t>(t) + j;
-            const int64_t lb = pos / P.BS;
-            const int off = static_cast<int>(pos % P.BS);
-            const int32_t phys = lb < P.maxb ? P.table[static_cast<size_t>(b) * P.maxb + lb] : -1;
-            if (phys < 0 || phys >= P.NB) {
-                bad = true;
+            const bool keep = !rollback && j <= m;
+            const size_t runs = static_cast<size_t>(P.L) * 2;
+            const uint16_t* src = keep ? P.scratch + (static_cast<size_t>(b) * (P.G + 1) + j) * runs * P.hd
+                                       : nullptr;
+            if (VEC) {
+                const int nv = P.hd / 8;  // 16-byte vectors per run
+                const size_t total = runs * nv;
+                for (size_t e = threadIdx.x; e < total; e += kThreads) {
+                    const size_t run = e / nv, w = e % nv;  // run = layer * 2 + (K|V)
+                    uint16_t* dst = P.pool + ((run * P.NB + phys) * P.BS + off) * P.hd + w * 8;
+                    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+                    if (keep) v = *reinterpret_cast<const uint4*>(src + run * P.hd + w * 8);
+                    *reinterpret_cast<uint4*>(dst) = v;
+                }
             } else {
-                const bool keep = j <= m;
-                const size_t runs = static_cast<size_t>(P.L) * 2;
-                const uint16_t* src = P.scratch + (static_cast<size_t>(b) * (P.G + 1) + j) * runs * P.hd;
-                if (VEC) {
-                    const int nv = P.hd / 8;  // 16-byte vectors per run
-                    const size_t total = runs * nv;
-                    for (size_t e = threadIdx.x; e < total; e += kThreads) {
-                        const size_t run = e / nv, w = e % nv;  // run = layer * 2 + (K|V)
-                        uint16_t* dst = P.pool + ((run * P.NB + phys) * P.BS + off) * P.hd + w * 8;
-                        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-                        if (keep) v = *reinterpret_cast<const uint4*>(src + run * P.hd + w * 8);
-                        *reinterpret_cast<uint4*>(dst) = v;
-                    }
-                } else {
-                    const size_t total = runs * P.hd;
-                    for (size_t e = threadIdx.x; e < total; e += kThreads) {
-                        const size_t run = e / P.hd, w = e % P.hd;
-                        uint16_t* dst = P.pool + ((run * P.NB + phys) * P.BS + off) * P.hd + w;
-                        *dst = keep ? src[run * P.hd + w] : static_cast<uint16_t>(0);
-                    }
+                const size_t total = runs * P.hd;
+                for (size_t e = threadIdx.x; e < total; e += kThreads) {
+                    const size_t run = e / P.hd, w = e % P.hd;
+                    uint16_t* dst = P.pool + ((run * P.NB + phys) * P.BS + off) * P.hd + w;
+                    *dst = keep ? src[run * P.hd + w] : static_cast<uint16_t>(0);
                 }
             }
         }
@@ -93,7 +101,7 @@ __global__ __launch_bounds__(kThreads) void k_commit(CommitParams P) {
     }
     __syncthreads();
     if (s_last && threadIdx.x == 0 && g >= 0 && g <= P.G && m >= 0 && m <= g && t >= 0)
-        P.seq_lens[b] = t + m + 1;
+        P.seq_lens[b] = t + (rollback ? min(m + 1, g) : m + 1);
 }
 
 __global__ void k_fill_zero(uint32_t* p, size_t n) {
@@ -111,6 +119,11 @@ bool valid_kv(const specdec_kv_desc_t* d) {
     if (static_cast<int64_t>(d->num_kv_heads) * d->head_dim > (1 << 24)) return false;
     return true;
 }
+
+specdec_status_t launch_commit(const specdec_kv_desc_t* d, const void* scratch_kv, void* kv_pool,
+                               const int32_t* block_table, const int32_t* accept_count,
+                               const int32_t* gamma, int32_t* seq_lens, uint32_t* flags,
+                               void* workspace, hipStream_t stream);
 
 }  // namespace
 }  // namespace specdec
@@ -133,6 +146,17 @@ extern "C" specdec_status_t specdec_commit_kv(const specdec_kv_desc_t* d, const 
     if (workspace_bytes < specdec_commit_kv_workspace_bytes(d)) return SPECDEC_ERR_WORKSPACE_TOO_SMALL;
     if ((reinterpret_cast<uintptr_t>(workspace) & 3u) != 0) return SPECDEC_ERR_INVALID_ARGUMENT;
     if (d->batch == 0) return SPECDEC_OK;
+    return launch_commit(d, scratch_kv, kv_pool, block_table, accept_count, gamma, seq_lens, flags,
+                         workspace, stream);
+}
+
+namespace specdec {
+namespace {
+
+specdec_status_t launch_commit(const specdec_kv_desc_t* d, const void* scratch_kv, void* kv_pool,
+                               const int32_t* block_table, const int32_t* accept_count,
+                               const int32_t* gamma, int32_t* seq_lens, uint32_t* flags,
+                               void* workspace, hipStream_t stream) {
     CommitParams P{};
     P.scratch = static_cast<const uint16_t*>(scratch_kv);
     P.pool = static_cast<uint16_t*>(kv_pool);
@@ -159,6 +183,25 @@ extern "C" specdec_status_t specdec_commit_kv(const specdec_kv_desc_t* d, const 
     else
         hipLaunchKernelGGL(k_commit<false>, grid, dim3(kThreads), 0, stream, P);
     return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_DEVICE;
+}
+
+}  // namespace
+}  // namespace specdec
+
+extern "C" specdec_status_t specdec_rollback_kv(const specdec_kv_desc_t* d, void* kv_pool,
+                                                const int32_t* block_table,
+                                                const int32_t* accept_count, const int32_t* gamma,
+                                                int32_t* seq_lens, uint32_t* flags,
+                                                void* workspace, size_t workspace_bytes,
+                                                hipStream_t stream) {
+    if (!valid_kv(d)) return SPECDEC_ERR_INVALID_ARGUMENT;
+    if (!kv_pool || !block_table || !accept_count || !seq_lens || !workspace)
+        return SPECDEC_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < specdec_commit_kv_workspace_bytes(d)) return SPECDEC_ERR_WORKSPACE_TOO_SMALL;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 3u) != 0) return SPECDEC_ERR_INVALID_ARGUMENT;
+    if (d->batch == 0) return SPECDEC_OK;
+    return launch_commit(d, nullptr, kv_pool, block_table, accept_count, gamma, seq_lens, flags,
+                         workspace, stream);
 }
 
 extern "C" specdec_status_t specdec_workspace_clear(void* workspace, size_t bytes, hipStream_t stream) {

@@ -764,14 +764,12 @@ __global__ __launch_bounds__(kThreads) void k_decide_trunc(VerifyParams P) {
 
     if (w == 0) {
         const int i = l;
-        int32_t* out = P.out_tokens + static_cast<size_t>(b) * (P.G + 1);
-        if (i <= P.G) out[i] = i < m ? s_d[i] : (i == m ? token : -1);
+        fl2 |= write_round(P, b, m, i < m ? s_d[i] : token);
         if (i < P.G) {
             if (P.p_draft) P.p_draft[static_cast<size_t>(b) * P.G + i] = i < g ? s_p[i] : 0.0f;
             if (P.q_draft) P.q_draft[static_cast<size_t>(b) * P.G + i] = i < g ? s_q[i] : 0.0f;
         }
         if (i == 0) {
-            P.accept_count[b] = m;
             if (P.residual_mass) P.residual_mass[b] = R_report;
             if (P.flags) P.flags[b] = s_fl | fl2;
         }

@@ -484,14 +484,12 @@ __global__ __launch_bounds__(kThreads) void k_decide_sample(VerifyParams P) {
     if (token == 0x7fffffff) token = lastp;
 
     if (w == 0) {
-        int32_t* out = P.out_tokens + static_cast<size_t>(b) * (P.G + 1);
-        if (i <= P.G) out[i] = i < m ? d : (i == m ? token : -1);
+        fl2 |= write_round(P, b, m, i < m ? d : token);
         if (i < P.G) {
             if (P.p_draft) P.p_draft[static_cast<size_t>(b) * P.G + i] = pd;
             if (P.q_draft) P.q_draft[static_cast<size_t>(b) * P.G + i] = qd;
         }
         if (i == 0) {
-            P.accept_count[b] = m;
             if (P.residual_mass) P.residual_mass[b] = R_report;
             if (P.flags) P.flags[b] = s_fl | fl2;
         }
@@ -554,12 +552,8 @@ __global__ __launch_bounds__(kThreads) void k_decide_greedy(VerifyParams P) {
     const uint64_t mask = __ballot(acc);
     const int m = min(g, static_cast<int>(__builtin_ctzll(~mask)));
     fl = wave_or(fl);
-    int32_t* out = P.out_tokens + static_cast<size_t>(b) * (P.G + 1);
-    if (i <= P.G) out[i] = i < m ? d : (i == m ? s_arg[m] : -1);
-    if (i == 0) {
-        P.accept_count[b] = m;
-        if (P.flags) P.flags[b] = fl;
-    }
+    fl |= write_round(P, b, m, i < m ? d : s_arg[m]);
+    if (i == 0 && P.flags) P.flags[b] = fl;
 }
 
 // ------------------------------------------------------------------ host side
@@ -601,7 +595,7 @@ bool valid_desc(const specdec_verify_desc_t* d) {
     // at most 1024 sampling chunks of 256 lanes x 2 x 16 bytes per row
     if (d->vocab > 1024 * kThreads * kUnroll2 * (d->dtype == SPECDEC_BF16 ? 8 : 4)) return false;
     if (d->mode != SPECDEC_SAMPLE && d->mode != SPECDEC_GREEDY) return false;
-    if (d->reserved != 0) return false;
+    if (d->eos_token < -1 || d->eos_token >= d->vocab) return false;
     if (d->mode == SPECDEC_SAMPLE) {
         const float T = d->temperature;
         if (!(T > 0.0f) || !(T < 3.0e38f)) return false;
@@ -690,7 +684,8 @@ specdec_status_t launch_all(const specdec_verify_desc_t* d, const VerifyParams& 
 
 specdec_status_t verify_impl(const specdec_verify_desc_t* d, const void* target_logits,
                              const void* draft_logits, const int32_t* draft_tokens,
-                             const int32_t* gamma, int32_t* accept_count, int32_t* out_tokens,
+                             const int32_t* gamma, const int32_t* max_tokens,
+                             int32_t* accept_count, int32_t* num_tokens, int32_t* out_tokens,
                              float* p_draft, float* q_draft, float* residual_mass, uint32_t* flags,
                              void* workspace, size_t workspace_bytes, hipStream_t stream,
                              hipEvent_t* ev) {
@@ -711,7 +706,9 @@ specdec_status_t verify_impl(const specdec_verify_desc_t* d, const void* target_
     P.draft = draft_logits;
     P.tokens = draft_tokens;
     P.gamma = gamma;
+    P.max_tokens = max_tokens;
     P.accept_count = accept_count;
+    P.num_tokens = num_tokens;
     P.out_tokens = out_tokens;
     P.p_draft = p_draft;
     P.q_draft = q_draft;
@@ -738,6 +735,7 @@ specdec_status_t verify_impl(const specdec_verify_desc_t* d, const void* target_
     P.key0 = static_cast<uint32_t>(d->seed & 0xffffffffu);
     P.key1 = static_cast<uint32_t>(d->seed >> 32);
     P.round = d->round;
+    P.eos = d->eos_token;
 
     const bool bf16 = d->dtype == SPECDEC_BF16;
     const size_t es = bf16 ? 2 : 4;
@@ -764,21 +762,23 @@ extern "C" size_t specdec_verify_workspace_bytes(const specdec_verify_desc_t* de
 extern "C" specdec_status_t specdec_verify(const specdec_verify_desc_t* d,
                                            const void* target_logits, const void* draft_logits,
                                            const int32_t* draft_tokens, const int32_t* gamma,
-                                           int32_t* accept_count, int32_t* out_tokens,
+                                           const int32_t* max_tokens, int32_t* accept_count,
+                                           int32_t* num_tokens, int32_t* out_tokens,
                                            float* p_draft, float* q_draft, float* residual_mass,
                                            uint32_t* flags, void* workspace,
                                            size_t workspace_bytes, hipStream_t stream) {
-    return verify_impl(d, target_logits, draft_logits, draft_tokens, gamma, accept_count,
-                       out_tokens, p_draft, q_draft, residual_mass, flags, workspace,
-                       workspace_bytes, stream, nullptr);
+    return verify_impl(d, target_logits, draft_logits, draft_tokens, gamma, max_tokens,
+                       accept_count, num_tokens, out_tokens, p_draft, q_draft, residual_mass,
+                       flags, workspace, workspace_bytes, stream, nullptr);
 }
 
 extern "C" specdec_status_t specdec_verify_profiled(
     const specdec_verify_desc_t* d, const void* target_logits, const void* draft_logits,
-    const int32_t* draft_tokens, const int32_t* gamma, int32_t* accept_count,
-    int32_t* out_tokens, float* p_draft, float* q_draft, float* residual_mass, uint32_t* flags,
-    void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* stage_events) {
-    return verify_impl(d, target_logits, draft_logits, draft_tokens, gamma, accept_count,
-                       out_tokens, p_draft, q_draft, residual_mass, flags, workspace,
-                       workspace_bytes, stream, stage_events);
+    const int32_t* draft_tokens, const int32_t* gamma, const int32_t* max_tokens,
+    int32_t* accept_count, int32_t* num_tokens, int32_t* out_tokens, float* p_draft,
+    float* q_draft, float* residual_mass, uint32_t* flags, void* workspace,
+    size_t workspace_bytes, hipStream_t stream, hipEvent_t* stage_events) {
+    return verify_impl(d, target_logits, draft_logits, draft_tokens, gamma, max_tokens,
+                       accept_count, num_tokens, out_tokens, p_draft, q_draft, residual_mass,
+                       flags, workspace, workspace_bytes, stream, stage_events);
 }

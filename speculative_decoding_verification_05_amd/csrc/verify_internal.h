@@ -27,7 +27,9 @@ struct VerifyParams {
     const void* draft;
     const int32_t* tokens;
     const int32_t* gamma;
+    const int32_t* max_tokens;  // [B] token budget of the round, or null
     int32_t* accept_count;
+    int32_t* num_tokens;        // [B] or null
     int32_t* out_tokens;
     float* p_draft;
     float* q_draft;
@@ -44,6 +46,7 @@ struct VerifyParams {
     int wpr, cpw;       // sampling pass: workgroups per request, chunks per workgroup
     float c;            // log2(e) / T
     uint32_t key0, key1, round;
+    int eos;            // end-of-sequence token, -1: none
     // truncation (top-k / top-p) mode
     int top_k;          // 0 or >= V: no top-k
     float top_p;        // 1: no top-p
@@ -100,6 +103,40 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t total, u
     }
     __syncthreads();
     return s_last;
+}
+
+// Round end, on one wave (lane i = position i, i <= G).  The list the round
+// would commit is c_0..c_m: the accepted drafts d_0..d_{m-1}, then the drawn
+// token x; lane i passes c_i (ignored past m).  The list is cut after its
+// first end-of-sequence token and after the request's token budget (AI-infra
+// KB M013 s.03; "Speculative decoding tutorial" s.11 and s.5.2).  Writes
+// out_tokens (-1 past the cut), accept_count (drafts left: min(m, n)) and
+// num_tokens (n); returns the EOS / LENGTH flag bits (same in every lane).
+__device__ __forceinline__ uint32_t write_round(const VerifyParams& P, int b, int m, int c) {
+    const int i = threadIdx.x % kWave;
+    int n = m + 1;
+    uint32_t fl = 0;
+    int e = 64;
+    if (P.eos >= 0) {
+        const uint64_t hit = __ballot(i <= m && c == P.eos);
+        if (hit) e = __builtin_ctzll(hit);
+        n = min(n, e + 1);
+    }
+    if (P.max_tokens) {
+        const int cap = max(P.max_tokens[b], 0);
+        if (cap <= n) {
+            n = cap;
+            fl |= SPECDEC_FLAG_LENGTH;
+        }
+    }
+    if (e < n) fl |= SPECDEC_FLAG_EOS;
+    int32_t* out = P.out_tokens + static_cast<size_t>(b) * (P.G + 1);
+    if (i <= P.G) out[i] = i < n ? c : -1;
+    if (i == 0) {
+        P.accept_count[b] = min(m, n);
+        if (P.num_tokens) P.num_tokens[b] = n;
+    }
+    return fl;
 }
 
 // Sum over the kThreads lanes of a workgroup (same value returned to all).

@@ -24,6 +24,11 @@ pages; sizes are the full-scale cases used for parity and timing):
 * ``b512_ragged_v262144_kv`` B=512, gamma_i in U{1..8}, V=262144, bf16, T=1.0,
                               paged KV commit (32 layers x 8 heads x 128).
 
+The two KV workloads also carry a draft model's cache shape for the draft-cache
+rollback (the pages give none; a small model of the same family is assumed):
+24 layers x 2 heads x 64 beside the 28 x 4 x 128 target, and 18 layers x
+1 head x 256 beside the 32 x 8 x 128 target.
+
 The proposer itself is outside the verify step; draft tokens are emulated here
 by a Gumbel-max draw from the draft logits at the workload temperature
 (``argmax(z/T + G)``, G standard Gumbel), which is an exact categorical sample
@@ -43,6 +48,7 @@ import numpy as np
 # Stream tags: one independent stream per (request, purpose).
 _TAG_TARGET, _TAG_DRAFT, _TAG_TOKENS, _TAG_SIGMA, _TAG_GAMMA = 0, 1, 2, 3, 4
 _TAG_KV, _TAG_CTX, _TAG_ZIPF, _TAG_SWAP = 5, 6, 7, 8
+_TAG_DRAFT_KV = 9
 
 BF16_QNAN = np.uint16(0x7FC0)      # fill for padded (never used) logits rows
 KV_POISON = np.uint16(0x7FA5)      # fill for untouched KV-pool entries (a NaN)
@@ -79,6 +85,7 @@ class Workload:
     top_p: float = 1.0
     ragged: bool = False        # gamma_i ~ U{1..gamma_max}
     kv: Optional[KVShape] = None
+    draft_kv: Optional[KVShape] = None   # the draft model's cache (rollback)
     data_seed: int = 0
     verify_seed: int = 0
 
@@ -100,13 +107,15 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
              data_seed=1002, verify_seed=44),
     Workload("b256_g7_v151936_greedy_kv", 256, 7, 151936, "bf16", "greedy", 1.0, 3.0,
              "top_swap", swap_rate=0.25,
-             kv=KVShape(28, 4, 128, 16, 512, 4096), data_seed=1003, verify_seed=45),
+             kv=KVShape(28, 4, 128, 16, 512, 4096), draft_kv=KVShape(24, 2, 64, 16, 512, 4096),
+             data_seed=1003, verify_seed=45),
     Workload("b128_g4_v128256_topk50_topp09", 128, 4, 128256, "bf16", "sample", 0.7, 4.0,
              "noise_fixed", draft_sigma=0.8, zipf_s=1.1, top_k=50, top_p=0.9,
              data_seed=1004, verify_seed=46),
     Workload("b512_ragged_v262144_kv", 512, 8, 262144, "bf16", "sample", 1.0, 3.0,
              "noise_fixed", draft_sigma=0.6, ragged=True,
-             kv=KVShape(32, 8, 128, 16, 1024, 8192), data_seed=1005, verify_seed=47),
+             kv=KVShape(32, 8, 128, 16, 1024, 8192), draft_kv=KVShape(18, 1, 256, 16, 1024, 8192),
+             data_seed=1005, verify_seed=47),
 ]}
 
 HEADLINE = "b64_g4_v128256_bf16"
@@ -269,7 +278,7 @@ def kv_pool_shape(wl: Workload, num_blocks: int):
 
 
 def make_kv_inputs(wl: Workload, with_pool: bool = True,
-                   threads: Optional[int] = None) -> KVInputs:
+                   threads: Optional[int] = None, with_scratch: bool = True) -> KVInputs:
     """Scratch K/V for the gamma+1 verified slots, block table and context lengths.
 
     Only the (at most two) physical blocks that a request's commit window
@@ -296,18 +305,50 @@ def make_kv_inputs(wl: Workload, with_pool: bool = True,
         for blk in range(first[b], last[b] + 1):
             table[b, blk] = perm[k]
             k += 1
-    scratch = np.empty((B, G + 1, L, 2, H, D), dtype=np.uint16)
+    scratch = np.empty((B, G + 1, L, 2, H, D) if with_scratch else (0,), dtype=np.uint16)
 
     def one(b: int) -> None:
         r = _rng(wl.data_seed, b, _TAG_KV)
         scratch[b] = f32_to_bf16_bits(r.standard_normal((G + 1, L, 2, H, D), dtype=np.float32))
 
-    with ThreadPoolExecutor(threads or _pool_threads()) as ex:
-        list(ex.map(one, range(B)))
+    if with_scratch:
+        with ThreadPoolExecutor(threads or _pool_threads()) as ex:
+            list(ex.map(one, range(B)))
     pool = None
     if with_pool:
         pool = np.full(kv_pool_shape(wl, num_blocks), KV_POISON, dtype=np.uint16)
     return KVInputs(scratch, pool, table, seq, num_blocks)
+
+
+def make_draft_kv_inputs(wl: Workload, kv: Optional[KVInputs] = None,
+                         threads: Optional[int] = None):
+    """The draft model's paged cache at the end of proposing.
+
+    It shares the target's block table and context lengths (one table per
+    request for both models) and has its own pool of the same number of
+    blocks, shaped by ``wl.draft_kv``.  Positions t_i .. t_i + gamma_i - 1 hold
+    the draft's own K/V, written while it proposed (random bf16); every other
+    entry is poison.  Returns (pool, block_table, seq_lens, num_blocks).
+    """
+    if kv is None:
+        kv = make_kv_inputs(wl, with_pool=False, threads=threads, with_scratch=False)
+    dk = wl.draft_kv
+    assert dk is not None and dk.block_size == wl.kv.block_size
+    shape = (dk.layers, 2, kv.num_blocks, dk.block_size, dk.kv_heads, dk.head_dim)
+    pool = np.full(shape, KV_POISON, dtype=np.uint16)
+    bs = dk.block_size
+    for b in range(wl.batch):
+        g = request_gamma(wl, b)
+        if g == 0:
+            continue
+        r = _rng(wl.data_seed, b, _TAG_DRAFT_KV)
+        vals = f32_to_bf16_bits(r.standard_normal((g, dk.layers, 2, dk.kv_heads, dk.head_dim),
+                                                  dtype=np.float32))
+        for j in range(g):
+            pos = int(kv.seq_lens[b]) + j
+            blk = int(kv.block_table[b, pos // bs])
+            pool[:, :, blk, pos % bs] = vals[j]
+    return pool, kv.block_table, kv.seq_lens.copy(), kv.num_blocks
 
 
 def logits_bytes(wl: Workload, gamma: Optional[Sequence[int]] = None) -> int:

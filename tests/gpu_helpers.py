@@ -25,20 +25,22 @@ def to_dev(a: np.ndarray, dev):
 
 
 def gpu_verify(x, *, bf16, greedy=False, temperature=1.0, top_k=0, top_p=1.0, seed=0, round=0,
-               use_gamma=True, dev="cuda", reps=1):
+               use_gamma=True, dev="cuda", reps=1, eos_token=-1, max_tokens=None):
     """Run specdec_verify on inputs from the generator; returns numpy outputs."""
     import torch
     B, G1, V = x["target"].shape
     desc = sd.make_verify_desc(B, G1 - 1, V, bf16=bf16, greedy=greedy, temperature=temperature,
-                               top_k=top_k, top_p=top_p, seed=seed, round=round)
+                               top_k=top_k, top_p=top_p, seed=seed, round=round,
+                               eos_token=eos_token)
     ver = sd.Verifier(desc, dev)
     t = to_dev(x["target"], dev)
     d = None if greedy or x.get("draft") is None else to_dev(x["draft"], dev)
     tok = to_dev(x["draft_tokens"], dev)
     gam = to_dev(x["gamma"], dev) if use_gamma else None
+    mt = None if max_tokens is None else to_dev(np.asarray(max_tokens, np.int32), dev)
     outs = []
     for _ in range(reps):
-        r = ver(t, d, tok, gam)
+        r = ver(t, d, tok, gam, mt)
         torch.cuda.synchronize()
         outs.append({k: v.cpu().numpy() for k, v in r.items()})
     del t, d, tok, gam, ver
@@ -71,9 +73,12 @@ def compare(ref, got, gamma, greedy, requests=None, label=""):
                 errs.append(f"{label} request {b}: m gpu={m_got} oracle={m_ref}")
             if list(tok_got) != list(tok_ref):
                 errs.append(f"{label} request {b}: tokens gpu={list(tok_got)} oracle={list(tok_ref)}")
-        fl_got, fl_ref = int(got["flags"][b]) & 0xF, int(ref["flags"][k]) & 0xF
+        fl_got, fl_ref = int(got["flags"][b]) & 0x18F, int(ref["flags"][k]) & 0x18F
         if fl_got != fl_ref and npos < 0:
             errs.append(f"{label} request {b}: flags gpu={fl_got:#x} oracle={fl_ref:#x}")
+        if npos < 0 and int(got["num_tokens"][b]) != int(ref["num_tokens"][k]):
+            errs.append(f"{label} request {b}: num_tokens gpu={got['num_tokens'][b]} "
+                        f"oracle={ref['num_tokens'][k]}")
         if not greedy:
             lim = g if npos < 0 else min(g, npos)
             for i in range(lim):
@@ -91,7 +96,8 @@ def compare(ref, got, gamma, greedy, requests=None, label=""):
 
 
 def oracle_verify(x, *, greedy=False, temperature=1.0, top_k=0, top_p=1.0, seed=0, round=0,
-                  requests=None):
+                  requests=None, eos_token=-1, max_tokens=None):
     return oracle.verify(x["target"], None if greedy else x["draft"], x["draft_tokens"],
                          x["gamma"], greedy=greedy, temperature=temperature, top_k=top_k,
-                         top_p=top_p, seed=seed, round=round, requests=requests)
+                         top_p=top_p, seed=seed, round=round, requests=requests,
+                         eos_token=eos_token, max_tokens=max_tokens)

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert sd.specdec_abi_version() == 1
+    assert sd.specdec_abi_version() == 2
     for s in range(5):
         assert sd.status_string(s).startswith("SPECDEC_")
 
@@ -56,8 +56,8 @@ def call_verify(desc, ws_bytes=None, **ptrs):
     p.update(ptrs)
     nbytes = sd.specdec_verify_workspace_bytes(desc) if ws_bytes is None else ws_bytes
     return sd.lib().specdec_verify(ctypes.byref(desc), p["target"], p["draft"], p["tokens"],
-                                   p["gamma"], p["acc"], p["out"], None, None, None, None,
-                                   p["ws"], nbytes, None)
+                                   p["gamma"], None, p["acc"], None, p["out"], None, None, None,
+                                   None, p["ws"], nbytes, None)
 
 
 @pytest.mark.parametrize("bad", [
@@ -71,8 +71,8 @@ def test_bad_descriptors_are_rejected(bad):
     assert call_verify(d, ws_bytes=1 << 30) == sd.SPECDEC_ERR_INVALID_ARGUMENT
 
 
-def test_bad_dtype_mode_reserved():
-    for field, val in (("dtype", 7), ("mode", 5), ("reserved", 1)):
+def test_bad_dtype_mode_eos():
+    for field, val in (("dtype", 7), ("mode", 5), ("eos_token", -2), ("eos_token", 1000)):
         d = good_desc()
         setattr(d, field, val)
         assert call_verify(d, ws_bytes=1 << 30) == sd.SPECDEC_ERR_INVALID_ARGUMENT
@@ -112,3 +112,20 @@ def test_commit_descriptor_checks():
     st = sd.lib().specdec_commit_kv(ctypes.byref(ok), 16, 16, 16, 16, None, 16, None, 16, 0, None)
     assert st == sd.SPECDEC_ERR_WORKSPACE_TOO_SMALL
     assert sd.lib().specdec_workspace_clear(None, 16, None) == sd.SPECDEC_ERR_INVALID_ARGUMENT
+
+
+def test_rollback_descriptor_checks():
+    ok = sd.make_kv_desc(4, 7, 24, 2, 64, 16, 300, 8)
+    for field, val in (("num_layers", 0), ("head_dim", 0), ("gamma_max", 64)):
+        d = sd.make_kv_desc(4, 7, 24, 2, 64, 16, 300, 8)
+        setattr(d, field, val)
+        st = sd.lib().specdec_rollback_kv(ctypes.byref(d), 16, 16, 16, None, 16, None, 16,
+                                          1 << 20, None)
+        assert st == sd.SPECDEC_ERR_INVALID_ARGUMENT
+    for args in ((None, 16, 16, 16), (16, None, 16, 16), (16, 16, None, 16), (16, 16, 16, None)):
+        pool, table, acc, seq = args
+        st = sd.lib().specdec_rollback_kv(ctypes.byref(ok), pool, table, acc, None, seq, None, 16,
+                                          1 << 20, None)
+        assert st == sd.SPECDEC_ERR_INVALID_ARGUMENT
+    st = sd.lib().specdec_rollback_kv(ctypes.byref(ok), 16, 16, 16, None, 16, None, 16, 0, None)
+    assert st == sd.SPECDEC_ERR_WORKSPACE_TOO_SMALL

@@ -289,5 +289,6 @@ def test_truncation_unsupported_shapes_are_rejected():
         acc = torch.zeros(B, dtype=torch.int32, device="cuda")
         out = torch.zeros(B, G + 1, dtype=torch.int32, device="cuda")
         with pytest.raises(sd.SpecdecError) as e:
-            sd.specdec_verify(desc, t, d, tok, None, acc, out, None, None, None, None, ws)
+            sd.specdec_verify(desc, t, d, tok, None, None, acc, None, out, None, None, None, None,
+                              ws)
         assert e.value.status == sd.SPECDEC_ERR_UNSUPPORTED
