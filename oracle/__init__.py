@@ -25,6 +25,7 @@ FLAG_NONFINITE = 0x4
 FLAG_TOKEN_RANGE = 0x8
 FLAG_EOS = 0x80
 FLAG_LENGTH = 0x100
+FLAG_BAD_TREE = 0x200
 
 
 def _compile(src: str, out: str) -> None:
@@ -81,10 +82,13 @@ class Oracle:
         L.oracle_row_distribution.restype = ctypes.c_int
         L.oracle_philox4x32_10.argtypes = [P, P, P]
         L.oracle_philox4x32_10.restype = None
-        L.oracle_commit_kv.argtypes = [ctypes.c_int32] * 7 + [ctypes.c_int64, P, P, P, P, P, P]
+        L.oracle_commit_kv.argtypes = ([ctypes.c_int32] * 7 + [ctypes.c_int64, ctypes.c_int32]
+                                       + [P] * 7)
         L.oracle_commit_kv.restype = ctypes.c_int
         L.oracle_rollback_kv.argtypes = [ctypes.c_int32] * 7 + [ctypes.c_int64, P, P, P, P, P]
         L.oracle_rollback_kv.restype = ctypes.c_int
+        L.oracle_verify_tree.argtypes = [ctypes.c_int32] * 4 + [P, P, P, P, ctypes.c_int32] + [P] * 6
+        L.oracle_verify_tree.restype = ctypes.c_int
         self.lib = L
         self.path = path
 
@@ -167,10 +171,21 @@ class Oracle:
         return out
 
     def commit_kv(self, scratch: np.ndarray, pool: np.ndarray, block_table: np.ndarray,
-                  accept_count: np.ndarray, seq_lens: np.ndarray, gamma=None):
-        """Apply the commit to ``pool`` and ``seq_lens`` in place (numpy uint16/int32)."""
-        B, G1, L, two, H, D = scratch.shape
+                  accept_count: np.ndarray, seq_lens: np.ndarray, gamma=None, slot_map=None,
+                  gamma_max: Optional[int] = None):
+        """Apply the commit to ``pool`` and ``seq_lens`` in place (numpy uint16/int32).
+
+        slot_map [B][G+1] (tree paths) names the scratch slot of each window
+        position; gamma_max (G) then defaults to slot_map's width - 1."""
+        B, S, L, two, H, D = scratch.shape
         assert two == 2 and pool.dtype == np.uint16 and scratch.dtype == np.uint16
+        smap = None
+        if slot_map is not None:
+            smap = np.ascontiguousarray(slot_map, dtype=np.int32)
+            G1 = smap.shape[1] if gamma_max is None else gamma_max + 1
+            assert smap.shape == (B, G1)
+        else:
+            G1 = S if gamma_max is None else gamma_max + 1
         Lp, two2, NB, BS, Hp, Dp = pool.shape
         assert (Lp, two2, Hp, Dp) == (L, 2, H, D)
         assert pool.flags.c_contiguous and seq_lens.flags.c_contiguous
@@ -178,12 +193,35 @@ class Oracle:
         acc = np.ascontiguousarray(accept_count, dtype=np.int32)
         gam = None if gamma is None else np.ascontiguousarray(gamma, dtype=np.int32)
         assert seq_lens.dtype == np.int32
-        rc = self.lib.oracle_commit_kv(B, G1 - 1, L, H, D, BS, bt.shape[1], NB,
-                                    _ptr(np.ascontiguousarray(scratch)), _ptr(pool), _ptr(bt),
-                                    _ptr(acc), _ptr(gam), _ptr(seq_lens))
+        rc = self.lib.oracle_commit_kv(B, G1 - 1, L, H, D, BS, bt.shape[1], NB, S,
+                                    _ptr(np.ascontiguousarray(scratch)), _ptr(smap), _ptr(pool),
+                                    _ptr(bt), _ptr(acc), _ptr(gam), _ptr(seq_lens))
         if rc != 0:
             raise ValueError(f"oracle_commit_kv rejected its arguments (code {rc})")
 
+
+    def verify_tree(self, target: np.ndarray, tokens: np.ndarray, parents: np.ndarray,
+                    num_nodes: Optional[np.ndarray] = None, *, eos_token: int = -1,
+                    max_tokens: Optional[np.ndarray] = None):
+        """Greedy tree verification; returns a dict of arrays."""
+        target = np.ascontiguousarray(target)
+        B, N, V = target.shape
+        tok = np.ascontiguousarray(tokens, dtype=np.int32)
+        par = np.ascontiguousarray(parents, dtype=np.int32)
+        assert tok.shape == (B, N) and par.shape == (B, N)
+        nn = None if num_nodes is None else np.ascontiguousarray(num_nodes, dtype=np.int32)
+        mt = None if max_tokens is None else np.ascontiguousarray(max_tokens, dtype=np.int32)
+        out = {"accept_count": np.zeros(B, np.int32), "num_tokens": np.zeros(B, np.int32),
+               "out_tokens": np.zeros((B, N), np.int32), "path": np.zeros((B, N), np.int32),
+               "flags": np.zeros(B, np.uint32)}
+        rc = self.lib.oracle_verify_tree(B, N, V, int(target.dtype == np.uint16), _ptr(target),
+                                         _ptr(tok), _ptr(par), _ptr(nn), int(eos_token), _ptr(mt),
+                                         _ptr(out["accept_count"]), _ptr(out["num_tokens"]),
+                                         _ptr(out["out_tokens"]), _ptr(out["path"]),
+                                         _ptr(out["flags"]))
+        if rc != 0:
+            raise ValueError(f"oracle_verify_tree rejected its arguments (code {rc})")
+        return out
 
     def rollback_kv(self, pool: np.ndarray, block_table: np.ndarray, accept_count: np.ndarray,
                     seq_lens: np.ndarray, gamma_max: int, gamma=None):
@@ -232,3 +270,7 @@ def commit_kv(*args, **kw):
 
 def rollback_kv(*args, **kw):
     return default().rollback_kv(*args, **kw)
+
+
+def verify_tree(*args, **kw):
+    return default().verify_tree(*args, **kw)

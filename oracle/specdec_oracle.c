@@ -420,14 +420,18 @@ int oracle_verify(const oracle_verify_args* a, const void* target, const void* d
 /* Keep the K/V of the pending token and the accepted drafts, invalidate the
  * rejected slots and set the new length ([KB] s.06; [TUT] s.5.2: trim to
  * t+m, then the replacement makes t+m+1; [APP] s.5.4: accepted entries are
- * written into the cache, the rest dropped).  Slot j of the scratch holds
- * position t+j; slots 0..m are copied, m+1..gamma_i zero-filled. */
+ * written into the cache, the rest dropped).  Position t+j takes scratch slot
+ * j (chain) or the slot of the path's node at depth j (tree: [APP] s.5.3,
+ * only the accepted path becomes history); positions up to t+m are written,
+ * t+m+1 .. t+gamma_i zero-filled. */
 int oracle_commit_kv(int32_t B, int32_t G, int32_t L, int32_t H, int32_t D, int32_t bs,
-                     int32_t max_blocks, int64_t num_blocks, const uint16_t* scratch,
+                     int32_t max_blocks, int64_t num_blocks, int32_t scratch_slots,
+                     const uint16_t* scratch, const int32_t* slot_map,
                      uint16_t* pool, const int32_t* block_table, const int32_t* accept_count,
                      const int32_t* gamma, int32_t* seq_lens)
 {
     const size_t row = (size_t)H * (size_t)D;
+    const int32_t S = scratch_slots > 0 ? scratch_slots : G + 1;
     for (int32_t b = 0; b < B; ++b) {
         const int32_t gb = gamma ? gamma[b] : G;
         const int32_t m = accept_count[b];
@@ -444,8 +448,10 @@ int oracle_commit_kv(int32_t B, int32_t G, int32_t L, int32_t H, int32_t D, int3
                     uint16_t* dst = pool + ((((size_t)l * 2 + kv) * (size_t)num_blocks + (size_t)blk)
                                             * (size_t)bs + (size_t)off) * row;
                     if (j <= m) {
+                        const int32_t slot = slot_map ? slot_map[(size_t)b * (G + 1) + j] : j;
+                        if (slot < 0 || slot >= S) return -4;
                         const uint16_t* src = scratch
-                            + ((((size_t)b * (G + 1) + j) * L + l) * 2 + kv) * row;
+                            + ((((size_t)b * S + slot) * L + l) * 2 + kv) * row;
                         memcpy(dst, src, row * sizeof(uint16_t));
                     } else {
                         memset(dst, 0, row * sizeof(uint16_t));
@@ -494,6 +500,70 @@ int oracle_rollback_kv(int32_t B, int32_t G, int32_t L, int32_t H, int32_t D, in
         const int32_t gb = gamma ? gamma[b] : G;
         const int32_t keep = accept_count[b] + 1 < gb ? accept_count[b] + 1 : gb;
         seq_lens[b] = seq_lens[b] + keep;
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------- tree */
+
+/* Greedy verification of a draft tree ([APP] s.5.3: the target checks every
+ * node of the tree in one forward and the longest accepted root-to-leaf path
+ * is kept; [TUT] s.13.3 and s.14: tree speculation verifies several
+ * branches at once).  The greedy rule of [TUT] s.3-4 / [KB] s.03 applies
+ * along every edge: the target's row after a node judges that node's
+ * children, and a child is accepted when its token is the row's argmax
+ * (lowest index on ties) and its parent was accepted.  The committed path
+ * ends at the deepest accepted node (lowest node index among equally deep
+ * ones); the token after it is the argmax of that node's row, which is the
+ * correction when it has children and the bonus when it is a leaf.  The
+ * committed list is then cut at EOS / budget exactly as for a chain. */
+int oracle_verify_tree(int32_t B, int32_t N, int32_t V, int32_t is_bf16, const void* target,
+                       const int32_t* tokens, const int32_t* parents, const int32_t* num_nodes,
+                       int32_t eos_token, const int32_t* max_tokens, int32_t* accept_count,
+                       int32_t* num_tokens, int32_t* out_tokens, int32_t* path, uint32_t* flags)
+{
+    if (B < 0 || N < 1 || N > 64 || V < 1 || !target || !tokens || !parents || !accept_count
+        || !out_tokens || !path)
+        return -1;
+    for (int32_t b = 0; b < B; ++b) {
+        const int32_t n = num_nodes ? num_nodes[b] : N;
+        if (n < 1 || n > N) return -2;
+        const int32_t* tok = tokens + (size_t)b * N;
+        const int32_t* par = parents + (size_t)b * N;
+        uint32_t fl = 0;
+        int32_t choice[64], depth[64], ok[64];
+        for (int32_t j = 0; j < n; ++j)
+            choice[j] = row_argmax(row_ptr(target, is_bf16, (int64_t)b * N + j, V), is_bf16, V);
+        /* nodes in index order: a parent always precedes its children */
+        ok[0] = 1;
+        depth[0] = 0;
+        for (int32_t j = 1; j < n; ++j) {
+            ok[j] = 0;
+            depth[j] = 0;
+            if (par[j] < 0 || par[j] >= j) { fl |= ORACLE_FLAG_BAD_TREE; continue; }
+            depth[j] = depth[par[j]] + 1;
+            if (tok[j] < 0 || tok[j] >= V) { fl |= ORACLE_FLAG_TOKEN_RANGE; continue; }
+            ok[j] = ok[par[j]] && tok[j] == choice[par[j]];
+        }
+        int32_t best = 0;
+        for (int32_t j = 1; j < n; ++j)
+            if (ok[j] && depth[j] > depth[best]) best = j;
+        const int32_t m = depth[best];
+        int32_t* pth = path + (size_t)b * N;
+        int32_t* out = out_tokens + (size_t)b * N;
+        for (int32_t j = 0; j < N; ++j) { pth[j] = -1; out[j] = -1; }
+        for (int32_t x = best; ; x = par[x]) {
+            pth[depth[x]] = x;
+            if (x == 0) break;
+        }
+        for (int32_t k = 1; k <= m; ++k) out[k - 1] = tok[pth[k]];
+        out[m] = choice[best];
+        const int32_t budget = max_tokens ? (max_tokens[b] < 0 ? 0 : max_tokens[b]) : -1;
+        int32_t kept_m = 0;
+        const int32_t nt = round_end(m, N - 1, out, eos_token, budget, &fl, &kept_m);
+        accept_count[b] = kept_m;
+        if (num_tokens) num_tokens[b] = nt;
+        if (flags) flags[b] = fl;
     }
     return 0;
 }

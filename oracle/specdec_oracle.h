@@ -73,15 +73,40 @@ int oracle_row_distribution(const void* row, int32_t is_bf16, int32_t vocab,
 /* Philox4x32-10 block: out = philox(ctr, key). */
 void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
 
+/* Greedy verification of a draft tree.
+ *   target  [B][N][V]: row j is the target's distribution after the path from
+ *           the root (node 0, the pending token) to node j
+ *   tokens  [B][N] int32 (node 0's entry ignored), parents [B][N] int32
+ *           (parents[b][0] ignored; 0 <= parent < j otherwise)
+ *   num_nodes [B] in [1, N] or NULL (N)
+ * Outputs per request: accept_count (depth of the committed path after the
+ * EOS / budget cut), num_tokens (may be NULL), out_tokens [B][N] (the path's
+ * tokens, then the target's choice after its last node; -1 padded),
+ * path [B][N] (node of each depth along the accepted path, root first, -1
+ * padded; not cut), flags [B] (ORACLE_FLAG_BAD_TREE for a malformed parent,
+ * ORACLE_FLAG_TOKEN_RANGE for a token outside [0,V); such nodes reject).
+ * Returns 0, or a negative value on a malformed argument. */
+#define ORACLE_FLAG_BAD_TREE 0x200u
+int oracle_verify_tree(int32_t batch, int32_t num_nodes_max, int32_t vocab, int32_t is_bf16,
+                       const void* target, const int32_t* tokens, const int32_t* parents,
+                       const int32_t* num_nodes, int32_t eos_token, const int32_t* max_tokens,
+                       int32_t* accept_count, int32_t* num_tokens, int32_t* out_tokens,
+                       int32_t* path, uint32_t* flags);
+
 /* Commit the verified K/V slots of every request into the paged pool.
- *   scratch  [B][G+1][L][2][H][D] bf16 bits; slot j holds position t_i + j
+ *   scratch  [B][S][L][2][H][D] bf16 bits, S = scratch_slots (0: G+1)
+ *   slot_map [B][G+1] or NULL: position t_i + j takes scratch slot
+ *            slot_map[i][j] (NULL: slot j, the chain case)
  *   pool     [L][2][num_blocks][block][H][D] bf16 bits
  *   block_table [B][max_blocks], accept_count [B], gamma [B] (NULL: G)
  *   seq_lens [B] in: t_i, out: t_i + m_i + 1
+ * Positions t_i .. t_i + m_i receive their slots, t_i + m_i + 1 .. t_i + gamma_i
+ * are zero-filled.
  * Returns 0, or a negative value if a needed block-table entry is invalid. */
 int oracle_commit_kv(int32_t batch, int32_t gamma_max, int32_t layers, int32_t kv_heads,
                      int32_t head_dim, int32_t block_size, int32_t max_blocks,
-                     int64_t num_blocks, const uint16_t* scratch, uint16_t* pool,
+                     int64_t num_blocks, int32_t scratch_slots, const uint16_t* scratch,
+                     const int32_t* slot_map, uint16_t* pool,
                      const int32_t* block_table, const int32_t* accept_count,
                      const int32_t* gamma, int32_t* seq_lens);
 

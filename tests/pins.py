@@ -344,6 +344,125 @@ def pin_rollback_invariants(orc, B=7):
         errs.append("a block outside every table changed")
     return errs
 
+
+# ------------------------------------------------- tree verification (greedy)
+
+def pin_tree_walkthrough(orc):
+    """The drawing's tree with hand-derived outcomes (tests/golden/tree_walkthrough.txt)."""
+    parents = np.array([[-1, 0, 1, 2, 3, 2, 5]], np.int32)
+    V = 100
+    rng = np.random.default_rng(71)
+    errs = []
+    for r in golden_rows("tree_walkthrough.txt"):
+        cols = [c.strip() for c in " ".join(r).split("|")]
+        name = cols[0]
+        toks = [int(x) for x in cols[1].split()]
+        choice = [int(x) for x in cols[2].split()]
+        want_path = [int(x) for x in cols[3].split()]
+        want_out = [int(x) for x in cols[4].split()]
+        want_m = int(cols[5])
+        rows = _greedy_rows(choice, V, rng)[None]
+        got = orc.verify_tree(rows, np.array([[0] + toks], np.int32), parents)
+        path = [int(x) for x in got["path"][0] if x >= 0]
+        out = [int(x) for x in got["out_tokens"][0] if x >= 0]
+        if path != want_path or out != want_out or int(got["accept_count"][0]) != want_m:
+            errs.append(f"{name}: path {path} out {out} m {got['accept_count'][0]}; "
+                        f"want {want_path} {want_out} {want_m}")
+    return errs
+
+
+def _random_tree(rng, n):
+    par = np.full(n, -1, np.int32)
+    for j in range(1, n):
+        par[j] = rng.integers(0, j)
+    return par
+
+
+def pin_tree_brute_force(orc, B=150):
+    """Every root-to-node path checked edge by edge with numpy.argmax; the
+    deepest fully matching path (lowest node on ties) must be the oracle's."""
+    rng = np.random.default_rng(73)
+    N, V = 12, 6
+    z = rng.integers(0, 4, (B, N, V)).astype(np.float32)   # many ties
+    am = np.argmax(z, axis=2)
+    par = np.stack([_random_tree(rng, N) for _ in range(B)])
+    tok = rng.integers(0, V, (B, N)).astype(np.int32)
+    hit = rng.random((B, N)) < 0.6
+    for b in range(B):
+        for j in range(1, N):
+            if hit[b, j]:
+                tok[b, j] = am[b, par[b, j]]
+    nn = rng.integers(1, N + 1, B).astype(np.int32)
+    got = orc.verify_tree(z, tok, par, nn)
+    errs = []
+    for b in range(B):
+        best, best_path = 0, [0]
+        for j in range(int(nn[b])):
+            p = [j]
+            while p[-1] != 0:
+                p.append(int(par[b, p[-1]]))
+            p = p[::-1]
+            if all(tok[b, p[k + 1]] == am[b, p[k]] for k in range(len(p) - 1)):
+                if len(p) - 1 > len(best_path) - 1:
+                    best, best_path = j, p
+        want_out = [int(tok[b, x]) for x in best_path[1:]] + [int(am[b, best])]
+        path = [int(x) for x in got["path"][b] if x >= 0]
+        out = [int(x) for x in got["out_tokens"][b] if x >= 0]
+        if path != best_path or out != want_out:
+            errs.append(f"request {b}: path {path} out {out}; brute force {best_path} {want_out}")
+    return errs
+
+
+def pin_tree_chain_equals_chain(orc, B=80):
+    """A tree that is a single chain verifies exactly like the chain verifier."""
+    rng = np.random.default_rng(79)
+    G, V = 5, 9
+    z = rng.standard_normal((B, G + 1, V)).astype(np.float32)
+    am = np.argmax(z, axis=2)
+    d = am[:, :G].copy().astype(np.int32)
+    flip = rng.random((B, G)) < 0.3
+    d[flip] = (d[flip] + 1) % V
+    chain = orc.verify(z, None, d, greedy=True)
+    par = np.tile(np.arange(-1, G, dtype=np.int32), (B, 1))
+    tok = np.concatenate([np.zeros((B, 1), np.int32), d], axis=1)
+    tree = orc.verify_tree(z, tok, par)
+    errs = []
+    if not np.array_equal(chain["accept_count"], tree["accept_count"]):
+        errs.append("accept counts differ from the chain verifier")
+    if not np.array_equal(chain["out_tokens"], tree["out_tokens"]):
+        errs.append("committed tokens differ from the chain verifier")
+    return errs
+
+
+def pin_commit_slot_map(orc):
+    """Commit with a per-request slot map (tree paths) vs numpy fancy indexing."""
+    rng = np.random.default_rng(83)
+    B, G, S, L, H, D, bs = 6, 4, 9, 2, 2, 4, 4
+    t = rng.integers(0, 14, B).astype(np.int32)
+    gam = rng.integers(0, G + 1, B).astype(np.int32)
+    m = np.array([rng.integers(0, g + 1) for g in gam], np.int32)
+    smap = np.stack([np.concatenate([[0], rng.choice(np.arange(1, S), G, replace=False)])
+                     for _ in range(B)]).astype(np.int32)
+    max_blocks = (14 + G + bs) // bs
+    nb = B * max_blocks + 3
+    table = rng.permutation(nb)[:B * max_blocks].reshape(B, max_blocks).astype(np.int32)
+    scratch = rng.integers(0, 2 ** 16, (B, S, L, 2, H, D)).astype(np.uint16)
+    pool = np.full((L, 2, nb, bs, H, D), 0xBEEF, np.uint16)
+    want = pool.copy()
+    for b in range(B):
+        for j in range(gam[b] + 1):
+            pos = t[b] + j
+            blk, off = table[b, pos // bs], pos % bs
+            want[:, :, blk, off] = scratch[b, smap[b, j]] if j <= m[b] else 0
+    seq = t.copy()
+    orc.commit_kv(scratch, pool, table, m, seq, gam, slot_map=smap)
+    errs = []
+    if not np.array_equal(pool, want):
+        errs.append(f"pool differs at {np.argwhere(pool != want)[:3].tolist()}")
+    if not np.array_equal(seq, t + m + 1):
+        errs.append("seq_lens != t+m+1")
+    return errs
+
 # ------------------------------------------------- closed form at fixed alpha
 
 def _fixed_alpha_batch(alpha, gamma, B):
@@ -645,4 +764,8 @@ ALL_PINS = {
     "round_end_autoregressive": pin_round_end_autoregressive,
     "round_end_prefix": pin_round_end_prefix,
     "rollback_invariants": pin_rollback_invariants,
+    "tree_walkthrough": pin_tree_walkthrough,
+    "tree_brute_force": pin_tree_brute_force,
+    "tree_chain_equals_chain": pin_tree_chain_equals_chain,
+    "commit_slot_map": pin_commit_slot_map,
 }

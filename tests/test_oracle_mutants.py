@@ -69,6 +69,17 @@ MUTANTS = [
     ("rollback_length_past_written",
      "const int32_t keep = accept_count[b] + 1 < gb ? accept_count[b] + 1 : gb;",
      "const int32_t keep = accept_count[b] + 1;", ["rollback_invariants"]),
+    ("tree_node_judged_by_its_own_row", "ok[j] = ok[par[j]] && tok[j] == choice[par[j]];",
+     "ok[j] = ok[par[j]] && tok[j] == choice[j];", ["tree_walkthrough", "tree_brute_force"]),
+    ("tree_ignores_parent_rejection", "ok[j] = ok[par[j]] && tok[j] == choice[par[j]];",
+     "ok[j] = tok[j] == choice[par[j]];", ["tree_walkthrough", "tree_brute_force"]),
+    ("tree_tie_to_highest_node", "if (ok[j] && depth[j] > depth[best]) best = j;",
+     "if (ok[j] && depth[j] >= depth[best]) best = j;", ["tree_walkthrough", "tree_brute_force"]),
+    ("tree_next_token_from_parent_row", "out[m] = choice[best];",
+     "out[m] = choice[best ? par[best] : 0];", ["tree_walkthrough", "tree_chain_equals_chain"]),
+    ("commit_ignores_slot_map",
+     "const int32_t slot = slot_map ? slot_map[(size_t)b * (G + 1) + j] : j;",
+     "const int32_t slot = j;", ["commit_slot_map"]),
 ]
 
 
