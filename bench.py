@@ -111,6 +111,8 @@ def main() -> int:
         log(f"calibration copy: {args.pmc_copy_mib} MiB read + {args.pmc_copy_mib} MiB written")
         del src, dst
     wl0 = synth.WORKLOADS[args.workload or synth.HEADLINE]
+    if wl0.tree is not None:
+        return bench_tree(args, wl0)
     greedy = wl0.mode == "greedy"
     bf16 = wl0.dtype == "bf16"
     per_set = synth.logits_bytes(wl0)
@@ -164,7 +166,7 @@ def main() -> int:
     def commit(k: int) -> None:
         kv["seq"].copy_(kv["seq0"])
         sd.specdec_commit_kv(kv["desc"], kv["scratch"], kv["pool"], kv["table"],
-                             ver.accept_count, dev_in[k]["gamma"], kv["seq"], None, kv["ws"])
+                             ver.accept_count, dev_in[k]["gamma"], None, kv["seq"], None, kv["ws"])
 
     def rollback(k: int) -> None:
         kv["dseq"].copy_(kv["dseq0"])
@@ -265,7 +267,7 @@ def main() -> int:
             e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
             e[0].record()
             sd.specdec_commit_kv(kv["desc"], kv["scratch"], kv["pool"], kv["table"],
-                                 ver.accept_count, d["gamma"], kv["seq"], None, kv["ws"])
+                                 ver.accept_count, d["gamma"], None, kv["seq"], None, kv["ws"])
             e[1].record()
             e[2].record()
             sd.specdec_rollback_kv(kv["ddesc"], kv["dpool"], kv["table"], ver.accept_count,
@@ -367,6 +369,171 @@ def main() -> int:
                      "kernel": ("k_stats_greedy" if greedy else
                                 "k_truncate" if (wl0.top_k or wl0.top_p < 1.0) else "k_stats_sample"),
                      "kernel_avg_us": k1_avg * 1e6, "bytes_per_launch": alg_k1},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def bench_tree(args, wl0) -> int:
+    """Greedy tree verification + path commit: a step is specdec_verify_tree
+    (statistics pass over every node's row, the tree decision) followed by
+    specdec_commit_kv with the kept path as the slot map."""
+    import torch
+    import speculative_decoding_verification_05_amd as sd
+    from speculative_decoding_verification_05_amd import synth
+
+    dev = torch.device("cuda:0")
+    B, N, V = wl0.batch, wl0.gamma_max + 1, wl0.vocab
+    per_set = B * N * V * wl0.elem_bytes
+    sets = args.sets or max(1, int(np.ceil(2 * 256e6 / per_set)) + 1)
+    log(f"workload {wl0.name}: {per_set / 1e6:.2f} MB of logits per set, {sets} rotating sets")
+    host, dev_in = [], []
+    for k in range(sets):
+        x = synth.make_tree_inputs(dataclasses.replace(wl0, data_seed=wl0.data_seed + 100 * k))
+        host.append(x)
+        dev_in.append({n: torch.from_numpy(v.view(np.int16) if v.dtype == np.uint16 else v).to(dev)
+                       for n, v in x.items()})
+        log(f"  input set {k} uploaded")
+    kvin = synth.make_kv_inputs(wl0)
+    K = wl0.kv
+    kdesc = sd.make_kv_desc(B, N - 1, K.layers, K.kv_heads, K.head_dim, K.block_size,
+                            kvin.block_table.shape[1], kvin.num_blocks, scratch_slots=N)
+    depth = np.array([synth.kv_window(wl0, b) for b in range(B)], np.int32)
+    scratch = torch.from_numpy(kvin.scratch.view(np.int16)).to(dev)
+    pool = torch.from_numpy(kvin.pool.view(np.int16)).to(dev)
+    table = torch.from_numpy(kvin.block_table).to(dev)
+    seq0 = torch.from_numpy(kvin.seq_lens).to(dev)
+    seq = seq0.clone()
+    depth_d = torch.from_numpy(depth).to(dev)
+    kws = torch.zeros(sd.specdec_commit_kv_workspace_bytes(kdesc), dtype=torch.uint8, device=dev)
+    tdesc = sd.make_tree_desc(B, N, V, bf16=wl0.dtype == "bf16")
+    ws = torch.zeros(sd.specdec_verify_tree_workspace_bytes(tdesc), dtype=torch.uint8, device=dev)
+    i32 = torch.int32
+    acc = torch.zeros(B, dtype=i32, device=dev)
+    ntok = torch.zeros(B, dtype=i32, device=dev)
+    out = torch.zeros(B, N, dtype=i32, device=dev)
+    path = torch.zeros(B, N, dtype=i32, device=dev)
+    flags = torch.zeros(B, dtype=i32, device=dev)
+
+    def verify(k, ev=None):
+        d = dev_in[k]
+        if ev is None:
+            sd.specdec_verify_tree(tdesc, d["target"], d["tokens"], d["parents"], d["num_nodes"],
+                                   None, acc, ntok, out, path, flags, ws)
+        else:
+            sd.specdec_verify_tree_profiled(tdesc, d["target"], d["tokens"], d["parents"],
+                                            d["num_nodes"], None, acc, ntok, out, path, flags, ws,
+                                            ev)
+
+    def commit():
+        seq.copy_(seq0)
+        sd.specdec_commit_kv(kdesc, scratch, pool, table, acc, depth_d, path, seq, None, kws)
+
+    def step(k):
+        verify(k)
+        commit()
+
+    eager = []
+    for k in range(sets):
+        step(k)
+        torch.cuda.synchronize()
+        eager.append((acc.clone(), out.clone()))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(0)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for k in range(sets):
+            step(k)
+    for _ in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        if not (torch.equal(acc, eager[-1][0]) and torch.equal(out, eager[-1][1])):
+            log("graph replay differs from eager launches")
+            return 1
+    reps = max(1, args.steps // sets)
+    steps = reps * sets
+    wreps = max(1, args.warmup // sets)
+    for _ in range(wreps):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        graph.replay()
+    torch.cuda.synchronize()
+    sec_per_step = (time.perf_counter() - t0) / steps
+
+    # live per-kernel times
+    n_prof = max(sets, (args.profile_steps // sets) * sets)
+    ev = sd.HipEvents(4 * n_prof)
+    tc = []
+    for j in range(n_prof):
+        verify(j % sets, ev.handles[4 * j:4 * j + 4])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        commit()
+        e1.record()
+        tc.append((e0, e1))
+    torch.cuda.synchronize()
+    k1 = np.array([ev.elapsed_ms(4 * j, 4 * j + 1) for j in range(n_prof)]) * 1e-3
+    k2 = np.array([ev.elapsed_ms(4 * j + 2, 4 * j + 3) for j in range(n_prof)]) * 1e-3
+    kc = np.array([a.elapsed_time(b) for a, b in tc]) * 1e-3
+    ev.close()
+    # algorithmic bytes: every node's row once + tokens and parents + outputs
+    alg_k1 = float(per_set + B * N * 8 + B * (2 * N + 3) * 4)
+    achieved = alg_k1 / float(k1.mean()) / 1e9
+    slot = K.layers * 2 * K.kv_heads * K.head_dim * 2
+    cbytes = []
+    for a, _ in eager:
+        m = a.cpu().numpy().astype(np.int64)
+        cbytes.append(float(((m + 1) * 2 + (depth - m)).sum() * slot))
+    cb = float(np.mean(cbytes))
+    depth_mean = float(np.mean([a.float().mean().item() for a, _ in eager]))
+    log(f"step {sec_per_step * 1e6:.2f} us (graph); stats kernel avg {k1.mean() * 1e6:.2f} us; "
+        f"tree decision {k2.mean() * 1e6:.2f} us; path commit {kc.mean() * 1e6:.2f} us")
+    log(f"stats kernel {achieved:.1f} GB/s = {100 * achieved / HBM_PEAK_GBPS:.1f}% of "
+        f"{HBM_PEAK_GBPS:.0f} GB/s; commit {cb / kc.mean() / 1e9:.1f} GB/s; mean kept depth "
+        f"{depth_mean:.3f}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        x = host[0]
+        reps_c, t_s = 0, time.perf_counter()
+        while True:
+            oracle.verify_tree(x["target"], x["tokens"], x["parents"], x["num_nodes"])
+            reps_c += 1
+            t_c = time.perf_counter() - t_s
+            if t_c >= args.cpu_seconds or reps_c >= 50:
+                break
+        cpu = {"value": reps_c * B * (N - 1) / t_c, "unit": "tree nodes/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"{reps_c} pass(es) over all {B} trees of input set 0 ({t_c:.1f} s, "
+                         f"single-threaded C, double precision)"}
+    res = {
+        "metric": f"verified tree nodes/sec ({wl0.name})",
+        "value": B * (N - 1) / sec_per_step,
+        "unit": "tree nodes/s",
+        "n_gpus": 1, "steps": steps, "warmup": wreps * sets, "ms_per_step": sec_per_step * 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl0.name, "batch": B, "tree_nodes": N, "vocab": V,
+                   "logits": wl0.dtype, "mode": "greedy tree", "kv_commit": True,
+                   "rotating_input_sets": sets, "launch": "hipgraph",
+                   "committed_tokens_per_s": B * (depth_mean + 1) / sec_per_step},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "k_stats_greedy",
+                     "kernel_avg_us": float(k1.mean()) * 1e6, "bytes_per_launch": alg_k1},
+        "kernels": {"stats": {"avg_us": float(k1.mean()) * 1e6, "bytes_per_launch": alg_k1,
+                              "GBps": achieved, "frac": achieved / HBM_PEAK_GBPS},
+                    "k_decide_tree": {"avg_us": float(k2.mean()) * 1e6},
+                    "k_commit": {"avg_us": float(kc.mean()) * 1e6, "bytes_per_launch": cb,
+                                 "GBps": cb / kc.mean() / 1e9,
+                                 "frac": cb / kc.mean() / 1e9 / HBM_PEAK_GBPS}},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

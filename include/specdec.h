@@ -79,6 +79,7 @@ typedef enum specdec_mode { SPECDEC_SAMPLE = 0, SPECDEC_GREEDY = 1 } specdec_mod
 #define SPECDEC_FLAG_TRUNC_OVERFLOW    0x40u /* verify: a kept set exceeded 1024 tokens (ties): clipped */
 #define SPECDEC_FLAG_EOS               0x80u /* verify: the committed list ends with the EOS token */
 #define SPECDEC_FLAG_LENGTH            0x100u /* verify: the token budget ended the committed list */
+#define SPECDEC_FLAG_BAD_TREE          0x200u /* tree: a parent index outside [0, node): node rejected */
 
 /* ------------------------------------------------------------------ verify */
 
@@ -203,7 +204,8 @@ typedef struct specdec_kv_desc {
     int32_t head_dim;           /* D >= 1 */
     int32_t block_size;         /* tokens per physical block, >= 1 */
     int32_t max_blocks_per_req; /* columns of the block table */
-    int32_t reserved;           /* must be 0 */
+    int32_t scratch_slots;      /* S: K/V slots per request in the scratch; 0 = G+1
+                                   (specdec_commit_kv only; must be 0 for rollback) */
     int64_t num_blocks;         /* physical blocks in the pool */
 } specdec_kv_desc_t;
 
@@ -212,9 +214,15 @@ typedef struct specdec_kv_desc {
 size_t specdec_commit_kv_workspace_bytes(const specdec_kv_desc_t* desc);
 
 /* Commit the verified slots of one round into a paged K/V cache.
- *   scratch_kv  [B][G+1][L][2][H][D] bf16: the K (index 0) and V (index 1)
- *       the verify forward produced; slot j of request b belongs to position
+ *   scratch_kv  [B][S][L][2][H][D] bf16: the K (index 0) and V (index 1)
+ *       the verify forward produced, S = desc->scratch_slots (0: G+1).
+ *       Without a slot map, slot j of request b belongs to position
  *       seq_lens[b] + j (slot 0 = the pending token).
+ *   slot_map    [B][G+1] int32 or NULL: position seq_lens[b] + j takes slot
+ *       slot_map[b][j] (only j <= m_b is read).  For a tree round this is
+ *       specdec_verify_tree's `path` ("The apprentice's draft" s.5.3: only the
+ *       accepted path becomes history); a slot outside [0, S) skips that
+ *       position and flags SPECDEC_FLAG_BAD_BLOCK.
  *   kv_pool     [L][2][num_blocks][block_size][H][D] bf16, updated in place.
  *   block_table [B][max_blocks_per_req] int32: physical block of each logical
  *       block; entries covering positions t_b .. t_b + gamma_b must be valid.
@@ -234,9 +242,79 @@ size_t specdec_commit_kv_workspace_bytes(const specdec_kv_desc_t* desc);
 specdec_status_t specdec_commit_kv(const specdec_kv_desc_t* desc,
                                    const void* scratch_kv, void* kv_pool,
                                    const int32_t* block_table, const int32_t* accept_count,
-                                   const int32_t* gamma, int32_t* seq_lens, uint32_t* flags,
+                                   const int32_t* gamma, const int32_t* slot_map,
+                                   int32_t* seq_lens, uint32_t* flags,
                                    void* workspace, size_t workspace_bytes,
                                    hipStream_t stream);
+
+/* ------------------------------------------------------------ tree verify */
+
+typedef struct specdec_tree_desc {
+    int32_t batch;        /* B >= 0 requests */
+    int32_t num_nodes;    /* N in [1, 64]: padded nodes per tree, node 0 = root */
+    int32_t vocab;        /* V >= 1, as for specdec_verify */
+    int32_t dtype;        /* specdec_dtype_t of the target logits */
+    int32_t eos_token;    /* -1: none; else the EOS id in [0, V) */
+    int32_t reserved;     /* must be 0 */
+} specdec_tree_desc_t;
+
+/* Bytes of device workspace specdec_verify_tree needs (0 on a bad descriptor). */
+size_t specdec_verify_tree_workspace_bytes(const specdec_tree_desc_t* desc);
+
+/* Greedy verification of a draft tree ("The apprentice's draft", s.5.3: the
+ * target checks all nodes of a draft tree in one forward and the longest
+ * accepted path is kept; "Speculative decoding tutorial" s.13.3 and s.14:
+ * tree speculation verifies several candidate branches at once).  The greedy
+ * rule of specdec_verify holds on every edge: node j (j >= 1) is kept iff its
+ * parent was kept and its token equals the argmax of the parent's target row
+ * (raw logits, lowest index on ties).  The committed path ends at the deepest
+ * kept node (lowest node index among equally deep ones); the next token is
+ * the argmax of that node's row (a correction if it has children, else the
+ * bonus).  The committed list is cut at EOS / max_tokens as in specdec_verify.
+ * Sampling over trees is not provided (the pages give no rule for it).
+ * Inputs (device):
+ *   target_logits [B][N][V] dtype: row j is the target's distribution after
+ *       the path root..j (the verify forward over the tree with a tree mask);
+ *       node 0 is the pending token.
+ *   node_tokens   [B][N] int32: token of node j (entry 0 ignored).
+ *   parents       [B][N] int32: parent of node j, in [0, j) (entry 0
+ *       ignored); nodes come in topological order.  A bad parent rejects the
+ *       node (and so its subtree) and flags SPECDEC_FLAG_BAD_TREE.
+ *   num_nodes     [B] int32 in [1, N], or NULL (= N); rows and entries past
+ *       it are never read (clamped into [1, N]).
+ *   max_tokens    [B] int32 or NULL: token budget, as for specdec_verify.
+ * Outputs (device):
+ *   accept_count  [B] int32: depth of the committed path (drafts kept, after
+ *       the round-end cut).
+ *   num_tokens    [B] int32 or NULL: tokens committed this round.
+ *   out_tokens    [B][N] int32: the path's tokens, then the next token, -1
+ *       after (cut as for specdec_verify).
+ *   path          [B][N] int32: node at each depth of the kept path (path[0]
+ *       = 0), -1 after; feed it to specdec_commit_kv as the slot map with
+ *       scratch_slots = N.
+ *   flags         [B] uint32 or NULL: BAD_TREE, TOKEN_RANGE, NONFINITE,
+ *       EOS, LENGTH.
+ * Errors: INVALID_ARGUMENT (bad descriptor, NULL required pointer,
+ *   misaligned workspace), WORKSPACE_TOO_SMALL; nothing is enqueued. */
+specdec_status_t specdec_verify_tree(const specdec_tree_desc_t* desc, const void* target_logits,
+                                     const int32_t* node_tokens, const int32_t* parents,
+                                     const int32_t* num_nodes, const int32_t* max_tokens,
+                                     int32_t* accept_count, int32_t* num_tokens,
+                                     int32_t* out_tokens, int32_t* path, uint32_t* flags,
+                                     void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
+/* specdec_verify_tree with per-kernel timing: stage_events as for
+ * specdec_verify_profiled ([0]/[1] around the statistics pass, [2]/[3]
+ * around the tree decision kernel).  Everything else as specdec_verify_tree. */
+specdec_status_t specdec_verify_tree_profiled(const specdec_tree_desc_t* desc,
+                                              const void* target_logits,
+                                              const int32_t* node_tokens, const int32_t* parents,
+                                              const int32_t* num_nodes, const int32_t* max_tokens,
+                                              int32_t* accept_count, int32_t* num_tokens,
+                                              int32_t* out_tokens, int32_t* path, uint32_t* flags,
+                                              void* workspace, size_t workspace_bytes,
+                                              hipStream_t stream, hipEvent_t* stage_events);
 
 /* Bring the draft model's paged cache back to the committed sequence after
  * specdec_verify (AI-infra KB M013 s.06: the target cache and the draft cache

@@ -32,10 +32,13 @@ FLAG_BAD_GAMMA = 0x20
 FLAG_TRUNC_OVERFLOW = 0x40
 FLAG_EOS = 0x80
 FLAG_LENGTH = 0x100
+FLAG_BAD_TREE = 0x200
 
 # exported symbols of include/specdec.h
 EXPORTS = ("specdec_verify_workspace_bytes", "specdec_verify", "specdec_verify_profiled",
            "specdec_commit_kv_workspace_bytes", "specdec_commit_kv", "specdec_rollback_kv",
+           "specdec_verify_tree_workspace_bytes", "specdec_verify_tree",
+           "specdec_verify_tree_profiled",
            "specdec_workspace_clear", "specdec_status_string", "specdec_abi_version")
 
 
@@ -52,8 +55,14 @@ class KVDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("gamma_max", ctypes.c_int32),
                 ("num_layers", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
-                ("max_blocks_per_req", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("max_blocks_per_req", ctypes.c_int32), ("scratch_slots", ctypes.c_int32),
                 ("num_blocks", ctypes.c_int64)]
+
+
+class TreeDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_nodes", ctypes.c_int32),
+                ("vocab", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("eos_token", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class SpecdecError(RuntimeError):
@@ -81,10 +90,16 @@ def lib() -> ctypes.CDLL:
         L.specdec_verify_profiled.restype = ctypes.c_int
         L.specdec_commit_kv_workspace_bytes.argtypes = [ctypes.POINTER(KVDesc)]
         L.specdec_commit_kv_workspace_bytes.restype = S
-        L.specdec_commit_kv.argtypes = [ctypes.POINTER(KVDesc)] + [P] * 8 + [S, P]
+        L.specdec_commit_kv.argtypes = [ctypes.POINTER(KVDesc)] + [P] * 9 + [S, P]
         L.specdec_commit_kv.restype = ctypes.c_int
         L.specdec_rollback_kv.argtypes = [ctypes.POINTER(KVDesc)] + [P] * 7 + [S, P]
         L.specdec_rollback_kv.restype = ctypes.c_int
+        L.specdec_verify_tree_workspace_bytes.argtypes = [ctypes.POINTER(TreeDesc)]
+        L.specdec_verify_tree_workspace_bytes.restype = S
+        L.specdec_verify_tree.argtypes = [ctypes.POINTER(TreeDesc)] + [P] * 11 + [S, P]
+        L.specdec_verify_tree.restype = ctypes.c_int
+        L.specdec_verify_tree_profiled.argtypes = [ctypes.POINTER(TreeDesc)] + [P] * 11 + [S, P, P]
+        L.specdec_verify_tree_profiled.restype = ctypes.c_int
         L.specdec_workspace_clear.argtypes = [P, S, P]
         L.specdec_workspace_clear.restype = ctypes.c_int
         L.specdec_status_string.argtypes = [ctypes.c_int]
@@ -131,9 +146,51 @@ def make_verify_desc(batch, gamma_max, vocab, *, bf16=True, greedy=False, temper
 
 
 def make_kv_desc(batch, gamma_max, num_layers, num_kv_heads, head_dim, block_size,
-                 max_blocks_per_req, num_blocks) -> KVDesc:
+                 max_blocks_per_req, num_blocks, scratch_slots=0) -> KVDesc:
     return KVDesc(int(batch), int(gamma_max), int(num_layers), int(num_kv_heads),
-                  int(head_dim), int(block_size), int(max_blocks_per_req), 0, int(num_blocks))
+                  int(head_dim), int(block_size), int(max_blocks_per_req), int(scratch_slots),
+                  int(num_blocks))
+
+
+def make_tree_desc(batch, num_nodes, vocab, *, bf16=True, eos_token=-1) -> TreeDesc:
+    return TreeDesc(int(batch), int(num_nodes), int(vocab), SPECDEC_BF16 if bf16 else SPECDEC_F32,
+                    int(eos_token), 0)
+
+
+def specdec_verify_tree_workspace_bytes(desc: TreeDesc) -> int:
+    return int(lib().specdec_verify_tree_workspace_bytes(ctypes.byref(desc)))
+
+
+def specdec_verify_tree(desc: TreeDesc, target_logits, node_tokens, parents, num_nodes,
+                        max_tokens, accept_count, num_tokens, out_tokens, path, flags, workspace,
+                        workspace_bytes: Optional[int] = None, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = lib().specdec_verify_tree(ctypes.byref(desc), _ptr(target_logits), _ptr(node_tokens),
+                                   _ptr(parents), _ptr(num_nodes), _ptr(max_tokens),
+                                   _ptr(accept_count), _ptr(num_tokens), _ptr(out_tokens),
+                                   _ptr(path), _ptr(flags), _ptr(workspace),
+                                   int(workspace_bytes), _stream(stream))
+    if st != SPECDEC_OK:
+        raise SpecdecError(st, "specdec_verify_tree")
+
+
+def specdec_verify_tree_profiled(desc: TreeDesc, target_logits, node_tokens, parents, num_nodes,
+                                 max_tokens, accept_count, num_tokens, out_tokens, path, flags,
+                                 workspace, stage_events, workspace_bytes: Optional[int] = None,
+                                 stream=None) -> None:
+    """stage_events: four raw hipEvent_t handles (ints; None entries allowed)."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    handles = (ctypes.c_void_p * 4)(*[None if e is None else int(e) for e in stage_events])
+    st = lib().specdec_verify_tree_profiled(ctypes.byref(desc), _ptr(target_logits),
+                                            _ptr(node_tokens), _ptr(parents), _ptr(num_nodes),
+                                            _ptr(max_tokens), _ptr(accept_count),
+                                            _ptr(num_tokens), _ptr(out_tokens), _ptr(path),
+                                            _ptr(flags), _ptr(workspace), int(workspace_bytes),
+                                            _stream(stream), handles)
+    if st != SPECDEC_OK:
+        raise SpecdecError(st, "specdec_verify_tree_profiled")
 
 
 def specdec_verify_workspace_bytes(desc: VerifyDesc) -> int:
@@ -179,13 +236,13 @@ def specdec_verify_profiled(desc: VerifyDesc, target_logits, draft_logits, draft
 
 
 def specdec_commit_kv(desc: KVDesc, scratch_kv, kv_pool, block_table, accept_count, gamma,
-                      seq_lens, flags, workspace, workspace_bytes: Optional[int] = None,
+                      slot_map, seq_lens, flags, workspace, workspace_bytes: Optional[int] = None,
                       stream=None) -> None:
     if workspace_bytes is None:
         workspace_bytes = workspace.numel() * workspace.element_size()
     st = lib().specdec_commit_kv(ctypes.byref(desc), _ptr(scratch_kv), _ptr(kv_pool),
                                  _ptr(block_table), _ptr(accept_count), _ptr(gamma),
-                                 _ptr(seq_lens), _ptr(flags), _ptr(workspace),
+                                 _ptr(slot_map), _ptr(seq_lens), _ptr(flags), _ptr(workspace),
                                  int(workspace_bytes), _stream(stream))
     if st != SPECDEC_OK:
         raise SpecdecError(st, "specdec_commit_kv")

@@ -31,7 +31,8 @@ namespace specdec {
 namespace {
 
 struct CommitParams {
-    const uint16_t* scratch;   // [B][G+1][L][2][H][D]; null: draft-cache rollback
+    const uint16_t* scratch;   // [B][S][L][2][H][D]; null: draft-cache rollback
+    const int32_t* slot_map;   // [B][G+1] scratch slot per window position, or null (identity)
     uint16_t* pool;            // [L][2][NB][BS][H][D]
     const int32_t* table;      // [B][maxb]
     const int32_t* accept;
@@ -39,7 +40,7 @@ struct CommitParams {
     int32_t* seq_lens;
     uint32_t* flags;
     uint32_t* cnt;             // [B]
-    int B, G, L, H, D, BS, maxb;
+    int B, G, L, H, D, BS, maxb, S;
     int64_t NB;
     int hd;                    // H * D elements per run
 };
@@ -66,9 +67,12 @@ __global__ __launch_bounds__(kThreads) void k_commit(CommitParams P) {
         } else {
             const bool keep = !rollback && j <= m;
             const size_t runs = static_cast<size_t>(P.L) * 2;
-            const uint16_t* src = keep ? P.scratch + (static_cast<size_t>(b) * (P.G + 1) + j) * runs * P.hd
+            const int slot = !keep ? 0 : P.slot_map ? P.slot_map[static_cast<size_t>(b) * (P.G + 1) + j] : j;
+            const uint16_t* src = keep ? P.scratch + (static_cast<size_t>(b) * P.S + slot) * runs * P.hd
                                        : nullptr;
-            if (VEC) {
+            if (slot < 0 || slot >= P.S) {
+                bad = true;
+            } else if (VEC) {
                 const int nv = P.hd / 8;  // 16-byte vectors per run
                 const size_t total = runs * nv;
                 for (size_t e = threadIdx.x; e < total; e += kThreads) {
@@ -115,12 +119,13 @@ bool valid_kv(const specdec_kv_desc_t* d) {
     if (d->batch < 0 || d->batch > 65535 || d->gamma_max < 0 || d->gamma_max > 63) return false;
     if (d->num_layers < 1 || d->num_kv_heads < 1 || d->head_dim < 1 || d->block_size < 1)
         return false;
-    if (d->max_blocks_per_req < 1 || d->num_blocks < 1 || d->reserved != 0) return false;
+    if (d->max_blocks_per_req < 1 || d->num_blocks < 1 || d->scratch_slots < 0) return false;
     if (static_cast<int64_t>(d->num_kv_heads) * d->head_dim > (1 << 24)) return false;
     return true;
 }
 
-specdec_status_t launch_commit(const specdec_kv_desc_t* d, const void* scratch_kv, void* kv_pool,
+specdec_status_t launch_commit(const specdec_kv_desc_t* d, const void* scratch_kv,
+                               const int32_t* slot_map, void* kv_pool,
                                const int32_t* block_table, const int32_t* accept_count,
                                const int32_t* gamma, int32_t* seq_lens, uint32_t* flags,
                                void* workspace, hipStream_t stream);
@@ -138,27 +143,34 @@ extern "C" size_t specdec_commit_kv_workspace_bytes(const specdec_kv_desc_t* d) 
 extern "C" specdec_status_t specdec_commit_kv(const specdec_kv_desc_t* d, const void* scratch_kv,
                                               void* kv_pool, const int32_t* block_table,
                                               const int32_t* accept_count, const int32_t* gamma,
-                                              int32_t* seq_lens, uint32_t* flags, void* workspace,
+                                              const int32_t* slot_map, int32_t* seq_lens,
+                                              uint32_t* flags, void* workspace,
                                               size_t workspace_bytes, hipStream_t stream) {
     if (!valid_kv(d)) return SPECDEC_ERR_INVALID_ARGUMENT;
     if (!scratch_kv || !kv_pool || !block_table || !accept_count || !seq_lens || !workspace)
         return SPECDEC_ERR_INVALID_ARGUMENT;
+    // without a slot map, window position j reads slot j: S must cover G+1
+    if (!slot_map && d->scratch_slots != 0 && d->scratch_slots < d->gamma_max + 1)
+        return SPECDEC_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < specdec_commit_kv_workspace_bytes(d)) return SPECDEC_ERR_WORKSPACE_TOO_SMALL;
     if ((reinterpret_cast<uintptr_t>(workspace) & 3u) != 0) return SPECDEC_ERR_INVALID_ARGUMENT;
     if (d->batch == 0) return SPECDEC_OK;
-    return launch_commit(d, scratch_kv, kv_pool, block_table, accept_count, gamma, seq_lens, flags,
-                         workspace, stream);
+    return launch_commit(d, scratch_kv, slot_map, kv_pool, block_table, accept_count, gamma,
+                         seq_lens, flags, workspace, stream);
 }
 
 namespace specdec {
 namespace {
 
-specdec_status_t launch_commit(const specdec_kv_desc_t* d, const void* scratch_kv, void* kv_pool,
+specdec_status_t launch_commit(const specdec_kv_desc_t* d, const void* scratch_kv,
+                               const int32_t* slot_map, void* kv_pool,
                                const int32_t* block_table, const int32_t* accept_count,
                                const int32_t* gamma, int32_t* seq_lens, uint32_t* flags,
                                void* workspace, hipStream_t stream) {
     CommitParams P{};
     P.scratch = static_cast<const uint16_t*>(scratch_kv);
+    P.slot_map = slot_map;
+    P.S = d->scratch_slots > 0 ? d->scratch_slots : d->gamma_max + 1;
     P.pool = static_cast<uint16_t*>(kv_pool);
     P.table = block_table;
     P.accept = accept_count;
@@ -197,11 +209,12 @@ extern "C" specdec_status_t specdec_rollback_kv(const specdec_kv_desc_t* d, void
     if (!valid_kv(d)) return SPECDEC_ERR_INVALID_ARGUMENT;
     if (!kv_pool || !block_table || !accept_count || !seq_lens || !workspace)
         return SPECDEC_ERR_INVALID_ARGUMENT;
+    if (d->scratch_slots != 0) return SPECDEC_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < specdec_commit_kv_workspace_bytes(d)) return SPECDEC_ERR_WORKSPACE_TOO_SMALL;
     if ((reinterpret_cast<uintptr_t>(workspace) & 3u) != 0) return SPECDEC_ERR_INVALID_ARGUMENT;
     if (d->batch == 0) return SPECDEC_OK;
-    return launch_commit(d, nullptr, kv_pool, block_table, accept_count, gamma, seq_lens, flags,
-                         workspace, stream);
+    return launch_commit(d, nullptr, nullptr, kv_pool, block_table, accept_count, gamma, seq_lens,
+                         flags, workspace, stream);
 }
 
 extern "C" specdec_status_t specdec_workspace_clear(void* workspace, size_t bytes, hipStream_t stream) {

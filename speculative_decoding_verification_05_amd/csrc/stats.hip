@@ -112,6 +112,7 @@ __global__ __launch_bounds__(kThreads) void k_stats(VerifyParams P) {
     const int lo = ci * P.chunk;
     const int hi = min(P.V, lo + P.chunk);
     auto keep = [&]() {
+        if (P.nodes) return i < tree_nodes(P, b);
         if (!P.gamma) return true;
         const int g = request_gamma(P, b);
         return is_target ? i <= g : i < g;

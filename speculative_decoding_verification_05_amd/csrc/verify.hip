@@ -558,12 +558,6 @@ __global__ __launch_bounds__(kThreads) void k_decide_greedy(VerifyParams P) {
 
 // ------------------------------------------------------------------ host side
 
-struct Layout {
-    int rows, nc, chunk, nc2, chunk2, wpr, cpw;
-    bool trunc, wide;
-    size_t off_cnt, off_part, off_csum, off_nuc, total;
-};
-
 // Truncation mode: sampling with an effective top-k or with top-p.
 bool truncation_mode(const specdec_verify_desc_t* d) {
     return d->mode == SPECDEC_SAMPLE &&
@@ -604,6 +598,8 @@ bool valid_desc(const specdec_verify_desc_t* d) {
     }
     return true;
 }
+
+}  // namespace
 
 // Chunking.  Statistics pass: about one round of workgroups resident at once
 // (8 per CU x 256 CUs), so that every workgroup streams from the start and
@@ -650,6 +646,8 @@ Layout make_layout(const specdec_verify_desc_t* d) {
     L.total = off;
     return L;
 }
+
+namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

@@ -27,6 +27,9 @@ struct VerifyParams {
     const void* draft;
     const int32_t* tokens;
     const int32_t* gamma;
+    const int32_t* nodes;       // tree mode: [B] node counts (rows used), or null
+    const int32_t* parents;     // tree mode: [B][G+1] parent of each node
+    int32_t* path;              // tree mode: [B][G+1] kept path (output)
     const int32_t* max_tokens;  // [B] token budget of the round, or null
     int32_t* accept_count;
     int32_t* num_tokens;        // [B] or null
@@ -58,6 +61,12 @@ struct VerifyParams {
 __device__ __forceinline__ int request_gamma(const VerifyParams& P, int b) {
     const int g = P.gamma ? P.gamma[b] : P.G;
     return min(max(g, 0), P.G);
+}
+
+// Tree mode: nodes of request b clamped into [1, G+1] (G+1 = padded nodes).
+__device__ __forceinline__ int tree_nodes(const VerifyParams& P, int b) {
+    const int n = P.nodes ? P.nodes[b] : P.G + 1;
+    return min(max(n, 1), P.G + 1);
 }
 
 __device__ __forceinline__ uint32_t gamma_flag(const VerifyParams& P, int b) {
@@ -152,6 +161,15 @@ __device__ __forceinline__ float block_sum(float v) {
     for (int k = 1; k < kWaves; ++k) r += s_v[k];
     return r;
 }
+
+// Workspace layout and chunking of one verify call (shared by the chain and
+// tree entry points).
+struct Layout {
+    int rows, nc, chunk, nc2, chunk2, wpr, cpw;
+    bool trunc, wide;
+    size_t off_cnt, off_part, off_csum, off_nuc, total;
+};
+Layout make_layout(const specdec_verify_desc_t* d);
 
 // The statistics pass (one partial per chunk of every used row); start/stop
 // events (both null, or both set) bracket the kernel.

@@ -24,6 +24,16 @@ pages; sizes are the full-scale cases used for parity and timing):
 * ``b512_ragged_v262144_kv`` B=512, gamma_i in U{1..8}, V=262144, bf16, T=1.0,
                               paged KV commit (32 layers x 8 heads x 128).
 
+* ``tree_b64_n16_v151936_greedy_kv``  B=64 draft trees of 16 nodes (depth 5,
+                              the fixed topology TREE16 below), V=151936, bf16,
+                              greedy tree verification + path commit into the
+                              28 x 4 x 128 paged cache.  The k children of a
+                              node carry the target's k top-ranked tokens
+                              after it, the first child (the deepest branch)
+                              the top-1, except that at rate 0.25 the top-1
+                              sits at another child (or, for a single child,
+                              is replaced by the second-ranked token).
+
 The two KV workloads also carry a draft model's cache shape for the draft-cache
 rollback (the pages give none; a small model of the same family is assumed):
 24 layers x 2 heads x 64 beside the 28 x 4 x 128 target, and 18 layers x
@@ -49,6 +59,12 @@ import numpy as np
 _TAG_TARGET, _TAG_DRAFT, _TAG_TOKENS, _TAG_SIGMA, _TAG_GAMMA = 0, 1, 2, 3, 4
 _TAG_KV, _TAG_CTX, _TAG_ZIPF, _TAG_SWAP = 5, 6, 7, 8
 _TAG_DRAFT_KV = 9
+_TAG_TREE = 10
+
+# A 16-node draft tree of depth 5 (node 0 = the pending token): four
+# candidates for the first position, then narrowing branches, the shape of
+# the multi-candidate trees that tree speculation verifies in one forward.
+TREE16 = (-1, 0, 0, 0, 0, 1, 1, 1, 2, 2, 5, 5, 8, 10, 12, 13)
 
 BF16_QNAN = np.uint16(0x7FC0)      # fill for padded (never used) logits rows
 KV_POISON = np.uint16(0x7FA5)      # fill for untouched KV-pool entries (a NaN)
@@ -86,6 +102,7 @@ class Workload:
     ragged: bool = False        # gamma_i ~ U{1..gamma_max}
     kv: Optional[KVShape] = None
     draft_kv: Optional[KVShape] = None   # the draft model's cache (rollback)
+    tree: Optional[tuple] = None         # tree workloads: parent of each node (node 0 = root)
     data_seed: int = 0
     verify_seed: int = 0
 
@@ -112,6 +129,9 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
     Workload("b128_g4_v128256_topk50_topp09", 128, 4, 128256, "bf16", "sample", 0.7, 4.0,
              "noise_fixed", draft_sigma=0.8, zipf_s=1.1, top_k=50, top_p=0.9,
              data_seed=1004, verify_seed=46),
+    Workload("tree_b64_n16_v151936_greedy_kv", 64, 15, 151936, "bf16", "greedy", 1.0, 3.0,
+             "top_swap", swap_rate=0.25, tree=TREE16,
+             kv=KVShape(28, 4, 128, 16, 512, 4096), data_seed=1006, verify_seed=48),
     Workload("b512_ragged_v262144_kv", 512, 8, 262144, "bf16", "sample", 1.0, 3.0,
              "noise_fixed", draft_sigma=0.6, ragged=True,
              kv=KVShape(32, 8, 128, 16, 1024, 8192), draft_kv=KVShape(18, 1, 256, 16, 1024, 8192),
@@ -277,6 +297,69 @@ def kv_pool_shape(wl: Workload, num_blocks: int):
     return (kv.layers, 2, num_blocks, kv.block_size, kv.kv_heads, kv.head_dim)
 
 
+def tree_depths(parents: Sequence[int]) -> np.ndarray:
+    """Depth of every node of a parent array (node 0 = root)."""
+    d = np.zeros(len(parents), np.int32)
+    for j in range(1, len(parents)):
+        d[j] = d[parents[j]] + 1
+    return d
+
+
+def kv_window(wl: Workload, b: int) -> int:
+    """Last window offset the commit of request b may touch: gamma_b for a
+    chain, the tree's depth for a tree."""
+    if wl.tree is not None:
+        return int(tree_depths(wl.tree).max())
+    return request_gamma(wl, b)
+
+
+def make_tree_inputs(wl: Workload, threads: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Greedy tree verification inputs: ``target`` [B][N][V] (row j = the
+    target after the path to node j), ``tokens`` [B][N], ``parents`` [B][N]
+    (wl.tree for every request), ``num_nodes`` [B]."""
+    par = np.array(wl.tree, np.int32)
+    N, V, B = len(par), wl.vocab, wl.batch
+    assert N == wl.gamma_max + 1
+    kids = [[j for j in range(1, N) if par[j] == p] for p in range(N)]
+    target = np.empty((B, N, V), dtype=np.uint16 if wl.dtype == "bf16" else np.float32)
+    tokens = np.zeros((B, N), np.int32)
+
+    def one(b: int) -> None:
+        rt = _rng(wl.data_seed, b, _TAG_TARGET)
+        z = rt.standard_normal((N, V), dtype=np.float32) * np.float32(wl.target_sigma)
+        if wl.dtype == "bf16":
+            target[b] = f32_to_bf16_bits(z)
+            zv = bf16_bits_to_f32(target[b])
+        else:
+            target[b] = z
+            zv = z
+        rtree = _rng(wl.data_seed, b, _TAG_TREE)
+        coins = rtree.random(N)
+        for p in range(N):
+            k = len(kids[p])
+            if k == 0:
+                continue
+            top = np.argpartition(zv[p], V - (k + 1))[V - (k + 1):]
+            top = top[np.lexsort((top, -zv[p][top]))]     # rank order, lowest index first
+            ranked = list(top[:k])
+            if coins[p] < wl.swap_rate:
+                # the draft's first candidate is not the target's choice: the
+                # target's token sits at another child, or nowhere when the
+                # node has a single child
+                if k > 1:
+                    c = int(rtree.integers(1, k))
+                    ranked[0], ranked[c] = ranked[c], ranked[0]
+                else:
+                    ranked[0] = top[k]
+            for c, j in enumerate(kids[p]):
+                tokens[b, j] = ranked[c]
+
+    with ThreadPoolExecutor(threads or _pool_threads()) as ex:
+        list(ex.map(one, range(B)))
+    return {"target": target, "tokens": tokens, "parents": np.tile(par, (B, 1)),
+            "num_nodes": np.full(B, N, np.int32)}
+
+
 def make_kv_inputs(wl: Workload, with_pool: bool = True,
                    threads: Optional[int] = None, with_scratch: bool = True) -> KVInputs:
     """Scratch K/V for the gamma+1 verified slots, block table and context lengths.
@@ -292,7 +375,7 @@ def make_kv_inputs(wl: Workload, with_pool: bool = True,
     L, H, D, bs = kv.layers, kv.kv_heads, kv.head_dim, kv.block_size
     seq = np.array([int(_rng(wl.data_seed, b, _TAG_CTX).integers(kv.ctx_lo, kv.ctx_hi + 1))
                     for b in range(B)], dtype=np.int32)
-    gam = np.array([request_gamma(wl, b) for b in range(B)], dtype=np.int32)
+    gam = np.array([kv_window(wl, b) for b in range(B)], dtype=np.int32)
     max_blocks = (kv.ctx_hi + G + 1 + bs - 1) // bs
     first = seq // bs
     last = (seq + gam) // bs

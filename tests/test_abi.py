@@ -103,13 +103,15 @@ def test_commit_descriptor_checks():
     ok = sd.make_kv_desc(4, 7, 28, 4, 128, 16, 300, 8)
     assert sd.specdec_commit_kv_workspace_bytes(ok) >= 16
     for field, val in (("num_layers", 0), ("block_size", 0), ("num_blocks", 0),
-                       ("gamma_max", 64), ("reserved", 2)):
+                       ("gamma_max", 64), ("scratch_slots", -1)):
         d = sd.make_kv_desc(4, 7, 28, 4, 128, 16, 300, 8)
         setattr(d, field, val)
         assert sd.specdec_commit_kv_workspace_bytes(d) == 0
-        st = sd.lib().specdec_commit_kv(ctypes.byref(d), 1, 1, 1, 1, None, 1, None, 16, 1 << 20, None)
+        st = sd.lib().specdec_commit_kv(ctypes.byref(d), 1, 1, 1, 1, None, None, 1, None, 16,
+                                        1 << 20, None)
         assert st == sd.SPECDEC_ERR_INVALID_ARGUMENT
-    st = sd.lib().specdec_commit_kv(ctypes.byref(ok), 16, 16, 16, 16, None, 16, None, 16, 0, None)
+    st = sd.lib().specdec_commit_kv(ctypes.byref(ok), 16, 16, 16, 16, None, None, 16, None, 16, 0,
+                                    None)
     assert st == sd.SPECDEC_ERR_WORKSPACE_TOO_SMALL
     assert sd.lib().specdec_workspace_clear(None, 16, None) == sd.SPECDEC_ERR_INVALID_ARGUMENT
 
@@ -129,3 +131,35 @@ def test_rollback_descriptor_checks():
         assert st == sd.SPECDEC_ERR_INVALID_ARGUMENT
     st = sd.lib().specdec_rollback_kv(ctypes.byref(ok), 16, 16, 16, None, 16, None, 16, 0, None)
     assert st == sd.SPECDEC_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_tree_descriptor_checks():
+    ok = sd.make_tree_desc(4, 16, 1000)
+    assert sd.specdec_verify_tree_workspace_bytes(ok) > 0
+    for field, val in (("num_nodes", 0), ("num_nodes", 65), ("vocab", 0), ("dtype", 3),
+                       ("eos_token", 1000), ("eos_token", -2), ("reserved", 1), ("batch", -1)):
+        d = sd.make_tree_desc(4, 16, 1000)
+        setattr(d, field, val)
+        assert sd.specdec_verify_tree_workspace_bytes(d) == 0
+        st = sd.lib().specdec_verify_tree(ctypes.byref(d), 16, 16, 16, None, None, 16, None, 16, 16,
+                                          None, 256, 1 << 20, None)
+        assert st == sd.SPECDEC_ERR_INVALID_ARGUMENT, (field, val)
+    n = sd.specdec_verify_tree_workspace_bytes(ok)
+    for i in range(5):
+        args = [16, 16, 16, None, None, 16, None, 16, 16, None, 256]
+        args[[0, 1, 2, 5, 7][i]] = None
+        st = sd.lib().specdec_verify_tree(ctypes.byref(ok), *args[:10], 256, n, None)
+        assert st == sd.SPECDEC_ERR_INVALID_ARGUMENT
+    st = sd.lib().specdec_verify_tree(ctypes.byref(ok), 16, 16, 16, None, None, 16, None, 16, 16,
+                                      None, 256, n - 1, None)
+    assert st == sd.SPECDEC_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_commit_slot_count_must_cover_the_window():
+    d = sd.make_kv_desc(4, 7, 2, 2, 64, 16, 300, 8, scratch_slots=4)
+    st = sd.lib().specdec_commit_kv(ctypes.byref(d), 16, 16, 16, 16, None, None, 16, None, 16,
+                                    1 << 20, None)
+    assert st == sd.SPECDEC_ERR_INVALID_ARGUMENT     # no slot map: needs G+1 = 8 slots
+    st = sd.lib().specdec_rollback_kv(ctypes.byref(d), 16, 16, 16, None, 16, None, 16, 1 << 20,
+                                      None)
+    assert st == sd.SPECDEC_ERR_INVALID_ARGUMENT     # rollback takes no scratch

@@ -36,7 +36,7 @@ def run_commit(wl, kv, accept, gamma, dev="cuda", flags=False, table=None):
     acc = accept if not isinstance(accept, np.ndarray) else to_dev(accept, dev)
     gam = None if gamma is None else to_dev(gamma, dev)
     sd.specdec_commit_kv(desc, to_dev(kv.scratch, dev), pool, to_dev(table, dev), acc, gam,
-                         seq, fl, ws)
+                         None, seq, fl, ws)
     torch.cuda.synchronize()
     out = pool.cpu().numpy().view(np.uint16), seq.cpu().numpy()
     if flags:

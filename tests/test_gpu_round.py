@@ -176,7 +176,8 @@ def test_round_in_hip_graph_replays():
 
     def round_():
         ver(t_dev, None, tok_dev, None, mt_dev)
-        sd.specdec_commit_kv(tdesc, scratch, pool, tbl, ver.accept_count, None, seq, None, ws_t)
+        sd.specdec_commit_kv(tdesc, scratch, pool, tbl, ver.accept_count, None, None, seq, None,
+                             ws_t)
         sd.specdec_rollback_kv(ddesc, dpool_d, tbl, ver.accept_count, None, dseq_d, None, ws_d)
 
     # the oracle's round
