@@ -30,6 +30,8 @@
 namespace specdec {
 namespace {
 
+constexpr int kCopyUnroll = 8;  // 16-byte vectors per lane in flight while copying a slot
+
 struct CommitParams {
     const uint16_t* scratch;   // [B][S][L][2][H][D]; null: draft-cache rollback
     const int32_t* slot_map;   // [B][G+1] scratch slot per window position, or null (identity)
@@ -48,39 +50,71 @@ struct CommitParams {
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) void k_commit(CommitParams P) {
     const int j = blockIdx.x, b = blockIdx.y;
+    // independent loads first (the slot map entry is in bounds for every j)
     const int g = P.gamma ? P.gamma[b] : P.G;
     const int m = P.accept[b];
     const int t = P.seq_lens[b];
+    const int mapped = P.slot_map ? P.slot_map[static_cast<size_t>(b) * (P.G + 1) + j] : j;
     const bool rollback = P.scratch == nullptr;
+    const bool valid = g >= 0 && g <= P.G && m >= 0 && m <= g && t >= 0;
+    if (!valid || j > g) {
+        // past the window, or a request left untouched (flagged once)
+        const bool bad = (g < 0 || g > P.G) || (!valid && j == 0);
+        if (bad && threadIdx.x == 0 && P.flags) atomicOr(P.flags + b, SPECDEC_FLAG_BAD_BLOCK);
+        return;
+    }
+    const bool work = rollback ? (j > m && j < g) : true;
+    const int64_t pos = static_cast<int64_t>(t) + j;
+    const int64_t lb = pos / P.BS;
+    const int off = static_cast<int>(pos % P.BS);
+    const int32_t phys = (work && lb < P.maxb) ? P.table[static_cast<size_t>(b) * P.maxb + lb] : -1;
+    // The new length is written by the last of the window's g+1 workgroups to
+    // arrive.  Every wave of each of them has read t before the barrier, so
+    // none can see an advanced length: no fence is needed, only the
+    // device-scope counter.  The arrival is issued before the copy so that
+    // its round trip overlaps the copy's.
+    __syncthreads();
+    uint32_t arrived = 0;
+    if (threadIdx.x == 0) arrived = atomicAdd(P.cnt + b, 1u);
     bool bad = false;
-    if (g < 0 || g > P.G) {
-        bad = true;
-    } else if (m < 0 || m > g || t < 0) {
-        bad = j == 0;  // flagged once; nothing of the request is touched
-    } else if (rollback ? (j > m && j < g) : j <= g) {
-        const int64_t pos = static_cast<int64_t>(t) + j;
-        const int64_t lb = pos / P.BS;
-        const int off = static_cast<int>(pos % P.BS);
-        const int32_t phys = lb < P.maxb ? P.table[static_cast<size_t>(b) * P.maxb + lb] : -1;
+    if (work) {
         if (phys < 0 || phys >= P.NB) {
             bad = true;
         } else {
             const bool keep = !rollback && j <= m;
             const size_t runs = static_cast<size_t>(P.L) * 2;
-            const int slot = !keep ? 0 : P.slot_map ? P.slot_map[static_cast<size_t>(b) * (P.G + 1) + j] : j;
+            const int slot = keep ? mapped : 0;
             const uint16_t* src = keep ? P.scratch + (static_cast<size_t>(b) * P.S + slot) * runs * P.hd
                                        : nullptr;
             if (slot < 0 || slot >= P.S) {
                 bad = true;
             } else if (VEC) {
+                // kCopyUnroll vectors per lane in flight: all loads of a group
+                // are issued before its stores
                 const int nv = P.hd / 8;  // 16-byte vectors per run
-                const size_t total = runs * nv;
-                for (size_t e = threadIdx.x; e < total; e += kThreads) {
-                    const size_t run = e / nv, w = e % nv;  // run = layer * 2 + (K|V)
-                    uint16_t* dst = P.pool + ((run * P.NB + phys) * P.BS + off) * P.hd + w * 8;
-                    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-                    if (keep) v = *reinterpret_cast<const uint4*>(src + run * P.hd + w * 8);
-                    *reinterpret_cast<uint4*>(dst) = v;
+                const int total = static_cast<int>(runs) * nv;
+                for (int e0 = threadIdx.x; e0 < total; e0 += kThreads * kCopyUnroll) {
+                    uint4 v[kCopyUnroll];
+#pragma unroll
+                    for (int u = 0; u < kCopyUnroll; ++u) {
+                        const int e = e0 + u * kThreads;
+                        v[u] = make_uint4(0u, 0u, 0u, 0u);
+                        if (keep && e < total) {
+                            const int run = e / nv, w = e - run * nv;
+                            const u32x4_t x = __builtin_nontemporal_load(
+                                reinterpret_cast<const u32x4_t*>(src + static_cast<size_t>(run) * P.hd + w * 8));
+                            v[u] = make_uint4(x.x, x.y, x.z, x.w);
+                        }
+                    }
+#pragma unroll
+                    for (int u = 0; u < kCopyUnroll; ++u) {
+                        const int e = e0 + u * kThreads;
+                        if (e < total) {
+                            const int run = e / nv, w = e - run * nv;  // run = layer * 2 + (K|V)
+                            uint16_t* dst = P.pool + ((static_cast<size_t>(run) * P.NB + phys) * P.BS + off) * P.hd + w * 8;
+                            *reinterpret_cast<uint4*>(dst) = v[u];
+                        }
+                    }
                 }
             } else {
                 const size_t total = runs * P.hd;
@@ -92,20 +126,13 @@ __global__ __launch_bounds__(kThreads) void k_commit(CommitParams P) {
             }
         }
     }
-    if (bad && threadIdx.x == 0 && P.flags) atomicOr(P.flags + b, SPECDEC_FLAG_BAD_BLOCK);
-    // Every lane read t before this point (its copies used it), so once all
-    // G+1 workgroups of the request have arrived nobody reads the old length
-    // any more: no fence is needed, only the device-scope counter.
-    __shared__ int s_last;
-    __syncthreads();
     if (threadIdx.x == 0) {
-        const uint32_t old = atomicAdd(P.cnt + b, 1u);
-        s_last = (old == static_cast<uint32_t>(P.G));  // G+1 slots per request
-        if (s_last) atomicExch(P.cnt + b, 0u);
+        if (bad && P.flags) atomicOr(P.flags + b, SPECDEC_FLAG_BAD_BLOCK);
+        if (arrived == static_cast<uint32_t>(g)) {
+            atomicExch(P.cnt + b, 0u);  // ready for the next call
+            P.seq_lens[b] = t + (rollback ? min(m + 1, g) : m + 1);
+        }
     }
-    __syncthreads();
-    if (s_last && threadIdx.x == 0 && g >= 0 && g <= P.G && m >= 0 && m <= g && t >= 0)
-        P.seq_lens[b] = t + (rollback ? min(m + 1, g) : m + 1);
 }
 
 __global__ void k_fill_zero(uint32_t* p, size_t n) {
@@ -121,6 +148,9 @@ bool valid_kv(const specdec_kv_desc_t* d) {
         return false;
     if (d->max_blocks_per_req < 1 || d->num_blocks < 1 || d->scratch_slots < 0) return false;
     if (static_cast<int64_t>(d->num_kv_heads) * d->head_dim > (1 << 24)) return false;
+    // element offsets inside one slot stay in 32-bit range
+    if (static_cast<int64_t>(d->num_layers) * 2 * d->num_kv_heads * d->head_dim >= (int64_t{1} << 31))
+        return false;
     return true;
 }
 
