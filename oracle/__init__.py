@@ -89,6 +89,9 @@ class Oracle:
         L.oracle_rollback_kv.restype = ctypes.c_int
         L.oracle_verify_tree.argtypes = [ctypes.c_int32] * 4 + [P, P, P, P, ctypes.c_int32] + [P] * 6
         L.oracle_verify_tree.restype = ctypes.c_int
+        L.oracle_propose_ngram.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_int32, P, P, P]
+        L.oracle_propose_ngram.restype = ctypes.c_int
         self.lib = L
         self.path = path
 
@@ -223,6 +226,21 @@ class Oracle:
             raise ValueError(f"oracle_verify_tree rejected its arguments (code {rc})")
         return out
 
+    def propose_ngram(self, history: np.ndarray, hist_len: np.ndarray, n_min: int, n_max: int,
+                      gamma_max: int):
+        """Prompt-lookup proposal; returns (draft_tokens [B][G], num_drafts [B], match_len [B])."""
+        h = np.ascontiguousarray(history, dtype=np.int32)
+        ln = np.ascontiguousarray(hist_len, dtype=np.int32)
+        B, Lmax = h.shape
+        toks = np.zeros((B, gamma_max), np.int32)
+        nd = np.zeros(B, np.int32)
+        ml = np.zeros(B, np.int32)
+        rc = self.lib.oracle_propose_ngram(B, Lmax, _ptr(h), _ptr(ln), int(n_min), int(n_max),
+                                           int(gamma_max), _ptr(toks), _ptr(nd), _ptr(ml))
+        if rc != 0:
+            raise ValueError(f"oracle_propose_ngram rejected its arguments (code {rc})")
+        return toks, nd, ml
+
     def rollback_kv(self, pool: np.ndarray, block_table: np.ndarray, accept_count: np.ndarray,
                     seq_lens: np.ndarray, gamma_max: int, gamma=None):
         """Roll back a draft cache in place (``pool`` uint16, ``seq_lens`` int32)."""
@@ -274,3 +292,7 @@ def rollback_kv(*args, **kw):
 
 def verify_tree(*args, **kw):
     return default().verify_tree(*args, **kw)
+
+
+def propose_ngram(*args, **kw):
+    return default().propose_ngram(*args, **kw)

@@ -255,7 +255,7 @@ int oracle_verify(const oracle_verify_args* a, const void* target, const void* d
     if (B < 0 || G < 0 || G > 63 || V < 1 || !target || !draft_tokens || !accept_count
         || !out_tokens)
         return -1;
-    if (!a->greedy && (!draft || !(a->temperature > 0.0))) return -2;
+    if (!a->greedy && !(a->temperature > 0.0)) return -2;
     if (!req_ids && n != B) return -3;
 
     double* P = NULL; /* target distributions, rows 0..gamma_b, each V */
@@ -300,7 +300,7 @@ int oracle_verify(const oracle_verify_args* a, const void* target, const void* d
             if (residual_mass) residual_mass[k] = 0.0;
             committed_m = m;
         } else {
-            for (int32_t i = 0; i < gb; ++i)
+            for (int32_t i = 0; i < gb && draft; ++i)
                 if (row_nonfinite(row_ptr(draft, a->is_bf16, (int64_t)b * G + i, V), a->is_bf16, V))
                     fl |= ORACLE_FLAG_NONFINITE;
             /* p_i, q_i: the actual sampling distributions ([KB] s.04). */
@@ -312,6 +312,15 @@ int oracle_verify(const oracle_verify_args* a, const void* target, const void* d
                 if (nc) note_near(&near, i);
             }
             for (int32_t i = 0; i < gb; ++i) {
+                if (!draft) {
+                    /* No draft rows: the proposer is deterministic (n-gram
+                     * lookup), so q_i is the point mass on d_i ([KB] s.08:
+                     * such candidates need their probability representation
+                     * stated; the exact rule of s.04 is then applied as is). */
+                    for (int64_t v = 0; v < V; ++v) Q[(size_t)i * V + v] = 0.0;
+                    if (d[i] >= 0 && d[i] < V) Q[(size_t)i * V + d[i]] = 1.0;
+                    continue;
+                }
                 int32_t nc = 0;
                 oracle_row_distribution(row_ptr(draft, a->is_bf16, (int64_t)b * G + i, V),
                                         a->is_bf16, V, a->temperature, a->top_k, a->top_p,
@@ -564,6 +573,53 @@ int oracle_verify_tree(int32_t B, int32_t N, int32_t V, int32_t is_bf16, const v
         accept_count[b] = kept_m;
         if (num_tokens) num_tokens[b] = nt;
         if (flags) flags[b] = fl;
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------- n-gram */
+
+/* Prompt-lookup / n-gram proposal ([KB] s.08: candidates found from repeated
+ * patterns in the text; [MATH]: pattern-based drafting searches the existing
+ * context for a matching sequence at near-zero cost; [TUT] s.13.1 and s.14:
+ * prompt lookup / n-gram candidates come from the prompt or the history).
+ * For n = n_max down to n_min: the last n tokens of the history are searched
+ * for their most recent earlier occurrence (one that ends before the last
+ * position); the first n that has one wins, and the tokens that follow the
+ * occurrence, at most gamma_max of them and never past the history's end,
+ * are the proposal.  No occurrence: nothing is proposed. */
+int oracle_propose_ngram(int32_t B, int32_t max_len, const int32_t* history,
+                         const int32_t* hist_len, int32_t n_min, int32_t n_max, int32_t G,
+                         int32_t* draft_tokens, int32_t* num_drafts, int32_t* match_len)
+{
+    if (B < 0 || max_len < 1 || n_min < 1 || n_max < n_min || G < 0 || !history || !hist_len
+        || !draft_tokens || !num_drafts)
+        return -1;
+    for (int32_t b = 0; b < B; ++b) {
+        const int32_t L = hist_len[b];
+        if (L < 0 || L > max_len) return -2;
+        const int32_t* h = history + (size_t)b * max_len;
+        int32_t* out = draft_tokens + (size_t)b * G;
+        for (int32_t i = 0; i < G; ++i) out[i] = -1;
+        num_drafts[b] = 0;
+        if (match_len) match_len[b] = 0;
+        for (int32_t n = n_max; n >= n_min; --n) {
+            if (L < n + 1) continue;
+            int32_t found = -1;
+            for (int32_t s = L - n - 1; s >= 0 && found < 0; --s) {
+                int32_t same = 1;
+                for (int32_t k = 0; k < n; ++k)
+                    if (h[s + k] != h[L - n + k]) { same = 0; break; }
+                if (same) found = s;
+            }
+            if (found < 0) continue;
+            const int32_t first = found + n;       /* the token after the occurrence */
+            int32_t cnt = L - first < G ? L - first : G;
+            for (int32_t i = 0; i < cnt; ++i) out[i] = h[first + i];
+            num_drafts[b] = cnt;
+            if (match_len) match_len[b] = n;
+            break;
+        }
     }
     return 0;
 }

@@ -8,7 +8,8 @@
  *
  * Layouts match the device layouts so the same host buffers feed both sides:
  *   target  [B][G+1][V]  float32 or bfloat16 bit patterns (uint16)
- *   draft   [B][G][V]    same type (unused in greedy mode, may be NULL)
+ *   draft   [B][G][V]    same type (unused in greedy mode; NULL in sampling
+ *                        mode: point-mass drafts, q_i = 1 at d_i)
  *   tokens  [B][G] int32, gamma [B] int32 (NULL: every request uses G)
  */
 #ifndef SPECDEC_ORACLE_H
@@ -121,6 +122,17 @@ int oracle_rollback_kv(int32_t batch, int32_t gamma_max, int32_t layers, int32_t
                        int32_t head_dim, int32_t block_size, int32_t max_blocks,
                        int64_t num_blocks, uint16_t* pool, const int32_t* block_table,
                        const int32_t* accept_count, const int32_t* gamma, int32_t* seq_lens);
+
+/* Prompt-lookup / n-gram proposal.
+ *   history [B][max_len] int32, hist_len [B] in [0, max_len]
+ *   draft_tokens [B][gamma_max] (-1 padded), num_drafts [B] (0: no match),
+ *   match_len [B] (the n that matched, 0 if none; may be NULL)
+ * For n = n_max down to n_min, the last n tokens are looked up at their most
+ * recent earlier occurrence; the tokens after it (at most gamma_max, not past
+ * the end) are proposed.  Returns 0, or a negative value on bad arguments. */
+int oracle_propose_ngram(int32_t batch, int32_t max_len, const int32_t* history,
+                         const int32_t* hist_len, int32_t n_min, int32_t n_max, int32_t gamma_max,
+                         int32_t* draft_tokens, int32_t* num_drafts, int32_t* match_len);
 
 #ifdef __cplusplus
 }

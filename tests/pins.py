@@ -463,6 +463,82 @@ def pin_commit_slot_map(orc):
         errs.append("seq_lens != t+m+1")
     return errs
 
+
+# ------------------------------------------------- n-gram / prompt lookup
+
+def pin_ngram_worked_cases(orc):
+    errs = []
+    for r in golden_rows("ngram_lookup.txt"):
+        cols = [c.strip() for c in " ".join(r).split("|")]
+        name = cols[0]
+        n_min, n_max, gam = [int(x) for x in cols[1].split()]
+        hist = [int(x) for x in cols[2].split()]
+        want = [int(x) for x in cols[3].split()]
+        want_n = int(cols[4])
+        h = np.array([hist + [0] * 3], np.int32)        # padded row: only hist_len is read
+        toks, nd, ml = orc.propose_ngram(h, np.array([len(hist)]), n_min, n_max, gam)
+        got = [int(x) for x in toks[0][:nd[0]]]
+        if got != want or int(ml[0]) != want_n or np.any(toks[0][nd[0]:] != -1):
+            errs.append(f"{name}: proposal {got} (n={ml[0]}), want {want} (n={want_n})")
+    return errs
+
+
+def _ngram_brute(hist, n_min, n_max, gam):
+    """Tuple search over every earlier start, latest first."""
+    L = len(hist)
+    for n in range(n_max, n_min - 1, -1):
+        if L < n + 1:
+            continue
+        tail = tuple(hist[L - n:])
+        starts = [s for s in range(0, L - n) if tuple(hist[s:s + n]) == tail]
+        if starts:
+            s = max(starts)
+            return list(hist[s + n:s + n + gam]), n
+    return [], 0
+
+
+def pin_ngram_brute_force(orc, B=300):
+    rng = np.random.default_rng(101)
+    Lmax, errs = 60, []
+    h = rng.integers(0, 5, (B, Lmax)).astype(np.int32)
+    ln = rng.integers(0, Lmax + 1, B).astype(np.int32)
+    for n_min, n_max, gam in ((1, 4, 5), (2, 3, 8), (3, 6, 1)):
+        toks, nd, ml = orc.propose_ngram(h, ln, n_min, n_max, gam)
+        for b in range(B):
+            want, wn = _ngram_brute(list(h[b, :ln[b]]), n_min, n_max, gam)
+            got = [int(x) for x in toks[b][:nd[b]]]
+            if got != want or int(ml[b]) != wn:
+                errs.append(f"request {b} ({n_min},{n_max},{gam}): {got} n={ml[b]}, "
+                            f"want {want} n={wn}")
+    return errs
+
+
+# ------------------------------------------------- point-mass (deterministic) drafts
+
+def pin_point_mass_acceptance(orc, B=200_000):
+    """q = point mass on d: the first draft is kept with probability p(d) and
+    the committed first token is distributed as p (exact rule of [KB] s.04
+    with q(d) = 1; distribution preserved, [TUT] s.7)."""
+    p = np.array([0.1, 0.45, 0.3, 0.15])
+    errs = []
+    for d0 in (1, 3):
+        tgt = np.empty((B, 2, 4), np.float32)
+        tgt[:] = _ln_f32(p)
+        d = np.full((B, 1), d0, np.int32)
+        r = orc.verify(tgt, None, d, temperature=1.0, seed=7 + d0)
+        acc = r["accept_count"].astype(np.float64)
+        se = math.sqrt(p[d0] * (1 - p[d0]) / B)
+        if abs(acc.mean() - p[d0]) > 4 * se:
+            errs.append(f"d={d0}: acceptance {acc.mean():.5f} vs p(d) {p[d0]} (4 SE {4 * se:.5f})")
+        first = r["out_tokens"][:, 0]
+        cnt = np.bincount(first, minlength=4)
+        if stats.chisquare(cnt, p * B).pvalue < P_MIN:
+            errs.append(f"d={d0}: first committed token {cnt} not distributed as p")
+        rejected = r["accept_count"] == 0
+        if np.any(first[rejected] == d0):
+            errs.append(f"d={d0}: a rejection committed the rejected token itself")
+    return errs
+
 # ------------------------------------------------- closed form at fixed alpha
 
 def _fixed_alpha_batch(alpha, gamma, B):
@@ -768,4 +844,7 @@ ALL_PINS = {
     "tree_brute_force": pin_tree_brute_force,
     "tree_chain_equals_chain": pin_tree_chain_equals_chain,
     "commit_slot_map": pin_commit_slot_map,
+    "ngram_worked_cases": pin_ngram_worked_cases,
+    "ngram_brute_force": pin_ngram_brute_force,
+    "point_mass_acceptance": pin_point_mass_acceptance,
 }

@@ -80,6 +80,20 @@ MUTANTS = [
     ("commit_ignores_slot_map",
      "const int32_t slot = slot_map ? slot_map[(size_t)b * (G + 1) + j] : j;",
      "const int32_t slot = j;", ["commit_slot_map"]),
+    ("ngram_earliest_occurrence",
+     "for (int32_t s = L - n - 1; s >= 0 && found < 0; --s) {",
+     "for (int32_t s = 0; s <= L - n - 1 && found < 0; ++s) {",
+     ["ngram_worked_cases", "ngram_brute_force"]),
+    ("ngram_shortest_first", "for (int32_t n = n_max; n >= n_min; --n) {",
+     "for (int32_t n = n_min; n <= n_max; ++n) {", ["ngram_worked_cases", "ngram_brute_force"]),
+    ("ngram_matches_itself", "for (int32_t s = L - n - 1; s >= 0 && found < 0; --s) {",
+     "for (int32_t s = L - n; s >= 0 && found < 0; --s) {",
+     ["ngram_worked_cases", "ngram_brute_force"]),
+    ("ngram_skips_next_token", "const int32_t first = found + n;",
+     "const int32_t first = found + n + 1;", ["ngram_worked_cases", "ngram_brute_force"]),
+    ("point_mass_misplaced", "if (d[i] >= 0 && d[i] < V) Q[(size_t)i * V + d[i]] = 1.0;",
+     "if (d[i] >= 0 && d[i] < V) Q[(size_t)i * V + (d[i] + 1) % V] = 1.0;",
+     ["point_mass_acceptance"]),
 ]
 
 
