@@ -25,7 +25,7 @@ def test_oracle_rejects_malformed_arguments():
     import numpy as np
     t = np.zeros((1, 2, 4), np.float32)
     with pytest.raises(ValueError):
-        oracle.verify(t, None, np.zeros((1, 1), np.int32), temperature=1.0)  # no draft rows
+        oracle.verify(t, None, np.zeros((1, 1), np.int32), temperature=0.0)  # T must be > 0
     with pytest.raises(ValueError):
         oracle.verify(t, np.zeros((1, 1, 4), np.float32), np.zeros((1, 1), np.int32),
                       np.array([3], np.int32), temperature=1.0)  # gamma_i > gamma_max
