@@ -113,6 +113,8 @@ def main() -> int:
     wl0 = synth.WORKLOADS[args.workload or synth.HEADLINE]
     if wl0.tree is not None:
         return bench_tree(args, wl0)
+    if wl0.ngram is not None:
+        return bench_ngram(args, wl0)
     greedy = wl0.mode == "greedy"
     bf16 = wl0.dtype == "bf16"
     per_set = synth.logits_bytes(wl0)
@@ -534,6 +536,113 @@ def bench_tree(args, wl0) -> int:
                     "k_commit": {"avg_us": float(kc.mean()) * 1e6, "bytes_per_launch": cb,
                                  "GBps": cb / kc.mean() / 1e9,
                                  "frac": cb / kc.mean() / 1e9 / HBM_PEAK_GBPS}},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def bench_ngram(args, wl0) -> int:
+    """Prompt-lookup drafting: a step is one specdec_propose_ngram call over the
+    batch of token histories (one read of every history row)."""
+    import torch
+    import speculative_decoding_verification_05_amd as sd
+    from speculative_decoding_verification_05_amd import synth
+
+    dev = torch.device("cuda:0")
+    B, G = wl0.batch, wl0.gamma_max
+    n_min, n_max = wl0.ngram[:2]
+    sets = args.sets or 4
+    host, dev_in = [], []
+    for k in range(sets):
+        x = synth.make_ngram_inputs(dataclasses.replace(wl0, data_seed=wl0.data_seed + 100 * k))
+        host.append(x)
+        dev_in.append({n: torch.from_numpy(v).to(dev) for n, v in x.items()})
+    Lmax = host[0]["history"].shape[1]
+    log(f"workload {wl0.name}: {sets} input sets of {B} histories "
+        f"({np.mean([h['hist_len'].mean() for h in host]):.0f} tokens on average)")
+    desc = sd.make_ngram_desc(B, Lmax, n_min, n_max, G)
+    toks = torch.empty(B, G, dtype=torch.int32, device=dev)
+    nd = torch.empty(B, dtype=torch.int32, device=dev)
+    ml = torch.empty(B, dtype=torch.int32, device=dev)
+
+    def step(k):
+        sd.specdec_propose_ngram(desc, dev_in[k]["history"], dev_in[k]["hist_len"], toks, nd, ml)
+
+    eager = []
+    for k in range(sets):
+        step(k)
+        torch.cuda.synchronize()
+        eager.append(nd.clone())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(0)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for k in range(sets):
+            step(k)
+    graph.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(nd, eager[-1]):
+        log("graph replay differs from eager launches")
+        return 1
+    reps = max(1, args.steps // sets)
+    steps = reps * sets
+    wreps = max(1, args.warmup // sets)
+    for _ in range(wreps):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        graph.replay()
+    torch.cuda.synchronize()
+    sec_per_step = (time.perf_counter() - t0) / steps
+    # kernel time alone: events around each launch on the launching stream
+    n_prof = max(sets, (args.profile_steps // sets) * sets)
+    evs = []
+    for j in range(n_prof):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        step(j % sets)
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    kt = np.array([a.elapsed_time(b) for a, b in evs]) * 1e-3
+    alg = float(np.mean([h["hist_len"].sum() for h in host])) * 4 + B * 4 + B * (G + 2) * 4
+    achieved = alg / float(kt.mean()) / 1e9
+    proposed = float(np.mean([e.sum().item() for e in eager]))
+    log(f"step {sec_per_step * 1e6:.2f} us (graph); propose kernel avg {kt.mean() * 1e6:.2f} us "
+        f"(events); {achieved:.1f} GB/s = {100 * achieved / HBM_PEAK_GBPS:.1f}% of "
+        f"{HBM_PEAK_GBPS:.0f} GB/s; {proposed:.0f} tokens proposed per step")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        x = host[0]
+        reps_c, t_s = 0, time.perf_counter()
+        while True:
+            oracle.propose_ngram(x["history"], x["hist_len"], n_min, n_max, G)
+            reps_c += 1
+            t_c = time.perf_counter() - t_s
+            if t_c >= args.cpu_seconds or reps_c >= 2000:
+                break
+        cpu = {"value": reps_c * B / t_c, "unit": "requests/s", "cores": 1, "kind": "oracle",
+               "sample": f"{reps_c} pass(es) over all {B} histories of input set 0 ({t_c:.1f} s, "
+                         f"single-threaded C)"}
+    res = {
+        "metric": f"proposing requests/sec ({wl0.name})", "value": B / sec_per_step,
+        "unit": "requests/s", "n_gpus": 1, "steps": steps, "warmup": wreps * sets,
+        "ms_per_step": sec_per_step * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int32", "data": "synthetic",
+        "config": {"workload": wl0.name, "batch": B, "max_len": Lmax, "n_min": n_min,
+                   "n_max": n_max, "gamma_max": G, "rotating_input_sets": sets,
+                   "launch": "hipgraph", "proposed_tokens_per_s": proposed / sec_per_step},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "k_propose_ngram", "kernel_avg_us": float(kt.mean()) * 1e6,
+                     "bytes_per_launch": alg},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -124,7 +124,13 @@ size_t specdec_verify_workspace_bytes(const specdec_verify_desc_t* desc);
  *       pending token, i.e. the last committed token whose K/V is not yet in
  *       the cache); row gamma_b yields the bonus token.
  *   draft_logits  [B][G][V] dtype: row i is the draft distribution that
- *       proposed draft token i.  Not read in GREEDY mode (may be NULL).
+ *       proposed draft token i.  Not read in GREEDY mode (may be NULL).  NULL
+ *       in SAMPLE mode means a deterministic proposer (specdec_propose_ngram):
+ *       q_i is the point mass on d_i, so draft i is accepted with probability
+ *       p_i(d_i) and a rejection draws from p_i with d_i removed (AI-infra KB
+ *       M013 s.08 asks for the candidates' probability representation; the
+ *       rule of s.04 then applies unchanged).  Not combined with truncation
+ *       (UNSUPPORTED).
  *   draft_tokens  [B][G] int32: the proposed tokens d_0..d_{gamma_b - 1}.
  *   gamma         [B] int32 in [0, G], or NULL (every request uses G).  Rows
  *       and tokens past gamma_b are never read.  A value outside [0, G] is
@@ -315,6 +321,42 @@ specdec_status_t specdec_verify_tree_profiled(const specdec_tree_desc_t* desc,
                                               int32_t* out_tokens, int32_t* path, uint32_t* flags,
                                               void* workspace, size_t workspace_bytes,
                                               hipStream_t stream, hipEvent_t* stage_events);
+
+/* ------------------------------------------------------------ n-gram drafts */
+
+typedef struct specdec_ngram_desc {
+    int32_t batch;        /* B >= 0 requests */
+    int32_t max_len;      /* row stride of the history, in [1, 2^24) */
+    int32_t n_min;        /* shortest n-gram matched, >= 1 */
+    int32_t n_max;        /* longest n-gram matched, in [n_min, 32] */
+    int32_t gamma_max;    /* G in [0, 63]: most tokens proposed */
+    int32_t reserved;     /* must be 0 */
+} specdec_ngram_desc_t;
+
+/* Prompt-lookup / n-gram drafting (AI-infra KB M013 s.08: candidates from
+ * repeated patterns in the text; "The math behind the speedup": pattern-based
+ * drafting searches the existing context for a matching sequence at near-zero
+ * cost; "Speculative decoding tutorial" s.13.1 and s.14: prompt lookup and
+ * n-gram candidates come from the prompt or the history).  For n = n_max down
+ * to n_min, the last n tokens of a request's history are looked up at their
+ * most recent earlier occurrence (one that ends before the last position);
+ * the first n with an occurrence wins and the tokens following it, at most G
+ * and never past the end of the history, are proposed.
+ *   history      [B][max_len] int32 (device): committed tokens, the pending
+ *       token last; only the first hist_len[b] entries of a row are read.
+ *   hist_len     [B] int32 (device), clamped into [0, max_len].
+ *   draft_tokens [B][G] int32 out: the proposal, -1 after it.
+ *   num_drafts   [B] int32 out: its length (0: no occurrence); pass it to
+ *       specdec_verify as `gamma`.
+ *   match_len    [B] int32 out or NULL: the n that matched (0 if none).
+ * The proposer is deterministic, so its q is a point mass: verify its
+ * proposals with specdec_verify in GREEDY mode, or in SAMPLE mode with
+ * draft_logits = NULL.  No workspace; nothing is allocated.
+ * Errors: INVALID_ARGUMENT for a bad descriptor or a NULL required pointer. */
+specdec_status_t specdec_propose_ngram(const specdec_ngram_desc_t* desc, const int32_t* history,
+                                       const int32_t* hist_len, int32_t* draft_tokens,
+                                       int32_t* num_drafts, int32_t* match_len,
+                                       hipStream_t stream);
 
 /* Bring the draft model's paged cache back to the committed sequence after
  * specdec_verify (AI-infra KB M013 s.06: the target cache and the draft cache

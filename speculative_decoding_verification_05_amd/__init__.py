@@ -38,7 +38,7 @@ FLAG_BAD_TREE = 0x200
 EXPORTS = ("specdec_verify_workspace_bytes", "specdec_verify", "specdec_verify_profiled",
            "specdec_commit_kv_workspace_bytes", "specdec_commit_kv", "specdec_rollback_kv",
            "specdec_verify_tree_workspace_bytes", "specdec_verify_tree",
-           "specdec_verify_tree_profiled",
+           "specdec_verify_tree_profiled", "specdec_propose_ngram",
            "specdec_workspace_clear", "specdec_status_string", "specdec_abi_version")
 
 
@@ -57,6 +57,12 @@ class KVDesc(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("max_blocks_per_req", ctypes.c_int32), ("scratch_slots", ctypes.c_int32),
                 ("num_blocks", ctypes.c_int64)]
+
+
+class NgramDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("max_len", ctypes.c_int32),
+                ("n_min", ctypes.c_int32), ("n_max", ctypes.c_int32),
+                ("gamma_max", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class TreeDesc(ctypes.Structure):
@@ -100,6 +106,8 @@ def lib() -> ctypes.CDLL:
         L.specdec_verify_tree.restype = ctypes.c_int
         L.specdec_verify_tree_profiled.argtypes = [ctypes.POINTER(TreeDesc)] + [P] * 11 + [S, P, P]
         L.specdec_verify_tree_profiled.restype = ctypes.c_int
+        L.specdec_propose_ngram.argtypes = [ctypes.POINTER(NgramDesc)] + [P] * 6
+        L.specdec_propose_ngram.restype = ctypes.c_int
         L.specdec_workspace_clear.argtypes = [P, S, P]
         L.specdec_workspace_clear.restype = ctypes.c_int
         L.specdec_status_string.argtypes = [ctypes.c_int]
@@ -155,6 +163,19 @@ def make_kv_desc(batch, gamma_max, num_layers, num_kv_heads, head_dim, block_siz
 def make_tree_desc(batch, num_nodes, vocab, *, bf16=True, eos_token=-1) -> TreeDesc:
     return TreeDesc(int(batch), int(num_nodes), int(vocab), SPECDEC_BF16 if bf16 else SPECDEC_F32,
                     int(eos_token), 0)
+
+
+def make_ngram_desc(batch, max_len, n_min, n_max, gamma_max) -> NgramDesc:
+    return NgramDesc(int(batch), int(max_len), int(n_min), int(n_max), int(gamma_max), 0)
+
+
+def specdec_propose_ngram(desc: NgramDesc, history, hist_len, draft_tokens, num_drafts,
+                          match_len=None, stream=None) -> None:
+    st = lib().specdec_propose_ngram(ctypes.byref(desc), _ptr(history), _ptr(hist_len),
+                                     _ptr(draft_tokens), _ptr(num_drafts), _ptr(match_len),
+                                     _stream(stream))
+    if st != SPECDEC_OK:
+        raise SpecdecError(st, "specdec_propose_ngram")
 
 
 def specdec_verify_tree_workspace_bytes(desc: TreeDesc) -> int:

@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libspecdec.so")
-SOURCES = ["stats.hip", "verify.hip", "truncate.hip", "tree.hip", "commit.hip"]
+SOURCES = ["stats.hip", "verify.hip", "truncate.hip", "tree.hip", "ngram.hip", "commit.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -10,7 +10,10 @@
 //     normalize(max(p_m - q_m, 0)), otherwise from p_gamma (same tutorial
 //     s.7.2 and s.5.3; KB M013 s.05);
 //   - greedy mode keeps draft i iff it equals argmax of target row i and emits
-//     the argmax at the first mismatch (tutorial s.3-4; KB M013 s.03).
+//     the argmax at the first mismatch (tutorial s.3-4; KB M013 s.03);
+//   - without draft rows (a deterministic proposer such as n-gram lookup),
+//     q_i is the point mass on d_i: the test becomes u_i < p_i(d_i) and the
+//     residual is p_m without d_m (KB M013 s.08 and s.04).
 //
 // Kernels (all HBM-bandwidth bound, no matrix cores: nothing is a contraction):
 //   k_stats          (stats.hip) the one full pass over every used row, one
@@ -33,6 +36,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <algorithm>
+
 namespace specdec {
 namespace {
 
@@ -45,6 +50,7 @@ struct MassRows {
     const void* p;
     const void* q;
     float mp, isp, mq, isq, c;
+    int point;  // point-mass draft: this token carries no residual mass (-1: none)
 };
 
 __device__ __forceinline__ float mass_at(const MassRows& a, float zp, float zq) {
@@ -85,10 +91,13 @@ __device__ __forceinline__ float lane_mass(const ChunkRegs<BF16, VEC>& r, const 
         const Vec<BF16> vp = widen<BF16>(r.p[u]);
         Vec<BF16> vq;
         if (a.q) vq = widen<BF16>(r.q[u]);
+        const int e = lo + (u * kThreads + threadIdx.x) * N;
         float s = 0.0f;
 #pragma unroll
-        for (int k = 0; k < N; ++k) s += mass_at(a, vp.x[k], a.q ? vq.x[k] : 0.0f);
-        const int e = lo + (u * kThreads + threadIdx.x) * N;
+        for (int k = 0; k < N; ++k) {
+            const float r = mass_at(a, vp.x[k], a.q ? vq.x[k] : 0.0f);
+            s += (e + k == a.point) ? 0.0f : r;
+        }
         acc += (e < hi) ? s : 0.0f;
     }
     return acc;
@@ -106,7 +115,7 @@ __device__ float lane_mass_elements(const MassRows& a, int lo, int hi) {
             if (e + k >= hi) break;
             const float zp = load_logit<BF16>(a.p, e + k);
             const float zq = a.q ? load_logit<BF16>(a.q, e + k) : 0.0f;
-            acc += mass_at(a, zp, zq);
+            if (e + k != a.point) acc += mass_at(a, zp, zq);
         }
     }
     return acc;
@@ -249,7 +258,8 @@ __device__ int search_chunk(const MassRows& a, int lo, int hi, float base, float
         float run = 0.0f;
 #pragma unroll
         for (int k = 0; k < N; ++k) {
-            const float r = (e + k < hi) ? mass_at(a, vp[u].x[k], a.q ? vq[u].x[k] : 0.0f) : 0.0f;
+            const float r = (e + k < hi && e + k != a.point)
+                                 ? mass_at(a, vp[u].x[k], a.q ? vq[u].x[k] : 0.0f) : 0.0f;
             if (r > 0.0f) lastp = e + k;
             run += r;
             inc[k] = run;
@@ -298,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void k_decide_sample(VerifyParams P) {
     __shared__ float4 s_part[kMaxPart];
     __shared__ float2 s_stat[127];
     __shared__ float s_csum[1024];
-    __shared__ int s_m;
+    __shared__ int s_m, s_dm;
     __shared__ uint32_t s_fl;
     __shared__ float s_R;
     const int wg = blockIdx.x, b = blockIdx.y;
@@ -352,15 +362,22 @@ __global__ __launch_bounds__(kThreads) void k_decide_sample(VerifyParams P) {
         }
         if (i < g) {
             const float2 t = s_stat[i];
-            const float2 q = s_stat[P.G + 1 + i];
-            if (!(q.x < pos_inf()) || !(q.y == q.y)) fl |= SPECDEC_FLAG_NONFINITE;
+            float2 q = make_float2(0.0f, 1.0f);
+            if (!P.point) {
+                q = s_stat[P.G + 1 + i];
+                if (!(q.x < pos_inf()) || !(q.y == q.y)) fl |= SPECDEC_FLAG_NONFINITE;
+            }
             float a = 0.0f;
             if (d >= 0 && d < P.V) {
                 const int cd = d / P.chunk;
                 const float zt = s_part[i * P.nc + cd].z;
-                const float zq = s_part[(P.G + 1 + i) * P.nc + cd].z;
                 pd = exp2f((zt - t.x) * c) / t.y;
-                qd = exp2f((zq - q.x) * c) / q.y;
+                if (P.point) {
+                    qd = 1.0f;  // point-mass draft: q_i(d_i) = 1
+                } else {
+                    const float zq = s_part[(P.G + 1 + i) * P.nc + cd].z;
+                    qd = exp2f((zq - q.x) * c) / q.y;
+                }
                 if (qd > 0.0f) a = fminf(1.0f, pd / qd);
                 else a = pd > 0.0f ? 1.0f : 0.0f;
             } else {
@@ -375,7 +392,8 @@ __global__ __launch_bounds__(kThreads) void k_decide_sample(VerifyParams P) {
         const uint64_t mask = __ballot(acc);
         const int m = min(g, static_cast<int>(__builtin_ctzll(~mask)));
         fl = wave_or(fl);
-        if (l == 0) { s_m = m; s_fl = fl; }
+        const int dm = lane_value(d, min(m, kWave - 1));  // the rejected draft (m < g)
+        if (l == 0) { s_m = m; s_fl = fl; s_dm = dm; }
     }
     __syncthreads();
     const int m = s_m;
@@ -391,7 +409,11 @@ __global__ __launch_bounds__(kThreads) void k_decide_sample(VerifyParams P) {
     a.q = nullptr;
     a.mq = 0.0f;
     a.isq = 0.0f;
-    if (resid) {
+    a.point = -1;
+    if (resid && P.point) {
+        // max(p - delta_d, 0): p itself without the rejected token
+        a.point = s_dm;
+    } else if (resid) {
         const float2 tq = s_stat[P.G + 1 + m];
         a.q = draft_row(P, b, m, BF16);
         a.mq = tq.x;
@@ -463,6 +485,7 @@ __global__ __launch_bounds__(kThreads) void k_decide_sample(VerifyParams P) {
             // empty residual: draw from p_m instead (never divide by zero)
             fl2 |= SPECDEC_FLAG_RESIDUAL_FALLBACK;
             a.q = nullptr;
+            a.point = -1;
             for (int k = 0; k < P.nc2; ++k) {
                 const float v = chunk_mass<BF16, VEC>(a, k * P.chunk2, min(P.V, (k + 1) * P.chunk2));
                 if (threadIdx.x == 0) s_csum[k] = v;
@@ -606,13 +629,13 @@ bool valid_desc(const specdec_verify_desc_t* d) {
 // none waits for a slot; whole tiles per chunk.  Sampling pass: one tile of
 // 256 lanes x 2 vectors per chunk (at most 1024 per row), each workgroup
 // taking a run of consecutive chunks of one request.
-Layout make_layout(const specdec_verify_desc_t* d) {
+Layout make_layout(const specdec_verify_desc_t* d, bool point) {
     Layout L{};
     const bool bf16 = d->dtype == SPECDEC_BF16;
     const int n = bf16 ? 8 : 4;
     const int tile = kThreads * n * kUnroll;
     const int vt = (d->vocab + tile - 1) / tile;
-    L.rows = d->mode == SPECDEC_SAMPLE ? 2 * d->gamma_max + 1 : d->gamma_max + 1;
+    L.rows = (d->mode == SPECDEC_SAMPLE && !point) ? 2 * d->gamma_max + 1 : d->gamma_max + 1;
     const double rows_total = static_cast<double>(d->batch > 0 ? d->batch : 1) * L.rows;
     int nc_want = static_cast<int>(2048.0 / rows_total);
     nc_want = nc_want < 1 ? 1 : nc_want;
@@ -692,9 +715,10 @@ specdec_status_t verify_impl(const specdec_verify_desc_t* d, const void* target_
     if (!target_logits || !accept_count || !out_tokens || !workspace)
         return SPECDEC_ERR_INVALID_ARGUMENT;
     if (d->gamma_max > 0 && !draft_tokens) return SPECDEC_ERR_INVALID_ARGUMENT;
-    if (sample && d->gamma_max > 0 && !draft_logits) return SPECDEC_ERR_INVALID_ARGUMENT;
-    if (truncation_mode(d) && !truncation_supported(d)) return SPECDEC_ERR_UNSUPPORTED;
-    const Layout L = make_layout(d);
+    // sampling without draft rows: point-mass drafts of a deterministic proposer
+    const bool point = sample && !draft_logits;
+    if (truncation_mode(d) && (point || !truncation_supported(d))) return SPECDEC_ERR_UNSUPPORTED;
+    const Layout L = make_layout(d, point);
     if (workspace_bytes < L.total) return SPECDEC_ERR_WORKSPACE_TOO_SMALL;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return SPECDEC_ERR_INVALID_ARGUMENT;
     if (d->batch == 0) return SPECDEC_OK;
@@ -734,6 +758,7 @@ specdec_status_t verify_impl(const specdec_verify_desc_t* d, const void* target_
     P.key1 = static_cast<uint32_t>(d->seed >> 32);
     P.round = d->round;
     P.eos = d->eos_token;
+    P.point = point;
 
     const bool bf16 = d->dtype == SPECDEC_BF16;
     const size_t es = bf16 ? 2 : 4;
@@ -754,7 +779,8 @@ using namespace specdec;
 
 extern "C" size_t specdec_verify_workspace_bytes(const specdec_verify_desc_t* desc) {
     if (!valid_desc(desc)) return 0;
-    return make_layout(desc).total;
+    // enough for draft rows and for point-mass drafts alike
+    return std::max(make_layout(desc, false).total, make_layout(desc, true).total);
 }
 
 extern "C" specdec_status_t specdec_verify(const specdec_verify_desc_t* d,

@@ -50,6 +50,7 @@ struct VerifyParams {
     float c;            // log2(e) / T
     uint32_t key0, key1, round;
     int eos;            // end-of-sequence token, -1: none
+    bool point;         // sampling with point-mass drafts: no draft rows, q_i = delta(d_i)
     // truncation (top-k / top-p) mode
     int top_k;          // 0 or >= V: no top-k
     float top_p;        // 1: no top-p
@@ -169,7 +170,8 @@ struct Layout {
     bool trunc, wide;
     size_t off_cnt, off_part, off_csum, off_nuc, total;
 };
-Layout make_layout(const specdec_verify_desc_t* d);
+// point: sampling with point-mass drafts (no draft rows)
+Layout make_layout(const specdec_verify_desc_t* d, bool point = false);
 
 // The statistics pass (one partial per chunk of every used row); start/stop
 // events (both null, or both set) bracket the kernel.

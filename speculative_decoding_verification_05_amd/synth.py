@@ -34,6 +34,16 @@ pages; sizes are the full-scale cases used for parity and timing):
                               sits at another child (or, for a single child,
                               is replaced by the second-ranked token).
 
+* ``ngram_b512_ctx1k8k_g8``  prompt-lookup drafting over B=512 histories of
+                              U{1024..8192} tokens (the ragged recipe's context
+                              lengths), ids below 262144, n from 4 down to 2,
+                              up to 8 tokens proposed.  A history is built
+                              from segments of U{8..64} tokens: with
+                              probability 1/2 a copy of an earlier span,
+                              otherwise fresh Zipf(1.1)-ranked tokens (a
+                              per-request random rank order), so n-grams recur
+                              as in repetitive text.
+
 The two KV workloads also carry a draft model's cache shape for the draft-cache
 rollback (the pages give none; a small model of the same family is assumed):
 24 layers x 2 heads x 64 beside the 28 x 4 x 128 target, and 18 layers x
@@ -60,6 +70,7 @@ _TAG_TARGET, _TAG_DRAFT, _TAG_TOKENS, _TAG_SIGMA, _TAG_GAMMA = 0, 1, 2, 3, 4
 _TAG_KV, _TAG_CTX, _TAG_ZIPF, _TAG_SWAP = 5, 6, 7, 8
 _TAG_DRAFT_KV = 9
 _TAG_TREE = 10
+_TAG_HIST = 11
 
 # A 16-node draft tree of depth 5 (node 0 = the pending token): four
 # candidates for the first position, then narrowing branches, the shape of
@@ -103,6 +114,7 @@ class Workload:
     kv: Optional[KVShape] = None
     draft_kv: Optional[KVShape] = None   # the draft model's cache (rollback)
     tree: Optional[tuple] = None         # tree workloads: parent of each node (node 0 = root)
+    ngram: Optional[tuple] = None        # n-gram workloads: (n_min, n_max, ctx_lo, ctx_hi)
     data_seed: int = 0
     verify_seed: int = 0
 
@@ -132,6 +144,8 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
     Workload("tree_b64_n16_v151936_greedy_kv", 64, 15, 151936, "bf16", "greedy", 1.0, 3.0,
              "top_swap", swap_rate=0.25, tree=TREE16,
              kv=KVShape(28, 4, 128, 16, 512, 4096), data_seed=1006, verify_seed=48),
+    Workload("ngram_b512_ctx1k8k_g8", 512, 8, 262144, "bf16", "greedy", 1.0, 0.0,
+             "history", zipf_s=1.1, ngram=(2, 4, 1024, 8192), data_seed=1007, verify_seed=49),
     Workload("b512_ragged_v262144_kv", 512, 8, 262144, "bf16", "sample", 1.0, 3.0,
              "noise_fixed", draft_sigma=0.6, ragged=True,
              kv=KVShape(32, 8, 128, 16, 1024, 8192), draft_kv=KVShape(18, 1, 256, 16, 1024, 8192),
@@ -358,6 +372,42 @@ def make_tree_inputs(wl: Workload, threads: Optional[int] = None) -> Dict[str, n
         list(ex.map(one, range(B)))
     return {"target": target, "tokens": tokens, "parents": np.tile(par, (B, 1)),
             "num_nodes": np.full(B, N, np.int32)}
+
+
+def make_ngram_inputs(wl: Workload, threads: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Token histories for prompt-lookup drafting: ``history`` [B][max_len]
+    int32 (-1 past a row's length) and ``hist_len`` [B].  Lengths follow the
+    workload's context range (``ngram[2] .. ngram[3]``)."""
+    B, V = wl.batch, wl.vocab
+    lo, hi = wl.ngram[2], wl.ngram[3]
+    lens = np.array([int(_rng(wl.data_seed, b, _TAG_CTX).integers(lo, hi + 1)) for b in range(B)],
+                    np.int32)
+    hist = np.full((B, hi), -1, np.int32)
+    # Zipf(s) over token ranks 1..V, by inverse CDF on a shared table
+    w = 1.0 / np.arange(1, V + 1, dtype=np.float64) ** wl.zipf_s
+    cdf = np.cumsum(w / w.sum())
+
+    def one(b: int) -> None:
+        r = _rng(wl.data_seed, b, _TAG_HIST)
+        perm = r.permutation(V).astype(np.int32)
+        L = int(lens[b])
+        out = np.empty(L, np.int32)
+        n = 0
+        while n < L:
+            seg = int(r.integers(8, 65))
+            seg = min(seg, L - n)
+            if n >= seg and r.random() < 0.5:
+                st = int(r.integers(0, n - seg + 1))
+                out[n:n + seg] = out[st:st + seg]
+            else:
+                ranks = np.searchsorted(cdf, r.random(seg), side="right")
+                out[n:n + seg] = perm[np.minimum(ranks, V - 1)]
+            n += seg
+        hist[b, :L] = out
+
+    with ThreadPoolExecutor(threads or _pool_threads()) as ex:
+        list(ex.map(one, range(B)))
+    return {"history": hist, "hist_len": lens}
 
 
 def make_kv_inputs(wl: Workload, with_pool: bool = True,

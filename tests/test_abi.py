@@ -80,7 +80,8 @@ def test_bad_dtype_mode_eos():
 
 def test_null_pointers_and_workspace():
     d = good_desc()
-    for name in ("target", "draft", "tokens", "acc", "out", "ws"):
+    # (a NULL draft is valid in sampling mode: point-mass drafts)
+    for name in ("target", "tokens", "acc", "out", "ws"):
         assert call_verify(d, **{name: None}) == sd.SPECDEC_ERR_INVALID_ARGUMENT, name
     assert call_verify(d, ws=0x10010) == sd.SPECDEC_ERR_INVALID_ARGUMENT  # misaligned
     n = sd.specdec_verify_workspace_bytes(d)
@@ -163,3 +164,33 @@ def test_commit_slot_count_must_cover_the_window():
     st = sd.lib().specdec_rollback_kv(ctypes.byref(d), 16, 16, 16, None, 16, None, 16, 1 << 20,
                                       None)
     assert st == sd.SPECDEC_ERR_INVALID_ARGUMENT     # rollback takes no scratch
+
+
+def test_point_mass_drafts_with_truncation_are_unsupported():
+    d = good_desc(top_k=50)
+    assert call_verify(d, draft=None, ws_bytes=1 << 30) == sd.SPECDEC_ERR_UNSUPPORTED
+
+
+def test_workspace_covers_point_mass_layout():
+    for G in (1, 4, 8):
+        d = good_desc(gamma_max=G, vocab=262144, batch=512)
+        assert sd.specdec_verify_workspace_bytes(d) > 0
+
+
+def test_ngram_descriptor_checks():
+    ok = sd.make_ngram_desc(4, 100, 1, 4, 8)
+    for field, val in (("batch", -1), ("max_len", 0), ("max_len", 1 << 24), ("n_min", 0),
+                       ("n_max", 33), ("gamma_max", 64), ("gamma_max", -1), ("reserved", 1)):
+        d = sd.make_ngram_desc(4, 100, 1, 4, 8)
+        setattr(d, field, val)
+        st = sd.lib().specdec_propose_ngram(ctypes.byref(d), 16, 16, 16, 16, None, None)
+        assert st == sd.SPECDEC_ERR_INVALID_ARGUMENT, (field, val)
+    d = sd.make_ngram_desc(4, 100, 3, 2, 8)     # n_max < n_min
+    assert sd.lib().specdec_propose_ngram(ctypes.byref(d), 16, 16, 16, 16, None, None) == \
+        sd.SPECDEC_ERR_INVALID_ARGUMENT
+    for args in ((None, 16, 16, 16), (16, None, 16, 16), (16, 16, None, 16), (16, 16, 16, None)):
+        st = sd.lib().specdec_propose_ngram(ctypes.byref(ok), *args, None, None)
+        assert st == sd.SPECDEC_ERR_INVALID_ARGUMENT
+    empty = sd.make_ngram_desc(0, 100, 1, 4, 8)
+    assert sd.lib().specdec_propose_ngram(ctypes.byref(empty), 16, 16, 16, 16, None, None) == \
+        sd.SPECDEC_OK
