@@ -351,12 +351,20 @@ typedef struct specdec_ngram_desc {
  *   match_len    [B] int32 out or NULL: the n that matched (0 if none).
  * The proposer is deterministic, so its q is a point mass: verify its
  * proposals with specdec_verify in GREEDY mode, or in SAMPLE mode with
- * draft_logits = NULL.  No workspace; nothing is allocated.
- * Errors: INVALID_ARGUMENT for a bad descriptor or a NULL required pointer. */
+ * draft_logits = NULL.
+ * Errors: INVALID_ARGUMENT for a bad descriptor, a NULL required pointer or a
+ * misaligned workspace; WORKSPACE_TOO_SMALL.  Nothing is enqueued then. */
 specdec_status_t specdec_propose_ngram(const specdec_ngram_desc_t* desc, const int32_t* history,
                                        const int32_t* hist_len, int32_t* draft_tokens,
                                        int32_t* num_drafts, int32_t* match_len,
+                                       void* workspace, size_t workspace_bytes,
                                        hipStream_t stream);
+
+/* Bytes of device workspace specdec_propose_ngram needs (0 on a bad
+ * descriptor): per-request best-match keys and arrival counters, which must
+ * be zero before first use (allocate zero-filled or specdec_workspace_clear);
+ * every completed call leaves them zero. */
+size_t specdec_propose_ngram_workspace_bytes(const specdec_ngram_desc_t* desc);
 
 /* Bring the draft model's paged cache back to the committed sequence after
  * specdec_verify (AI-infra KB M013 s.06: the target cache and the draft cache

@@ -39,6 +39,7 @@ EXPORTS = ("specdec_verify_workspace_bytes", "specdec_verify", "specdec_verify_p
            "specdec_commit_kv_workspace_bytes", "specdec_commit_kv", "specdec_rollback_kv",
            "specdec_verify_tree_workspace_bytes", "specdec_verify_tree",
            "specdec_verify_tree_profiled", "specdec_propose_ngram",
+           "specdec_propose_ngram_workspace_bytes",
            "specdec_workspace_clear", "specdec_status_string", "specdec_abi_version")
 
 
@@ -106,8 +107,10 @@ def lib() -> ctypes.CDLL:
         L.specdec_verify_tree.restype = ctypes.c_int
         L.specdec_verify_tree_profiled.argtypes = [ctypes.POINTER(TreeDesc)] + [P] * 11 + [S, P, P]
         L.specdec_verify_tree_profiled.restype = ctypes.c_int
-        L.specdec_propose_ngram.argtypes = [ctypes.POINTER(NgramDesc)] + [P] * 6
+        L.specdec_propose_ngram.argtypes = [ctypes.POINTER(NgramDesc)] + [P] * 6 + [S, P]
         L.specdec_propose_ngram.restype = ctypes.c_int
+        L.specdec_propose_ngram_workspace_bytes.argtypes = [ctypes.POINTER(NgramDesc)]
+        L.specdec_propose_ngram_workspace_bytes.restype = S
         L.specdec_workspace_clear.argtypes = [P, S, P]
         L.specdec_workspace_clear.restype = ctypes.c_int
         L.specdec_status_string.argtypes = [ctypes.c_int]
@@ -169,11 +172,18 @@ def make_ngram_desc(batch, max_len, n_min, n_max, gamma_max) -> NgramDesc:
     return NgramDesc(int(batch), int(max_len), int(n_min), int(n_max), int(gamma_max), 0)
 
 
+def specdec_propose_ngram_workspace_bytes(desc: NgramDesc) -> int:
+    return int(lib().specdec_propose_ngram_workspace_bytes(ctypes.byref(desc)))
+
+
 def specdec_propose_ngram(desc: NgramDesc, history, hist_len, draft_tokens, num_drafts,
-                          match_len=None, stream=None) -> None:
+                          match_len, workspace, workspace_bytes: Optional[int] = None,
+                          stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
     st = lib().specdec_propose_ngram(ctypes.byref(desc), _ptr(history), _ptr(hist_len),
                                      _ptr(draft_tokens), _ptr(num_drafts), _ptr(match_len),
-                                     _stream(stream))
+                                     _ptr(workspace), int(workspace_bytes), _stream(stream))
     if st != SPECDEC_OK:
         raise SpecdecError(st, "specdec_propose_ngram")
 

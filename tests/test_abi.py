@@ -183,14 +183,22 @@ def test_ngram_descriptor_checks():
                        ("n_max", 33), ("gamma_max", 64), ("gamma_max", -1), ("reserved", 1)):
         d = sd.make_ngram_desc(4, 100, 1, 4, 8)
         setattr(d, field, val)
-        st = sd.lib().specdec_propose_ngram(ctypes.byref(d), 16, 16, 16, 16, None, None)
+        assert sd.specdec_propose_ngram_workspace_bytes(d) == 0
+        st = sd.lib().specdec_propose_ngram(ctypes.byref(d), 16, 16, 16, 16, None, 256, 1 << 20,
+                                            None)
         assert st == sd.SPECDEC_ERR_INVALID_ARGUMENT, (field, val)
     d = sd.make_ngram_desc(4, 100, 3, 2, 8)     # n_max < n_min
-    assert sd.lib().specdec_propose_ngram(ctypes.byref(d), 16, 16, 16, 16, None, None) == \
-        sd.SPECDEC_ERR_INVALID_ARGUMENT
+    assert sd.lib().specdec_propose_ngram(ctypes.byref(d), 16, 16, 16, 16, None, 256, 1 << 20,
+                                          None) == sd.SPECDEC_ERR_INVALID_ARGUMENT
+    n = sd.specdec_propose_ngram_workspace_bytes(ok)
+    assert n >= 32
     for args in ((None, 16, 16, 16), (16, None, 16, 16), (16, 16, None, 16), (16, 16, 16, None)):
-        st = sd.lib().specdec_propose_ngram(ctypes.byref(ok), *args, None, None)
+        st = sd.lib().specdec_propose_ngram(ctypes.byref(ok), *args, None, 256, n, None)
         assert st == sd.SPECDEC_ERR_INVALID_ARGUMENT
+    assert sd.lib().specdec_propose_ngram(ctypes.byref(ok), 16, 16, 16, 16, None, None, n, None) == \
+        sd.SPECDEC_ERR_INVALID_ARGUMENT
+    assert sd.lib().specdec_propose_ngram(ctypes.byref(ok), 16, 16, 16, 16, None, 256, n - 1,
+                                          None) == sd.SPECDEC_ERR_WORKSPACE_TOO_SMALL
     empty = sd.make_ngram_desc(0, 100, 1, 4, 8)
-    assert sd.lib().specdec_propose_ngram(ctypes.byref(empty), 16, 16, 16, 16, None, None) == \
-        sd.SPECDEC_OK
+    assert sd.lib().specdec_propose_ngram(ctypes.byref(empty), 16, 16, 16, 16, None, 256, 256,
+                                          None) == sd.SPECDEC_OK

@@ -30,10 +30,12 @@ def gpu_propose(hist, lens, n_min, n_max, gam, dev="cuda"):
     import torch
     B, Lmax = hist.shape
     desc = sd.make_ngram_desc(B, Lmax, n_min, n_max, gam)
+    ws = torch.zeros(sd.specdec_propose_ngram_workspace_bytes(desc), dtype=torch.uint8, device=dev)
     toks = torch.full((B, max(gam, 1)), -7, dtype=torch.int32, device=dev)
     nd = torch.full((B,), -7, dtype=torch.int32, device=dev)
     ml = torch.full((B,), -7, dtype=torch.int32, device=dev)
-    sd.specdec_propose_ngram(desc, to_dev(hist, dev), to_dev(lens, dev), toks, nd, ml)
+    for _ in range(2):   # the second call checks that the first left the workspace clear
+        sd.specdec_propose_ngram(desc, to_dev(hist, dev), to_dev(lens, dev), toks, nd, ml, ws)
     torch.cuda.synchronize()
     return toks.cpu().numpy()[:, :gam], nd.cpu().numpy(), ml.cpu().numpy()
 
@@ -124,9 +126,11 @@ def test_propose_then_verify_on_device():
     hist = x["history"] % V
     hist[x["history"] < 0] = -1
     desc = sd.make_ngram_desc(wl.batch, hist.shape[1], n_min, n_max, G)
+    ws = torch.zeros(sd.specdec_propose_ngram_workspace_bytes(desc), dtype=torch.uint8, device=dev)
     toks = torch.empty(wl.batch, G, dtype=torch.int32, device=dev)
     nd = torch.empty(wl.batch, dtype=torch.int32, device=dev)
-    sd.specdec_propose_ngram(desc, to_dev(hist, dev), to_dev(x["hist_len"], dev), toks, nd)
+    sd.specdec_propose_ngram(desc, to_dev(hist, dev), to_dev(x["hist_len"], dev), toks, nd, None,
+                             ws)
     lw = W[synth.HEADLINE].scaled(wl.batch, V, gamma_max=G)
     logits = synth.make_verify_inputs(lw)
     vdesc = sd.make_verify_desc(wl.batch, G, V, temperature=lw.temperature, seed=5)
