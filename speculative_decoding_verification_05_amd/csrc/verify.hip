@@ -218,81 +218,81 @@ __device__ float chunk_mass(const MassRows& a, int lo, int hi) {
 }
 
 // First v of the chunk [lo, hi) with base + prefix(v) > target, scanning the
-// mass in ascending token order: the chunk's vectors are all loaded first,
-// then each group of kThreads vectors gets a block prefix sum.  Returns
-// 0x7fffffff if none; *last_pos receives the chunk's largest v with mass > 0.
+// mass in ascending token order.  Lane l holds the kUnroll2*N consecutive
+// elements starting at lo + l*kUnroll2*N (every load issued at once), so one
+// block-wide exclusive scan of the lane totals gives each lane its offset.
+// Returns 0x7fffffff if none; *last_pos receives the chunk's largest v with
+// mass > 0.
 template <bool BF16, bool VEC>
 __device__ int search_chunk(const MassRows& a, int lo, int hi, float base, float target,
                             int* last_pos) {
     constexpr int N = Vec<BF16>::N;
+    constexpr int PER = kUnroll2 * N;  // elements per lane
     __shared__ float s_wtot[kWaves];
-    __shared__ float s_tile_end;
-    __shared__ int s_found, s_last;
+    __shared__ int s_found[kWaves], s_last[kWaves];
     const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
-    // every load of the chunk in flight at once (clamped, no branches)
+    const int e0 = lo + threadIdx.x * PER;
     Vec<BF16> vp[kUnroll2], vq[kUnroll2];
-    if constexpr (VEC) {
-        ChunkRegs<BF16, VEC> raw;
-        load_chunk<BF16, VEC>(raw, a, lo, hi);
 #pragma unroll
-        for (int u = 0; u < kUnroll2; ++u) {
-            vp[u] = widen<BF16>(raw.p[u]);
-            if (a.q) vq[u] = widen<BF16>(raw.q[u]);
-        }
-    } else {
-#pragma unroll
-        for (int u = 0; u < kUnroll2; ++u) {
-            const int e = lo + (u * kThreads + threadIdx.x) * N;
+    for (int u = 0; u < kUnroll2; ++u) {
+        const int e = e0 + u * N;
+        if constexpr (VEC) {
+            // clamped into the row: a vector lies wholly inside [lo, hi) or past it
+            const int ec = min(e, hi - N);
+            vp[u] = widen<BF16>(load16<BF16>(a.p, ec));
+            if (a.q) vq[u] = widen<BF16>(load16<BF16>(a.q, ec));
+        } else {
             vp[u] = load_vec<BF16, VEC>(a.p, e, hi, neg_inf());
             if (a.q) vq[u] = load_vec<BF16, VEC>(a.q, e, hi, neg_inf());
         }
     }
-    __syncthreads();
-    if (threadIdx.x == 0) { s_found = 0x7fffffff; s_last = -1; }
-    float tile_base = base;
+    float r[PER];
+    float run = 0.0f;
+    int lastp = -1;
 #pragma unroll
-    for (int u = 0; u < kUnroll2; ++u) {
-        const int e = lo + (u * kThreads + threadIdx.x) * N;
-        float inc[N];
-        int lastp = -1;
-        float run = 0.0f;
+    for (int u = 0; u < kUnroll2; ++u)
 #pragma unroll
         for (int k = 0; k < N; ++k) {
-            const float r = (e + k < hi && e + k != a.point)
-                                 ? mass_at(a, vp[u].x[k], a.q ? vq[u].x[k] : 0.0f) : 0.0f;
-            if (r > 0.0f) lastp = e + k;
-            run += r;
-            inc[k] = run;
+            const int v = e0 + u * N + k;
+            const float x = (v < hi && v != a.point) ? mass_at(a, vp[u].x[k], a.q ? vq[u].x[k] : 0.0f) : 0.0f;
+            if (x > 0.0f) lastp = v;
+            r[u * N + k] = x;
+            run += x;
         }
-        // exclusive scan of lane totals: inclusive within the wave, shifted
-        const float x = wave_prefix_sum(run);
-        const float ex = wave_shift_right(x);
-        __syncthreads();
-        if (l == kWave - 1) s_wtot[w] = x;
-        __syncthreads();
-        float woff = 0.0f;
-        for (int k = 0; k < w; ++k) woff += s_wtot[k];
-        const float lane_base = tile_base + (woff + ex);
-        int first = 0x7fffffff;
+    // exclusive scan of the lane totals: inclusive within the wave, shifted,
+    // plus the totals of the waves before
+    const float incl = wave_prefix_sum(run);
+    const float ex = wave_shift_right(incl);
+    if (l == kWave - 1) s_wtot[w] = incl;
+    __syncthreads();
+    float woff = 0.0f;
+    for (int k = 0; k < w; ++k) woff += s_wtot[k];
+    float acc = base + (woff + ex);
+    int first = 0x7fffffff;
 #pragma unroll
-        for (int k = N - 1; k >= 0; --k)
-            if (lane_base + inc[k] > target) first = e + k;
-        // lanes hold ascending token ranges: the lowest crossing lane has the
-        // wave's first crossing, the highest lane with mass its last token
-        // with mass; one LDS atomic per wave
-        const uint64_t cross = __ballot(first != 0x7fffffff);
-        const uint64_t pos = __ballot(lastp >= 0);
-        const int f = lane_value(first, cross ? __builtin_ctzll(cross) : 0);
-        const int lp = lane_value(lastp, pos ? 63 - __builtin_clzll(pos) : 0);
-        if (l == 0 && cross) atomicMin(&s_found, f);
-        if (l == 0 && pos) atomicMax(&s_last, lp);
-        if (threadIdx.x == kThreads - 1) s_tile_end = lane_base + inc[N - 1];
-        __syncthreads();
-        tile_base = s_tile_end;
+    for (int k = 0; k < PER; ++k) {
+        acc += r[k];
+        if (first == 0x7fffffff && acc > target) first = e0 + k;
+    }
+    // lanes hold ascending token ranges: the lowest crossing lane has the
+    // first crossing, the highest lane with mass the last token with mass
+    const uint64_t cross = __ballot(first != 0x7fffffff);
+    const uint64_t pos = __ballot(lastp >= 0);
+    const int f = cross ? lane_value(first, __builtin_ctzll(cross)) : 0x7fffffff;
+    const int lp = pos ? lane_value(lastp, 63 - __builtin_clzll(pos)) : -1;
+    if (l == 0) {
+        s_found[w] = f;
+        s_last[w] = lp;
     }
     __syncthreads();
-    *last_pos = s_last;
-    return s_found;
+    int found = 0x7fffffff, last = -1;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) {
+        found = min(found, s_found[k]);
+        last = max(last, s_last[k]);
+    }
+    *last_pos = last;
+    return found;
 }
 
 // Stage the request's chunk partials in LDS with one batch of independent
@@ -310,17 +310,25 @@ __global__ __launch_bounds__(kThreads) void k_decide_sample(VerifyParams P) {
     __shared__ float s_csum[1024];
     __shared__ int s_m, s_dm;
     __shared__ uint32_t s_fl;
-    __shared__ float s_R;
+    __shared__ float s_R, s_um;
     const int wg = blockIdx.x, b = blockIdx.y;
     const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
     const int i = l;
     const float c = P.c;
 
-    // (0) independent loads first: partials, the drafted tokens, gamma_b
+    // (0) independent loads first: partials, the drafted tokens, gamma_b;
+    // the uniforms of position i (lane i of wave 0) while they are in flight
     stage_partials(P, b, s_part);
     int d = -1;
     if (w == 0 && i < P.G) d = P.tokens[static_cast<size_t>(b) * P.G + i];
     const int g = request_gamma(P, b);
+    float u_acc = 0.0f, u_draw = 0.0f;
+    if (w == 0) {
+        const uint4 r = philox4x32_10(make_uint4(static_cast<uint32_t>(i), static_cast<uint32_t>(b),
+                                                 P.round, 0u), P.key0, P.key1);
+        u_acc = uniform24(r.x);
+        u_draw = uniform24(r.y);
+    }
     __syncthreads();
 
     // (1) (max, sum) of every used row from its chunk partials: a lane per
@@ -383,9 +391,7 @@ __global__ __launch_bounds__(kThreads) void k_decide_sample(VerifyParams P) {
             } else {
                 fl |= SPECDEC_FLAG_TOKEN_RANGE;
             }
-            const uint4 r = philox4x32_10(make_uint4(static_cast<uint32_t>(i), static_cast<uint32_t>(b),
-                                                     P.round, 0u), P.key0, P.key1);
-            acc = uniform24(r.x) < a;
+            acc = u_acc < a;
         } else {
             d = -1;
         }
@@ -393,7 +399,8 @@ __global__ __launch_bounds__(kThreads) void k_decide_sample(VerifyParams P) {
         const int m = min(g, static_cast<int>(__builtin_ctzll(~mask)));
         fl = wave_or(fl);
         const int dm = lane_value(d, min(m, kWave - 1));  // the rejected draft (m < g)
-        if (l == 0) { s_m = m; s_fl = fl; s_dm = dm; }
+        const float um = lane_value(u_draw, min(m, kWave - 1));  // the draw's uniform
+        if (l == 0) { s_m = m; s_fl = fl; s_dm = dm; s_um = um; }
     }
     __syncthreads();
     const int m = s_m;
@@ -494,9 +501,7 @@ __global__ __launch_bounds__(kThreads) void k_decide_sample(VerifyParams P) {
             total();
         }
     }
-    const uint4 rnd = philox4x32_10(make_uint4(static_cast<uint32_t>(m), static_cast<uint32_t>(b),
-                                               P.round, 0u), P.key0, P.key1);
-    const float target = uniform24(rnd.y) * s_R;
+    const float target = s_um * s_R;
     pick(target);
     int lastp;
     const int l2 = s_chunk * P.chunk2, h2 = min(P.V, l2 + P.chunk2);
