@@ -76,8 +76,8 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<BF16, VEC>& r, const MassRo
 #pragma unroll
     for (int u = 0; u < kUnroll2; ++u) {
         const int e = min(lo + (u * kThreads + threadIdx.x) * N, hi - N);
-        r.p[u] = load16<BF16>(a.p, e);
-        if (a.q) r.q[u] = load16<BF16>(a.q, e);
+        r.p[u] = load16_stream<BF16>(a.p, e);
+        if (a.q) r.q[u] = load16_stream<BF16>(a.q, e);
     }
 }
 
@@ -145,10 +145,10 @@ __device__ __forceinline__ void block_sums(float (&v)[NV]) {
 
 // Masses of chunks [k0, k1) published to csum[k].  The loads of a group of
 // GROUP chunks are issued together and the group's sums reduced at once.
-// GROUP = kMassGroupWide: a workgroup's whole share (at most that many
-// chunks) in one group.  Smaller GROUP (long shares): the next group's loads
-// are in flight while the current one is reduced, in fewer registers.
-// Returns the OR of the publish() results (the dependency for arrive_last).
+// A share of at most GROUP chunks is one group; a longer share is walked in
+// groups with the next group's loads in flight while the current one is
+// reduced.  Returns the OR of the publish() results (the dependency for
+// arrive_last).
 template <bool BF16, bool VEC, int GROUP>
 __device__ uint32_t mass_chunks(const MassRows& a, int k0, int k1, int chunk2, int V, uint32_t* csum) {
     uint32_t dep = 0;
@@ -177,11 +177,9 @@ __device__ uint32_t mass_chunks(const MassRows& a, int k0, int k1, int chunk2, i
             }
         };
         ChunkRegs<BF16, VEC> cur[GROUP];
-        if constexpr (GROUP == kMassGroupWide) {
-            for (int kb = k0; kb < k1; kb += GROUP) {
-                load_group(cur, kb);
-                reduce_group(cur, kb);
-            }
+        if (k1 - k0 <= GROUP) {
+            load_group(cur, k0);
+            reduce_group(cur, k0);
         } else {
             ChunkRegs<BF16, VEC> nxt[GROUP];
             load_group(cur, k0);
@@ -658,11 +656,14 @@ Layout make_layout(const specdec_verify_desc_t* d, bool point) {
     // double-buffered kind
     const int bb = d->batch > 0 ? d->batch : 1;
     const int w512 = max(1, static_cast<int>(512.0 / bb + 0.5));
-    L.wide = L.nc2 <= kMassGroupWide * w512;
-    int wpr = L.wide ? w512 : max(1, static_cast<int>(1024.0 / bb + 0.5));
+    const bool short_share = L.nc2 <= kMassGroupWide * w512;
+    int wpr = short_share ? w512 : max(1, static_cast<int>(1024.0 / bb + 0.5));
     wpr = env_int("SPECDEC_SAMPLE_WPR", wpr > L.nc2 ? L.nc2 : wpr);
     L.cpw = (L.nc2 + wpr - 1) / wpr;
     L.wpr = (L.nc2 + L.cpw - 1) / L.cpw;
+    // a share of up to kMassGroupWide chunks is loaded as one group of
+    // exactly its size; longer shares go in double-buffered pairs
+    L.group = L.cpw <= kMassGroupWide ? L.cpw : kMassGroupChunks;
     const size_t B = static_cast<size_t>(d->batch);
     size_t off = 0;
     L.off_cnt = off; off = align256(off + B * 4);
@@ -700,10 +701,13 @@ specdec_status_t launch_all(const specdec_verify_desc_t* d, const VerifyParams& 
     if (greedy) {
         launch(k_decide_greedy, dim3(d->batch), e2, e3);
     } else {
-        if (L.wide)
-            launch(k_decide_sample<BF16, VEC, kMassGroupWide>, dim3(L.wpr, d->batch), e2, e3);
-        else
-            launch(k_decide_sample<BF16, VEC, kMassGroupChunks>, dim3(L.wpr, d->batch), e2, e3);
+        const dim3 grid(L.wpr, d->batch);
+        switch (L.group) {
+            case 1: launch(k_decide_sample<BF16, VEC, 1>, grid, e2, e3); break;
+            case 3: launch(k_decide_sample<BF16, VEC, 3>, grid, e2, e3); break;
+            case 4: launch(k_decide_sample<BF16, VEC, 4>, grid, e2, e3); break;
+            default: launch(k_decide_sample<BF16, VEC, 2>, grid, e2, e3); break;
+        }
     }
     return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_DEVICE;
 }

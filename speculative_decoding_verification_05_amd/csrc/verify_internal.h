@@ -167,7 +167,8 @@ __device__ __forceinline__ float block_sum(float v) {
 // tree entry points).
 struct Layout {
     int rows, nc, chunk, nc2, chunk2, wpr, cpw;
-    bool trunc, wide;
+    int group;          // sampling-pass chunks loaded together (1..kMassGroupWide)
+    bool trunc;
     size_t off_cnt, off_part, off_csum, off_nuc, total;
 };
 // point: sampling with point-mass drafts (no draft rows)
