@@ -228,6 +228,7 @@ __device__ void select_in_wave(const VerifyParams& P, int b, int s, int C, bool 
         s_i[C + l] = 0x7fffffff;
     }
     int rank = 0, lower = 0;
+#pragma unroll 4
     for (int j0 = 0; j0 < C; j0 += 4) {
         const float4 zj = *reinterpret_cast<const float4*>(s_z + j0);
         const int4 ij = *reinterpret_cast<const int4*>(s_i + j0);
@@ -254,6 +255,7 @@ __device__ void select_in_wave(const VerifyParams& P, int b, int s, int C, bool 
     s_e[l] = e;
     s_r[l] = in ? rank : 0x7fffffff;
     float pre = 0.0f;
+#pragma unroll 4
     for (int j0 = 0; j0 < C; j0 += 4) {
         const float4 ej = *reinterpret_cast<const float4*>(s_e + j0);
         const int4 rj = *reinterpret_cast<const int4*>(s_r + j0);
@@ -297,6 +299,8 @@ __global__ __launch_bounds__(kThreads) void k_trunc_select(VerifyParams P) {
     __shared__ float s_wt[kWaves];
     __shared__ int s_count, s_cut;
     __shared__ int s_cw[kWaves];
+    __shared__ uint32_t s_hist[kThreads];
+    __shared__ int s_sel[3];
     constexpr int N = Vec<BF16>::N;
     constexpr int TILE = kThreads * N * kUnroll;
     // widened bf16 values share the low 16 key bits: searching the top 16 is exact
@@ -342,38 +346,64 @@ __global__ __launch_bounds__(kThreads) void k_trunc_select(VerifyParams P) {
     stream_tiles<BF16, VEC>(rp, V, visit);
     bad |= __ballot(v1 == pos_inf());
 
-    // k-th largest of the values zr[0..R) over the wave's lanes, by a
-    // bitwise search over keys compared as floats (key_value is monotone)
-    auto wave_kth = [&](const float* zr, auto R_t) {
-        constexpr int R = decltype(R_t)::value;
-        uint32_t key = 0;
-        for (int bit = 31; bit >= LO; --bit) {
-            const uint32_t trial = key | (1u << bit);
-            const float tf = key_value(trial);
-            int cnt = 0;
-#pragma unroll
-            for (int j = 0; j < R; ++j) cnt += __popcll(__ballot(zr[j] >= tf));
-            if (cnt >= P.top_k) key = trial;
-        }
-        return key_value(key);
-    };
-
     // (2) the bound: the k-th largest of the 4 x 256 tracked maxima, a lower
-    // bound on the row's k-th largest logit (every wave runs the same search
-    // over the staged values)
+    // bound on the row's k-th largest logit.  Radix select over the order-
+    // preserving keys, 8 bits a round from the top (the top 16 bits decide a
+    // widened bf16 exactly): an LDS histogram of the digit among the keys
+    // that share the digits chosen so far, then one wave scans the bins from
+    // the top for the one where the running count reaches k.
     float bound = neg_inf();
     if (t == 0) s_count = 0;
     if (use_k) {
-        s_z[t] = v1;
-        s_z[kThreads + t] = v2;
-        s_z[2 * kThreads + t] = v3;
-        s_z[3 * kThreads + t] = v4;
-        __syncthreads();
-        constexpr int R = 4 * kThreads / kWave;
-        float zr[R];
+        constexpr int ROUNDS = (32 - LO) / 8;
+        const uint32_t kk[4] = {ordered_key(v1), ordered_key(v2), ordered_key(v3), ordered_key(v4)};
+        uint32_t prefix = 0;
+        int need = P.top_k;
+        bool found = true;
 #pragma unroll
-        for (int j = 0; j < R; ++j) zr[j] = s_z[j * kWave + l];
-        bound = wave_kth(zr, std::integral_constant<int, R>{});
+        for (int r = 0; r < ROUNDS; ++r) {
+            const int shift = 24 - 8 * r;
+            s_hist[t] = 0u;  // kThreads == 256 bins
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bool same = r == 0 || (kk[j] >> (shift + 8)) == (prefix >> (shift + 8));
+                if (same) atomicAdd(&s_hist[(kk[j] >> shift) & 255u], 1u);
+            }
+            __syncthreads();
+            if (w == 0) {
+                // lane l holds bins 255-4l .. 252-4l (descending)
+                int cnt[4];
+                int tot = 0;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    cnt[q] = static_cast<int>(s_hist[255 - 4 * l - q]);
+                    tot += cnt[q];
+                }
+                const int incl = wave_scan(tot, 0, [](int x, int y) { return x + y; });
+                const int excl = incl - tot;
+                const uint64_t hit = __ballot(incl >= need);
+                if (hit) {
+                    const int src = __builtin_ctzll(hit);
+                    int digit = 0, rest = 0;
+                    if (l == src) {
+                        int run = excl;
+                        for (int q = 0; q < 4; ++q) {
+                            if (run + cnt[q] >= need) { digit = 255 - 4 * l - q; rest = need - run; break; }
+                            run += cnt[q];
+                        }
+                    }
+                    if (l == src) { s_sel[0] = digit; s_sel[1] = rest; s_sel[2] = 1; }
+                } else if (l == 0) {
+                    s_sel[2] = 0;  // fewer than k keys share the prefix: no finite bound
+                }
+            }
+            __syncthreads();
+            if (!s_sel[2]) { found = false; break; }
+            prefix |= static_cast<uint32_t>(s_sel[0]) << shift;
+            need = s_sel[1];
+        }
+        bound = found ? key_value(prefix) : neg_inf();
     }
     __syncthreads();
 
