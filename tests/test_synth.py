@@ -59,3 +59,55 @@ def test_kv_window_blocks_are_distinct_and_in_range():
         for j in range(8):
             assert kv.block_table[b, (t + j) // 16] >= 0
     assert np.all(kv.pool == synth.KV_POISON)
+
+
+def test_tree_inputs_follow_the_recipe():
+    wl = synth.WORKLOADS["tree_b64_n16_v151936_greedy_kv"].scaled(6, 3000)
+    x = synth.make_tree_inputs(wl)
+    par = np.array(synth.TREE16)
+    assert x["target"].shape == (6, 16, 3000) and np.all(x["parents"] == par)
+    assert synth.tree_depths(par).max() == 5
+    z = synth.bf16_bits_to_f32(x["target"])
+    kids = [[j for j in range(1, 16) if par[j] == p] for p in range(16)]
+    for b in range(6):
+        for p, ks in enumerate(kids):
+            if not ks:
+                continue
+            order = np.lexsort((np.arange(3000), -z[b, p]))
+            top = set(order[:len(ks) + 1].tolist())
+            toks = [int(x["tokens"][b, j]) for j in ks]
+            assert len(set(toks)) == len(toks)          # distinct siblings
+            assert set(toks) <= top                      # the target's top-ranked tokens
+    again = synth.make_tree_inputs(wl)
+    assert np.array_equal(again["tokens"], x["tokens"])
+
+
+def test_ngram_histories_repeat():
+    wl = synth.WORKLOADS["ngram_b512_ctx1k8k_g8"].scaled(24)
+    x = synth.make_ngram_inputs(wl)
+    lo, hi = wl.ngram[2], wl.ngram[3]
+    L = x["hist_len"]
+    assert np.all((L >= lo) & (L <= hi))
+    for b in range(24):
+        h = x["history"][b]
+        assert np.all(h[:L[b]] >= 0) and np.all(h[:L[b]] < wl.vocab) and np.all(h[L[b]:] == -1)
+        # copied spans make 8-grams recur far more than chance would
+        grams = {tuple(h[i:i + 8]) for i in range(L[b] - 8)}
+        assert len(grams) < 0.9 * (L[b] - 8)
+
+
+def test_draft_kv_holds_the_proposer_window():
+    wl = synth.WORKLOADS["b512_ragged_v262144_kv"].scaled(10, 64)
+    pool, table, seq, nb = synth.make_draft_kv_inputs(wl)
+    dk = wl.draft_kv
+    assert pool.shape == (dk.layers, 2, nb, dk.block_size, dk.kv_heads, dk.head_dim)
+    written = 0
+    for b in range(10):
+        g = synth.request_gamma(wl, b)
+        for j in range(g):
+            pos = seq[b] + j
+            blk = table[b, pos // dk.block_size]
+            assert np.all(pool[:, :, blk, pos % dk.block_size] != synth.KV_POISON)
+            written += 1
+    per_pos = dk.layers * 2 * dk.kv_heads * dk.head_dim
+    assert int((pool != synth.KV_POISON).sum()) == written * per_pos
