@@ -11,10 +11,12 @@ timing, and rotate over several independent input sets whose total exceeds the
 
 Timing: W warmup steps, then exactly K steps replayed from a HIP graph,
 bracketed by torch.cuda.synchronize(); value = verified positions / second.
-The roofline entry is the statistics kernel (the dominant one): its
-algorithmic bytes per launch (every used logits row read once, plus draft
-tokens and outputs) over its average duration, timed live with start/stop
-events that bracket the kernel itself (specdec_verify_profiled).
+The roofline entry is the dominant kernel: the one-kernel sampling verify
+(statistics and decision workgroups in one launch), or the statistics
+kernel on the greedy and truncation paths (and with SPECDEC_FUSED=0).  It is
+the kernel's algorithmic bytes per launch (every used logits row read once,
+plus draft tokens and outputs) over its average duration, timed live with
+start/stop events that bracket the kernel itself (specdec_verify_profiled).
 cpu_baseline: the CPU oracle (single-threaded C, double precision) run on the
 same input set for a bounded time.
 
@@ -92,7 +94,7 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         log("bench.py measures the verify-and-commit step on one GPU; there is no multi-GPU "
-            "path in this build (requests would shard across GPUs with no exchange). "
+            "path (requests would shard across GPUs with no exchange). "
             "Run it with --gpus 1.")
         return 2
 
@@ -303,11 +305,23 @@ def main() -> int:
     out_bytes = B * 4 + B * (G + 1) * 4 + (0 if greedy else B * G * 8 + B * 4) + B * 4
     alg_k1 = float(np.mean([synth.logits_bytes(wl0, g) for g in gam_sets])) + B * G * 4 + out_bytes
     achieved = alg_k1 / k1_avg / 1e9
-    log(f"step {sec_per_step * 1e6:.2f} us ({'graph' if graph is not None else 'eager'}); "
-        f"stats kernel avg {k1_avg * 1e6:.2f} us (p10 {np.percentile(k1, 10) * 1e6:.2f}, "
-        f"p90 {np.percentile(k1, 90) * 1e6:.2f}); decision kernel avg {k2.mean() * 1e6:.2f} us")
-    log(f"stats kernel {achieved:.1f} GB/s = {100 * achieved / HBM_PEAK_GBPS:.1f}% of "
-        f"{HBM_PEAK_GBPS:.0f} GB/s; whole step {alg_k1 / sec_per_step / 1e9:.1f} GB/s")
+    trunc = bool(wl0.top_k) or wl0.top_p < 1.0
+    # sampling without truncation runs as one kernel (statistics + decision)
+    fused = not greedy and not trunc and os.environ.get("SPECDEC_FUSED", "1")[:1] != "0"
+    kname = ("k_stats_greedy" if greedy else "k_truncate" if trunc else
+             "k_verify_fused" if fused else "k_stats_sample")
+    if fused:
+        log(f"step {sec_per_step * 1e6:.2f} us ({'graph' if graph is not None else 'eager'}); "
+            f"one-kernel verify avg {k1_avg * 1e6:.2f} us (p10 {np.percentile(k1, 10) * 1e6:.2f}, "
+            f"p90 {np.percentile(k1, 90) * 1e6:.2f})")
+        log(f"one-kernel verify {achieved:.1f} GB/s = {100 * achieved / HBM_PEAK_GBPS:.1f}% of "
+            f"{HBM_PEAK_GBPS:.0f} GB/s; whole step {alg_k1 / sec_per_step / 1e9:.1f} GB/s")
+    else:
+        log(f"step {sec_per_step * 1e6:.2f} us ({'graph' if graph is not None else 'eager'}); "
+            f"stats kernel avg {k1_avg * 1e6:.2f} us (p10 {np.percentile(k1, 10) * 1e6:.2f}, "
+            f"p90 {np.percentile(k1, 90) * 1e6:.2f}); decision kernel avg {k2.mean() * 1e6:.2f} us")
+        log(f"stats kernel {achieved:.1f} GB/s = {100 * achieved / HBM_PEAK_GBPS:.1f}% of "
+            f"{HBM_PEAK_GBPS:.0f} GB/s; whole step {alg_k1 / sec_per_step / 1e9:.1f} GB/s")
     log(f"mean accepted {np.mean([a.mean() for a in acc]):.3f} of {G}; histogram of m: "
         f"{np.bincount(np.concatenate(acc), minlength=G + 1).tolist()}; "
         f"committed tokens/s {committed / sec_per_step:.3e}")
@@ -362,14 +376,16 @@ def main() -> int:
                    "launch": "hipgraph" if graph is not None else "eager",
                    "committed_tokens_per_s": committed / sec_per_step,
                    "step_GBps": alg_k1 / sec_per_step / 1e9},
-        "kernels": dict({"stats": {"avg_us": k1_avg * 1e6, "bytes_per_launch": alg_k1,
-                                   "GBps": achieved, "frac": achieved / HBM_PEAK_GBPS},
-                         "decision": {"avg_us": float(k2.mean()) * 1e6}}, **kernels),
+        "kernels": dict(({"verify_fused": {"avg_us": k1_avg * 1e6, "bytes_per_launch": alg_k1,
+                                           "GBps": achieved, "frac": achieved / HBM_PEAK_GBPS}}
+                          if fused else
+                          {"stats": {"avg_us": k1_avg * 1e6, "bytes_per_launch": alg_k1,
+                                     "GBps": achieved, "frac": achieved / HBM_PEAK_GBPS},
+                           "decision": {"avg_us": float(k2.mean()) * 1e6}}), **kernels),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic(f"k_stats_sample__{wl0.name}") if not greedy else None,
-                     "kernel": ("k_stats_greedy" if greedy else
-                                "k_truncate" if (wl0.top_k or wl0.top_p < 1.0) else "k_stats_sample"),
+                     "traffic": measured_traffic(f"{kname}__{wl0.name}") if not greedy else None,
+                     "kernel": kname,
                      "kernel_avg_us": k1_avg * 1e6, "bytes_per_launch": alg_k1},
         "cpu_baseline": cpu,
     }

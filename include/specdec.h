@@ -80,6 +80,9 @@ typedef enum specdec_mode { SPECDEC_SAMPLE = 0, SPECDEC_GREEDY = 1 } specdec_mod
 #define SPECDEC_FLAG_EOS               0x80u /* verify: the committed list ends with the EOS token */
 #define SPECDEC_FLAG_LENGTH            0x100u /* verify: the token budget ended the committed list */
 #define SPECDEC_FLAG_BAD_TREE          0x200u /* tree: a parent index outside [0, node): node rejected */
+#define SPECDEC_FLAG_WAIT_TIMEOUT      0x400u /* verify: the one-kernel path gave up waiting for the
+                                                 request's statistics (20 ms): its outputs are
+                                                 invalid and the workspace must be cleared */
 
 /* ------------------------------------------------------------------ verify */
 
@@ -103,7 +106,9 @@ typedef struct specdec_verify_desc {
  * per-request arrival counters.  Its counter words must be zero before the
  * first call that uses it (allocate it zero-filled, or run
  * specdec_workspace_clear once); every completed call leaves them zero again,
- * so one workspace serves any number of ordered calls.  Rounded to 256 B. */
+ * so one workspace serves any number of ordered calls with one descriptor.
+ * Clear it again before using it with another descriptor (the counters of one
+ * layout may lie where another left partials).  Rounded to 256 B. */
 size_t specdec_verify_workspace_bytes(const specdec_verify_desc_t* desc);
 
 /* Verify one round for B requests.
@@ -187,7 +192,9 @@ specdec_status_t specdec_verify(const specdec_verify_desc_t* desc,
  * statistics pass kernel (the one full read of the logits), [2]/[3] at the
  * start/end of the decision kernel (acceptance tests and, when sampling, the
  * correction/bonus draw).  The events bracket the kernels' execution
- * (hipExtLaunchKernel), not the enqueue.
+ * (hipExtLaunchKernel), not the enqueue.  Sampling without truncation runs
+ * both passes in one kernel: [0]/[1] bracket that kernel and [2]/[3] are
+ * recorded right after it.
  * Everything else, including every error, is as for specdec_verify. */
 specdec_status_t specdec_verify_profiled(const specdec_verify_desc_t* desc,
                                          const void* target_logits, const void* draft_logits,

@@ -33,6 +33,7 @@ FLAG_TRUNC_OVERFLOW = 0x40
 FLAG_EOS = 0x80
 FLAG_LENGTH = 0x100
 FLAG_BAD_TREE = 0x200
+FLAG_WAIT_TIMEOUT = 0x400
 
 # exported symbols of include/specdec.h
 EXPORTS = ("specdec_verify_workspace_bytes", "specdec_verify", "specdec_verify_profiled",

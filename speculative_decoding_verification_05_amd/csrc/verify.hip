@@ -28,9 +28,18 @@
 //                    prefix sum, and writes every output of the request.
 //   k_decide_greedy  one workgroup per request: row argmaxes from the
 //                    partials, the argmax-equality prefix and every output.
-// The only cross-workgroup hand-off (chunk masses inside k_decide_sample)
-// uses device-scope atomics; nothing ever waits on another workgroup.
-#include "verify_internal.h"
+//   k_verify_fused   sampling without truncation in one launch: the
+//                    statistics workgroups of every request come first in
+//                    launch order, then the decision workgroups, each of
+//                    which waits (bounded) until its request's partials are
+//                    published.  Same arithmetic as the two kernels above,
+//                    same results; it saves the kernel boundary and lets the
+//                    decision workgroups start while the last rows stream.
+// Cross-workgroup hand-offs use device-scope atomics.  In the two-kernel
+// path nothing waits on another workgroup; in the one-kernel path only
+// decision workgroups wait, and only on statistics workgroups that precede
+// them in launch order and never wait themselves.
+#include "stats_stream.h"
 
 #include <hip/hip_ext.h>
 #include <stdint.h>
@@ -301,22 +310,96 @@ __device__ __forceinline__ void stage_partials(const VerifyParams& P, int b, flo
     for (int t = threadIdx.x; t < n; t += kThreads) s_part[t] = src[t];
 }
 
-template <bool BF16, bool VEC, int GROUP>
-__global__ __launch_bounds__(kThreads) void k_decide_sample(VerifyParams P) {
+// Waits for request b's statistics in the one-kernel path.  The (max, sum)
+// word of every used (row, chunk) is nonzero once published (a published
+// pair never has all-zero bits: a chunk's sum is >= 1 unless its max is
+// -inf, whose bits are nonzero), and zero at rest.  Lane 0 first polls the
+// word of the request's last used (row, chunk) in launch order, the one
+// usually published last; then every word is read (and, if still zero,
+// polled) by a lane of its own.  Polls sleep in between, and atomic reads
+// see the device-scope exchanges that published the words.  A wait longer
+// than P.wait_ticks of the 100 MHz constant clock gives up; returns true
+// (to every lane) if any wait did.
+__device__ bool wait_partials(const VerifyParams& P, int b, int g, float4* s_part) {
+    const int n = P.rows * P.nc;
+    unsigned long long* rdy = reinterpret_cast<unsigned long long*>(P.ready) + static_cast<size_t>(b) * n;
+    const uint64_t t0 = wall_clock64();
+    bool late = false;
+    if (threadIdx.x == 0) {
+        const int s_last = P.point ? g : (g > 0 ? P.G + g : 0);
+        unsigned long long* last = rdy + s_last * P.nc + P.nc - 1;
+        while (atomicOr(last, 0ull) == 0ull) {
+            if (wall_clock64() - t0 > P.wait_ticks) { late = true; break; }
+            __builtin_amdgcn_s_sleep(16);
+        }
+    }
+    for (int t = threadIdx.x; t < n; t += kThreads) {
+        const int s = t / P.nc;
+        const bool used = (s <= P.G) ? (s <= g) : (s - (P.G + 1) < g);
+        unsigned long long v = 0;
+        if (used) {
+            while ((v = atomicOr(rdy + t, 0ull)) == 0ull) {
+                if (wall_clock64() - t0 > P.wait_ticks) { late = true; break; }
+                __builtin_amdgcn_s_sleep(16);
+            }
+        }
+        s_part[t] = make_float4(__uint_as_float(static_cast<uint32_t>(v)),
+                                __uint_as_float(static_cast<uint32_t>(v >> 32)), 0.0f, 0.0f);
+    }
+    return __syncthreads_or(late);
+}
+
+// Back to zero for the next call: every used word of request b (run by the
+// request's last decision workgroup, after every workgroup has read them).
+__device__ __forceinline__ void clear_partials(const VerifyParams& P, int b, int g) {
+    const int n = P.rows * P.nc;
+    unsigned long long* rdy = reinterpret_cast<unsigned long long*>(P.ready) + static_cast<size_t>(b) * n;
+    for (int t = threadIdx.x; t < n; t += kThreads) {
+        const int s = t / P.nc;
+        const bool used = (s <= P.G) ? (s <= g) : (s - (P.G + 1) < g);
+        if (used) atomicExch(rdy + t, 0ull);
+    }
+}
+
+// arrive_last for the decision workgroups of the one-kernel path: a
+// workgroup whose wait timed out also adds 1 << 16, so the last to arrive
+// learns (in *any_late) whether any workgroup of the request worked on
+// unpublished statistics.
+__device__ __forceinline__ bool arrive_last_marked(uint32_t* counter, uint32_t total, uint32_t dep,
+                                                   bool late, bool* any_late) {
+    __shared__ int s_last, s_late;
+    if (threadIdx.x == 0) {
+        uint32_t zero = 0u;
+        asm volatile("" : "+v"(zero) : "v"(dep));
+        const uint32_t old = atomicAdd(counter + zero, late ? 0x10001u : 1u);
+        s_last = ((old & 0xffffu) == total - 1);
+        s_late = late || (old >> 16) != 0;
+        if (s_last) atomicExch(counter, 0u);  // ready for the next call
+    }
+    __syncthreads();
+    *any_late = s_late;
+    return s_last;
+}
+
+// Decision workgroup wg of request b.  FUSED: the statistics come from the
+// same kernel's statistics workgroups (wait_partials), and the drafted
+// tokens' logits are read from the rows directly; otherwise from the
+// partials the statistics kernel stored.
+template <bool BF16, bool VEC, int GROUP, bool FUSED>
+__device__ __forceinline__ void decide_sample(const VerifyParams& P, const int wg, const int b) {
     __shared__ float4 s_part[kMaxPart];
     __shared__ float2 s_stat[127];
     __shared__ float s_csum[1024];
     __shared__ int s_m, s_dm;
     __shared__ uint32_t s_fl;
     __shared__ float s_R, s_um;
-    const int wg = blockIdx.x, b = blockIdx.y;
     const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
     const int i = l;
     const float c = P.c;
 
     // (0) independent loads first: partials, the drafted tokens, gamma_b;
     // the uniforms of position i (lane i of wave 0) while they are in flight
-    stage_partials(P, b, s_part);
+    if constexpr (!FUSED) stage_partials(P, b, s_part);
     int d = -1;
     if (w == 0 && i < P.G) d = P.tokens[static_cast<size_t>(b) * P.G + i];
     const int g = request_gamma(P, b);
@@ -327,7 +410,23 @@ __global__ __launch_bounds__(kThreads) void k_decide_sample(VerifyParams P) {
         u_acc = uniform24(r.x);
         u_draw = uniform24(r.y);
     }
-    __syncthreads();
+    // logits of the drafted token in target row i and draft row i
+    float zt = 0.0f, zq = 0.0f;
+    bool late = false;
+    if constexpr (FUSED) {
+        if (w == 0 && i < g && d >= 0 && d < P.V) {
+            zt = load_logit<BF16>(target_row(P, b, i, BF16), d);
+            if (!P.point) zq = load_logit<BF16>(draft_row(P, b, i, BF16), d);
+        }
+        late = wait_partials(P, b, g, s_part);
+    } else {
+        __syncthreads();
+        if (w == 0 && i < g && d >= 0 && d < P.V) {
+            const int cd = d / P.chunk;
+            zt = s_part[i * P.nc + cd].z;
+            if (!P.point) zq = s_part[(P.G + 1 + i) * P.nc + cd].z;
+        }
+    }
 
     // (1) (max, sum) of every used row from its chunk partials: a lane per
     // row over a few partials, else a wave per row
@@ -375,13 +474,10 @@ __global__ __launch_bounds__(kThreads) void k_decide_sample(VerifyParams P) {
             }
             float a = 0.0f;
             if (d >= 0 && d < P.V) {
-                const int cd = d / P.chunk;
-                const float zt = s_part[i * P.nc + cd].z;
                 pd = exp2f((zt - t.x) * c) / t.y;
                 if (P.point) {
                     qd = 1.0f;  // point-mass draft: q_i(d_i) = 1
                 } else {
-                    const float zq = s_part[(P.G + 1 + i) * P.nc + cd].z;
                     qd = exp2f((zq - q.x) * c) / q.y;
                 }
                 if (qd > 0.0f) a = fminf(1.0f, pd / qd);
@@ -427,7 +523,12 @@ __global__ __launch_bounds__(kThreads) void k_decide_sample(VerifyParams P) {
     uint32_t* csum = P.csum + static_cast<size_t>(b) * P.nc2;
     const int k0 = wg * P.cpw, k1 = min(P.nc2, k0 + P.cpw);
     const uint32_t dep = mass_chunks<BF16, VEC, GROUP>(a, k0, k1, P.chunk2, P.V, csum);
-    if (!arrive_last(P.cnt + b, static_cast<uint32_t>(P.wpr), dep)) return;
+    if constexpr (FUSED) {
+        if (!arrive_last_marked(P.cnt + b, static_cast<uint32_t>(P.wpr), dep, late, &late)) return;
+        clear_partials(P, b, g);
+    } else {
+        if (!arrive_last(P.cnt + b, static_cast<uint32_t>(P.wpr), dep)) return;
+    }
 
     // (4) last workgroup of the request: R, the chunk where the running mass
     // passes u*R, the token inside it, then every output of the request.
@@ -517,9 +618,77 @@ __global__ __launch_bounds__(kThreads) void k_decide_sample(VerifyParams P) {
         }
         if (i == 0) {
             if (P.residual_mass) P.residual_mass[b] = R_report;
-            if (P.flags) P.flags[b] = s_fl | fl2;
+            if (P.flags) P.flags[b] = s_fl | fl2 | (late ? SPECDEC_FLAG_WAIT_TIMEOUT : 0u);
         }
     }
+}
+
+template <bool BF16, bool VEC, int GROUP>
+__global__ __launch_bounds__(kThreads) void k_decide_sample(VerifyParams P) {
+    decide_sample<BF16, VEC, GROUP, false>(P, blockIdx.x, blockIdx.y);
+}
+
+// ------------------------------------------------------------------ one-kernel sampling verify
+
+// Workgroup roles of the one-kernel path, in launch order.  Request j
+// contributes its S = rows x nc statistics workgroups; the W = wpr decision
+// workgroups of request j are placed right after the statistics workgroups
+// of request j + lag (after the last request's when j + lag >= B).  So every
+// decision workgroup comes later in launch order than each statistics
+// workgroup it waits for, and those never wait: with workgroups dispatched
+// in launch order, every wait ends (and a bounded wait guards the rest).
+struct Role {
+    bool stats;
+    int b;
+    int k;  // statistics: row * nc + chunk; decision: workgroup of the request
+};
+
+__device__ __forceinline__ Role fused_role(const VerifyParams& P, int x) {
+    const int S = P.rows * P.nc, W = P.wpr, lag = P.lag;
+    if (x < lag * S) return Role{true, x / S, x % S};
+    x -= lag * S;
+    const int mid = (P.B - lag) * (S + W);
+    if (x < mid) {
+        const int j = lag + x / (S + W), r = x % (S + W);
+        if (r < S) return Role{true, j, r};
+        return Role{false, j - lag, r - S};
+    }
+    x -= mid;
+    return Role{false, P.B - lag + x / W, x % W};
+}
+
+// Statistics workgroup of the one-kernel path: the chunk's (max, sum) pair,
+// published as one 64-bit word with a device-scope atomic exchange whose
+// result is not awaited (an atomic with return, or an arrival counter
+// behind it, waits a memory round trip that the full HBM stream makes long).
+template <bool BF16, bool VEC>
+__device__ __forceinline__ void fused_stats(const VerifyParams& P, int b, int k) {
+    const int s = k / P.nc, ci = k % P.nc;
+    const bool is_target = s <= P.G;
+    const int i = is_target ? s : s - (P.G + 1);
+    const void* rp = is_target ? target_row(P, b, i, BF16) : draft_row(P, b, i, BF16);
+    const int lo = ci * P.chunk;
+    const int hi = min(P.V, lo + P.chunk);
+    auto keep = [&]() {
+        if (!P.gamma) return true;
+        const int g = request_gamma(P, b);
+        return is_target ? i <= g : i < g;
+    };
+    MaxSum r;
+    if (!chunk_maxsum<BF16, VEC>(rp, lo, hi, P.c, keep, &r)) return;
+    if (threadIdx.x == 0) {
+        const unsigned long long v =
+            (static_cast<unsigned long long>(__float_as_uint(r.s)) << 32) | __float_as_uint(r.m);
+        atomicExch(reinterpret_cast<unsigned long long*>(P.ready) +
+                       static_cast<size_t>(b) * P.rows * P.nc + k, v);
+    }
+}
+
+template <bool BF16, bool VEC, int GROUP>
+__global__ __launch_bounds__(kThreads) void k_verify_fused(VerifyParams P) {
+    const Role r = fused_role(P, blockIdx.x);
+    if (r.stats) fused_stats<BF16, VEC>(P, r.b, r.k);
+    else decide_sample<BF16, VEC, GROUP, true>(P, r.k, r.b);
 }
 
 // ------------------------------------------------------------------ greedy decision
@@ -607,6 +776,29 @@ int env_int(const char* name, int dflt) {
     return v > 0 ? v : dflt;
 }
 
+// The one-kernel sampling path (statistics and decision in one launch).
+// SPECDEC_FUSED=0 selects the two-kernel path.
+bool fused_enabled() {
+    const char* s = getenv("SPECDEC_FUSED");
+    return !(s && s[0] == '0');
+}
+
+// Bound of a decision workgroup's wait for its statistics: 20 ms of the
+// 100 MHz constant clock; SPECDEC_FUSED_WAIT_TICKS overrides (tests force
+// the timeout path with a tiny bound).
+uint64_t fused_wait_ticks() {
+    const char* s = getenv("SPECDEC_FUSED_WAIT_TICKS");
+    return (s && *s) ? strtoull(s, nullptr, 10) : 2000000ull;
+}
+
+// Decision workgroups of request j trail the statistics of request j + lag;
+// SPECDEC_FUSED_LAG overrides (0..B).
+int fused_lag(int B) {
+    const char* s = getenv("SPECDEC_FUSED_LAG");
+    const int v = (s && *s) ? atoi(s) : B;
+    return std::min(std::max(v, 0), B);
+}
+
 bool valid_desc(const specdec_verify_desc_t* d) {
     if (!d) return false;
     if (d->batch < 0 || d->batch > 65535 || d->gamma_max < 0 || d->gamma_max > 63 || d->vocab < 1)
@@ -657,16 +849,23 @@ Layout make_layout(const specdec_verify_desc_t* d, bool point) {
     const int bb = d->batch > 0 ? d->batch : 1;
     const int w512 = max(1, static_cast<int>(512.0 / bb + 0.5));
     const bool short_share = L.nc2 <= kMassGroupWide * w512;
-    int wpr = short_share ? w512 : max(1, static_cast<int>(1024.0 / bb + 0.5));
-    wpr = env_int("SPECDEC_SAMPLE_WPR", wpr > L.nc2 ? L.nc2 : wpr);
+    const int wpr0 = short_share ? w512 : max(1, static_cast<int>(1024.0 / bb + 0.5));
+    const int wpr = env_int("SPECDEC_SAMPLE_WPR", wpr0 > L.nc2 ? L.nc2 : wpr0);
     L.cpw = (L.nc2 + wpr - 1) / wpr;
     L.wpr = (L.nc2 + L.cpw - 1) / L.cpw;
     // a share of up to kMassGroupWide chunks is loaded as one group of
     // exactly its size; longer shares go in double-buffered pairs
     L.group = L.cpw <= kMassGroupWide ? L.cpw : kMassGroupChunks;
+    // one-kernel path: twice as many decision workgroups, one chunk per
+    // group (measured fastest on B=64 x V=128256 and B=512 x V=262144)
+    const int fwpr = env_int("SPECDEC_SAMPLE_WPR", std::min(L.nc2, 2 * wpr0));
+    L.fcpw = (L.nc2 + fwpr - 1) / fwpr;
+    L.fwpr = (L.nc2 + L.fcpw - 1) / L.fcpw;
     const size_t B = static_cast<size_t>(d->batch);
     size_t off = 0;
+    // zero at rest: arrival counters, ready words
     L.off_cnt = off; off = align256(off + B * 4);
+    L.off_ready = off; off = align256(off + B * L.rows * L.nc * sizeof(uint64_t));
     L.off_part = off; off = align256(off + B * L.rows * L.nc * sizeof(float4));
     L.off_csum = off; off = align256(off + B * L.nc2 * sizeof(uint32_t));
     L.trunc = truncation_mode(d);
@@ -685,7 +884,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // themselves (hipExtLaunchKernel), not the host-side enqueue.
 template <bool BF16, bool VEC>
 specdec_status_t launch_all(const specdec_verify_desc_t* d, const VerifyParams& P, const Layout& L,
-                            hipStream_t stream, hipEvent_t* ev) {
+                            bool fused, hipStream_t stream, hipEvent_t* ev) {
     const dim3 block(kThreads);
     hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
     hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
@@ -696,6 +895,17 @@ specdec_status_t launch_all(const specdec_verify_desc_t* d, const VerifyParams& 
             hipLaunchKernelGGL(kernel, grid, block, 0, stream, P);
     };
     const bool greedy = d->mode == SPECDEC_GREEDY;
+    if (fused) {
+        // one kernel: statistics and decision workgroups interleaved
+        // (one chunk per group keeps the register count near the statistics
+        // pass's, so that the streaming workgroups keep their occupancy)
+        const dim3 grid(static_cast<unsigned>(d->batch) * (L.rows * L.nc + L.fwpr));
+        launch(k_verify_fused<BF16, VEC, 1>, grid, e0, e1);
+        // the decision runs inside that kernel: its events mark the end
+        if (e2 && hipEventRecord(e2, stream) != hipSuccess) return SPECDEC_ERR_DEVICE;
+        if (e3 && hipEventRecord(e3, stream) != hipSuccess) return SPECDEC_ERR_DEVICE;
+        return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_DEVICE;
+    }
     if (launch_stats(P, BF16, VEC, greedy, dim3(L.nc, L.rows, d->batch), stream, e0, e1) != SPECDEC_OK)
         return SPECDEC_ERR_DEVICE;
     if (greedy) {
@@ -747,6 +957,7 @@ specdec_status_t verify_impl(const specdec_verify_desc_t* d, const void* target_
     P.flags = flags;
     char* ws = static_cast<char*>(workspace);
     P.cnt = reinterpret_cast<uint32_t*>(ws + L.off_cnt);
+    P.ready = reinterpret_cast<uint64_t*>(ws + L.off_ready);
     P.part = reinterpret_cast<float4*>(ws + L.off_part);
     P.csum = reinterpret_cast<uint32_t*>(ws + L.off_csum);
     P.nuc = reinterpret_cast<uint2*>(ws + L.off_nuc);
@@ -760,8 +971,12 @@ specdec_status_t verify_impl(const specdec_verify_desc_t* d, const void* target_
     P.chunk = L.chunk;
     P.nc2 = L.nc2;
     P.chunk2 = L.chunk2;
-    P.wpr = L.wpr;
-    P.cpw = L.cpw;
+    // sampling without truncation runs as one kernel unless SPECDEC_FUSED=0
+    const bool fused = sample && !L.trunc && fused_enabled();
+    P.wpr = fused ? L.fwpr : L.wpr;
+    P.cpw = fused ? L.fcpw : L.cpw;
+    P.lag = fused_lag(d->batch);
+    P.wait_ticks = fused_wait_ticks();
     P.c = sample ? static_cast<float>(1.4426950408889634 / static_cast<double>(d->temperature)) : 1.0f;
     P.key0 = static_cast<uint32_t>(d->seed & 0xffffffffu);
     P.key1 = static_cast<uint32_t>(d->seed >> 32);
@@ -775,10 +990,10 @@ specdec_status_t verify_impl(const specdec_verify_desc_t* d, const void* target_
                      (static_cast<size_t>(d->vocab) * es) % 16 == 0;
     if (L.trunc) return launch_truncated(P, bf16, vec, stream, ev);
     if (bf16)
-        return vec ? launch_all<true, true>(d, P, L, stream, ev)
-                   : launch_all<true, false>(d, P, L, stream, ev);
-    return vec ? launch_all<false, true>(d, P, L, stream, ev)
-               : launch_all<false, false>(d, P, L, stream, ev);
+        return vec ? launch_all<true, true>(d, P, L, fused, stream, ev)
+                   : launch_all<true, false>(d, P, L, fused, stream, ev);
+    return vec ? launch_all<false, true>(d, P, L, fused, stream, ev)
+               : launch_all<false, false>(d, P, L, fused, stream, ev);
 }
 
 }  // namespace

@@ -42,6 +42,9 @@ struct VerifyParams {
     float4* part;       // [B][R][nc] chunk partials, R = 2G+1 (sample) or G+1 (greedy)
     uint32_t* cnt;      // [B] arrivals in the sampling pass
     uint32_t* csum;     // [B][nc2] chunk masses of the sampling pass (float bits)
+    uint64_t* ready;    // [B][R][nc] one-kernel path: published (max, sum) words, 0 at rest
+    int lag;            // one-kernel path: decision workgroups trail by this many requests
+    uint64_t wait_ticks;  // one-kernel path: bound of a decision workgroup's wait
     int B, G, V;
     int rows;           // R
     int nc, chunk;      // statistics pass: chunks per row, elements per chunk
@@ -168,8 +171,9 @@ __device__ __forceinline__ float block_sum(float v) {
 struct Layout {
     int rows, nc, chunk, nc2, chunk2, wpr, cpw;
     int group;          // sampling-pass chunks loaded together (1..kMassGroupWide)
+    int fwpr, fcpw;     // one-kernel path: decision workgroups per request, chunks each
     bool trunc;
-    size_t off_cnt, off_part, off_csum, off_nuc, total;
+    size_t off_cnt, off_ready, off_part, off_csum, off_nuc, total;
 };
 // point: sampling with point-mass drafts (no draft rows)
 Layout make_layout(const specdec_verify_desc_t* d, bool point = false);

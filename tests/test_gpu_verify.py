@@ -167,6 +167,101 @@ def test_no_gamma_array_means_gamma_max():
         assert np.array_equal(a[k], b[k]), k
 
 
+# ------------------------------------------------------------ one-kernel path
+
+def _env(**kv):
+    """Set (value) or unset (None) environment variables; returns the old values."""
+    import os
+    old = {k: os.environ.get(k) for k in kv}
+    for k, v in kv.items():
+        if v is None:
+            os.environ.pop(k, None)
+        else:
+            os.environ[k] = str(v)
+    return old
+
+
+ONE_KERNEL_CASES = [
+    ("headline B=16", lambda: W[synth.HEADLINE].scaled(16, 128256), True),
+    ("ragged B=40 V=3001", lambda: W["b512_ragged_v262144_kv"].scaled(40, 3001), True),
+    ("fp32 B=8", lambda: W["b8_g4_v32000_f32"], True),
+    ("point-mass drafts B=24", lambda: W[synth.HEADLINE].scaled(24, 20000), False),
+]
+
+
+@pytest.mark.parametrize("label,make,with_draft", ONE_KERNEL_CASES, ids=[c[0] for c in ONE_KERNEL_CASES])
+def test_one_kernel_path_matches_two_kernel_path(label, make, with_draft):
+    """Sampling verify in one launch (statistics and decision workgroups
+    interleaved, decisions trailing by `lag` requests) writes the same bytes
+    as the statistics kernel followed by the decision kernel, at every lag."""
+    wl = make()
+    x = synth.make_verify_inputs(wl)
+    if not with_draft:
+        x["draft"] = None
+    args = dict(bf16=wl.dtype == "bf16", temperature=wl.temperature, seed=wl.verify_seed)
+    old = _env(SPECDEC_FUSED=0, SPECDEC_FUSED_LAG=None)
+    try:
+        say(f"[one-kernel] {label}: two-kernel path")
+        ref = gpu_verify(x, **args)
+        for lag in sorted({0, 1, 3, wl.batch}):
+            _env(SPECDEC_FUSED=1, SPECDEC_FUSED_LAG=lag)
+            say(f"[one-kernel] {label}: lag {lag}, two calls")
+            outs = gpu_verify(x, reps=2, **args)
+            for o in outs:
+                for k in ref:
+                    assert np.array_equal(o[k], ref[k]), (label, lag, k)
+                assert not np.any(o["flags"] & sd.FLAG_WAIT_TIMEOUT)
+    finally:
+        _env(**old)
+    # and the oracle agrees (exact decisions, as in the other sampling tests)
+    oref = oracle_verify(x, temperature=wl.temperature, seed=wl.verify_seed)
+    errs, _ = compare(oref, ref, x["gamma"], False, None, label)
+    assert not errs, "\n".join(errs[:20])
+
+
+def test_one_kernel_wait_timeout_is_flagged():
+    """With the wait bound forced to zero ticks and every decision workgroup
+    right behind its own request's statistics, decisions give up before the
+    statistics land: each request is then either flagged WAIT_TIMEOUT or
+    identical to the two-kernel path.  Statistics that land after their
+    request's decision leave words set: after a workspace clear the next
+    call is identical again."""
+    import torch
+    from gpu_helpers import to_dev
+    wl = W[synth.HEADLINE].scaled(16, 60000)
+    x = synth.make_verify_inputs(wl)
+    desc = sd.make_verify_desc(wl.batch, wl.gamma_max, wl.vocab, temperature=wl.temperature,
+                               seed=wl.verify_seed)
+    ver = sd.Verifier(desc, "cuda")
+    t, d = to_dev(x["target"], "cuda"), to_dev(x["draft"], "cuda")
+    tok, gam = to_dev(x["draft_tokens"], "cuda"), to_dev(x["gamma"], "cuda")
+
+    def run():
+        out = {k: v.cpu().numpy() for k, v in ver(t, d, tok, gam).items()}
+        torch.cuda.synchronize()
+        return out
+
+    old = _env(SPECDEC_FUSED=0, SPECDEC_FUSED_LAG=None, SPECDEC_FUSED_WAIT_TICKS=None)
+    try:
+        ref = run()
+        _env(SPECDEC_FUSED=1, SPECDEC_FUSED_LAG=0, SPECDEC_FUSED_WAIT_TICKS=0)
+        say("[one-kernel] forced wait timeout")
+        r = run()
+        late = (r["flags"] & sd.FLAG_WAIT_TIMEOUT) != 0
+        say(f"  requests flagged WAIT_TIMEOUT: {int(late.sum())} of {wl.batch}")
+        same = np.all(r["out_tokens"] == ref["out_tokens"], axis=1) & \
+            (r["accept_count"] == ref["accept_count"]) & \
+            (r["residual_mass"].view(np.uint32) == ref["residual_mass"].view(np.uint32))
+        assert np.all(late | same)
+        _env(SPECDEC_FUSED_LAG=None, SPECDEC_FUSED_WAIT_TICKS=None)
+        sd.specdec_workspace_clear(ver.workspace)
+        r2 = run()
+    finally:
+        _env(**old)
+    for k in ref:
+        assert np.array_equal(r2[k], ref[k]), k
+
+
 # ------------------------------------------------------------ greedy
 
 @pytest.mark.parametrize("batch,vocab", [(32, 151936), (16, 10001), (5, 64)])
