@@ -267,7 +267,7 @@ __device__ void select_in_wave(const VerifyParams& P, int b, int s, int C, bool 
     int Nk = K;
     if (P.top_p < 1.0f) {
         const float goal = P.top_p * lane_value(pre, lane_of(in && rank == K - 1));
-        Nk = min(K, __popcll(__ballot(in && rank < K && pre < goal)) + 1);
+        Nk = min(K, static_cast<int>(__popcll(__ballot(in && rank < K && pre < goal))) + 1);
     }
     const float Sn = lane_value(pre, lane_of(in && rank == Nk - 1));
     // the kept tokens by ascending index: every candidate at its index rank,

@@ -84,7 +84,7 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<BF16, VEC>& r, const MassRo
     constexpr int N = Vec<BF16>::N;
 #pragma unroll
     for (int u = 0; u < kUnroll2; ++u) {
-        const int e = min(lo + (u * kThreads + threadIdx.x) * N, hi - N);
+        const int e = min(lo + (u * kThreads + static_cast<int>(threadIdx.x)) * N, hi - N);
         r.p[u] = load16_stream<BF16>(a.p, e);
         if (a.q) r.q[u] = load16_stream<BF16>(a.q, e);
     }
@@ -130,77 +130,60 @@ __device__ float lane_mass_elements(const MassRows& a, int lo, int hi) {
     return acc;
 }
 
-// Sums over the kThreads lanes of NV values at once (one LDS exchange).
-template <int NV>
-__device__ __forceinline__ void block_sums(float (&v)[NV]) {
-    __shared__ float s_v[NV][kWaves];
-    const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
-#pragma unroll
-    for (int j = 0; j < NV; ++j) v[j] = wave_sum(v[j]);
-    __syncthreads();
-    if (l == 0) {
-#pragma unroll
-        for (int j = 0; j < NV; ++j) s_v[j][w] = v[j];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-        float r = s_v[j][0];
-#pragma unroll
-        for (int k = 1; k < kWaves; ++k) r += s_v[j][k];
-        v[j] = r;
-    }
-}
-
-// Masses of chunks [k0, k1) published to csum[k].  The loads of a group of
-// GROUP chunks are issued together and the group's sums reduced at once.
-// A share of at most GROUP chunks is one group; a longer share is walked in
-// groups with the next group's loads in flight while the current one is
-// reduced.  Returns the OR of the publish() results (the dependency for
-// arrive_last).
+// Masses of chunks [k0, k1) published to csum[k].  Loads go in groups of
+// GROUP chunks, into two register sets in turn (no copies between them), so
+// the next group's loads are in flight while the current group is reduced.
+// Nothing inside the walk waits on other waves or on memory writes: each
+// chunk's wave sums go to LDS (scr: kWaves floats per chunk), and after one
+// barrier thread 0 adds them in wave order and publishes the whole batch at
+// once (batches of 1024 / kWaves chunks).  Returns the OR of the publish()
+// results (the dependency for arrive_last).
 template <bool BF16, bool VEC, int GROUP>
-__device__ uint32_t mass_chunks(const MassRows& a, int k0, int k1, int chunk2, int V, uint32_t* csum) {
+__device__ uint32_t mass_chunks(const MassRows& a, int k0, int k1, int chunk2, int V, uint32_t* csum,
+                                float* scr) {
     uint32_t dep = 0;
     if (k0 >= k1) return dep;
     if constexpr (VEC) {
-        auto load_group = [&](ChunkRegs<BF16, VEC>(&r)[GROUP], int kb) {
+        const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+        constexpr int kBatch = 1024 / kWaves;
+        for (int b0 = k0; b0 < k1; b0 += kBatch) {
+            const int b1 = min(k1, b0 + kBatch);
+            auto load_group = [&](ChunkRegs<BF16, VEC>(&r)[GROUP], int kb) {
 #pragma unroll
-            for (int j = 0; j < GROUP; ++j) {
-                const int k = min(kb + j, k1 - 1);  // past k1: the last chunk again, discarded
-                load_chunk<BF16, VEC>(r[j], a, k * chunk2, min(V, (k + 1) * chunk2));
-            }
-        };
-        auto reduce_group = [&](ChunkRegs<BF16, VEC>(&r)[GROUP], int kb) {
-            float part[GROUP];
+                for (int j = 0; j < GROUP; ++j) {
+                    const int k = min(kb + j, b1 - 1);  // past b1: the last chunk again, unused
+                    load_chunk<BF16, VEC>(r[j], a, k * chunk2, min(V, (k + 1) * chunk2));
+                }
+            };
+            auto reduce_group = [&](ChunkRegs<BF16, VEC>(&r)[GROUP], int kb) {
 #pragma unroll
-            for (int j = 0; j < GROUP; ++j) {
-                const int k = min(kb + j, k1 - 1);
-                const int lo = k * chunk2, hi = min(V, lo + chunk2);
-                part[j] = lane_mass<BF16, VEC>(r[j], a, lo, hi);
+                for (int j = 0; j < GROUP; ++j) {
+                    if (kb + j >= b1) break;
+                    const int lo = (kb + j) * chunk2, hi = min(V, lo + chunk2);
+                    const float s = wave_sum(lane_mass<BF16, VEC>(r[j], a, lo, hi));
+                    if (l == 0) scr[(kb + j - b0) * kWaves + w] = s;
+                }
+            };
+            ChunkRegs<BF16, VEC> ra[GROUP], rb[GROUP];
+            load_group(ra, b0);
+            for (int kb = b0; kb < b1; kb += 2 * GROUP) {
+                if (kb + GROUP < b1) load_group(rb, kb + GROUP);
+                reduce_group(ra, kb);
+                if (kb + GROUP >= b1) break;
+                if (kb + 2 * GROUP < b1) load_group(ra, kb + 2 * GROUP);
+                reduce_group(rb, kb + GROUP);
             }
-            block_sums(part);
+            __syncthreads();
             if (threadIdx.x == 0) {
+                for (int k = b0; k < b1; ++k) {
+                    const float* s = scr + (k - b0) * kWaves;
+                    float t = s[0];
 #pragma unroll
-                for (int j = 0; j < GROUP; ++j)
-                    if (kb + j < k1) dep |= publish(csum + kb + j, __float_as_uint(part[j]));
-            }
-        };
-        ChunkRegs<BF16, VEC> cur[GROUP];
-        if (k1 - k0 <= GROUP) {
-            load_group(cur, k0);
-            reduce_group(cur, k0);
-        } else {
-            ChunkRegs<BF16, VEC> nxt[GROUP];
-            load_group(cur, k0);
-            for (int kb = k0; kb < k1; kb += GROUP) {
-                const bool more = kb + GROUP < k1;
-                if (more) load_group(nxt, kb + GROUP);
-                reduce_group(cur, kb);
-                if (more) {
-#pragma unroll
-                    for (int j = 0; j < GROUP; ++j) cur[j] = nxt[j];
+                    for (int q = 1; q < kWaves; ++q) t += s[q];
+                    dep |= publish(csum + k, __float_as_uint(t));
                 }
             }
+            __syncthreads();  // scr is reused by the next batch and by the caller
         }
     } else {
         for (int k = k0; k < k1; ++k) {
@@ -402,7 +385,9 @@ __device__ __forceinline__ void decide_sample(const VerifyParams& P, const int w
     if constexpr (!FUSED) stage_partials(P, b, s_part);
     int d = -1;
     if (w == 0 && i < P.G) d = P.tokens[static_cast<size_t>(b) * P.G + i];
-    const int g = request_gamma(P, b);
+    // gamma_b read once: clamped into [0, G], flagged if it was outside
+    const int graw = P.gamma ? P.gamma[b] : P.G;
+    const int g = min(max(graw, 0), P.G);
     float u_acc = 0.0f, u_draw = 0.0f;
     if (w == 0) {
         const uint4 r = philox4x32_10(make_uint4(static_cast<uint32_t>(i), static_cast<uint32_t>(b),
@@ -459,7 +444,7 @@ __device__ __forceinline__ void decide_sample(const VerifyParams& P, const int w
     // (2) acceptance tests, lane i = position i of wave 0; m from a ballot
     float pd = 0.0f, qd = 0.0f;
     if (w == 0) {
-        uint32_t fl = (i == 0) ? gamma_flag(P, b) : 0u;
+        uint32_t fl = (i == 0 && (graw < 0 || graw > P.G)) ? SPECDEC_FLAG_BAD_GAMMA : 0u;
         bool acc = false;
         if (i <= g) {
             const float2 t = s_stat[i];
@@ -522,7 +507,7 @@ __device__ __forceinline__ void decide_sample(const VerifyParams& P, const int w
     }
     uint32_t* csum = P.csum + static_cast<size_t>(b) * P.nc2;
     const int k0 = wg * P.cpw, k1 = min(P.nc2, k0 + P.cpw);
-    const uint32_t dep = mass_chunks<BF16, VEC, GROUP>(a, k0, k1, P.chunk2, P.V, csum);
+    const uint32_t dep = mass_chunks<BF16, VEC, GROUP>(a, k0, k1, P.chunk2, P.V, csum, s_csum);
     if constexpr (FUSED) {
         if (!arrive_last_marked(P.cnt + b, static_cast<uint32_t>(P.wpr), dep, late, &late)) return;
         clear_partials(P, b, g);
@@ -685,7 +670,7 @@ __device__ __forceinline__ void fused_stats(const VerifyParams& P, int b, int k)
 }
 
 template <bool BF16, bool VEC, int GROUP>
-__global__ __launch_bounds__(kThreads) void k_verify_fused(VerifyParams P) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) void k_verify_fused(VerifyParams P) {
     const Role r = fused_role(P, blockIdx.x);
     if (r.stats) fused_stats<BF16, VEC>(P, r.b, r.k);
     else decide_sample<BF16, VEC, GROUP, true>(P, r.k, r.b);
@@ -703,7 +688,8 @@ __global__ __launch_bounds__(kThreads) void k_decide_greedy(VerifyParams P) {
     const int i = l;
     int d = -1;
     if (w == 0 && i < P.G) d = P.tokens[static_cast<size_t>(b) * P.G + i];
-    const int g = request_gamma(P, b);
+    const int graw = P.gamma ? P.gamma[b] : P.G;  // read once, clamped, flagged below
+    const int g = min(max(graw, 0), P.G);
     __syncthreads();
     // a lane per row over a few partials, else a wave per row
     auto part_argmax = [&](int s, int k0, int step, ArgMax& best, uint32_t& nan) {
@@ -735,7 +721,7 @@ __global__ __launch_bounds__(kThreads) void k_decide_greedy(VerifyParams P) {
     }
     __syncthreads();
     if (w != 0) return;
-    uint32_t fl = (i == 0) ? gamma_flag(P, b) : 0u;
+    uint32_t fl = (i == 0 && (graw < 0 || graw > P.G)) ? SPECDEC_FLAG_BAD_GAMMA : 0u;
     bool acc = false;
     if (i <= g && s_nan[i]) fl |= SPECDEC_FLAG_NONFINITE;
     if (i < g) {
