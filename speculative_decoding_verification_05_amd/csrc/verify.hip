@@ -520,28 +520,23 @@ __device__ __forceinline__ void decide_sample(const VerifyParams& P, const int w
     for (int k = threadIdx.x; k < P.nc2; k += kThreads) s_csum[k] = __uint_as_float(fetch(csum + k));
     __syncthreads();
     // Wave 0 walks the chunk sums in chunk order: lane l takes a run of
-    // consecutive chunks, and a wave prefix sum of the runs' totals gives
-    // each run its offset.  total() leaves R in s_R; pick() leaves the chunk
-    // where the running mass first passes `target` and the mass before it
-    // (or, if rounding leaves none, the last chunk with mass and +inf).
+    // consecutive chunks, and a wave prefix sum of the runs' totals gives R
+    // and each run its offset.  scan() leaves R in s_R, and in s_chunk /
+    // s_before the chunk where the running mass first passes u*R and the
+    // mass before it (or, if rounding leaves none, the last chunk with mass
+    // and +inf).
     __shared__ int s_chunk;
     __shared__ float s_before;
     const int per = (P.nc2 + kWave - 1) / kWave;
     const int r0 = l * per, r1 = min(P.nc2, r0 + per);
-    auto total = [&]() {
+    auto scan = [&]() {
         if (w == 0) {
             float run = 0.0f;
             for (int k = r0; k < r1; ++k) run += s_csum[k];
-            const float R = lane63(wave_prefix_sum(run));
-            if (l == 0) s_R = R;
-        }
-        __syncthreads();
-    };
-    auto pick = [&](float target) {
-        if (w == 0) {
-            float run = 0.0f;
-            for (int k = r0; k < r1; ++k) run += s_csum[k];
-            float before = wave_shift_right(wave_prefix_sum(run));
+            const float incl = wave_prefix_sum(run);
+            const float R = lane63(incl);
+            const float target = s_um * R;
+            float before = wave_shift_right(incl);
             int found = -1, lastk = -1;
             float fb = 0.0f;
             for (int k = r0; k < r1; ++k) {
@@ -563,13 +558,13 @@ __device__ __forceinline__ void decide_sample(const VerifyParams& P, const int w
                 cstar = pos ? lane_value(lastk, 63 - __builtin_clzll(pos)) : 0;
                 bef = pos_inf();  // no crossing: take its last token with mass
             }
-            if (l == 0) { s_chunk = cstar; s_before = bef; }
+            if (l == 0) { s_R = R; s_chunk = cstar; s_before = bef; }
         }
         __syncthreads();
     };
     uint32_t fl2 = 0;
     float R_report = 0.0f;
-    total();
+    scan();
     if (resid) {
         R_report = s_R;
         if (!(s_R > 0.0f)) {
@@ -582,11 +577,10 @@ __device__ __forceinline__ void decide_sample(const VerifyParams& P, const int w
                 if (threadIdx.x == 0) s_csum[k] = v;
             }
             __syncthreads();
-            total();
+            scan();
         }
     }
     const float target = s_um * s_R;
-    pick(target);
     int lastp;
     const int l2 = s_chunk * P.chunk2, h2 = min(P.V, l2 + P.chunk2);
     int token = search_chunk<BF16, VEC>(a, l2, h2, s_before, target, &lastp);
