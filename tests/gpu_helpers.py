@@ -2,6 +2,8 @@
 compare it with the CPU oracle on the same seeded inputs."""
 from __future__ import annotations
 
+import contextlib
+import os
 import sys
 
 import numpy as np
@@ -15,6 +17,26 @@ PROB_ABS, PROB_REL = 1e-5, 1e-4
 def say(msg: str) -> None:
     print(msg, flush=True)
     sys.stdout.flush()
+
+
+@contextlib.contextmanager
+def env(**kv):
+    """Environment variables set (value) or unset (None) for the block; the
+    library reads its tuning switches on every call."""
+    old = {k: os.environ.get(k) for k in kv}
+    try:
+        for k, v in kv.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = str(v)
+        yield
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
 
 
 def to_dev(a: np.ndarray, dev):
