@@ -63,7 +63,7 @@ typedef enum specdec_status {
     SPECDEC_OK = 0,
     SPECDEC_ERR_INVALID_ARGUMENT = 1,   /* bad descriptor, NULL or misaligned pointer */
     SPECDEC_ERR_WORKSPACE_TOO_SMALL = 2,
-    SPECDEC_ERR_UNSUPPORTED = 3,        /* valid request this build does not implement */
+    SPECDEC_ERR_UNSUPPORTED = 3,        /* valid request the library does not implement */
     SPECDEC_ERR_DEVICE = 4              /* the HIP runtime refused a launch */
 } specdec_status_t;
 

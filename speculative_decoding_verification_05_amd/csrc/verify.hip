@@ -739,7 +739,7 @@ bool truncation_mode(const specdec_verify_desc_t* d) {
            ((d->top_k > 0 && d->top_k < d->vocab) || d->top_p < 1.0f);
 }
 
-// Truncation requests this build cannot serve (see specdec.h).
+// Truncation requests the kernels do not serve (see specdec.h).
 bool truncation_supported(const specdec_verify_desc_t* d) {
     const bool use_k = d->top_k > 0 && d->top_k < d->vocab;
     if (use_k && d->top_k > kNucCap) return false;
