@@ -708,7 +708,8 @@ def bench_ngram(args, wl0) -> int:
                    "launch": "hipgraph", "proposed_tokens_per_s": proposed / sec_per_step},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "kernel": "k_propose_ngram", "kernel_avg_us": k_us * 1e6,
+                     "kernel": "k_propose_ngram_whole" if Lmax <= 8192 else "k_propose_ngram",
+                     "kernel_avg_us": k_us * 1e6,
                      "bytes_per_launch": alg},
         "cpu_baseline": cpu,
     }

@@ -11,11 +11,13 @@
 //
 // Equivalent single pass: for every end position e <= L-2 let l(e) be the
 // length of the common suffix of h[..e] and h[..L-1], capped at n_max.  The
-// winner maximises (l(e), e) over the e with l(e) >= n_min.  The history is
-// split into segments of end positions, one workgroup each; a lane keeps the
-// best packed key (l << 24 | e) of its positions, a block maximum that of the
-// segment, and a device-scope atomic maximum that of the request; the last
-// segment to arrive writes the proposal.  One read of the history: bound by
+// winner maximises (l(e), e) over the e with l(e) >= n_min.  A lane keeps
+// the best packed key (l << 24 | e) of its positions and a block maximum
+// that of the workgroup.  Rows of at most 8192 tokens take one 1024-lane
+// workgroup per request, the whole history in LDS (k_propose_ngram_whole);
+// longer rows are split into segments of end positions, one workgroup each,
+// combined by a device-scope atomic maximum, and the last segment to arrive
+// writes the proposal (k_propose_ngram).  One read of the history: bound by
 // HBM bandwidth and, for short histories, by latency.
 #include "verify_internal.h"
 
@@ -121,6 +123,65 @@ __global__ __launch_bounds__(kThreads) void k_propose_ngram(NgramParams P) {
     }
 }
 
+// Rows of at most kWhole tokens: one workgroup per request.  After the
+// length, every token of the history is loaded at once (8 per lane) and kept
+// in LDS; positions are scored as in k_propose_ngram and the proposal is read
+// back from LDS: two memory round trips and no combine across workgroups.
+constexpr int kWhole = 8192;
+constexpr int kWholeThreads = 1024;  // 16 waves: 8 positions per lane, as in a segment
+constexpr int kWholePerLane = kWhole / kWholeThreads;
+constexpr int kWholeWaves = kWholeThreads / kWave;
+
+__global__ __launch_bounds__(kWholeThreads) void k_propose_ngram_whole(NgramParams P) {
+    __shared__ int32_t s_h[kWhole];
+    __shared__ uint32_t s_w[kWholeWaves];
+    const int b = blockIdx.x;
+    const int l = threadIdx.x;
+    const int32_t* h = P.history + static_cast<size_t>(b) * P.max_len;
+    const int L = min(max(P.hist_len[b], 0), P.max_len);
+    int32_t v[kWholePerLane];
+#pragma unroll
+    for (int i = 0; i < kWholePerLane; ++i) {
+        const int e = l + i * kWholeThreads;
+        v[i] = e < L ? h[e] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < kWholePerLane; ++i) {
+        const int e = l + i * kWholeThreads;
+        if (e < L) s_h[e] = v[i];
+    }
+    __syncthreads();
+    const int e_end = L - 1;  // end positions e < L-1
+    const int32_t last = L > 0 ? s_h[L - 1] : 0;
+    uint32_t best = 0;  // (l << 24) | e; 0: none
+#pragma unroll
+    for (int i = 0; i < kWholePerLane; ++i) {
+        const int e = l + i * kWholeThreads;
+        if (e < e_end && v[i] == last) {
+            int k = 1;
+            while (k < P.n_max && e - k >= 0 && s_h[e - k] == s_h[L - 1 - k]) ++k;
+            if (k >= P.n_min) {
+                const uint32_t key = (static_cast<uint32_t>(k) << 24) | static_cast<uint32_t>(e);
+                best = key > best ? key : best;
+            }
+        }
+    }
+    best = wave_umax(best);
+    if (l % kWave == 0) s_w[l / kWave] = best;
+    __syncthreads();
+    uint32_t key = s_w[0];
+#pragma unroll
+    for (int w = 1; w < kWholeWaves; ++w) key = s_w[w] > key ? s_w[w] : key;
+    const int n = static_cast<int>(key >> 24);
+    const int first = static_cast<int>(key & 0xffffffu) + 1;  // the token after the occurrence
+    const int cnt = key ? min(P.G, L - first) : 0;
+    if (l < P.G) P.tokens[static_cast<size_t>(b) * P.G + l] = l < cnt ? s_h[first + l] : -1;
+    if (l == 0) {
+        P.count[b] = cnt;
+        if (P.match) P.match[b] = n;
+    }
+}
+
 bool valid_ngram(const specdec_ngram_desc_t* d) {
     if (!d) return false;
     if (d->batch < 0 || d->batch > 65535 || d->max_len < 1 || d->max_len >= (1 << 24)) return false;
@@ -166,7 +227,11 @@ extern "C" specdec_status_t specdec_propose_ngram(const specdec_ngram_desc_t* d,
     P.n_min = d->n_min;
     P.n_max = d->n_max;
     P.G = d->gamma_max;
-    const int nseg = (d->max_len + kSeg - 1) / kSeg;
-    hipLaunchKernelGGL(k_propose_ngram, dim3(nseg, d->batch), dim3(kThreads), 0, stream, P);
+    if (d->max_len <= kWhole) {
+        hipLaunchKernelGGL(k_propose_ngram_whole, dim3(d->batch), dim3(kWholeThreads), 0, stream, P);
+    } else {
+        const int nseg = (d->max_len + kSeg - 1) / kSeg;
+        hipLaunchKernelGGL(k_propose_ngram, dim3(nseg, d->batch), dim3(kThreads), 0, stream, P);
+    }
     return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_DEVICE;
 }

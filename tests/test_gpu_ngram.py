@@ -65,10 +65,12 @@ def test_worked_cases():
 
 @pytest.mark.parametrize("B,Lmax,vocab,n_min,n_max,gam", [
     (200, 60, 5, 1, 4, 5), (64, 300, 3, 2, 8, 8), (40, 20000, 40, 3, 32, 63),
-    (16, 17000, 2, 1, 32, 7), (30, 9000, 1000, 1, 2, 0)])
+    (16, 17000, 2, 1, 32, 7), (30, 9000, 1000, 1, 2, 0), (12, 8192, 7, 1, 6, 8),
+    (12, 8193, 7, 1, 6, 8)])
 def test_random_histories(B, Lmax, vocab, n_min, n_max, gam):
-    """Small alphabets (many matches), lengths 0..Lmax including several LDS
-    segments with halos (> 8192 tokens), n_max = 32, gamma 0 and 63."""
+    """Small alphabets (many matches), lengths 0..Lmax: rows of up to 8192
+    tokens (one workgroup per request) and longer rows (several LDS segments
+    with halos), n_max = 32, gamma 0 and 63."""
     rng = np.random.default_rng(B + Lmax)
     hist = rng.integers(0, vocab, (B, Lmax)).astype(np.int32)
     lens = rng.integers(0, Lmax + 1, B).astype(np.int32)
