@@ -3,6 +3,7 @@ random shapes (batch, gamma_max, vocabulary, dtype, ragged gamma, point-mass
 drafts, temperature): every output byte-equal, on two calls in a row with one
 workspace; a third of the cases also against the CPU oracle."""
 import dataclasses
+import os
 
 import numpy as np
 import pytest
@@ -35,7 +36,9 @@ def _cases(n=48, seed=20261202):
     return out
 
 
-CASES = _cases()
+# SPECDEC_RANDOM_CASES / SPECDEC_RANDOM_SEED widen the sweep for a longer run
+CASES = _cases(int(os.environ.get("SPECDEC_RANDOM_CASES", 48)),
+               int(os.environ.get("SPECDEC_RANDOM_SEED", 20261202)))
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"b{c['batch']}g{c['gamma_max']}v{c['vocab']}"
