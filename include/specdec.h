@@ -135,7 +135,8 @@ size_t specdec_verify_workspace_bytes(const specdec_verify_desc_t* desc);
  *       p_i(d_i) and a rejection draws from p_i with d_i removed (AI-infra KB
  *       M013 s.08 asks for the candidates' probability representation; the
  *       rule of s.04 then applies unchanged).  Not combined with truncation
- *       (UNSUPPORTED).
+ *       (UNSUPPORTED) when G > 0; with G = 0 there are no draft rows and
+ *       NULL is simply the absent array.
  *   draft_tokens  [B][G] int32: the proposed tokens d_0..d_{gamma_b - 1}.
  *   gamma         [B] int32 in [0, G], or NULL (every request uses G).  Rows
  *       and tokens past gamma_b are never read.  A value outside [0, G] is

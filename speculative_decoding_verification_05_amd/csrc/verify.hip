@@ -915,7 +915,8 @@ specdec_status_t verify_impl(const specdec_verify_desc_t* d, const void* target_
         return SPECDEC_ERR_INVALID_ARGUMENT;
     if (d->gamma_max > 0 && !draft_tokens) return SPECDEC_ERR_INVALID_ARGUMENT;
     // sampling without draft rows: point-mass drafts of a deterministic proposer
-    const bool point = sample && !draft_logits;
+    // (with gamma_max = 0 there is no draft row either way)
+    const bool point = sample && !draft_logits && d->gamma_max > 0;
     if (truncation_mode(d) && (point || !truncation_supported(d))) return SPECDEC_ERR_UNSUPPORTED;
     const Layout L = make_layout(d, point);
     if (workspace_bytes < L.total) return SPECDEC_ERR_WORKSPACE_TOO_SMALL;

@@ -1,0 +1,72 @@
+"""specdec_verify against the CPU oracle on seeded random small shapes in
+every mode: sampling (draft rows or point-mass drafts), greedy, and
+truncated sampling (top-k, top-p, both), with ragged gamma, EOS tokens and
+token budgets.  The comparison is element by element as in the other parity
+tests (near-threshold decisions excluded and counted)."""
+import dataclasses
+import os
+
+import numpy as np
+import pytest
+
+from speculative_decoding_verification_05_amd import synth
+from gpu_helpers import compare, gpu_verify, oracle_verify, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        mode = str(rng.choice(["sample", "point", "greedy", "topk", "topp", "topkp"]))
+        B = int(rng.choice([1, 3, 8, 21]))
+        G = int(rng.integers(0, 9))
+        V = int(rng.choice([2, 17, 300, 2048, 5000, 32000]))
+        if mode == "topp" and V > 2048:
+            V = 2048  # top-p without an effective top-k: vocabularies up to 2048
+        if B * (2 * G + 1) * V > 3_000_000:
+            continue
+        top_k = int(rng.integers(1, min(V, 200) + 1)) if mode in ("topk", "topkp") else 0
+        top_p = float(rng.uniform(0.3, 0.99)) if mode in ("topp", "topkp") else 1.0
+        out.append(dict(mode=mode, batch=B, gamma_max=G, vocab=V, top_k=top_k, top_p=top_p,
+                        dtype=str(rng.choice(["bf16", "f32"])),
+                        ragged=bool(rng.random() < 0.5) and G > 0,
+                        temperature=float(rng.choice([0.6, 1.0, 1.4])),
+                        eos=int(rng.integers(-1, V)) if rng.random() < 0.3 else -1,
+                        budget=bool(rng.random() < 0.3),
+                        data_seed=int(rng.integers(1, 1 << 30)),
+                        verify_seed=int(rng.integers(0, 1 << 62))))
+    return out
+
+
+CASES = _cases(int(os.environ.get("SPECDEC_RANDOM_CASES", 36)),
+               int(os.environ.get("SPECDEC_RANDOM_SEED", 7700)))
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c['mode']}-b{c['batch']}g{c['gamma_max']}"
+                                              f"v{c['vocab']}{c['dtype']}" for c in CASES])
+def test_random_against_oracle(case):
+    greedy = case["mode"] == "greedy"
+    wl = dataclasses.replace(synth.WORKLOADS[synth.HEADLINE], name="random", batch=case["batch"],
+                             gamma_max=case["gamma_max"], vocab=case["vocab"], dtype=case["dtype"],
+                             ragged=case["ragged"], temperature=case["temperature"],
+                             mode="greedy" if greedy else "sample",
+                             data_seed=case["data_seed"], verify_seed=case["verify_seed"])
+    say(f"[random vs oracle] {case}")
+    x = synth.make_verify_inputs(wl, need_draft_logits=not greedy)
+    if case["mode"] == "point":
+        x["draft"] = None
+    if greedy:
+        x["draft"] = None
+    budget = None
+    if case["budget"]:
+        budget = np.random.default_rng(case["data_seed"]).integers(0, case["gamma_max"] + 3,
+                                                                   case["batch"]).tolist()
+    args = dict(temperature=wl.temperature, top_k=case["top_k"], top_p=case["top_p"],
+                seed=wl.verify_seed, eos_token=case["eos"], max_tokens=budget)
+    got = gpu_verify(x, bf16=wl.dtype == "bf16", greedy=greedy, **args)
+    ref = oracle_verify(x, greedy=greedy, **args)
+    errs, near = compare(ref, got, x["gamma"], greedy, None, case["mode"])
+    say(f"  near-threshold requests: {near}")
+    assert not errs, "\n".join(errs[:20])
