@@ -714,6 +714,41 @@ def pin_strict_comparisons(orc):
     return errs
 
 
+def pin_near_threshold(orc):
+    """near_pos against the page's example: with d = option B the acceptance
+    threshold is min(1, p/q) = 3/5; the rejected draw's residual is [1, 0, 0]
+    (CDF edges 0 and 1); the bonus draw samples p = [1/2, 3/10, 1/5] (CDF
+    edges 1/2 and 4/5).  A uniform within 1e-6 of one of these is reported at
+    its position, one 3e-6 away or more is not (the logits are float32, so the
+    thresholds are exact only to ~1e-7)."""
+    g = golden_map("three_option_example.txt")
+    p = np.array([float(Fraction(x)) for x in g["p"]])
+    q = np.array([float(Fraction(x)) for x in g["q"]])
+    a = float(Fraction(g["accept_probability"][1]))
+    cases = [  # (u_accept[0], u_sample[0], u_sample[1], expected near_pos)
+        (a - 5e-7, 0.5, 0.65, 0), (a + 5e-7, 0.5, 0.65, 0),      # accept test at 3/5
+        (a - 3e-6, 0.5, 0.65, -1), (a + 3e-6, 0.5, 0.65, -1),   # clear of it
+        (0.9, 4e-7, 0.65, 0), (0.9, 0.5, 0.65, -1),             # rejected: edge at 0
+        (0.1, 0.5, 0.5 + 4e-7, 1), (0.1, 0.5, 0.8 - 4e-7, 1),   # bonus: edges 1/2, 4/5
+        (0.1, 0.5, 0.5 + 3e-6, -1), (0.1, 0.5, 0.65, -1),
+    ]
+    B = len(cases)
+    tgt = np.empty((B, 2, 3), np.float32)
+    tgt[:] = _ln_f32(p)
+    drf = np.empty((B, 1, 3), np.float32)
+    drf[:] = _ln_f32(q)
+    d = np.ones((B, 1), np.int32)
+    ua = np.array([[c[0], 0.5] for c in cases])
+    us = np.array([[c[1], c[2]] for c in cases])
+    r = orc.verify(tgt, drf, d, temperature=1.0, u_accept=ua, u_sample=us)
+    errs = []
+    for k, c in enumerate(cases):
+        if int(r["near_pos"][k]) != c[3]:
+            errs.append(f"case {k} (u_a={c[0]:.7f}, u_s={c[1]:.7f}/{c[2]:.7f}): near_pos "
+                        f"{int(r['near_pos'][k])}, want {c[3]}")
+    return errs
+
+
 def pin_invariants(orc):
     """R = sum [p-q]+ = 1 - sum min(p,q) at the rejected position; at most
     gamma+1 committed tokens; the accepted prefix is the drafts; -1 padding."""
@@ -823,6 +858,7 @@ def pin_commit_numpy(orc):
 ALL_PINS = {
     "philox_kat": pin_philox_kat,
     "three_option_grid": pin_three_option_grid,
+    "near_threshold": pin_near_threshold,
     "greedy_walkthrough": pin_greedy_walkthrough,
     "greedy_matches_numpy": pin_greedy_matches_numpy,
     "expected_advance": pin_expected_advance,

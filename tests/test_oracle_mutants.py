@@ -43,6 +43,12 @@ MUTANTS = [
      ["expected_advance"]),
     ("cdf_non_strict", "if (C > target_mass)", "if (C >= target_mass)",
      ["strict_comparisons"]),
+    ("near_accept_not_noted", "if (fabs(ua[i] - acc_p) < NEAR_EPS) note_near(&near, i);",
+     "if (0) note_near(&near, i);", ["near_threshold"]),
+    ("near_draw_not_noted",
+     "if (fabs(us[m] - C_prev / R) < NEAR_EPS || fabs(us[m] - C / R) < NEAR_EPS)",
+     "if (0)", ["near_threshold"]),
+    ("near_window_too_wide", "#define NEAR_EPS 1e-6", "#define NEAR_EPS 1e-5", ["near_threshold"]),
     ("same_uniform_for_sampling", "*u_sample = (double)(w[1] >> 8)", "*u_sample = (double)(w[0] >> 8)",
      ["chisq_v8_g4", "chisq_v16_g4", "chisq_v3_g1"]),
     ("topk_drops_ties", "keep[v] = logit_at(row, is_bf16, v) >= tau;",
