@@ -9,6 +9,8 @@
   captured in a HIP graph and replayed, each replay checked against the
   oracle.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -222,3 +224,88 @@ def test_round_in_hip_graph_replays():
         graph.replay()
         check_state(f"replay {k}")
         say(f"[graph] replay {k} matches the oracle")
+
+
+def test_sampling_round_in_hip_graph_replays():
+    """Sampling verify (the one-kernel path: workgroups waiting on published
+    statistics, counters and words left at zero) -> target commit -> draft
+    rollback, captured once and replayed three times with eager verify calls
+    on other inputs in between; every replay must equal the eager round
+    byte for byte, and the eager round the oracle."""
+    import torch
+    wl = W["b512_ragged_v262144_kv"].scaled(24, 20000)
+    x = synth.make_verify_inputs(wl)
+    x2 = synth.make_verify_inputs(dataclasses.replace(wl, data_seed=wl.data_seed + 1))
+    kv = synth.make_kv_inputs(wl)
+    dpool, table, dseq, nb = synth.make_draft_kv_inputs(wl, kv)
+    K, DK = wl.kv, wl.draft_kv
+    dev = "cuda"
+    desc = sd.make_verify_desc(wl.batch, wl.gamma_max, wl.vocab, temperature=wl.temperature,
+                               seed=wl.verify_seed)
+    ver = sd.Verifier(desc, dev)
+    tdesc = sd.make_kv_desc(wl.batch, wl.gamma_max, K.layers, K.kv_heads, K.head_dim,
+                            K.block_size, table.shape[1], nb)
+    ddesc = sd.make_kv_desc(wl.batch, wl.gamma_max, DK.layers, DK.kv_heads, DK.head_dim,
+                            DK.block_size, table.shape[1], nb)
+    ws_t = torch.zeros(sd.specdec_commit_kv_workspace_bytes(tdesc), dtype=torch.uint8, device=dev)
+    ws_d = torch.zeros(sd.specdec_commit_kv_workspace_bytes(ddesc), dtype=torch.uint8, device=dev)
+    t_dev, d_dev = to_dev(x["target"], dev), to_dev(x["draft"], dev)
+    tok_dev, gam_dev = to_dev(x["draft_tokens"], dev), to_dev(x["gamma"], dev)
+    t2, d2 = to_dev(x2["target"], dev), to_dev(x2["draft"], dev)
+    tok2, gam2 = to_dev(x2["draft_tokens"], dev), to_dev(x2["gamma"], dev)
+    tbl = to_dev(table, dev)
+    scratch = to_dev(kv.scratch, dev)
+    pool0, seq0 = to_dev(kv.pool, dev), to_dev(kv.seq_lens, dev)
+    dpool0, dseq0 = to_dev(dpool, dev), to_dev(dseq, dev)
+    pool, seq, dpool_d, dseq_d = pool0.clone(), seq0.clone(), dpool0.clone(), dseq0.clone()
+
+    def round_():
+        ver(t_dev, d_dev, tok_dev, gam_dev)
+        sd.specdec_commit_kv(tdesc, scratch, pool, tbl, ver.accept_count, gam_dev, None, seq,
+                             None, ws_t)
+        sd.specdec_rollback_kv(ddesc, dpool_d, tbl, ver.accept_count, gam_dev, dseq_d, None, ws_d)
+
+    def state():
+        torch.cuda.synchronize()
+        outs = {k: v.cpu().numpy().copy() for k, v in
+                dict(accept=ver.accept_count, num=ver.num_tokens, out=ver.out_tokens,
+                     p=ver.p_draft, q=ver.q_draft, r=ver.residual_mass, fl=ver.flags,
+                     seq=seq, dseq=dseq_d).items()}
+        outs["pool"] = pool.cpu().numpy().copy()
+        outs["dpool"] = dpool_d.cpu().numpy().copy()
+        return outs
+
+    def reset():
+        pool.copy_(pool0)
+        seq.copy_(seq0)
+        dpool_d.copy_(dpool0)
+        dseq_d.copy_(dseq0)
+        ver.accept_count.fill_(-9)
+        ver.out_tokens.fill_(-9)
+
+    say("[graph] eager sampling round")
+    round_()
+    want = state()
+    ref = oracle.verify(x["target"], x["draft"], x["draft_tokens"], x["gamma"],
+                        temperature=wl.temperature, seed=wl.verify_seed)
+    got = {"accept_count": want["accept"], "out_tokens": want["out"], "flags": want["fl"],
+           "num_tokens": want["num"], "p_draft": want["p"], "q_draft": want["q"],
+           "residual_mass": want["r"]}
+    errs, near = compare(ref, got, x["gamma"], False, None, "sampling round")
+    assert not errs, "\n".join(errs[:20])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    reset()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=s):
+        round_()
+    for k in range(3):
+        ver(t2, d2, tok2, gam2)          # eager work on other inputs between replays
+        reset()
+        torch.cuda.synchronize()
+        graph.replay()
+        now = state()
+        for name in want:
+            assert np.array_equal(now[name], want[name]), (k, name)
+        say(f"[graph] sampling replay {k} matches the eager round")
