@@ -429,7 +429,7 @@ def main() -> int:
                            "decision": {"avg_us": float(k2.mean()) * 1e6}}), **kernels),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic(f"{kname}__{wl0.name}") if not greedy else None,
+                     "traffic": measured_traffic(f"{kname}__{wl0.name}"),
                      "kernel": kname,
                      "kernel_avg_us": k1_avg * 1e6, "bytes_per_launch": alg_k1},
         "cpu_baseline": cpu,
