@@ -202,3 +202,16 @@ def test_ngram_descriptor_checks():
     empty = sd.make_ngram_desc(0, 100, 1, 4, 8)
     assert sd.lib().specdec_propose_ngram(ctypes.byref(empty), 16, 16, 16, 16, None, 256, 256,
                                           None) == sd.SPECDEC_OK
+
+
+def test_flag_and_status_constants_match_header():
+    """The binding's flag bits and status codes are the header's."""
+    text = open(os.path.join(ROOT, "include", "specdec.h")).read()
+    flags = dict(re.findall(r"#define\s+SPECDEC_FLAG_([A-Z_]+)\s+(0x[0-9a-fA-F]+)u", text))
+    assert flags, "no SPECDEC_FLAG_ definitions found"
+    for name, val in flags.items():
+        assert getattr(sd, "FLAG_" + name) == int(val, 16), name
+    assert len(set(int(v, 16) for v in flags.values())) == len(flags)  # distinct bits
+    codes = dict(re.findall(r"SPECDEC_(OK|ERR_[A-Z_]+)\s*=\s*(\d+)", text))
+    for name, val in codes.items():
+        assert getattr(sd, "SPECDEC_" + name) == int(val), name
