@@ -9,8 +9,10 @@ bonus draw.  Inputs are synthetic (seeded generator), resident in HBM before
 timing, and rotate over several independent input sets whose total exceeds the
 256 MB Infinity Cache, so every step reads its logits from HBM.
 
-Timing: W warmup steps, then exactly K steps replayed from a HIP graph,
-bracketed by torch.cuda.synchronize(); value = verified positions / second.
+Timing: W warmup steps, then exactly K steps replayed from HIP graphs (each
+holds whole passes over the input sets, at least 16 steps, so that the launch
+gap between replays is amortized), bracketed by torch.cuda.synchronize();
+value = verified positions / second.
 The roofline entry is the dominant kernel: the one-kernel sampling verify
 (statistics and decision workgroups in one launch), or the statistics
 kernel on the greedy and truncation paths (and with SPECDEC_FUSED=0).  It is
@@ -24,9 +26,10 @@ its own slice of the requests.
 
 Other workloads (--workload) print the same JSON line for that recipe; the
 ones with a paged KV cache time a whole round: verify, the target's commit
-and the draft cache's rollback (seq_lens restored from a copy before every
-commit and rollback so that each step touches the same window).  Their JSON
-line also lists each kernel's average time and algorithmic bandwidth.
+and the draft cache's rollback.  Each step of a graph has its own cache
+lengths, all restored by one small copy at the graph's start, so that every
+step commits into the same window.  Their JSON line also lists each kernel's average time
+and algorithmic bandwidth.
 """
 from __future__ import annotations
 
@@ -45,6 +48,67 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E
 METRIC = "verified positions/sec + achieved HBM GB/s (% of peak), B=64 γ=4 V=128256"
+
+
+def steps_per_graph(sets: int, at_least: int) -> int:
+    """Whole passes over the input sets, at least `at_least` steps.  A graph
+    replay starts ~9 us after the previous one ends and its first kernel runs a
+    few us longer, so a graph holds many steps to keep that out of the
+    per-step time."""
+    return sets * max(1, -(-at_least // sets))
+
+
+class GraphSteps:
+    """Runs exactly n steps.  enqueue(n) puts steps 0..n-1 on the current stream
+    (step i reads input set i % sets); it is captured once per length used: a
+    graph of `per` steps replayed n // per times, then one of the n % per
+    remaining steps.  Each graph is replayed three times after capture, and each
+    replay must reproduce the eager outputs of its last step (check(i)); if one
+    does not, every run launches eagerly and `graphed` is False."""
+
+    def __init__(self, enqueue, per: int, check, use_graphs: bool = True):
+        self.enqueue, self.per, self.check = enqueue, per, check
+        self.graphs = {}
+        self.graphed = use_graphs
+
+    def _capture(self, n: int) -> bool:
+        import torch
+        if n == 0 or n in self.graphs:
+            return True
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self.enqueue(n)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.enqueue(n)
+        for _ in range(3):
+            g.replay()
+            torch.cuda.synchronize()
+            if not self.check(n - 1):
+                return False
+        self.graphs[n] = g
+        return True
+
+    def prepare(self, *counts: int) -> None:
+        """Capture and check every graph the given step counts need."""
+        for n in counts:
+            for size in ((self.per if n >= self.per else 0), n % self.per):
+                if self.graphed and not self._capture(size):
+                    log(f"graph replay of {size} steps differs from eager launches; "
+                        "timing eager launches")
+                    self.graphed = False
+
+    def run(self, n: int) -> None:
+        full, rem = divmod(n, self.per)
+        for size, count in ((self.per, full), (rem, 1 if rem else 0)):
+            for _ in range(count):
+                if self.graphed:
+                    self.graphs[size].replay()
+                else:
+                    self.enqueue(size)
 
 
 def log(msg: str) -> None:
@@ -120,7 +184,10 @@ def parse():
     ap.add_argument("--pmc-copy-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a dispatch of "
                          "known size to calibrate FETCH_SIZE / WRITE_SIZE counters)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("--steps must be at least 1 and --warmup at least 0")
+    return args
 
 
 def main() -> int:
@@ -170,6 +237,7 @@ def main() -> int:
              "gamma": torch.from_numpy(x["gamma"]).to(dev)}
         dev_in.append(d)
         log(f"  input set {k} uploaded")
+    per = steps_per_graph(sets, 16)
     kv = None
     if wl0.kv is not None:
         kvin = synth.make_kv_inputs(wl0)
@@ -180,8 +248,6 @@ def main() -> int:
               "scratch": torch.from_numpy(kvin.scratch.view(np.int16)).to(dev),
               "pool": torch.from_numpy(kvin.pool.view(np.int16)).to(dev),
               "table": torch.from_numpy(kvin.block_table).to(dev),
-              "seq0": torch.from_numpy(kvin.seq_lens).to(dev),
-              "seq": torch.from_numpy(kvin.seq_lens.copy()).to(dev),
               "ws": torch.zeros(sd.specdec_commit_kv_workspace_bytes(kdesc), dtype=torch.uint8,
                                 device=dev)}
         log(f"  paged KV pool {kvin.pool.nbytes / 1e6:.1f} MB uploaded")
@@ -189,9 +255,13 @@ def main() -> int:
         DK = wl0.draft_kv
         ddesc = sd.make_kv_desc(wl0.batch, wl0.gamma_max, DK.layers, DK.kv_heads, DK.head_dim,
                                 DK.block_size, kvin.block_table.shape[1], nb)
+        # cache lengths per step of a graph: [step][target | draft][B], all
+        # restored by one copy at the graph's start, so that every step
+        # commits into the same window
+        seqs0 = np.stack([np.stack([kvin.seq_lens, dseq])] * per).astype(np.int32)
         kv.update({"ddesc": ddesc, "dpool": torch.from_numpy(dpool.view(np.int16)).to(dev),
-                   "dseq0": torch.from_numpy(dseq).to(dev),
-                   "dseq": torch.from_numpy(dseq.copy()).to(dev),
+                   "seqs0": torch.from_numpy(seqs0).to(dev),
+                   "seqs": torch.from_numpy(seqs0.copy()).to(dev),
                    "dws": torch.zeros(sd.specdec_commit_kv_workspace_bytes(ddesc),
                                       dtype=torch.uint8, device=dev)})
         log(f"  draft KV pool {dpool.nbytes / 1e6:.1f} MB uploaded")
@@ -201,72 +271,53 @@ def main() -> int:
                                seed=wl0.verify_seed)
     ver = sd.Verifier(desc, dev)
 
-    def commit(k: int) -> None:
-        kv["seq"].copy_(kv["seq0"])
+    # step i reads input set i % sets and commits with the cache lengths of slot i
+    def commit(i: int) -> None:
         sd.specdec_commit_kv(kv["desc"], kv["scratch"], kv["pool"], kv["table"],
-                             ver.accept_count, dev_in[k]["gamma"], None, kv["seq"], None, kv["ws"])
+                             ver.accept_count, dev_in[i % sets]["gamma"], None, kv["seqs"][i, 0],
+                             None, kv["ws"])
 
-    def rollback(k: int) -> None:
-        kv["dseq"].copy_(kv["dseq0"])
+    def rollback(i: int) -> None:
         sd.specdec_rollback_kv(kv["ddesc"], kv["dpool"], kv["table"], ver.accept_count,
-                               dev_in[k]["gamma"], kv["dseq"], None, kv["dws"])
+                               dev_in[i % sets]["gamma"], kv["seqs"][i, 1], None, kv["dws"])
 
-    def step(k: int) -> None:
-        d = dev_in[k]
+    def reset() -> None:
+        if kv is not None:
+            kv["seqs"].copy_(kv["seqs0"])
+
+    def step(i: int) -> None:
+        d = dev_in[i % sets]
         ver(d["target"], d["draft"], d["tokens"], d["gamma"])
         if kv is not None:
-            commit(k)
-            rollback(k)
+            commit(i)
+            rollback(i)
 
-    # ---- eager reference outputs, then the graph of one pass over the sets
+    def enqueue(n: int) -> None:
+        reset()
+        for i in range(n):
+            step(i)
+
+    # ---- eager reference outputs, then the graphs
     eager = []
     names = ("accept_count", "out_tokens", "p_draft", "q_draft", "residual_mass", "flags")
+    reset()
     for k in range(sets):
         step(k)
         torch.cuda.synchronize()
         eager.append({n: getattr(ver, n).clone() for n in names})
     torch.cuda.synchronize()
 
-    graph = None
-    if not args.eager:
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            step(0)
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for k in range(sets):
-                step(k)
-        # every replay must reproduce the eager outputs of the last set
-        for _ in range(3):
-            graph.replay()
-            torch.cuda.synchronize()
-            for n in ("accept_count", "out_tokens"):
-                if not torch.equal(getattr(ver, n), eager[-1][n]):
-                    log(f"graph replay differs from eager launches in {n}; timing eager launches")
-                    graph = None
-                    break
-            if graph is None:
-                break
+    def check(i: int) -> bool:
+        return all(torch.equal(getattr(ver, n), eager[i % sets][n])
+                   for n in ("accept_count", "out_tokens"))
 
-    reps = max(1, args.steps // sets)
-    steps = reps * sets
-    wreps = max(1, args.warmup // sets)
-
-    def run(n_reps: int) -> None:
-        for _ in range(n_reps):
-            if graph is not None:
-                graph.replay()
-            else:
-                for k in range(sets):
-                    step(k)
-
-    run(wreps)
+    runner = GraphSteps(enqueue, per, check, use_graphs=not args.eager)
+    runner.prepare(args.warmup, args.steps)
+    steps = args.steps
+    runner.run(args.warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    run(reps)
+    runner.run(steps)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     sec_per_step = (t1 - t0) / steps
@@ -300,16 +351,13 @@ def main() -> int:
             k = j % sets
             d = dev_in[k]
             ver(d["target"], d["draft"], d["tokens"], d["gamma"])
-            kv["seq"].copy_(kv["seq0"])
-            kv["dseq"].copy_(kv["dseq0"])
+            reset()  # step k below commits with slot k's restored lengths
             e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
             e[0].record()
-            sd.specdec_commit_kv(kv["desc"], kv["scratch"], kv["pool"], kv["table"],
-                                 ver.accept_count, d["gamma"], None, kv["seq"], None, kv["ws"])
+            commit(k)
             e[1].record()
             e[2].record()
-            sd.specdec_rollback_kv(kv["ddesc"], kv["dpool"], kv["table"], ver.accept_count,
-                                   d["gamma"], kv["dseq"], None, kv["dws"])
+            rollback(k)
             e[3].record()
             tc.append(e)
         torch.cuda.synchronize()
@@ -345,13 +393,13 @@ def main() -> int:
     kname = ("k_stats_greedy" if greedy else "k_truncate" if trunc else
              "k_verify_fused" if fused else "k_stats_sample")
     if fused:
-        log(f"step {sec_per_step * 1e6:.2f} us ({'graph' if graph is not None else 'eager'}); "
+        log(f"step {sec_per_step * 1e6:.2f} us ({'graph' if runner.graphed else 'eager'}); "
             f"one-kernel verify avg {k1_avg * 1e6:.2f} us (p10 {np.percentile(k1, 10) * 1e6:.2f}, "
             f"p90 {np.percentile(k1, 90) * 1e6:.2f})")
         log(f"one-kernel verify {achieved:.1f} GB/s = {100 * achieved / HBM_PEAK_GBPS:.1f}% of "
             f"{HBM_PEAK_GBPS:.0f} GB/s; whole step {alg_k1 / sec_per_step / 1e9:.1f} GB/s")
     else:
-        log(f"step {sec_per_step * 1e6:.2f} us ({'graph' if graph is not None else 'eager'}); "
+        log(f"step {sec_per_step * 1e6:.2f} us ({'graph' if runner.graphed else 'eager'}); "
             f"stats kernel avg {k1_avg * 1e6:.2f} us (p10 {np.percentile(k1, 10) * 1e6:.2f}, "
             f"p90 {np.percentile(k1, 90) * 1e6:.2f}); decision kernel avg {k2.mean() * 1e6:.2f} us")
         log(f"stats kernel {achieved:.1f} GB/s = {100 * achieved / HBM_PEAK_GBPS:.1f}% of "
@@ -406,7 +454,7 @@ def main() -> int:
         "unit": "positions/s",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": wreps * sets,
+        "warmup": args.warmup,
         "ms_per_step": sec_per_step * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
@@ -417,8 +465,8 @@ def main() -> int:
                    "logits": wl0.dtype, "mode": wl0.mode, "temperature": wl0.temperature,
                    "top_k": wl0.top_k, "top_p": wl0.top_p, "kv_commit": wl0.kv is not None,
                    "draft_rollback": wl0.draft_kv is not None,
-                   "rotating_input_sets": sets,
-                   "launch": "hipgraph" if graph is not None else "eager",
+                   "rotating_input_sets": sets, "steps_per_graph": per,
+                   "launch": "hipgraph" if runner.graphed else "eager",
                    "committed_tokens_per_s": committed / sec_per_step,
                    "step_GBps": alg_k1 / sec_per_step / 1e9},
         "kernels": dict(({"verify_fused": {"avg_us": k1_avg * 1e6, "bytes_per_launch": alg_k1,
@@ -467,8 +515,10 @@ def bench_tree(args, wl0) -> int:
     scratch = torch.from_numpy(kvin.scratch.view(np.int16)).to(dev)
     pool = torch.from_numpy(kvin.pool.view(np.int16)).to(dev)
     table = torch.from_numpy(kvin.block_table).to(dev)
-    seq0 = torch.from_numpy(kvin.seq_lens).to(dev)
-    seq = seq0.clone()
+    # cache lengths per step of a graph, all restored by one copy at its start
+    per = steps_per_graph(sets, 16)
+    seqs0 = torch.from_numpy(np.stack([kvin.seq_lens] * per).astype(np.int32)).to(dev)
+    seqs = seqs0.clone()
     depth_d = torch.from_numpy(depth).to(dev)
     kws = torch.zeros(sd.specdec_commit_kv_workspace_bytes(kdesc), dtype=torch.uint8, device=dev)
     tdesc = sd.make_tree_desc(B, N, V, bf16=wl0.dtype == "bf16")
@@ -481,7 +531,7 @@ def bench_tree(args, wl0) -> int:
     flags = torch.zeros(B, dtype=i32, device=dev)
 
     def verify(k, ev=None):
-        d = dev_in[k]
+        d = dev_in[k % sets]
         if ev is None:
             sd.specdec_verify_tree(tdesc, d["target"], d["tokens"], d["parents"], d["num_nodes"],
                                    None, acc, ntok, out, path, flags, ws)
@@ -490,44 +540,38 @@ def bench_tree(args, wl0) -> int:
                                             d["num_nodes"], None, acc, ntok, out, path, flags, ws,
                                             ev)
 
-    def commit():
-        seq.copy_(seq0)
-        sd.specdec_commit_kv(kdesc, scratch, pool, table, acc, depth_d, path, seq, None, kws)
+    # step i reads input set i % sets and commits with the cache lengths of slot i
+    def commit(i):
+        sd.specdec_commit_kv(kdesc, scratch, pool, table, acc, depth_d, path, seqs[i], None, kws)
 
-    def step(k):
-        verify(k)
-        commit()
+    def step(i):
+        verify(i)
+        commit(i)
+
+    def enqueue(n):
+        seqs.copy_(seqs0)
+        for i in range(n):
+            step(i)
 
     eager = []
+    seqs.copy_(seqs0)
     for k in range(sets):
         step(k)
         torch.cuda.synchronize()
         eager.append((acc.clone(), out.clone()))
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        step(0)
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for k in range(sets):
-            step(k)
-    for _ in range(3):
-        graph.replay()
-        torch.cuda.synchronize()
-        if not (torch.equal(acc, eager[-1][0]) and torch.equal(out, eager[-1][1])):
-            log("graph replay differs from eager launches")
-            return 1
-    reps = max(1, args.steps // sets)
-    steps = reps * sets
-    wreps = max(1, args.warmup // sets)
-    for _ in range(wreps):
-        graph.replay()
+
+    def check(i):
+        return torch.equal(acc, eager[i % sets][0]) and torch.equal(out, eager[i % sets][1])
+
+    runner = GraphSteps(enqueue, per, check)
+    runner.prepare(args.warmup, args.steps)
+    if not runner.graphed:
+        return 1
+    steps = args.steps
+    runner.run(args.warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(reps):
-        graph.replay()
+    runner.run(steps)
     torch.cuda.synchronize()
     sec_per_step = (time.perf_counter() - t0) / steps
 
@@ -537,9 +581,10 @@ def bench_tree(args, wl0) -> int:
     tc = []
     for j in range(n_prof):
         verify(j % sets, ev.handles[4 * j:4 * j + 4])
+        seqs.copy_(seqs0)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        commit()
+        commit(j % sets)
         e1.record()
         tc.append((e0, e1))
     torch.cuda.synchronize()
@@ -591,12 +636,12 @@ def bench_tree(args, wl0) -> int:
         "metric": f"verified tree nodes/sec ({wl0.name})",
         "value": B * (N - 1) / sec_per_step,
         "unit": "tree nodes/s",
-        "n_gpus": 1, "steps": steps, "warmup": wreps * sets, "ms_per_step": sec_per_step * 1e3,
+        "n_gpus": 1, "steps": steps, "warmup": args.warmup, "ms_per_step": sec_per_step * 1e3,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl0.name, "batch": B, "tree_nodes": N, "vocab": V,
                    "logits": wl0.dtype, "mode": "greedy tree", "kv_commit": True,
-                   "rotating_input_sets": sets, "launch": "hipgraph",
+                   "rotating_input_sets": sets, "steps_per_graph": per, "launch": "hipgraph",
                    "committed_tokens_per_s": B * (depth_mean + 1) / sec_per_step},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "k_stats_greedy",
@@ -639,39 +684,34 @@ def bench_ngram(args, wl0) -> int:
     nd = torch.empty(B, dtype=torch.int32, device=dev)
     ml = torch.empty(B, dtype=torch.int32, device=dev)
 
-    def step(k):
+    def step(i):  # step i reads input set i % sets
+        k = i % sets
         sd.specdec_propose_ngram(desc, dev_in[k]["history"], dev_in[k]["hist_len"], toks, nd, ml,
                                  ws)
+
+    def enqueue(n):
+        for i in range(n):
+            step(i)
 
     eager = []
     for k in range(sets):
         step(k)
         torch.cuda.synchronize()
-        eager.append(nd.clone())
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        step(0)
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for k in range(sets):
-            step(k)
-    graph.replay()
-    torch.cuda.synchronize()
-    if not torch.equal(nd, eager[-1]):
-        log("graph replay differs from eager launches")
+        eager.append((toks.clone(), nd.clone()))
+
+    def check(i):
+        return torch.equal(toks, eager[i % sets][0]) and torch.equal(nd, eager[i % sets][1])
+
+    per = steps_per_graph(sets, 64)
+    runner = GraphSteps(enqueue, per, check)
+    runner.prepare(args.warmup, args.steps)
+    if not runner.graphed:
         return 1
-    reps = max(1, args.steps // sets)
-    steps = reps * sets
-    wreps = max(1, args.warmup // sets)
-    for _ in range(wreps):
-        graph.replay()
+    steps = args.steps
+    runner.run(args.warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(reps):
-        graph.replay()
+    runner.run(steps)
     torch.cuda.synchronize()
     sec_per_step = (time.perf_counter() - t0) / steps
     # kernel time alone: events around each launch on the launching stream
@@ -690,7 +730,7 @@ def bench_ngram(args, wl0) -> int:
     # kernel duration plus the dispatch gap, the events' also the event overhead
     k_us = min(float(kt.mean()), sec_per_step)
     achieved = alg / k_us / 1e9
-    proposed = float(np.mean([e.sum().item() for e in eager]))
+    proposed = float(np.mean([e[1].sum().item() for e in eager]))
     log(f"step {sec_per_step * 1e6:.2f} us (graph); propose kernel avg {kt.mean() * 1e6:.2f} us "
         f"(events); {achieved:.1f} GB/s = {100 * achieved / HBM_PEAK_GBPS:.1f}% of "
         f"{HBM_PEAK_GBPS:.0f} GB/s; {proposed:.0f} tokens proposed per step")
@@ -717,11 +757,12 @@ def bench_ngram(args, wl0) -> int:
                              f"repeating its slice for {t_a:.1f} s (at least {passes} passes)"}
     res = {
         "metric": f"proposing requests/sec ({wl0.name})", "value": B / sec_per_step,
-        "unit": "requests/s", "n_gpus": 1, "steps": steps, "warmup": wreps * sets,
+        "unit": "requests/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
         "ms_per_step": sec_per_step * 1e3, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "int32", "data": "synthetic",
         "config": {"workload": wl0.name, "batch": B, "max_len": Lmax, "n_min": n_min,
                    "n_max": n_max, "gamma_max": G, "rotating_input_sets": sets,
+                   "steps_per_graph": per,
                    "launch": "hipgraph", "proposed_tokens_per_s": proposed / sec_per_step},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
