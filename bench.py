@@ -644,7 +644,9 @@ def bench_tree(args, wl0) -> int:
                    "rotating_input_sets": sets, "steps_per_graph": per, "launch": "hipgraph",
                    "committed_tokens_per_s": B * (depth_mean + 1) / sec_per_step},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None, "kernel": "k_stats_greedy",
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(f"k_stats_greedy__{wl0.name}"),
+                     "kernel": "k_stats_greedy",
                      "kernel_avg_us": float(k1.mean()) * 1e6, "bytes_per_launch": alg_k1},
         "kernels": {"stats": {"avg_us": float(k1.mean()) * 1e6, "bytes_per_launch": alg_k1,
                               "GBps": achieved, "frac": achieved / HBM_PEAK_GBPS},
@@ -729,6 +731,7 @@ def bench_ngram(args, wl0) -> int:
     # the step is this one kernel: its graph-replayed time per launch is the
     # kernel duration plus the dispatch gap, the events' also the event overhead
     k_us = min(float(kt.mean()), sec_per_step)
+    kname = "k_propose_ngram_whole" if Lmax <= 8192 else "k_propose_ngram"
     achieved = alg / k_us / 1e9
     proposed = float(np.mean([e[1].sum().item() for e in eager]))
     log(f"step {sec_per_step * 1e6:.2f} us (graph); propose kernel avg {kt.mean() * 1e6:.2f} us "
@@ -765,8 +768,9 @@ def bench_ngram(args, wl0) -> int:
                    "steps_per_graph": per,
                    "launch": "hipgraph", "proposed_tokens_per_s": proposed / sec_per_step},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "kernel": "k_propose_ngram_whole" if Lmax <= 8192 else "k_propose_ngram",
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(f"{kname}__{wl0.name}"),
+                     "kernel": kname,
                      "kernel_avg_us": k_us * 1e6,
                      "bytes_per_launch": alg},
         "cpu_baseline": cpu,

@@ -39,7 +39,6 @@
 
 #include <hip/hip_ext.h>
 
-#include <type_traits>
 
 namespace specdec {
 namespace {
@@ -176,38 +175,52 @@ __device__ __forceinline__ uint4 load_raw(const void* rp, int e, int V) {
     }
 }
 
-// One pass over a whole row in tiles of 256 lanes x kUnroll 16-byte vectors
-// (the next tile's loads in flight while the current one is visited), then
-// a clipped tail filled with -inf; f(r, t0, full) sees a lane's kUnroll raw
-// vectors of the tile at t0 (vector u holds tokens t0 + (u * 256 + lane) * N
-// ...); `full` is std::true_type for tiles wholly inside the row.
+// One pass over a whole row in tiles of 256 lanes x kUnroll 16-byte vectors;
+// f(r, t0) sees a lane's kUnroll raw vectors of the tile at t0 (vector u
+// holds tokens t0 + (u * 256 + lane) * N ...), -inf past V.  VEC: every
+// tile, the clipped last one included, goes through one pipeline (the next
+// tile's loads in flight while the current one is visited) with addresses
+// clamped into the row, so each byte of the row is fetched once; the last
+// tile's vectors past V (wholly past it: V is a multiple of N) become -inf
+// before its visit.
 template <bool BF16, bool VEC, class F>
 __device__ __forceinline__ void stream_tiles(const void* rp, int V, F&& f) {
     constexpr int N = Vec<BF16>::N;
     constexpr int TILE = kThreads * N * kUnroll;
     const int t = threadIdx.x;
-    const int full_end = VEC ? (V / TILE) * TILE : 0;
-    int t0 = 0;
-    if (t0 < full_end) {
+    if constexpr (VEC) {
+        const int ntiles = (V + TILE - 1) / TILE;
+        auto load_tile = [&](uint4 (&r)[kUnroll], int t0) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+                r[u] = load16_stream<BF16>(rp, min(t0 + (u * kThreads + t) * N, V - N));
+        };
         uint4 cur[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) cur[u] = load16_stream<BF16>(rp, t0 + (u * kThreads + t) * N);
-        for (; t0 < full_end; t0 += TILE) {
-            const int tn = min(t0 + TILE, full_end - TILE);  // re-loads the last tile once: no branch
+        load_tile(cur, 0);
+        for (int k = 0; k < ntiles; ++k) {
+            const int t0 = k * TILE;
             uint4 nxt[kUnroll];
+            if (k + 1 < ntiles) load_tile(nxt, t0 + TILE);
+            if (t0 + TILE > V) {
+                const uint32_t ninf = BF16 ? 0xff80ff80u : 0xff800000u;
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) nxt[u] = load16_stream<BF16>(rp, tn + (u * kThreads + t) * N);
-            f(cur, t0, std::true_type{});
+                for (int u = 0; u < kUnroll; ++u)
+                    if (t0 + (u * kThreads + t) * N >= V) cur[u] = make_uint4(ninf, ninf, ninf, ninf);
+            }
+            f(cur, t0);
+            if (k + 1 < ntiles) {
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) cur[u] = nxt[u];
+                for (int u = 0; u < kUnroll; ++u) cur[u] = nxt[u];
+            }
         }
-    }
-    for (; t0 < V; t0 += TILE) {
-        uint4 r[kUnroll];
+    } else {
+        for (int t0 = 0; t0 < V; t0 += TILE) {
+            uint4 r[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-            r[u] = narrow<BF16>(load_vec<BF16, VEC>(rp, t0 + (u * kThreads + t) * N, V, neg_inf()));
-        f(r, t0, std::false_type{});
+            for (int u = 0; u < kUnroll; ++u)
+                r[u] = narrow<BF16>(load_vec<BF16, false>(rp, t0 + (u * kThreads + t) * N, V, neg_inf()));
+            f(r, t0);
+        }
     }
 }
 
@@ -322,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void k_trunc_select(VerifyParams P) {
     float v1 = neg_inf(), v2 = neg_inf(), v3 = neg_inf(), v4 = neg_inf();
     int t1 = -1, t2 = -1, t3 = -1, t4 = -1;
     uint64_t bad = 0;  // wave-uniform: a NaN was seen
-    auto visit = [&](const uint4 (&r)[kUnroll], int t0, auto) {
+    auto visit = [&](const uint4 (&r)[kUnroll], int t0) {
         float m = neg_inf();  // the tail is filled with -inf; NaNs are skipped
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
@@ -436,9 +449,13 @@ __global__ __launch_bounds__(kThreads) void k_trunc_select(VerifyParams P) {
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
             if (j >= nt) break;
-            const int base = (tl[j] >= 0 ? tl[j] : 0) * TILE;
+            // only lanes with a tile to re-read load (the others' loads are
+            // masked off; their address stays inside the row all the same)
+            const int base = max(tl[j], 0) * TILE;
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) rv[j][u] = load_raw<BF16, VEC>(rp, base + (u * kThreads + t) * N, V);
+            for (int u = 0; u < kUnroll; ++u)
+                rv[j][u] = tl[j] >= 0 ? load_raw<BF16, VEC>(rp, base + (u * kThreads + t) * N, V)
+                                      : make_uint4(0u, 0u, 0u, 0u);
         }
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
@@ -463,10 +480,12 @@ __global__ __launch_bounds__(kThreads) void k_trunc_select(VerifyParams P) {
             const int lane = t - l + L;  // the heavy lane's thread index
             for (int tile0 = 0; tile0 < ntiles; tile0 += kWave) {
                 const int tile = tile0 + l;
-                const int base = (tile < ntiles ? tile : 0) * TILE;
+                const int base = min(tile, ntiles - 1) * TILE;
                 uint4 v[kUnroll];
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u) v[u] = load_raw<BF16, VEC>(rp, base + (u * kThreads + lane) * N, V);
+                for (int u = 0; u < kUnroll; ++u)
+                    v[u] = tile < ntiles ? load_raw<BF16, VEC>(rp, base + (u * kThreads + lane) * N, V)
+                                         : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
