@@ -45,6 +45,7 @@ namespace {
 
 constexpr int kSelCap = 2048;                 // LDS candidate slots per row
 constexpr int kWaveCap = kSelCap / kWaves;   // each wave's region of them
+static_assert(kTruncCap <= kSelCap, "a top-p-only row fits the candidate buffer whole");
 constexpr uint32_t kRowOverflow = 1u << 16;   // record header: kept set clipped
 constexpr uint32_t kRowNonfinite = 1u << 17;  // record header: NaN or +inf in the row
 
@@ -535,9 +536,11 @@ __global__ __launch_bounds__(kThreads) void k_trunc_select(VerifyParams P) {
         // Overflow (heavy ties, or very flat rows with a large k): the exact
         // k-th largest value by a bitwise search on ordered keys (largest key
         // t with count(key >= t) >= k), each step one read of the row, then
-        // the buffer is refilled with the elements at or above it.
+        // the buffer is refilled with the elements at or above it.  Without
+        // an effective top-k every element is a candidate (key 0 keeps all
+        // but NaNs; such rows have V <= kTruncCap <= kSelCap).
         uint32_t key = 0;
-        for (int bit = 31; bit >= 0; --bit) {
+        for (int bit = 31; use_k && bit >= 0; --bit) {
             const uint32_t trial = key | (1u << bit);
             int cnt = 0;
             for (int e0 = t * N; e0 < V; e0 += kThreads * N) {
