@@ -19,6 +19,7 @@ constexpr int kMassGroupWide = 4;    // sampling-pass chunks loaded at once (sho
 constexpr int kMassGroupChunks = 2;  // ... and per double-buffered group (long shares)
 constexpr int kSerialParts = 16;  // at most this many partials per row: one lane combines them
 constexpr int kNucCap = 1024;     // kept tokens recorded per row (and the top-k limit)
+constexpr size_t kResidCachedBytes = size_t{64} << 20;  // see verify_impl: residual loads cached up to this
 
 
 
@@ -54,6 +55,7 @@ struct VerifyParams {
     uint32_t key0, key1, round;
     int eos;            // end-of-sequence token, -1: none
     bool point;         // sampling with point-mass drafts: no draft rows, q_i = delta(d_i)
+    bool resid_cached;  // one-kernel sampling pass: ordinary (cached) loads for the residual / bonus rows
     // truncation (top-k / top-p) mode
     int top_k;          // 0 or >= V: no top-k
     float top_p;        // 1: no top-p

@@ -183,6 +183,8 @@ def _env(**kv):
 
 ONE_KERNEL_CASES = [
     ("headline B=16", lambda: W[synth.HEADLINE].scaled(16, 128256), True),
+    # B x 2 x V x 2 bytes above 64 MiB: the streaming-load variant of the residual pass
+    ("headline B=140", lambda: W[synth.HEADLINE].scaled(140, 128256), True),
     ("ragged B=40 V=3001", lambda: W["b512_ragged_v262144_kv"].scaled(40, 3001), True),
     ("fp32 B=8", lambda: W["b8_g4_v32000_f32"], True),
     ("point-mass drafts B=24", lambda: W[synth.HEADLINE].scaled(24, 20000), False),
