@@ -390,7 +390,7 @@ def main() -> int:
     trunc = bool(wl0.top_k) or wl0.top_p < 1.0
     # sampling without truncation runs as one kernel (statistics + decision)
     fused = not greedy and not trunc and os.environ.get("SPECDEC_FUSED", "1")[:1] != "0"
-    kname = ("k_stats_greedy" if greedy else "k_truncate" if trunc else
+    kname = ("k_stats_greedy" if greedy else "k_trunc_select" if trunc else
              "k_verify_fused" if fused else "k_stats_sample")
     if fused:
         log(f"step {sec_per_step * 1e6:.2f} us ({'graph' if runner.graphed else 'eager'}); "
