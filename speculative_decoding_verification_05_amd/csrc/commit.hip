@@ -68,6 +68,34 @@ __global__ __launch_bounds__(kThreads) void k_commit(CommitParams P) {
     const int64_t lb = pos / P.BS;
     const int off = static_cast<int>(pos % P.BS);
     const int32_t phys = (work && lb < P.maxb) ? P.table[static_cast<size_t>(b) * P.maxb + lb] : -1;
+    const bool keep = work && !rollback && j <= m;
+    const size_t runs = static_cast<size_t>(P.L) * 2;
+    const int slot = keep ? mapped : 0;
+    const bool slot_ok = slot >= 0 && slot < P.S;
+    const uint16_t* src = P.scratch ? P.scratch + (static_cast<size_t>(b) * P.S + (slot_ok ? slot : 0)) * runs * P.hd
+                                    : nullptr;
+    // VEC: kCopyUnroll 16-byte vectors per lane per group, all loads of a
+    // group issued before its stores.  The first group's source loads go out
+    // together with the block-table load above (they depend only on the
+    // slot), so the copy does not wait for the physical block first.
+    const int nv = P.hd / 8;  // 16-byte vectors per run
+    const int total = static_cast<int>(runs) * nv;
+    const bool load_src = keep && slot_ok;
+    uint4 v[kCopyUnroll];
+    auto load_group = [&](int e0) {
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+            const int e = e0 + u * kThreads;
+            v[u] = make_uint4(0u, 0u, 0u, 0u);
+            if (load_src && e < total) {
+                const int run = e / nv, w = e - run * nv;
+                const u32x4_t x = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4_t*>(src + static_cast<size_t>(run) * P.hd + w * 8));
+                v[u] = make_uint4(x.x, x.y, x.z, x.w);
+            }
+        }
+    };
+    if (VEC) load_group(threadIdx.x);
     // The new length is written by the last of the window's g+1 workgroups to
     // arrive.  Every wave of each of them has read t before the barrier, so
     // none can see an advanced length: no fence is needed, only the
@@ -81,31 +109,11 @@ __global__ __launch_bounds__(kThreads) void k_commit(CommitParams P) {
         if (phys < 0 || phys >= P.NB) {
             bad = true;
         } else {
-            const bool keep = !rollback && j <= m;
-            const size_t runs = static_cast<size_t>(P.L) * 2;
-            const int slot = keep ? mapped : 0;
-            const uint16_t* src = keep ? P.scratch + (static_cast<size_t>(b) * P.S + slot) * runs * P.hd
-                                       : nullptr;
-            if (slot < 0 || slot >= P.S) {
+            if (!slot_ok) {
                 bad = true;
             } else if (VEC) {
-                // kCopyUnroll vectors per lane in flight: all loads of a group
-                // are issued before its stores
-                const int nv = P.hd / 8;  // 16-byte vectors per run
-                const int total = static_cast<int>(runs) * nv;
                 for (int e0 = threadIdx.x; e0 < total; e0 += kThreads * kCopyUnroll) {
-                    uint4 v[kCopyUnroll];
-#pragma unroll
-                    for (int u = 0; u < kCopyUnroll; ++u) {
-                        const int e = e0 + u * kThreads;
-                        v[u] = make_uint4(0u, 0u, 0u, 0u);
-                        if (keep && e < total) {
-                            const int run = e / nv, w = e - run * nv;
-                            const u32x4_t x = __builtin_nontemporal_load(
-                                reinterpret_cast<const u32x4_t*>(src + static_cast<size_t>(run) * P.hd + w * 8));
-                            v[u] = make_uint4(x.x, x.y, x.z, x.w);
-                        }
-                    }
+                    if (e0 != static_cast<int>(threadIdx.x)) load_group(e0);
 #pragma unroll
                     for (int u = 0; u < kCopyUnroll; ++u) {
                         const int e = e0 + u * kThreads;
@@ -117,8 +125,8 @@ __global__ __launch_bounds__(kThreads) void k_commit(CommitParams P) {
                     }
                 }
             } else {
-                const size_t total = runs * P.hd;
-                for (size_t e = threadIdx.x; e < total; e += kThreads) {
+                const size_t n_el = runs * P.hd;
+                for (size_t e = threadIdx.x; e < n_el; e += kThreads) {
                     const size_t run = e / P.hd, w = e % P.hd;
                     uint16_t* dst = P.pool + ((run * P.NB + phys) * P.BS + off) * P.hd + w;
                     *dst = keep ? src[run * P.hd + w] : static_cast<uint16_t>(0);
