@@ -102,8 +102,8 @@ typedef struct specdec_verify_desc {
 } specdec_verify_desc_t;
 
 /* Bytes of device workspace specdec_verify needs for `desc` (0 on a bad
- * descriptor).  The workspace holds per-chunk partial statistics and
- * per-request arrival counters.  Its counter words must be zero before the
+ * descriptor).  The workspace holds per-chunk partial statistics, per-request
+ * arrival counters and hand-off words.  Its counter words must be zero before the
  * first call that uses it (allocate it zero-filled, or run
  * specdec_workspace_clear once); every completed call leaves them zero again,
  * so one workspace serves any number of ordered calls with one descriptor.

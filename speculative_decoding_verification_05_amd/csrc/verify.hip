@@ -136,17 +136,17 @@ __device__ float lane_mass_elements(const MassRows& a, int lo, int hi) {
     return acc;
 }
 
-// Masses of chunks [k0, k1) published to csum[k].  Loads go in groups of
-// GROUP chunks, into two register sets in turn (no copies between them), so
-// the next group's loads are in flight while the current group is reduced.
-// Nothing inside the walk waits on other waves or on memory writes: each
-// chunk's wave sums go to LDS (scr: kWaves floats per chunk), and after one
-// barrier thread 0 adds them in wave order and publishes the whole batch at
-// once (batches of 1024 / kWaves chunks).  Returns the OR of the publish()
-// results (the dependency for arrive_last).
-template <bool BF16, bool VEC, int GROUP, bool CACHED>
-__device__ uint32_t mass_chunks(const MassRows& a, int k0, int k1, int chunk2, int V, uint32_t* csum,
-                                float* scr) {
+// Masses of chunks [k0, k1), handed to emit(k, mass) by thread 0.  Loads go
+// in groups of GROUP chunks, into two register sets in turn (no copies
+// between them), so the next group's loads are in flight while the current
+// group is reduced.  Nothing inside the walk waits on other waves or on
+// memory writes: each chunk's wave sums go to LDS (scr: kWaves floats per
+// chunk), and after one barrier thread 0 adds them in wave order and emits
+// the whole batch at once (batches of 1024 / kWaves chunks).  Returns the OR
+// of emit's results (a dependency for arrive_last when emit publishes).
+template <bool BF16, bool VEC, int GROUP, bool CACHED, class Emit>
+__device__ uint32_t mass_chunks(const MassRows& a, int k0, int k1, int chunk2, int V, float* scr,
+                                Emit&& emit) {
     uint32_t dep = 0;
     if (k0 >= k1) return dep;
     if constexpr (VEC) {
@@ -186,7 +186,7 @@ __device__ uint32_t mass_chunks(const MassRows& a, int k0, int k1, int chunk2, i
                     float t = s[0];
 #pragma unroll
                     for (int q = 1; q < kWaves; ++q) t += s[q];
-                    dep |= publish(csum + k, __float_as_uint(t));
+                    dep |= emit(k, t);
                 }
             }
             __syncthreads();  // scr is reused by the next batch and by the caller
@@ -195,7 +195,7 @@ __device__ uint32_t mass_chunks(const MassRows& a, int k0, int k1, int chunk2, i
         for (int k = k0; k < k1; ++k) {
             const int lo = k * chunk2, hi = min(V, lo + chunk2);
             const float t = block_sum(lane_mass_elements<BF16>(a, lo, hi));
-            if (threadIdx.x == 0) dep |= publish(csum + k, __float_as_uint(t));
+            if (threadIdx.x == 0) dep |= emit(k, t);
         }
     }
     return dep;
@@ -350,24 +350,27 @@ __device__ __forceinline__ void clear_partials(const VerifyParams& P, int b, int
     }
 }
 
-// arrive_last for the decision workgroups of the one-kernel path: a
-// workgroup whose wait timed out also adds 1 << 16, so the last to arrive
-// learns (in *any_late) whether any workgroup of the request worked on
-// unpublished statistics.
-__device__ __forceinline__ bool arrive_last_marked(uint32_t* counter, uint32_t total, uint32_t dep,
-                                                   bool late, bool* any_late) {
-    __shared__ int s_last, s_late;
-    if (threadIdx.x == 0) {
-        uint32_t zero = 0u;
-        asm volatile("" : "+v"(zero) : "v"(dep));
-        const uint32_t old = atomicAdd(counter + zero, late ? 0x10001u : 1u);
-        s_last = ((old & 0xffffu) == total - 1);
-        s_late = late || (old >> 16) != 0;
-        if (s_last) atomicExch(counter, 0u);  // ready for the next call
+// One-kernel path: the chunk masses of request b's decision workgroups
+// other than the last, words [0, n) of cm.  Each publisher writes its word
+// once, (1 << 32) | mass bits, with bit 33 set if its own statistics wait
+// gave up, by an atomic exchange it does not wait for.  The last decision
+// workgroup (launched after all of them) reads them here, a lane per word:
+// each read is an exchange with zero, so a word is cleared for the next call
+// as it is taken.  Polls sleep in between, bounded like the statistics wait;
+// returns true (to every lane) if a wait gave up or a publisher was late.
+__device__ bool collect_masses(const VerifyParams& P, unsigned long long* cm, int n, float* s_csum) {
+    const uint64_t t0 = wall_clock64();
+    bool late = false;
+    for (int k = threadIdx.x; k < n; k += kThreads) {
+        unsigned long long v;
+        while ((v = atomicExch(cm + k, 0ull)) == 0ull) {
+            if (wall_clock64() - t0 > P.wait_ticks) { late = true; break; }
+            __builtin_amdgcn_s_sleep(16);
+        }
+        late |= ((v >> 33) & 1ull) != 0;
+        s_csum[k] = __uint_as_float(static_cast<uint32_t>(v));
     }
-    __syncthreads();
-    *any_late = s_late;
-    return s_last;
+    return __syncthreads_or(late);
 }
 
 // Decision workgroup wg of request b.  FUSED: the statistics come from the
@@ -511,20 +514,38 @@ __device__ __forceinline__ void decide_sample(const VerifyParams& P, const int w
         a.mq = tq.x;
         a.isq = 1.0f / tq.y;
     }
-    uint32_t* csum = P.csum + static_cast<size_t>(b) * P.nc2;
     const int k0 = wg * P.cpw, k1 = min(P.nc2, k0 + P.cpw);
-    const uint32_t dep = mass_chunks<BF16, VEC, GROUP, CACHED>(a, k0, k1, P.chunk2, P.V, csum, s_csum);
+    float* scr = reinterpret_cast<float*>(s_part);  // the partials are combined: free
     if constexpr (FUSED) {
-        if (!arrive_last_marked(P.cnt + b, static_cast<uint32_t>(P.wpr), dep, late, &late)) return;
+        // the request's last decision workgroup (chunks [k0, nc2)) keeps its
+        // masses in LDS and collects the others' published words
+        unsigned long long* cm = reinterpret_cast<unsigned long long*>(P.cmass) + static_cast<size_t>(b) * P.nc2;
+        mass_chunks<BF16, VEC, GROUP, CACHED>(a, k0, k1, P.chunk2, P.V, scr, [&](int k, float t) -> uint32_t {
+            s_csum[k] = t;
+            return 0u;
+        });
+        // (mass_chunks ends with a barrier: s_csum[k0, k1) is visible)
+        if (wg != P.wpr - 1) {
+            const unsigned long long tag = (1ull << 32) | (late ? (1ull << 33) : 0ull);
+            for (int k = k0 + threadIdx.x; k < k1; k += kThreads)
+                atomicExch(cm + k, tag | __float_as_uint(s_csum[k]));
+            return;
+        }
+        late = collect_masses(P, cm, k0, s_csum) || late;
+        // every decision workgroup of the request has read the statistics
+        // words before publishing its masses
         clear_partials(P, b, g);
     } else {
+        uint32_t* csum = P.csum + static_cast<size_t>(b) * P.nc2;
+        const uint32_t dep = mass_chunks<BF16, VEC, GROUP, CACHED>(
+            a, k0, k1, P.chunk2, P.V, scr, [&](int k, float t) { return publish(csum + k, __float_as_uint(t)); });
         if (!arrive_last(P.cnt + b, static_cast<uint32_t>(P.wpr), dep)) return;
+        for (int k = threadIdx.x; k < P.nc2; k += kThreads) s_csum[k] = __uint_as_float(fetch(csum + k));
+        __syncthreads();
     }
 
     // (4) last workgroup of the request: R, the chunk where the running mass
     // passes u*R, the token inside it, then every output of the request.
-    for (int k = threadIdx.x; k < P.nc2; k += kThreads) s_csum[k] = __uint_as_float(fetch(csum + k));
-    __syncthreads();
     // Wave 0 walks the chunk sums in chunk order: lane l takes a run of
     // consecutive chunks, and a wave prefix sum of the runs' totals gives R
     // and each run its offset.  scan() leaves R in s_R, and in s_chunk /
@@ -855,9 +876,10 @@ Layout make_layout(const specdec_verify_desc_t* d, bool point) {
     L.fwpr = (L.nc2 + L.fcpw - 1) / L.fcpw;
     const size_t B = static_cast<size_t>(d->batch);
     size_t off = 0;
-    // zero at rest: arrival counters, ready words
+    // zero at rest: arrival counters, ready words, chunk-mass words
     L.off_cnt = off; off = align256(off + B * 4);
     L.off_ready = off; off = align256(off + B * L.rows * L.nc * sizeof(uint64_t));
+    L.off_cmass = off; off = align256(off + B * L.nc2 * sizeof(uint64_t));
     L.off_part = off; off = align256(off + B * L.rows * L.nc * sizeof(float4));
     L.off_csum = off; off = align256(off + B * L.nc2 * sizeof(uint32_t));
     L.trunc = truncation_mode(d);
@@ -952,6 +974,7 @@ specdec_status_t verify_impl(const specdec_verify_desc_t* d, const void* target_
     char* ws = static_cast<char*>(workspace);
     P.cnt = reinterpret_cast<uint32_t*>(ws + L.off_cnt);
     P.ready = reinterpret_cast<uint64_t*>(ws + L.off_ready);
+    P.cmass = reinterpret_cast<uint64_t*>(ws + L.off_cmass);
     P.part = reinterpret_cast<float4*>(ws + L.off_part);
     P.csum = reinterpret_cast<uint32_t*>(ws + L.off_csum);
     P.nuc = reinterpret_cast<uint2*>(ws + L.off_nuc);

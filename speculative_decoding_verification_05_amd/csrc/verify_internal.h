@@ -44,6 +44,7 @@ struct VerifyParams {
     uint32_t* cnt;      // [B] arrivals in the sampling pass
     uint32_t* csum;     // [B][nc2] chunk masses of the sampling pass (float bits)
     uint64_t* ready;    // [B][R][nc] one-kernel path: published (max, sum) words, 0 at rest
+    uint64_t* cmass;    // [B][nc2] one-kernel path: published chunk masses, 0 at rest
     int lag;            // one-kernel path: decision workgroups trail by this many requests
     uint64_t wait_ticks;  // one-kernel path: bound of a decision workgroup's wait
     int B, G, V;
@@ -175,7 +176,7 @@ struct Layout {
     int group;          // sampling-pass chunks loaded together (1..kMassGroupWide)
     int fwpr, fcpw;     // one-kernel path: decision workgroups per request, chunks each
     bool trunc;
-    size_t off_cnt, off_ready, off_part, off_csum, off_nuc, total;
+    size_t off_cnt, off_ready, off_cmass, off_part, off_csum, off_nuc, total;
 };
 // point: sampling with point-mass drafts (no draft rows)
 Layout make_layout(const specdec_verify_desc_t* d, bool point = false);
