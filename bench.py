@@ -13,9 +13,10 @@ Timing: W warmup steps, then exactly K steps replayed from HIP graphs (each
 holds whole passes over the input sets, at least 16 steps, so that the launch
 gap between replays is amortized), bracketed by torch.cuda.synchronize();
 value = verified positions / second.
-The roofline entry is the dominant kernel: the one-kernel sampling verify
-(statistics and decision workgroups in one launch), or the statistics
-kernel on the greedy and truncation paths (and with SPECDEC_FUSED=0).  It is
+The roofline entry is the dominant kernel: the one-kernel verify of the
+sampling, greedy and tree paths (statistics and decision workgroups in one
+launch), the selection kernel on the truncation path, or the statistics
+kernel with SPECDEC_FUSED=0.  It is
 the kernel's algorithmic bytes per launch (every used logits row read once,
 plus draft tokens and outputs) over its average duration, timed live with
 start/stop events that bracket the kernel itself (specdec_verify_profiled).
@@ -388,10 +389,13 @@ def main() -> int:
     alg_k1 = float(np.mean([synth.logits_bytes(wl0, g) for g in gam_sets])) + B * G * 4 + out_bytes
     achieved = alg_k1 / k1_avg / 1e9
     trunc = bool(wl0.top_k) or wl0.top_p < 1.0
-    # sampling without truncation runs as one kernel (statistics + decision)
-    fused = not greedy and not trunc and os.environ.get("SPECDEC_FUSED", "1")[:1] != "0"
-    kname = ("k_stats_greedy" if greedy else "k_trunc_select" if trunc else
-             "k_verify_fused" if fused else "k_stats_sample")
+    # sampling without truncation and greedy verification run as one kernel
+    # (statistics + decision) unless SPECDEC_FUSED=0
+    fused = not trunc and os.environ.get("SPECDEC_FUSED", "1")[:1] != "0"
+    if greedy:
+        kname = "k_greedy_fused" if fused else "k_stats_greedy"
+    else:
+        kname = "k_trunc_select" if trunc else "k_verify_fused" if fused else "k_stats_sample"
     if fused:
         log(f"step {sec_per_step * 1e6:.2f} us ({'graph' if runner.graphed else 'eager'}); "
             f"one-kernel verify avg {k1_avg * 1e6:.2f} us (p10 {np.percentile(k1, 10) * 1e6:.2f}, "
@@ -469,8 +473,8 @@ def main() -> int:
                    "launch": "hipgraph" if runner.graphed else "eager",
                    "committed_tokens_per_s": committed / sec_per_step,
                    "step_GBps": alg_k1 / sec_per_step / 1e9},
-        "kernels": dict(({"verify_fused": {"avg_us": k1_avg * 1e6, "bytes_per_launch": alg_k1,
-                                           "GBps": achieved, "frac": achieved / HBM_PEAK_GBPS}}
+        "kernels": dict(({kname[2:]: {"avg_us": k1_avg * 1e6, "bytes_per_launch": alg_k1,
+                                      "GBps": achieved, "frac": achieved / HBM_PEAK_GBPS}}
                           if fused else
                           {"stats": {"avg_us": k1_avg * 1e6, "bytes_per_launch": alg_k1,
                                      "GBps": achieved, "frac": achieved / HBM_PEAK_GBPS},
@@ -602,11 +606,18 @@ def bench_tree(args, wl0) -> int:
         cbytes.append(float(((m + 1) * 2 + (depth - m)).sum() * slot))
     cb = float(np.mean(cbytes))
     depth_mean = float(np.mean([a.float().mean().item() for a, _ in eager]))
-    log(f"step {sec_per_step * 1e6:.2f} us (graph); stats kernel avg {k1.mean() * 1e6:.2f} us; "
-        f"tree decision {k2.mean() * 1e6:.2f} us; path commit {kc.mean() * 1e6:.2f} us")
-    log(f"stats kernel {achieved:.1f} GB/s = {100 * achieved / HBM_PEAK_GBPS:.1f}% of "
-        f"{HBM_PEAK_GBPS:.0f} GB/s; commit {cb / kc.mean() / 1e9:.1f} GB/s; mean kept depth "
-        f"{depth_mean:.3f}")
+    # the statistics and the tree decision run as one kernel unless SPECDEC_FUSED=0
+    fused = os.environ.get("SPECDEC_FUSED", "1")[:1] != "0"
+    kname = "k_tree_fused" if fused else "k_stats_greedy"
+    if fused:
+        log(f"step {sec_per_step * 1e6:.2f} us (graph); one-kernel tree verify avg "
+            f"{k1.mean() * 1e6:.2f} us; path commit {kc.mean() * 1e6:.2f} us")
+    else:
+        log(f"step {sec_per_step * 1e6:.2f} us (graph); stats kernel avg {k1.mean() * 1e6:.2f} us; "
+            f"tree decision {k2.mean() * 1e6:.2f} us; path commit {kc.mean() * 1e6:.2f} us")
+    log(f"{'one-kernel tree verify' if fused else 'stats kernel'} {achieved:.1f} GB/s = "
+        f"{100 * achieved / HBM_PEAK_GBPS:.1f}% of {HBM_PEAK_GBPS:.0f} GB/s; commit "
+        f"{cb / kc.mean() / 1e9:.1f} GB/s; mean kept depth {depth_mean:.3f}")
 
     cpu = cpu_all = None
     if not args.no_cpu_baseline:
@@ -645,15 +656,18 @@ def bench_tree(args, wl0) -> int:
                    "committed_tokens_per_s": B * (depth_mean + 1) / sec_per_step},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic(f"k_stats_greedy__{wl0.name}"),
-                     "kernel": "k_stats_greedy",
+                     "traffic": measured_traffic(f"{kname}__{wl0.name}"),
+                     "kernel": kname,
                      "kernel_avg_us": float(k1.mean()) * 1e6, "bytes_per_launch": alg_k1},
-        "kernels": {"stats": {"avg_us": float(k1.mean()) * 1e6, "bytes_per_launch": alg_k1,
-                              "GBps": achieved, "frac": achieved / HBM_PEAK_GBPS},
-                    "k_decide_tree": {"avg_us": float(k2.mean()) * 1e6},
-                    "k_commit": {"avg_us": float(kc.mean()) * 1e6, "bytes_per_launch": cb,
-                                 "GBps": cb / kc.mean() / 1e9,
-                                 "frac": cb / kc.mean() / 1e9 / HBM_PEAK_GBPS}},
+        "kernels": dict(({"tree_fused": {"avg_us": float(k1.mean()) * 1e6, "bytes_per_launch": alg_k1,
+                                         "GBps": achieved, "frac": achieved / HBM_PEAK_GBPS}}
+                         if fused else
+                         {"stats": {"avg_us": float(k1.mean()) * 1e6, "bytes_per_launch": alg_k1,
+                                    "GBps": achieved, "frac": achieved / HBM_PEAK_GBPS},
+                          "k_decide_tree": {"avg_us": float(k2.mean()) * 1e6}}),
+                        k_commit={"avg_us": float(kc.mean()) * 1e6, "bytes_per_launch": cb,
+                                  "GBps": cb / kc.mean() / 1e9,
+                                  "frac": cb / kc.mean() / 1e9 / HBM_PEAK_GBPS}),
         "cpu_baseline": cpu,
         "cpu_baseline_all_cores": cpu_all,
     }

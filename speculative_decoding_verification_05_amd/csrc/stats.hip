@@ -34,32 +34,12 @@ __global__ __launch_bounds__(kThreads) void k_stats(VerifyParams P) {
         const int g = request_gamma(P, b);
         return is_target ? i <= g : i < g;
     };
-    constexpr int N = Vec<BF16>::N;
     float4* slot = P.part + (static_cast<size_t>(b) * P.rows + s) * P.nc + ci;
     if constexpr (GREEDY) {
-        // Each lane visits its elements in ascending index order, so a strict
-        // ">" keeps the lowest index among equal maxima.
-        ArgMax best{neg_inf(), 0x7fffffff};
-        bool nan = false;
-        auto consume = [&](const Vec<BF16> (&v)[kUnroll], int t0) {
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int e = t0 + (u * kThreads + threadIdx.x) * N;
-#pragma unroll
-                for (int k = 0; k < N; ++k) {
-                    const float x = v[u].x[k];
-                    nan |= (x != x);
-                    const bool first = best.i == 0x7fffffff && e + k < hi;
-                    if (x > best.v || first) { best.v = x; best.i = e + k; }
-                }
-            }
-        };
-        if (!stream_row<BF16, VEC, kUnroll>(rp, lo, hi, consume, keep)) return;
-        const ArgMax r = block_argmax(best);
-        const bool any_nan = __syncthreads_or(nan);
-        if (threadIdx.x == 0)
-            *slot = make_float4(r.v, __uint_as_float(static_cast<uint32_t>(r.i) |
-                                                     (any_nan ? 0x80000000u : 0u)), 0.0f, 0.0f);
+        ArgMax r;
+        bool nan;
+        if (!chunk_argmax<BF16, VEC>(rp, lo, hi, keep, &r, &nan)) return;
+        if (threadIdx.x == 0) *slot = greedy_partial(r, nan);
     } else {
         // the token this row judges (target) or proposed (draft); its logit
         // rides along with the partial of the chunk that holds it

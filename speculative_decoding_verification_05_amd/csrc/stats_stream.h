@@ -1,8 +1,9 @@
 // Streaming helpers of the statistics pass, shared by the statistics kernel
-// (stats.hip) and the one-kernel sampling verify (verify.hip): one chunk of
-// one logits row read once with branch-free 16-byte loads, the online
-// softmax pair (max, sum of 2^((z - max) c)) of the softmax of z/T
-// (AI-infra KB M013 s.04; "Speculative decoding tutorial" s.7.1).
+// (stats.hip) and the one-kernel verify paths (verify.hip, tree.hip): one
+// chunk of one logits row read once with branch-free 16-byte loads, the
+// online softmax pair (max, sum of 2^((z - max) c)) of the softmax of z/T
+// (AI-infra KB M013 s.04; "Speculative decoding tutorial" s.7.1) or the
+// greedy (max, lowest index) pair (tutorial s.3-4).
 #pragma once
 
 #include "verify_internal.h"
@@ -120,6 +121,92 @@ __device__ __forceinline__ bool chunk_maxsum(const void* rp, int lo, int hi, flo
     if (!stream_row<BF16, VEC, kUnroll>(rp, lo, hi, consume, keep)) return false;
     *out = block_combine(MaxSum{m, sum}, c);
     return true;
+}
+
+// (max, lowest index) of elements [lo, hi) of row rp, combined over the
+// workgroup (every lane gets the pair), and whether a NaN was seen.  Each
+// lane visits its elements in ascending index order, so a strict ">" keeps
+// the lowest index among equal maxima.  keep() as in stream_row; returns
+// false if the row was abandoned.
+template <bool BF16, bool VEC, class K>
+__device__ __forceinline__ bool chunk_argmax(const void* rp, int lo, int hi, K&& keep, ArgMax* out,
+                                             bool* any_nan) {
+    constexpr int N = Vec<BF16>::N;
+    ArgMax best{neg_inf(), 0x7fffffff};
+    bool nan = false;
+    auto consume = [&](const Vec<BF16> (&v)[kUnroll], int t0) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int e = t0 + (u * kThreads + threadIdx.x) * N;
+#pragma unroll
+            for (int k = 0; k < N; ++k) {
+                const float x = v[u].x[k];
+                nan |= (x != x);
+                const bool first = best.i == 0x7fffffff && e + k < hi;
+                if (x > best.v || first) { best.v = x; best.i = e + k; }
+            }
+        }
+    };
+    if (!stream_row<BF16, VEC, kUnroll>(rp, lo, hi, consume, keep)) return false;
+    *out = block_argmax(best);
+    *any_nan = __syncthreads_or(nan);
+    return true;
+}
+
+// Greedy partials as the decision kernels stage them: x = the chunk's
+// maximum, y = the bits of its lowest index with bit 31 set if a NaN was seen.
+__device__ __forceinline__ float4 greedy_partial(const ArgMax& r, bool nan) {
+    return make_float4(r.v, __uint_as_float(static_cast<uint32_t>(r.i) | (nan ? 0x80000000u : 0u)),
+                       0.0f, 0.0f);
+}
+
+// One-kernel greedy paths: the same partial as one 64-bit word, maximum bits
+// low, index bits high with bit 30 set as the published mark (indices are
+// below 2^24), so a published word is never zero.
+__device__ __forceinline__ unsigned long long greedy_word(const ArgMax& r, bool nan) {
+    const uint32_t hi = static_cast<uint32_t>(r.i) | 0x40000000u | (nan ? 0x80000000u : 0u);
+    return (static_cast<unsigned long long>(hi) << 32) | __float_as_uint(r.v);
+}
+
+// The decision workgroup of request b in a one-kernel greedy path, the only
+// reader of the request's words: every word of a used row (used(s)) is taken
+// by a lane of its own with an exchange with zero (so it is cleared for the
+// next call as it is read), polled with sleeps until published, within
+// P.wait_ticks of the 100 MHz constant clock, and staged in s_part as
+// greedy_partial stores it.  Returns true (to every lane) if a wait gave up.
+template <class U>
+__device__ bool collect_greedy(const VerifyParams& P, int b, U&& used, float4* s_part) {
+    const int n = P.rows * P.nc;
+    unsigned long long* w = reinterpret_cast<unsigned long long*>(P.ready) + static_cast<size_t>(b) * n;
+    const uint64_t t0 = wall_clock64();
+    bool late = false;
+    for (int t = threadIdx.x; t < n; t += kThreads) {
+        if (!used(t / P.nc)) continue;
+        unsigned long long v;
+        while ((v = atomicExch(w + t, 0ull)) == 0ull) {
+            if (wall_clock64() - t0 > P.wait_ticks) { late = true; break; }
+            __builtin_amdgcn_s_sleep(16);
+        }
+        const uint32_t hi = static_cast<uint32_t>(v >> 32) & ~0x40000000u;
+        s_part[t] = make_float4(__uint_as_float(static_cast<uint32_t>(v)), __uint_as_float(hi), 0.0f, 0.0f);
+    }
+    return __syncthreads_or(late);
+}
+
+// Statistics workgroup of a one-kernel greedy path: chunk k % nc of target
+// row k / nc of request b (rows used(s) only), published as greedy_word with
+// an atomic exchange it does not wait for.
+template <bool BF16, bool VEC, class U>
+__device__ __forceinline__ void fused_greedy_stats(const VerifyParams& P, int b, int k, U&& used) {
+    const int s = k / P.nc, ci = k % P.nc;
+    const void* rp = target_row(P, b, s, BF16);
+    const int lo = ci * P.chunk, hi = min(P.V, lo + P.chunk);
+    ArgMax r;
+    bool nan;
+    if (!chunk_argmax<BF16, VEC>(rp, lo, hi, [&]() { return used(s); }, &r, &nan)) return;
+    if (threadIdx.x == 0)
+        atomicExch(reinterpret_cast<unsigned long long*>(P.ready) + static_cast<size_t>(b) * P.rows * P.nc + k,
+                   greedy_word(r, nan));
 }
 
 }  // namespace specdec

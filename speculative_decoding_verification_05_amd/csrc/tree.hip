@@ -11,16 +11,20 @@
 //     among equally deep ones) and is followed by g of that node.
 //
 // Kernels (HBM-bandwidth bound, no matrix cores):
-//   k_stats          (stats.hip) in greedy mode over the N rows of every tree:
-//                    one streaming read, one (max, lowest index) partial per
-//                    (chunk, row).
-//   k_decide_tree    one workgroup per request: row argmaxes from the
-//                    partials, then one wave with a lane per node: edge
-//                    matches, pointer jumping (log2 N rounds of lane
-//                    shuffles) for "every ancestor kept" and the depth, a
-//                    ballot for the deepest kept node, the path, and every
-//                    output (round end shared with specdec_verify).
-#include "verify_internal.h"
+//   k_tree_fused     (default) one launch: the statistics workgroups of every
+//                    request (greedy mode over the N rows of each tree, one
+//                    (max, lowest index) word per (chunk, row), published
+//                    with an atomic exchange), then one decision workgroup
+//                    per request, which collects its request's words (all
+//                    launched before it) and decides as k_decide_tree.
+//   k_stats          (stats.hip) + k_decide_tree, the two-kernel path
+//                    (SPECDEC_FUSED=0): one streaming read with one partial
+//                    per (chunk, row), then one workgroup per request.
+// The decision: row argmaxes from the partials, then one wave with a lane
+// per node: edge matches, pointer jumping (log2 N rounds of lane shuffles)
+// for "every ancestor kept" and the depth, a ballot for the deepest kept
+// node, the path, and every output (round end shared with specdec_verify).
+#include "stats_stream.h"
 
 #include <hip/hip_ext.h>
 #include <stdint.h>
@@ -28,24 +32,31 @@
 namespace specdec {
 namespace {
 
-__global__ __launch_bounds__(kThreads) void k_decide_tree(VerifyParams P) {
+// Tree decision of request b.  FUSED: the partials are the words the same
+// kernel's statistics workgroups publish (collect_greedy); otherwise those
+// the statistics kernel stored.
+template <bool FUSED>
+__device__ __forceinline__ void decide_tree(const VerifyParams& P, const int b) {
     __shared__ float4 s_part[kMaxPart];
     __shared__ int s_arg[64];
     __shared__ uint32_t s_nan[64];
     __shared__ int s_par[64];
     __shared__ int s_path[64];
-    const int b = blockIdx.x;
     const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
     const int N = P.G + 1;
     const int n = tree_nodes(P, b);
     // independent loads first: partials, the node's token and parent
-    const float4* src = P.part + static_cast<size_t>(b) * P.rows * P.nc;
-    for (int t = threadIdx.x; t < n * P.nc; t += kThreads) s_part[t] = src[t];
+    if constexpr (!FUSED) {
+        const float4* src = P.part + static_cast<size_t>(b) * P.rows * P.nc;
+        for (int t = threadIdx.x; t < n * P.nc; t += kThreads) s_part[t] = src[t];
+    }
     int tok = -1, par = 0;
     if (w == 0 && l < n && l > 0) {
         tok = P.tokens[static_cast<size_t>(b) * N + l];
         par = P.parents[static_cast<size_t>(b) * N + l];
     }
+    bool late = false;
+    if constexpr (FUSED) late = collect_greedy(P, b, [&](int s) { return s < n; }, s_part);
     __syncthreads();
     // argmax of every used row: a lane per row over a few partials, else a wave
     auto part_argmax = [&](int s, int k0, int step, ArgMax& best, uint32_t& nan) {
@@ -129,7 +140,26 @@ __global__ __launch_bounds__(kThreads) void k_decide_tree(VerifyParams P) {
     fl = wave_or(fl);
     fl |= write_round(P, b, m, c);
     if (l < N) P.path[static_cast<size_t>(b) * N + l] = node_k;
-    if (l == 0 && P.flags) P.flags[b] = fl;
+    if (l == 0 && P.flags) P.flags[b] = fl | (late ? SPECDEC_FLAG_WAIT_TIMEOUT : 0u);
+}
+
+__global__ __launch_bounds__(kThreads) void k_decide_tree(VerifyParams P) {
+    decide_tree<false>(P, blockIdx.x);
+}
+
+// One-kernel tree verify: the B x S statistics workgroups (S = N rows x nc,
+// request by request) first in launch order, then one decision workgroup per
+// request, which waits only on statistics workgroups launched before it.
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_tree_fused(VerifyParams P) {
+    const int S = P.rows * P.nc;
+    const int x = blockIdx.x;
+    if (x < P.B * S) {
+        const int b = x / S;
+        fused_greedy_stats<BF16, VEC>(P, b, x % S, [&](int s) { return s < tree_nodes(P, b); });
+    } else {
+        decide_tree<true>(P, x - P.B * S);
+    }
 }
 
 bool valid_tree(const specdec_tree_desc_t* d) {
@@ -198,6 +228,8 @@ specdec_status_t tree_impl(const specdec_tree_desc_t* d, const void* target_logi
     P.flags = flags;
     char* ws = static_cast<char*>(workspace);
     P.part = reinterpret_cast<float4*>(ws + L.off_part);
+    P.ready = reinterpret_cast<uint64_t*>(ws + L.off_ready);
+    P.wait_ticks = fused_wait_ticks();
     P.B = d->batch;
     P.G = d->num_nodes - 1;
     P.V = d->vocab;
@@ -210,6 +242,21 @@ specdec_status_t tree_impl(const specdec_tree_desc_t* d, const void* target_logi
     const size_t es = bf16 ? 2 : 4;
     const bool vec = (reinterpret_cast<uintptr_t>(target_logits) & 15u) == 0 &&
                      (static_cast<size_t>(d->vocab) * es) % 16 == 0;
+    if (fused_enabled()) {
+        // one kernel; ev[0]/ev[1] bracket it, ev[2]/ev[3] mark its end
+        const dim3 grid(static_cast<unsigned>(d->batch) * (L.rows * L.nc + 1));
+        auto launch = [&](auto kernel) {
+            if (ev)
+                hipExtLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, ev[0], ev[1], 0, P);
+            else
+                hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, P);
+        };
+        if (bf16) vec ? launch(k_tree_fused<true, true>) : launch(k_tree_fused<true, false>);
+        else vec ? launch(k_tree_fused<false, true>) : launch(k_tree_fused<false, false>);
+        if (ev && (hipEventRecord(ev[2], stream) != hipSuccess || hipEventRecord(ev[3], stream) != hipSuccess))
+            return SPECDEC_ERR_DEVICE;
+        return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_DEVICE;
+    }
     if (launch_stats(P, bf16, vec, true, dim3(L.nc, L.rows, d->batch), stream,
                      ev ? ev[0] : nullptr, ev ? ev[1] : nullptr) != SPECDEC_OK)
         return SPECDEC_ERR_DEVICE;

@@ -28,6 +28,10 @@
 //                    prefix sum, and writes every output of the request.
 //   k_decide_greedy  one workgroup per request: row argmaxes from the
 //                    partials, the argmax-equality prefix and every output.
+//   k_greedy_fused   greedy in one launch: the statistics workgroups publish
+//                    each chunk's (max, lowest index) as one 64-bit word, and
+//                    one decision workgroup per request, launched after all
+//                    of them, collects its words and decides as above.
 //   k_verify_fused   sampling without truncation in one launch: the
 //                    statistics workgroups of every request come first in
 //                    launch order, then the decision workgroups, each of
@@ -36,9 +40,10 @@
 //                    same results; it saves the kernel boundary and lets the
 //                    decision workgroups start while the last rows stream.
 // Cross-workgroup hand-offs use device-scope atomics.  In the two-kernel
-// path nothing waits on another workgroup; in the one-kernel path only
-// decision workgroups wait, and only on statistics workgroups that precede
-// them in launch order and never wait themselves.
+// paths nothing waits on another workgroup; in the one-kernel paths only
+// decision workgroups wait, and only on workgroups that precede them in
+// launch order (statistics workgroups, which never wait, and in sampling the
+// request's earlier decision workgroups, which wait only on statistics).
 #include "stats_stream.h"
 
 #include <hip/hip_ext.h>
@@ -700,18 +705,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) v
 
 // ------------------------------------------------------------------ greedy decision
 
-__global__ __launch_bounds__(kThreads) void k_decide_greedy(VerifyParams P) {
+// Greedy decision of request b.  FUSED: the partials are the words the same
+// kernel's statistics workgroups publish (collect_greedy); otherwise those
+// the statistics kernel stored.
+template <bool FUSED>
+__device__ __forceinline__ void decide_greedy(const VerifyParams& P, const int b) {
     __shared__ float4 s_part[kMaxPart];
     __shared__ int s_arg[64];
     __shared__ uint32_t s_nan[64];
-    const int b = blockIdx.x;
     const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
-    stage_partials(P, b, s_part);
+    if constexpr (!FUSED) stage_partials(P, b, s_part);
     const int i = l;
     int d = -1;
     if (w == 0 && i < P.G) d = P.tokens[static_cast<size_t>(b) * P.G + i];
     const int graw = P.gamma ? P.gamma[b] : P.G;  // read once, clamped, flagged below
     const int g = min(max(graw, 0), P.G);
+    bool late = false;
+    if constexpr (FUSED) late = collect_greedy(P, b, [&](int s) { return s <= g; }, s_part);
     __syncthreads();
     // a lane per row over a few partials, else a wave per row
     auto part_argmax = [&](int s, int k0, int step, ArgMax& best, uint32_t& nan) {
@@ -756,7 +766,26 @@ __global__ __launch_bounds__(kThreads) void k_decide_greedy(VerifyParams P) {
     const int m = min(g, static_cast<int>(__builtin_ctzll(~mask)));
     fl = wave_or(fl);
     fl |= write_round(P, b, m, i < m ? d : s_arg[m]);
-    if (i == 0 && P.flags) P.flags[b] = fl;
+    if (i == 0 && P.flags) P.flags[b] = fl | (late ? SPECDEC_FLAG_WAIT_TIMEOUT : 0u);
+}
+
+__global__ __launch_bounds__(kThreads) void k_decide_greedy(VerifyParams P) {
+    decide_greedy<false>(P, blockIdx.x);
+}
+
+// One-kernel greedy verify: the B x S statistics workgroups (S = rows x nc,
+// request by request) first in launch order, then one decision workgroup per
+// request, which waits only on statistics workgroups launched before it.
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_greedy_fused(VerifyParams P) {
+    const int S = P.rows * P.nc;
+    const int x = blockIdx.x;
+    if (x < P.B * S) {
+        const int b = x / S;
+        fused_greedy_stats<BF16, VEC>(P, b, x % S, [&](int s) { return s <= request_gamma(P, b); });
+    } else {
+        decide_greedy<true>(P, x - P.B * S);
+    }
 }
 
 // ------------------------------------------------------------------ host side
@@ -782,21 +811,6 @@ int env_int(const char* name, int dflt) {
     if (!s || !*s) return dflt;
     const int v = atoi(s);
     return v > 0 ? v : dflt;
-}
-
-// The one-kernel sampling path (statistics and decision in one launch).
-// SPECDEC_FUSED=0 selects the two-kernel path.
-bool fused_enabled() {
-    const char* s = getenv("SPECDEC_FUSED");
-    return !(s && s[0] == '0');
-}
-
-// Bound of a decision workgroup's wait for its statistics: 20 ms of the
-// 100 MHz constant clock; SPECDEC_FUSED_WAIT_TICKS overrides (tests force
-// the timeout path with a tiny bound).
-uint64_t fused_wait_ticks() {
-    const char* s = getenv("SPECDEC_FUSED_WAIT_TICKS");
-    return (s && *s) ? strtoull(s, nullptr, 10) : 2000000ull;
 }
 
 // Decision workgroups of request j trail the statistics of request j + lag;
@@ -909,6 +923,14 @@ specdec_status_t launch_all(const specdec_verify_desc_t* d, const VerifyParams& 
             hipLaunchKernelGGL(kernel, grid, block, 0, stream, P);
     };
     const bool greedy = d->mode == SPECDEC_GREEDY;
+    if (fused && greedy) {
+        const dim3 grid(static_cast<unsigned>(d->batch) * (L.rows * L.nc + 1));
+        launch(k_greedy_fused<BF16, VEC>, grid, e0, e1);
+        // the decision runs inside that kernel: its events mark the end
+        if (e2 && hipEventRecord(e2, stream) != hipSuccess) return SPECDEC_ERR_DEVICE;
+        if (e3 && hipEventRecord(e3, stream) != hipSuccess) return SPECDEC_ERR_DEVICE;
+        return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_DEVICE;
+    }
     if (fused) {
         // one kernel: statistics and decision workgroups interleaved
         // (one chunk per group keeps the register count near the statistics
@@ -988,10 +1010,11 @@ specdec_status_t verify_impl(const specdec_verify_desc_t* d, const void* target_
     P.chunk = L.chunk;
     P.nc2 = L.nc2;
     P.chunk2 = L.chunk2;
-    // sampling without truncation runs as one kernel unless SPECDEC_FUSED=0
-    const bool fused = sample && !L.trunc && fused_enabled();
-    P.wpr = fused ? L.fwpr : L.wpr;
-    P.cpw = fused ? L.fcpw : L.cpw;
+    // sampling without truncation and greedy verification run as one kernel
+    // unless SPECDEC_FUSED=0
+    const bool fused = !L.trunc && fused_enabled();
+    P.wpr = fused && sample ? L.fwpr : L.wpr;
+    P.cpw = fused && sample ? L.fcpw : L.cpw;
     P.lag = fused_lag(d->batch);
     P.wait_ticks = fused_wait_ticks();
     P.c = sample ? static_cast<float>(1.4426950408889634 / static_cast<double>(d->temperature)) : 1.0f;

@@ -8,6 +8,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 namespace specdec {
 
@@ -167,6 +168,22 @@ __device__ __forceinline__ float block_sum(float v) {
 #pragma unroll
     for (int k = 1; k < kWaves; ++k) r += s_v[k];
     return r;
+}
+
+// One-kernel paths (statistics and decision workgroups in one launch) for
+// sampling without truncation, greedy chains and greedy trees;
+// SPECDEC_FUSED=0 selects the two-kernel paths.
+inline bool fused_enabled() {
+    const char* s = getenv("SPECDEC_FUSED");
+    return !(s && s[0] == '0');
+}
+
+// Bound of a one-kernel decision workgroup's waits: 20 ms of the 100 MHz
+// constant clock; SPECDEC_FUSED_WAIT_TICKS overrides (tests force the
+// timeout path with a tiny bound).
+inline uint64_t fused_wait_ticks() {
+    const char* s = getenv("SPECDEC_FUSED_WAIT_TICKS");
+    return (s && *s) ? strtoull(s, nullptr, 10) : 2000000ull;
 }
 
 // Workspace layout and chunking of one verify call (shared by the chain and

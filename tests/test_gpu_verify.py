@@ -264,6 +264,73 @@ def test_one_kernel_wait_timeout_is_flagged():
         assert np.array_equal(r2[k], ref[k]), k
 
 
+GREEDY_ONE_KERNEL_CASES = [
+    ("greedy B=32 V=151936", lambda: W["b256_g7_v151936_greedy_kv"].scaled(32, 151936)),
+    ("ragged B=40 V=4096", lambda: W["b512_ragged_v262144_kv"].scaled(40, 4096)),
+    ("fp32 B=8", lambda: W["b8_g4_v32000_f32"]),
+]
+
+
+@pytest.mark.parametrize("label,make", GREEDY_ONE_KERNEL_CASES, ids=[c[0] for c in GREEDY_ONE_KERNEL_CASES])
+def test_one_kernel_greedy_matches_two_kernel_path(label, make):
+    """Greedy verify in one launch (statistics workgroups publish their
+    words, one decision workgroup per request collects them) writes the same
+    bytes as the statistics kernel followed by the decision kernel, on two
+    calls in a row with one workspace (the words are cleared as read)."""
+    wl = make()
+    x = synth.make_verify_inputs(wl, need_draft_logits=False)
+    args = dict(bf16=wl.dtype == "bf16", greedy=True)
+    old = _env(SPECDEC_FUSED=0)
+    try:
+        say(f"[one-kernel greedy] {label}: two-kernel path")
+        ref = gpu_verify(x, **args)
+        _env(SPECDEC_FUSED=1)
+        say(f"[one-kernel greedy] {label}: one kernel, two calls")
+        outs = gpu_verify(x, reps=2, **args)
+    finally:
+        _env(**old)
+    for o in outs:
+        for k in ref:
+            assert np.array_equal(o[k], ref[k]), (label, k)
+        assert not np.any(o["flags"] & sd.FLAG_WAIT_TIMEOUT)
+
+
+def test_one_kernel_greedy_wait_timeout_is_flagged():
+    """Greedy one-kernel path with the wait bound forced to zero ticks: each
+    request is flagged WAIT_TIMEOUT or identical to the two-kernel path, and
+    after a workspace clear the next call is identical again."""
+    import torch
+    from gpu_helpers import to_dev
+    wl = W["b256_g7_v151936_greedy_kv"].scaled(24, 60000)
+    x = synth.make_verify_inputs(wl, need_draft_logits=False)
+    desc = sd.make_verify_desc(wl.batch, wl.gamma_max, wl.vocab, greedy=True)
+    ver = sd.Verifier(desc, "cuda")
+    t, tok, gam = to_dev(x["target"], "cuda"), to_dev(x["draft_tokens"], "cuda"), to_dev(x["gamma"], "cuda")
+
+    def run():
+        out = {k: v.cpu().numpy() for k, v in ver(t, None, tok, gam).items()}
+        torch.cuda.synchronize()
+        return out
+
+    old = _env(SPECDEC_FUSED=0, SPECDEC_FUSED_WAIT_TICKS=None)
+    try:
+        ref = run()
+        _env(SPECDEC_FUSED=1, SPECDEC_FUSED_WAIT_TICKS=0)
+        say("[one-kernel greedy] forced wait timeout")
+        r = run()
+        late = (r["flags"] & sd.FLAG_WAIT_TIMEOUT) != 0
+        say(f"  requests flagged WAIT_TIMEOUT: {int(late.sum())} of {wl.batch}")
+        same = np.all(r["out_tokens"] == ref["out_tokens"], axis=1) & (r["accept_count"] == ref["accept_count"])
+        assert np.all(late | same)
+        _env(SPECDEC_FUSED_WAIT_TICKS=None)
+        sd.specdec_workspace_clear(ver.workspace)
+        r2 = run()
+    finally:
+        _env(**old)
+    for k in ref:
+        assert np.array_equal(r2[k], ref[k]), k
+
+
 # ------------------------------------------------------------ greedy
 
 @pytest.mark.parametrize("batch,vocab", [(32, 151936), (16, 10001), (5, 64)])
