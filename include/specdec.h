@@ -80,9 +80,11 @@ typedef enum specdec_mode { SPECDEC_SAMPLE = 0, SPECDEC_GREEDY = 1 } specdec_mod
 #define SPECDEC_FLAG_EOS               0x80u /* verify: the committed list ends with the EOS token */
 #define SPECDEC_FLAG_LENGTH            0x100u /* verify: the token budget ended the committed list */
 #define SPECDEC_FLAG_BAD_TREE          0x200u /* tree: a parent index outside [0, node): node rejected */
-#define SPECDEC_FLAG_WAIT_TIMEOUT      0x400u /* verify: the one-kernel path gave up waiting for the
-                                                 request's statistics (20 ms): its outputs are
-                                                 invalid and the workspace must be cleared */
+#define SPECDEC_FLAG_WAIT_TIMEOUT      0x400u /* verify, verify_tree: a one-kernel path (sampling
+                                                 without truncation, greedy, tree) gave up waiting
+                                                 for the request's statistics or chunk masses
+                                                 (20 ms): its outputs are invalid and the
+                                                 workspace must be cleared */
 
 /* ------------------------------------------------------------------ verify */
 
@@ -171,6 +173,10 @@ size_t specdec_verify_workspace_bytes(const specdec_verify_desc_t* desc);
  *   UNSUPPORTED, in SAMPLE mode with truncation (0 < top_k < V, or
  *   top_p < 1), when top_k > 1024, or for top_p < 1 without an effective
  *   top_k on a vocabulary above 2048.  In each case nothing is enqueued.
+ * Kernels: sampling without truncation and greedy verification run as one
+ *   kernel (statistics and decision workgroups in one launch; SPECDEC_FUSED=0
+ *   in the environment selects the two-kernel path, same results);
+ *   truncation runs a selection kernel, then a decision kernel.
  * Truncation: top-k keeps every token whose raw logit is >= the k-th largest
  *   raw logit (ties kept); top-p then keeps the shortest prefix, in order of
  *   raw logit descending and token index ascending, whose cumulative
@@ -193,9 +199,9 @@ specdec_status_t specdec_verify(const specdec_verify_desc_t* desc,
  * statistics pass kernel (the one full read of the logits), [2]/[3] at the
  * start/end of the decision kernel (acceptance tests and, when sampling, the
  * correction/bonus draw).  The events bracket the kernels' execution
- * (hipExtLaunchKernel), not the enqueue.  Sampling without truncation runs
- * both passes in one kernel: [0]/[1] bracket that kernel and [2]/[3] are
- * recorded right after it.
+ * (hipExtLaunchKernel), not the enqueue.  Sampling without truncation and
+ * greedy verification run both passes in one kernel: [0]/[1] bracket that
+ * kernel and [2]/[3] are recorded right after it.
  * Everything else, including every error, is as for specdec_verify. */
 specdec_status_t specdec_verify_profiled(const specdec_verify_desc_t* desc,
                                          const void* target_logits, const void* draft_logits,
@@ -307,7 +313,9 @@ size_t specdec_verify_tree_workspace_bytes(const specdec_tree_desc_t* desc);
  *       = 0), -1 after; feed it to specdec_commit_kv as the slot map with
  *       scratch_slots = N.
  *   flags         [B] uint32 or NULL: BAD_TREE, TOKEN_RANGE, NONFINITE,
- *       EOS, LENGTH.
+ *       EOS, LENGTH, WAIT_TIMEOUT.
+ * Runs as one kernel (statistics and decision workgroups in one launch);
+ * SPECDEC_FUSED=0 in the environment selects the two-kernel path.
  * Errors: INVALID_ARGUMENT (bad descriptor, NULL required pointer,
  *   misaligned workspace), WORKSPACE_TOO_SMALL; nothing is enqueued. */
 specdec_status_t specdec_verify_tree(const specdec_tree_desc_t* desc, const void* target_logits,
