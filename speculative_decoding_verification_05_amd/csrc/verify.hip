@@ -890,7 +890,8 @@ Layout make_layout(const specdec_verify_desc_t* d, bool point) {
     L.fwpr = (L.nc2 + L.fcpw - 1) / L.fcpw;
     const size_t B = static_cast<size_t>(d->batch);
     size_t off = 0;
-    // zero at rest: arrival counters, ready words, chunk-mass words
+    // zero at rest: arrival counters (two-kernel sampling path), statistics
+    // words and chunk-mass words (one-kernel paths)
     L.off_cnt = off; off = align256(off + B * 4);
     L.off_ready = off; off = align256(off + B * L.rows * L.nc * sizeof(uint64_t));
     L.off_cmass = off; off = align256(off + B * L.nc2 * sizeof(uint64_t));
