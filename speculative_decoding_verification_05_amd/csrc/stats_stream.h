@@ -106,7 +106,17 @@ __device__ __forceinline__ bool chunk_maxsum(const void* rp, int lo, int hi, flo
 #pragma unroll
             for (int k = 0; k < N; ++k) tm = fmaxf(tm, v[u].x[k]);
         const float mn = fmaxf(m, tm);
-        if (mn == neg_inf()) return;
+        if (mn == neg_inf()) {
+            // nothing finite yet in this lane (fmaxf skips NaNs): a NaN here
+            // still marks the row non-finite, as a +inf does (max +inf)
+            bool nan = false;
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+                for (int k = 0; k < N; ++k) nan |= v[u].x[k] != v[u].x[k];
+            if (nan) m = pos_inf();
+            return;
+        }
         float part = 0.0f;
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {

@@ -100,6 +100,61 @@ def test_ragged_full_size_sampled_requests():
     check_sample(wl, x, requests=req, label="ragged full (24 sampled requests)")
 
 
+def test_gamma_max_63_fills_the_wave():
+    """The largest gamma_max: 64 positions, the acceptance ballot spans a
+    whole wave.  Gamma 63 everywhere but one request with 0; one request
+    whose drafts equal its target rows accepts all 63 (sampling: p = q;
+    greedy: the drafts are the targets' argmaxes) and draws the bonus from
+    row 63."""
+    wl = W["b512_ragged_v262144_kv"].scaled(6, 3000, gamma_max=63, ragged=False)
+    x = synth.make_verify_inputs(wl)
+    assert np.all(x["gamma"] == 63)
+    x["gamma"][1] = 0
+    x["draft"][2] = x["target"][2, :63]
+    t32 = synth.bf16_bits_to_f32(x["target"]) if x["target"].dtype == np.uint16 else x["target"]
+    x["draft_tokens"][3] = np.argmax(t32[3, :63], axis=1).astype(np.int32)
+    _, got, _ = check_sample(wl, x, label="gamma_max 63 sampling")
+    assert got["accept_count"][2] == 63
+    _, gotg, _ = check_greedy(wl, x, label="gamma_max 63 greedy")
+    assert gotg["accept_count"][3] == 63
+
+
+def test_nan_rows_are_flagged():
+    """A used row that is all NaN, or whose first tile is all NaN, is flagged
+    NONFINITE (a NaN never reaches a finite maximum, so it must not vanish
+    from the statistics either); the other requests are exact."""
+    wl = W[synth.HEADLINE].scaled(6, 20000)
+    x = synth.make_verify_inputs(wl)
+    x["gamma"][:] = wl.gamma_max
+    nan = synth.BF16_QNAN
+    x["target"][0, 1, :] = nan             # a whole target row
+    x["draft"][1, 0, :] = nan              # a whole draft row
+    x["target"][2, 0, :8192] = nan         # the first tile of a row
+    for greedy in (False, True):
+        args = dict(bf16=True, greedy=greedy, temperature=wl.temperature, seed=wl.verify_seed)
+        got = gpu_verify(x, **args)
+        planted = [0, 2] if greedy else [0, 1, 2]  # greedy reads no draft rows
+        ref = oracle_verify(x, greedy=greedy, temperature=wl.temperature, seed=wl.verify_seed,
+                            requests=planted)
+        for k, b in enumerate(planted):
+            assert ref["flags"][k] & sd.FLAG_NONFINITE, (greedy, b)
+            assert got["flags"][b] & sd.FLAG_NONFINITE, (greedy, b, hex(int(got["flags"][b])))
+        rest = [3, 4, 5]
+        ref = oracle_verify(x, greedy=greedy, temperature=wl.temperature, seed=wl.verify_seed,
+                            requests=rest)
+        errs, _ = compare(ref, got, x["gamma"], greedy, rest, f"nan rows greedy={greedy}")
+        assert not errs, "\n".join(errs[:20])
+
+
+def test_largest_vocabulary():
+    """V at the limit: 1024 sampling-pass chunks per row (4194304 bf16 or
+    2097152 fp32 logits), sampling and greedy."""
+    check_sample(W[synth.HEADLINE].scaled(2, 1024 * 256 * 2 * 8, gamma_max=1), label="V max bf16")
+    check_sample(W["b8_g4_v32000_f32"].scaled(2, 1024 * 256 * 2 * 4, gamma_max=1), label="V max fp32")
+    check_greedy(W["b256_g7_v151936_greedy_kv"].scaled(2, 1024 * 256 * 2 * 8, gamma_max=1),
+                 label="V max greedy")
+
+
 def test_gamma_zero_is_a_plain_draw():
     wl = W[synth.HEADLINE].scaled(6, 5000)
     x = synth.make_verify_inputs(wl)
