@@ -120,3 +120,43 @@ def test_commit_bad_block_entry_is_flagged_and_skipped():
     assert fl[b] & sd.FLAG_BAD_BLOCK
     assert np.all(fl[[0, 1, 3, 4, 5]] == 0)
     assert np.array_equal(seq, kv.seq_lens + acc + 1)
+
+
+def test_commit_bad_slot_map_entry_is_flagged_and_skipped():
+    """A slot-map entry outside [0, S) skips its window position (the pool
+    keeps its old bytes there) and flags BAD_BLOCK; every other position and
+    request is committed as the oracle does with a valid map."""
+    import torch
+    wl = W["b256_g7_v151936_greedy_kv"].scaled(6, 64)
+    K = wl.kv
+    kv = synth.make_kv_inputs(wl)
+    G, B = wl.gamma_max, wl.batch
+    smap = np.tile(np.arange(G + 1, dtype=np.int32), (B, 1))
+    acc = np.full(B, 5, np.int32)
+    bad_b, bad_j = 2, 1
+    bad = smap.copy()
+    bad[bad_b, bad_j] = G + 1 + 3          # outside [0, S) with S = G + 1
+    desc = sd.make_kv_desc(B, G, K.layers, K.kv_heads, K.head_dim, K.block_size,
+                           kv.block_table.shape[1], kv.num_blocks, scratch_slots=G + 1)
+    ws = torch.zeros(sd.specdec_commit_kv_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    pool = to_dev(kv.pool, "cuda")
+    seq = to_dev(kv.seq_lens, "cuda")
+    fl = torch.zeros(B, dtype=torch.int32, device="cuda")
+    sd.specdec_commit_kv(desc, to_dev(kv.scratch, "cuda"), pool, to_dev(kv.block_table, "cuda"),
+                         to_dev(acc, "cuda"), None, to_dev(bad, "cuda"), seq, fl, ws)
+    torch.cuda.synchronize()
+    got_pool = pool.cpu().numpy().view(np.uint16)
+    got_seq, got_fl = seq.cpu().numpy(), fl.cpu().numpy()
+    want_pool = kv.pool.copy()
+    want_seq = kv.seq_lens.copy()
+    oracle.commit_kv(kv.scratch, want_pool, kv.block_table, acc, want_seq, None, slot_map=smap)
+    # the skipped position keeps what it held before the call
+    pos = int(kv.seq_lens[bad_b]) + bad_j
+    phys = int(kv.block_table[bad_b, pos // K.block_size])
+    view = want_pool.reshape(K.layers, 2, kv.num_blocks, K.block_size, -1)
+    view[:, :, phys, pos % K.block_size] = kv.pool.reshape(view.shape)[:, :, phys, pos % K.block_size]
+    assert got_fl[bad_b] & sd.FLAG_BAD_BLOCK
+    assert np.all(np.delete(got_fl, bad_b) == 0)
+    assert np.array_equal(got_seq, want_seq)
+    diff = np.argwhere(got_pool != want_pool)
+    assert diff.size == 0, f"pool differs at {diff[:5].tolist()}"
