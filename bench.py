@@ -27,7 +27,8 @@ its own slice of the requests.
 
 Other workloads (--workload) print the same JSON line for that recipe; the
 ones with a paged KV cache time a whole round: verify, the target's commit
-and the draft cache's rollback.  Each step of a graph has its own cache
+and the draft cache's rollback (one specdec_commit_and_rollback_kv launch;
+--separate-kv-calls times the two calls instead).  Each step of a graph has its own cache
 lengths, all restored by one small copy at the graph's start, so that every
 step commits into the same window.  Their JSON line also lists each kernel's average time
 and algorithmic bandwidth.
@@ -182,6 +183,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches, no graph")
+    ap.add_argument("--separate-kv-calls", action="store_true",
+                    help="KV recipes: commit and rollback as two calls instead of one launch")
     ap.add_argument("--pmc-copy-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a dispatch of "
                          "known size to calibrate FETCH_SIZE / WRITE_SIZE counters)")
@@ -286,12 +289,22 @@ def main() -> int:
         if kv is not None:
             kv["seqs"].copy_(kv["seqs0"])
 
+    def commit_and_rollback(i: int) -> None:
+        sd.specdec_commit_and_rollback_kv(kv["desc"], kv["scratch"], kv["pool"], kv["table"], None,
+                                          kv["seqs"][i, 0], None, kv["ws"], kv["ddesc"], kv["dpool"],
+                                          kv["table"], kv["seqs"][i, 1], None, kv["dws"],
+                                          ver.accept_count, dev_in[i % sets]["gamma"])
+
     def step(i: int) -> None:
         d = dev_in[i % sets]
         ver(d["target"], d["draft"], d["tokens"], d["gamma"])
         if kv is not None:
-            commit(i)
-            rollback(i)
+            if args.separate_kv_calls:
+                commit(i)
+                rollback(i)
+            else:
+                # the target's commit and the draft's rollback in one launch
+                commit_and_rollback(i)
 
     def enqueue(n: int) -> None:
         reset()
@@ -469,6 +482,8 @@ def main() -> int:
                    "logits": wl0.dtype, "mode": wl0.mode, "temperature": wl0.temperature,
                    "top_k": wl0.top_k, "top_p": wl0.top_p, "kv_commit": wl0.kv is not None,
                    "draft_rollback": wl0.draft_kv is not None,
+                   "commit_and_rollback": ("two launches" if args.separate_kv_calls else "one launch")
+                   if wl0.kv is not None else None,
                    "rotating_input_sets": sets, "steps_per_graph": per,
                    "launch": "hipgraph" if runner.graphed else "eager",
                    "committed_tokens_per_s": committed / sec_per_step,

@@ -15,6 +15,8 @@
  *                      invalidates the rejected slots and sets the new length.
  *   specdec_rollback_kv  brings the draft model's paged cache back to the
  *                      committed sequence.
+ *   specdec_commit_and_rollback_kv  both of the above for one round, in one
+ *                      launch.
  *
  * Passages defining these operations (page title, section):
  *   - "Speculative decoding tutorial: from distribution preservation and
@@ -409,6 +411,26 @@ specdec_status_t specdec_rollback_kv(const specdec_kv_desc_t* desc, void* kv_poo
                                      const int32_t* gamma, int32_t* seq_lens, uint32_t* flags,
                                      void* workspace, size_t workspace_bytes,
                                      hipStream_t stream);
+
+/* specdec_commit_kv on the target's cache and specdec_rollback_kv on the
+ * draft's, for the same round, in one launch (AI-infra KB M013 s.06: both
+ * caches return to the committed context after verification; both updates
+ * depend only on accept_count, so their workgroups run side by side).
+ * Arguments and results are exactly those of the two calls: the first group
+ * (desc ... workspace_bytes) as for specdec_commit_kv, the second (draft_desc
+ * ... draft_workspace_bytes) as for specdec_rollback_kv, with accept_count and
+ * gamma shared; the two descriptors must agree on batch and gamma_max.  Rows
+ * that do not take 16-byte vectors are served by two launches in order.
+ * Errors: as for the two calls, plus INVALID_ARGUMENT when batch or gamma_max
+ * differ; nothing is enqueued in any error case. */
+specdec_status_t specdec_commit_and_rollback_kv(
+    const specdec_kv_desc_t* desc, const void* scratch_kv, void* kv_pool,
+    const int32_t* block_table, const int32_t* slot_map, int32_t* seq_lens, uint32_t* flags,
+    void* workspace, size_t workspace_bytes,
+    const specdec_kv_desc_t* draft_desc, void* draft_pool, const int32_t* draft_block_table,
+    int32_t* draft_seq_lens, uint32_t* draft_flags, void* draft_workspace,
+    size_t draft_workspace_bytes,
+    const int32_t* accept_count, const int32_t* gamma, hipStream_t stream);
 
 /* ------------------------------------------------------------------ misc */
 

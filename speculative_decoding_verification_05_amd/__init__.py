@@ -38,6 +38,7 @@ FLAG_WAIT_TIMEOUT = 0x400
 # exported symbols of include/specdec.h
 EXPORTS = ("specdec_verify_workspace_bytes", "specdec_verify", "specdec_verify_profiled",
            "specdec_commit_kv_workspace_bytes", "specdec_commit_kv", "specdec_rollback_kv",
+           "specdec_commit_and_rollback_kv",
            "specdec_verify_tree_workspace_bytes", "specdec_verify_tree",
            "specdec_verify_tree_profiled", "specdec_propose_ngram",
            "specdec_propose_ngram_workspace_bytes",
@@ -102,6 +103,10 @@ def lib() -> ctypes.CDLL:
         L.specdec_commit_kv.restype = ctypes.c_int
         L.specdec_rollback_kv.argtypes = [ctypes.POINTER(KVDesc)] + [P] * 7 + [S, P]
         L.specdec_rollback_kv.restype = ctypes.c_int
+        L.specdec_commit_and_rollback_kv.argtypes = (
+            [ctypes.POINTER(KVDesc)] + [P] * 7 + [S] + [ctypes.POINTER(KVDesc)] + [P] * 5 + [S]
+            + [P] * 3)
+        L.specdec_commit_and_rollback_kv.restype = ctypes.c_int
         L.specdec_verify_tree_workspace_bytes.argtypes = [ctypes.POINTER(TreeDesc)]
         L.specdec_verify_tree_workspace_bytes.restype = S
         L.specdec_verify_tree.argtypes = [ctypes.POINTER(TreeDesc)] + [P] * 11 + [S, P]
@@ -290,6 +295,21 @@ def specdec_rollback_kv(desc: KVDesc, kv_pool, block_table, accept_count, gamma,
                                    _ptr(workspace), int(workspace_bytes), _stream(stream))
     if st != SPECDEC_OK:
         raise SpecdecError(st, "specdec_rollback_kv")
+
+
+def specdec_commit_and_rollback_kv(desc: KVDesc, scratch_kv, kv_pool, block_table, slot_map,
+                                   seq_lens, flags, workspace, draft_desc: KVDesc, draft_pool,
+                                   draft_block_table, draft_seq_lens, draft_flags,
+                                   draft_workspace, accept_count, gamma, stream=None) -> None:
+    st = lib().specdec_commit_and_rollback_kv(
+        ctypes.byref(desc), _ptr(scratch_kv), _ptr(kv_pool), _ptr(block_table), _ptr(slot_map),
+        _ptr(seq_lens), _ptr(flags), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        ctypes.byref(draft_desc), _ptr(draft_pool), _ptr(draft_block_table), _ptr(draft_seq_lens),
+        _ptr(draft_flags), _ptr(draft_workspace),
+        draft_workspace.numel() * draft_workspace.element_size(),
+        _ptr(accept_count), _ptr(gamma), _stream(stream))
+    if st != SPECDEC_OK:
+        raise SpecdecError(st, "specdec_commit_and_rollback_kv")
 
 
 def specdec_workspace_clear(workspace, nbytes: Optional[int] = None, stream=None) -> None:

@@ -47,9 +47,9 @@ struct CommitParams {
     int hd;                    // H * D elements per run
 };
 
+// Window position j of request b (one workgroup).
 template <bool VEC>
-__global__ __launch_bounds__(kThreads) void k_commit(CommitParams P) {
-    const int j = blockIdx.x, b = blockIdx.y;
+__device__ __forceinline__ void commit_slot(const CommitParams& P, const int j, const int b) {
     // independent loads first (the slot map entry is in bounds for every j)
     const int g = P.gamma ? P.gamma[b] : P.G;
     const int m = P.accept[b];
@@ -143,6 +143,20 @@ __global__ __launch_bounds__(kThreads) void k_commit(CommitParams P) {
     }
 }
 
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void k_commit(CommitParams P) {
+    commit_slot<VEC>(P, blockIdx.x, blockIdx.y);
+}
+
+// A target commit (z = 0) and a draft rollback (z = 1) of one round in one
+// launch: both depend only on the accept counts, so their workgroups run
+// side by side.  Each branch reads its own kernel argument directly.
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void k_commit_pair(CommitParams A, CommitParams R) {
+    if (blockIdx.z == 0) commit_slot<VEC>(A, blockIdx.x, blockIdx.y);
+    else commit_slot<VEC>(R, blockIdx.x, blockIdx.y);
+}
+
 __global__ void k_fill_zero(uint32_t* p, size_t n) {
     for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
          i += static_cast<size_t>(gridDim.x) * blockDim.x)
@@ -178,20 +192,48 @@ extern "C" size_t specdec_commit_kv_workspace_bytes(const specdec_kv_desc_t* d) 
     return (static_cast<size_t>(d->batch) * 4 + 255) & ~static_cast<size_t>(255);
 }
 
-extern "C" specdec_status_t specdec_commit_kv(const specdec_kv_desc_t* d, const void* scratch_kv,
-                                              void* kv_pool, const int32_t* block_table,
-                                              const int32_t* accept_count, const int32_t* gamma,
-                                              const int32_t* slot_map, int32_t* seq_lens,
-                                              uint32_t* flags, void* workspace,
-                                              size_t workspace_bytes, hipStream_t stream) {
+namespace specdec {
+namespace {
+
+// Host-side checks of a commit's arguments (accept_count checked by the callers).
+specdec_status_t check_commit(const specdec_kv_desc_t* d, const void* scratch_kv, void* kv_pool,
+                              const int32_t* block_table, const int32_t* slot_map,
+                              int32_t* seq_lens, void* workspace, size_t workspace_bytes) {
     if (!valid_kv(d)) return SPECDEC_ERR_INVALID_ARGUMENT;
-    if (!scratch_kv || !kv_pool || !block_table || !accept_count || !seq_lens || !workspace)
+    if (!scratch_kv || !kv_pool || !block_table || !seq_lens || !workspace)
         return SPECDEC_ERR_INVALID_ARGUMENT;
     // without a slot map, window position j reads slot j: S must cover G+1
     if (!slot_map && d->scratch_slots != 0 && d->scratch_slots < d->gamma_max + 1)
         return SPECDEC_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < specdec_commit_kv_workspace_bytes(d)) return SPECDEC_ERR_WORKSPACE_TOO_SMALL;
     if ((reinterpret_cast<uintptr_t>(workspace) & 3u) != 0) return SPECDEC_ERR_INVALID_ARGUMENT;
+    return SPECDEC_OK;
+}
+
+// ... and of a rollback's.
+specdec_status_t check_rollback(const specdec_kv_desc_t* d, void* kv_pool, const int32_t* block_table,
+                                int32_t* seq_lens, void* workspace, size_t workspace_bytes) {
+    if (!valid_kv(d)) return SPECDEC_ERR_INVALID_ARGUMENT;
+    if (!kv_pool || !block_table || !seq_lens || !workspace) return SPECDEC_ERR_INVALID_ARGUMENT;
+    if (d->scratch_slots != 0) return SPECDEC_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < specdec_commit_kv_workspace_bytes(d)) return SPECDEC_ERR_WORKSPACE_TOO_SMALL;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 3u) != 0) return SPECDEC_ERR_INVALID_ARGUMENT;
+    return SPECDEC_OK;
+}
+
+}  // namespace
+}  // namespace specdec
+
+extern "C" specdec_status_t specdec_commit_kv(const specdec_kv_desc_t* d, const void* scratch_kv,
+                                              void* kv_pool, const int32_t* block_table,
+                                              const int32_t* accept_count, const int32_t* gamma,
+                                              const int32_t* slot_map, int32_t* seq_lens,
+                                              uint32_t* flags, void* workspace,
+                                              size_t workspace_bytes, hipStream_t stream) {
+    const specdec_status_t st = check_commit(d, scratch_kv, kv_pool, block_table, slot_map, seq_lens,
+                                             workspace, workspace_bytes);
+    if (st != SPECDEC_OK) return st;
+    if (!accept_count) return SPECDEC_ERR_INVALID_ARGUMENT;
     if (d->batch == 0) return SPECDEC_OK;
     return launch_commit(d, scratch_kv, slot_map, kv_pool, block_table, accept_count, gamma,
                          seq_lens, flags, workspace, stream);
@@ -200,11 +242,12 @@ extern "C" specdec_status_t specdec_commit_kv(const specdec_kv_desc_t* d, const 
 namespace specdec {
 namespace {
 
-specdec_status_t launch_commit(const specdec_kv_desc_t* d, const void* scratch_kv,
-                               const int32_t* slot_map, void* kv_pool,
-                               const int32_t* block_table, const int32_t* accept_count,
-                               const int32_t* gamma, int32_t* seq_lens, uint32_t* flags,
-                               void* workspace, hipStream_t stream) {
+// Kernel parameters of one commit (scratch_kv null: a rollback); *vec:
+// whether 16-byte vectors fit the rows and both buffers' alignment.
+CommitParams commit_params(const specdec_kv_desc_t* d, const void* scratch_kv,
+                           const int32_t* slot_map, void* kv_pool, const int32_t* block_table,
+                           const int32_t* accept_count, const int32_t* gamma, int32_t* seq_lens,
+                           uint32_t* flags, void* workspace, bool* vec) {
     CommitParams P{};
     P.scratch = static_cast<const uint16_t*>(scratch_kv);
     P.slot_map = slot_map;
@@ -225,8 +268,19 @@ specdec_status_t launch_commit(const specdec_kv_desc_t* d, const void* scratch_k
     P.maxb = d->max_blocks_per_req;
     P.NB = d->num_blocks;
     P.hd = d->num_kv_heads * d->head_dim;
-    const bool vec = (P.hd % 8 == 0) && (reinterpret_cast<uintptr_t>(scratch_kv) & 15u) == 0 &&
-                     (reinterpret_cast<uintptr_t>(kv_pool) & 15u) == 0;
+    *vec = (P.hd % 8 == 0) && (reinterpret_cast<uintptr_t>(scratch_kv) & 15u) == 0 &&
+           (reinterpret_cast<uintptr_t>(kv_pool) & 15u) == 0;
+    return P;
+}
+
+specdec_status_t launch_commit(const specdec_kv_desc_t* d, const void* scratch_kv,
+                               const int32_t* slot_map, void* kv_pool,
+                               const int32_t* block_table, const int32_t* accept_count,
+                               const int32_t* gamma, int32_t* seq_lens, uint32_t* flags,
+                               void* workspace, hipStream_t stream) {
+    bool vec;
+    const CommitParams P = commit_params(d, scratch_kv, slot_map, kv_pool, block_table, accept_count,
+                                         gamma, seq_lens, flags, workspace, &vec);
     const dim3 grid(d->gamma_max + 1, d->batch);
     if (vec)
         hipLaunchKernelGGL(k_commit<true>, grid, dim3(kThreads), 0, stream, P);
@@ -244,15 +298,48 @@ extern "C" specdec_status_t specdec_rollback_kv(const specdec_kv_desc_t* d, void
                                                 int32_t* seq_lens, uint32_t* flags,
                                                 void* workspace, size_t workspace_bytes,
                                                 hipStream_t stream) {
-    if (!valid_kv(d)) return SPECDEC_ERR_INVALID_ARGUMENT;
-    if (!kv_pool || !block_table || !accept_count || !seq_lens || !workspace)
-        return SPECDEC_ERR_INVALID_ARGUMENT;
-    if (d->scratch_slots != 0) return SPECDEC_ERR_INVALID_ARGUMENT;
-    if (workspace_bytes < specdec_commit_kv_workspace_bytes(d)) return SPECDEC_ERR_WORKSPACE_TOO_SMALL;
-    if ((reinterpret_cast<uintptr_t>(workspace) & 3u) != 0) return SPECDEC_ERR_INVALID_ARGUMENT;
+    const specdec_status_t st = check_rollback(d, kv_pool, block_table, seq_lens, workspace,
+                                               workspace_bytes);
+    if (st != SPECDEC_OK) return st;
+    if (!accept_count) return SPECDEC_ERR_INVALID_ARGUMENT;
     if (d->batch == 0) return SPECDEC_OK;
     return launch_commit(d, nullptr, nullptr, kv_pool, block_table, accept_count, gamma, seq_lens,
                          flags, workspace, stream);
+}
+
+extern "C" specdec_status_t specdec_commit_and_rollback_kv(
+    const specdec_kv_desc_t* d, const void* scratch_kv, void* kv_pool, const int32_t* block_table,
+    const int32_t* slot_map, int32_t* seq_lens, uint32_t* flags, void* workspace,
+    size_t workspace_bytes, const specdec_kv_desc_t* dd, void* draft_pool,
+    const int32_t* draft_block_table, int32_t* draft_seq_lens, uint32_t* draft_flags,
+    void* draft_workspace, size_t draft_workspace_bytes, const int32_t* accept_count,
+    const int32_t* gamma, hipStream_t stream) {
+    specdec_status_t st = check_commit(d, scratch_kv, kv_pool, block_table, slot_map, seq_lens,
+                                       workspace, workspace_bytes);
+    if (st != SPECDEC_OK) return st;
+    st = check_rollback(dd, draft_pool, draft_block_table, draft_seq_lens, draft_workspace,
+                        draft_workspace_bytes);
+    if (st != SPECDEC_OK) return st;
+    if (!accept_count || d->batch != dd->batch || d->gamma_max != dd->gamma_max)
+        return SPECDEC_ERR_INVALID_ARGUMENT;
+    if (d->batch == 0) return SPECDEC_OK;
+    bool va, vr;
+    const CommitParams A = commit_params(d, scratch_kv, slot_map, kv_pool, block_table, accept_count,
+                                         gamma, seq_lens, flags, workspace, &va);
+    const CommitParams R = commit_params(dd, nullptr, nullptr, draft_pool, draft_block_table,
+                                         accept_count, gamma, draft_seq_lens, draft_flags,
+                                         draft_workspace, &vr);
+    if (!(va && vr)) {
+        // rows that do not take 16-byte vectors: the two launches one after the other
+        st = launch_commit(d, scratch_kv, slot_map, kv_pool, block_table, accept_count, gamma,
+                           seq_lens, flags, workspace, stream);
+        if (st != SPECDEC_OK) return st;
+        return launch_commit(dd, nullptr, nullptr, draft_pool, draft_block_table, accept_count,
+                             gamma, draft_seq_lens, draft_flags, draft_workspace, stream);
+    }
+    hipLaunchKernelGGL(k_commit_pair<true>, dim3(d->gamma_max + 1, d->batch, 2), dim3(kThreads), 0,
+                       stream, A, R);
+    return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_DEVICE;
 }
 
 extern "C" specdec_status_t specdec_workspace_clear(void* workspace, size_t bytes, hipStream_t stream) {

@@ -146,6 +146,61 @@ def test_rollback_matches_oracle(name, batch):
     assert diff.size == 0, f"pool differs at {diff[:5].tolist()}"
 
 
+@pytest.mark.parametrize("name,batch", [("b256_g7_v151936_greedy_kv", 64),
+                                        ("b512_ragged_v262144_kv", 48),
+                                        ("b256_g7_v151936_greedy_kv", 256)])
+def test_commit_and_rollback_in_one_launch(name, batch):
+    """specdec_commit_and_rollback_kv writes exactly what specdec_commit_kv and
+    specdec_rollback_kv write (both caches, lengths and flags byte for byte),
+    including a bogus block-table entry in one request, and agrees with the
+    oracle's rollback on the draft cache."""
+    import torch
+    wl = W[name] if batch == W[name].batch else W[name].scaled(batch, 64)
+    K, DK = wl.kv, wl.draft_kv
+    g = np.array([synth.request_gamma(wl, b) for b in range(wl.batch)], np.int32)
+    rng = np.random.default_rng(batch + 1)
+    acc = np.array([rng.integers(0, gg + 1) for gg in g], np.int32)
+    acc[::5] = g[::5]
+    gamma = g if wl.ragged else None
+    kv = synth.make_kv_inputs(wl)
+    table = kv.block_table.copy()
+    b_bad = 3
+    table[b_bad, (int(kv.seq_lens[b_bad]) + int(g[b_bad])) // K.block_size] = kv.num_blocks + 7
+    dpool, dtable, dseq, dnb = synth.make_draft_kv_inputs(wl, kv)
+    desc = sd.make_kv_desc(wl.batch, wl.gamma_max, K.layers, K.kv_heads, K.head_dim, K.block_size,
+                           table.shape[1], kv.num_blocks)
+    ddesc = sd.make_kv_desc(wl.batch, wl.gamma_max, DK.layers, DK.kv_heads, DK.head_dim,
+                            DK.block_size, dtable.shape[1], dnb)
+
+    def run(one_launch):
+        ws = torch.zeros(sd.specdec_commit_kv_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+        dws = torch.zeros(sd.specdec_commit_kv_workspace_bytes(ddesc), dtype=torch.uint8, device="cuda")
+        pool, seq = to_dev(kv.pool, "cuda"), to_dev(kv.seq_lens, "cuda")
+        dp, ds = to_dev(dpool, "cuda"), to_dev(dseq, "cuda")
+        fl = torch.zeros(wl.batch, dtype=torch.int32, device="cuda")
+        dfl = torch.zeros(wl.batch, dtype=torch.int32, device="cuda")
+        a, gm = to_dev(acc, "cuda"), None if gamma is None else to_dev(gamma, "cuda")
+        sc, tb, dtb = to_dev(kv.scratch, "cuda"), to_dev(table, "cuda"), to_dev(dtable, "cuda")
+        if one_launch:
+            sd.specdec_commit_and_rollback_kv(desc, sc, pool, tb, None, seq, fl, ws,
+                                              ddesc, dp, dtb, ds, dfl, dws, a, gm)
+        else:
+            sd.specdec_commit_kv(desc, sc, pool, tb, a, gm, None, seq, fl, ws)
+            sd.specdec_rollback_kv(ddesc, dp, dtb, a, gm, ds, dfl, dws)
+        torch.cuda.synchronize()
+        return [x.cpu().numpy() for x in (pool, seq, fl, dp, ds, dfl)]
+
+    say(f"[commit+rollback] {name} B={wl.batch}: two calls, then one launch")
+    ref = run(False)
+    got = run(True)
+    for k, (x, y) in enumerate(zip(got, ref)):
+        assert np.array_equal(x, y), ("pool", "seq", "flags", "draft pool", "draft seq", "draft flags")[k]
+    assert got[2][b_bad] & sd.FLAG_BAD_BLOCK
+    want_dpool, want_dseq = dpool.copy(), dseq.copy()
+    oracle.rollback_kv(want_dpool, dtable, acc, want_dseq, wl.gamma_max, gamma)
+    assert np.array_equal(got[3].view(np.uint16), want_dpool) and np.array_equal(got[4], want_dseq)
+
+
 # ------------------------------------------------------------ one round in a graph
 
 def test_round_in_hip_graph_replays():
