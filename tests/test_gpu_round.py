@@ -203,10 +203,12 @@ def test_commit_and_rollback_in_one_launch(name, batch):
 
 # ------------------------------------------------------------ one round in a graph
 
-def test_round_in_hip_graph_replays():
-    """verify (greedy, EOS and budget) -> target commit -> draft rollback,
-    captured once and replayed three times; before each replay the caches are
-    reset by eager copies, and each replay must equal the oracle."""
+@pytest.mark.parametrize("one_launch", [False, True], ids=["two calls", "one launch"])
+def test_round_in_hip_graph_replays(one_launch):
+    """verify (greedy, EOS and budget) -> target commit -> draft rollback (as
+    two calls, or as specdec_commit_and_rollback_kv), captured once and
+    replayed three times; before each replay the caches are reset by eager
+    copies, and each replay must equal the oracle."""
     import torch
     wl = W["b256_g7_v151936_greedy_kv"].scaled(32, 8192)
     x = synth.make_verify_inputs(wl, need_draft_logits=False)
@@ -233,6 +235,10 @@ def test_round_in_hip_graph_replays():
 
     def round_():
         ver(t_dev, None, tok_dev, None, mt_dev)
+        if one_launch:
+            sd.specdec_commit_and_rollback_kv(tdesc, scratch, pool, tbl, None, seq, None, ws_t, ddesc,
+                                              dpool_d, tbl, dseq_d, None, ws_d, ver.accept_count, None)
+            return
         sd.specdec_commit_kv(tdesc, scratch, pool, tbl, ver.accept_count, None, None, seq, None,
                              ws_t)
         sd.specdec_rollback_kv(ddesc, dpool_d, tbl, ver.accept_count, None, dseq_d, None, ws_d)
