@@ -216,6 +216,29 @@ specdec_status_t specdec_verify_profiled(const specdec_verify_desc_t* desc,
                                          void* workspace, size_t workspace_bytes,
                                          hipStream_t stream, hipEvent_t* stage_events);
 
+/* specdec_verify for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and errors as specdec_verify, without the
+ * workspace: the library uses its own, a 16 MiB device array per GPU (held
+ * until the process ends), located with hipGetSymbolAddress on the first call
+ * on each device, with that device current.  The call allocates nothing.
+ *   - WORKSPACE_TOO_SMALL when specdec_verify_workspace_bytes(desc) exceeds
+ *     16 MiB (nothing is enqueued).
+ *   - Each call first clears, on `stream`, the parts of the array that must be
+ *     zero (a fill kernel, no hipMemset), so consecutive calls may use any
+ *     descriptors.
+ *   - All calls on one GPU share the array: calls that overlap on one GPU
+ *     (different streams without ordering, several host threads) race.
+ *   - `stream` must belong to the current device. */
+specdec_status_t specdec_verify_noalloc(const specdec_verify_desc_t* desc,
+                                        const void* target_logits, const void* draft_logits,
+                                        const int32_t* draft_tokens, const int32_t* gamma,
+                                        const int32_t* max_tokens,
+                                        int32_t* accept_count, int32_t* num_tokens,
+                                        int32_t* out_tokens,
+                                        float* p_draft, float* q_draft, float* residual_mass,
+                                        uint32_t* flags, hipStream_t stream);
+
 /* ------------------------------------------------------------- commit K/V */
 
 typedef struct specdec_kv_desc {

@@ -42,7 +42,8 @@ EXPORTS = ("specdec_verify_workspace_bytes", "specdec_verify", "specdec_verify_p
            "specdec_verify_tree_workspace_bytes", "specdec_verify_tree",
            "specdec_verify_tree_profiled", "specdec_propose_ngram",
            "specdec_propose_ngram_workspace_bytes",
-           "specdec_workspace_clear", "specdec_status_string", "specdec_abi_version")
+           "specdec_workspace_clear", "specdec_status_string", "specdec_abi_version",
+           "specdec_verify_noalloc")
 
 
 class VerifyDesc(ctypes.Structure):
@@ -97,6 +98,8 @@ def lib() -> ctypes.CDLL:
         L.specdec_verify.restype = ctypes.c_int
         L.specdec_verify_profiled.argtypes = [ctypes.POINTER(VerifyDesc)] + [P] * 13 + [S, P, P]
         L.specdec_verify_profiled.restype = ctypes.c_int
+        L.specdec_verify_noalloc.argtypes = [ctypes.POINTER(VerifyDesc)] + [P] * 12 + [P]
+        L.specdec_verify_noalloc.restype = ctypes.c_int
         L.specdec_commit_kv_workspace_bytes.argtypes = [ctypes.POINTER(KVDesc)]
         L.specdec_commit_kv_workspace_bytes.restype = S
         L.specdec_commit_kv.argtypes = [ctypes.POINTER(KVDesc)] + [P] * 9 + [S, P]
@@ -252,6 +255,19 @@ def specdec_verify(desc: VerifyDesc, target_logits, draft_logits, draft_tokens, 
                               int(workspace_bytes), _stream(stream))
     if st != SPECDEC_OK:
         raise SpecdecError(st, "specdec_verify")
+
+
+def specdec_verify_noalloc(desc: VerifyDesc, target_logits, draft_logits, draft_tokens, gamma,
+                           max_tokens, accept_count, num_tokens, out_tokens, p_draft, q_draft,
+                           residual_mass, flags, stream=None) -> None:
+    """specdec_verify with the library's own per-GPU workspace (no allocation)."""
+    st = lib().specdec_verify_noalloc(ctypes.byref(desc), _ptr(target_logits), _ptr(draft_logits),
+                                      _ptr(draft_tokens), _ptr(gamma), _ptr(max_tokens),
+                                      _ptr(accept_count), _ptr(num_tokens),
+                                      _ptr(out_tokens), _ptr(p_draft), _ptr(q_draft),
+                                      _ptr(residual_mass), _ptr(flags), _stream(stream))
+    if st != SPECDEC_OK:
+        raise SpecdecError(st, "specdec_verify_noalloc")
 
 
 def specdec_verify_profiled(desc: VerifyDesc, target_logits, draft_logits, draft_tokens, gamma,

@@ -51,6 +51,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <mutex>
 
 namespace specdec {
 namespace {
@@ -908,6 +909,38 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+__global__ void k_zero_words(uint32_t* p, size_t n) {
+    for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
+         i += static_cast<size_t>(gridDim.x) * blockDim.x)
+        p[i] = 0u;
+}
+
+// ------------------------------------------------------------------ allocation-free variant
+// The workspace of specdec_verify_noalloc: a file-scope device array, one
+// copy per GPU the library runs on, held until the process ends.  Host code
+// never passes the array's name to a kernel (in host code it is only a
+// stand-in for the symbol): each device's address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kNoAllocBytes = size_t{16} << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+constexpr int kNoAllocDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kNoAllocDevices] = {};
+
+// The current device's copy of `scratch` (set up on its first use).
+specdec_status_t noalloc_workspace(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoAllocDevices) return SPECDEC_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SPECDEC_ERR_DEVICE;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return SPECDEC_OK;
+}
+
 // Launch the passes of one call.  ev (may be null) holds start/stop events of
 // the statistics pass and of the sampling pass; they bracket the kernels
 // themselves (hipExtLaunchKernel), not the host-side enqueue.
@@ -966,7 +999,7 @@ specdec_status_t verify_impl(const specdec_verify_desc_t* d, const void* target_
                              int32_t* accept_count, int32_t* num_tokens, int32_t* out_tokens,
                              float* p_draft, float* q_draft, float* residual_mass, uint32_t* flags,
                              void* workspace, size_t workspace_bytes, hipStream_t stream,
-                             hipEvent_t* ev) {
+                             hipEvent_t* ev, bool clear_counters = false) {
     if (!valid_desc(d)) return SPECDEC_ERR_INVALID_ARGUMENT;
     const bool sample = d->mode == SPECDEC_SAMPLE;
     if (!target_logits || !accept_count || !out_tokens || !workspace)
@@ -980,6 +1013,15 @@ specdec_status_t verify_impl(const specdec_verify_desc_t* d, const void* target_
     if (workspace_bytes < L.total) return SPECDEC_ERR_WORKSPACE_TOO_SMALL;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return SPECDEC_ERR_INVALID_ARGUMENT;
     if (d->batch == 0) return SPECDEC_OK;
+    if (clear_counters) {
+        // the sections that must be zero at first use (arrival counters and
+        // hand-off words) lie before the partials: one fill kernel
+        const size_t n = L.off_part / 4;
+        const unsigned grid = static_cast<unsigned>(std::min<size_t>((n + kThreads - 1) / kThreads, 1024));
+        hipLaunchKernelGGL(k_zero_words, dim3(grid), dim3(kThreads), 0, stream,
+                           static_cast<uint32_t*>(workspace), n);
+        if (hipGetLastError() != hipSuccess) return SPECDEC_ERR_DEVICE;
+    }
 
     VerifyParams P{};
     P.target = target_logits;
@@ -1079,4 +1121,21 @@ extern "C" specdec_status_t specdec_verify_profiled(
     return verify_impl(d, target_logits, draft_logits, draft_tokens, gamma, max_tokens,
                        accept_count, num_tokens, out_tokens, p_draft, q_draft, residual_mass,
                        flags, workspace, workspace_bytes, stream, stage_events);
+}
+
+extern "C" specdec_status_t specdec_verify_noalloc(
+    const specdec_verify_desc_t* d, const void* target_logits, const void* draft_logits,
+    const int32_t* draft_tokens, const int32_t* gamma, const int32_t* max_tokens,
+    int32_t* accept_count, int32_t* num_tokens, int32_t* out_tokens, float* p_draft,
+    float* q_draft, float* residual_mass, uint32_t* flags, hipStream_t stream) {
+    if (!valid_desc(d)) return SPECDEC_ERR_INVALID_ARGUMENT;
+    if (specdec_verify_workspace_bytes(d) > kNoAllocBytes) return SPECDEC_ERR_WORKSPACE_TOO_SMALL;
+    void* ws = nullptr;
+    const specdec_status_t st = noalloc_workspace(&ws);
+    if (st != SPECDEC_OK) return st;
+    // the array keeps the previous call's contents (maybe another layout):
+    // its zero-at-first-use sections are cleared on the stream first
+    return verify_impl(d, target_logits, draft_logits, draft_tokens, gamma, max_tokens,
+                       accept_count, num_tokens, out_tokens, p_draft, q_draft, residual_mass,
+                       flags, ws, kNoAllocBytes, stream, nullptr, true);
 }

@@ -215,3 +215,16 @@ def test_flag_and_status_constants_match_header():
     codes = dict(re.findall(r"SPECDEC_(OK|ERR_[A-Z_]+)\s*=\s*(\d+)", text))
     for name, val in codes.items():
         assert getattr(sd, "SPECDEC_" + name) == int(val), name
+
+
+def test_noalloc_refuses_oversized_descriptors_before_any_launch():
+    """specdec_verify_noalloc checks the descriptor and its workspace size on
+    the host: a request above the library's 16 MiB array is refused without
+    touching any argument (here, addresses nothing may dereference)."""
+    L = sd.lib()
+    desc = sd.make_verify_desc(512, 8, 262144, top_k=50, temperature=1.0)
+    assert sd.specdec_verify_workspace_bytes(desc) > 16 << 20
+    st = L.specdec_verify_noalloc(ctypes.byref(desc), *([16] * 12), None)
+    assert st == sd.SPECDEC_ERR_WORKSPACE_TOO_SMALL
+    bad = sd.make_verify_desc(4, 2, 1000, temperature=0.0)
+    assert L.specdec_verify_noalloc(ctypes.byref(bad), *([16] * 12), None) == sd.SPECDEC_ERR_INVALID_ARGUMENT
