@@ -15,8 +15,7 @@ gap between replays is amortized), bracketed by torch.cuda.synchronize();
 value = verified positions / second.
 The roofline entry is the dominant kernel: the one-kernel verify of the
 sampling, greedy and tree paths (statistics and decision workgroups in one
-launch), the selection kernel on the truncation path, or the statistics
-kernel with SPECDEC_FUSED=0.  It is
+launch), or the selection kernel on the truncation path.  It is
 the kernel's algorithmic bytes per launch (every used logits row read once,
 plus draft tokens and outputs) over its average duration, timed live with
 start/stop events that bracket the kernel itself (specdec_verify_profiled).
@@ -140,12 +139,13 @@ def measured_traffic(kernel_workload: str):
     return float(fields["traffic_bytes_per_launch"])
 
 
-def oracle_all_cores(run_slice, weights, seconds):
+def oracle_all_cores(run_slice, weights, seconds, firsts=None):
     """The oracle, as it stands, on every host core this process may use (at
     most 16, one GPU's share of the box): one thread per core, each running
     the oracle again and again over its own slice of the items (the oracle is
     C behind ctypes, which releases the GIL).  Returns (weight per second,
-    threads, seconds, passes)."""
+    threads, seconds, passes); firsts (a list), if given, receives
+    (slice, output of its first pass) per thread."""
     from concurrent.futures import ThreadPoolExecutor
     try:
         ncpu = len(os.sched_getaffinity(0))
@@ -159,7 +159,9 @@ def oracle_all_cores(run_slice, weights, seconds):
     def worker(ix):
         done, passes = 0.0, 0
         while True:
-            run_slice(ix)
+            r = run_slice(ix)
+            if passes == 0 and firsts is not None:
+                firsts.append((ix, r))
             done += float(np.sum(weights[ix]))
             passes += 1
             if time.perf_counter() >= stop:
@@ -170,6 +172,51 @@ def oracle_all_cores(run_slice, weights, seconds):
         out = list(ex.map(worker, slices))
     t = time.perf_counter() - t0
     return sum(d for d, _ in out) / t, nt, t, min(p for _, p in out)
+
+
+PROB_ABS, PROB_REL = 1e-5, 1e-4  # probabilities: 1e-5 absolute or 1e-4 relative
+
+
+def parity(ref, got, gamma, greedy):
+    """GPU outputs against the oracle's, request by request: accept count,
+    tokens, token count and flags bit-exact, p(d), q(d) and the residual mass
+    within tolerance.  A request whose oracle run met a draw within 1e-6 of
+    its threshold (near_pos >= 0) is compared up to that decision only and
+    counted.  Returns (requests compared, near-threshold requests, ids of
+    mismatching requests)."""
+    bad, near = [], 0
+    B = len(ref["accept_count"])
+    for b in range(B):
+        g, npos = int(gamma[b]), int(ref["near_pos"][b])
+        m_ref, m_got = int(ref["accept_count"][b]), int(got["accept_count"][b])
+        ok = True
+        if npos >= 0:
+            near += 1
+            ok &= not (m_got < npos <= m_ref)
+            ok &= list(got["out_tokens"][b][:npos]) == list(ref["out_tokens"][b][:npos])
+        else:
+            ok &= m_got == m_ref
+            ok &= list(got["out_tokens"][b]) == list(ref["out_tokens"][b])
+            ok &= int(got["num_tokens"][b]) == int(ref["num_tokens"][b])
+            ok &= (int(got["flags"][b]) & 0x18F) == (int(ref["flags"][b]) & 0x18F)
+        if not greedy:
+            for i in range(g if npos < 0 else min(g, npos)):
+                for k in ("p_draft", "q_draft"):
+                    a, r = float(got[k][b, i]), float(ref[k][b, i])
+                    ok &= abs(a - r) <= max(PROB_ABS, PROB_REL * abs(r))
+            if npos < 0:
+                a, r = float(got["residual_mass"][b]), float(ref["residual_mass"][b])
+                ok &= abs(a - r) <= max(PROB_ABS, PROB_REL * abs(r)) if m_ref < g else a == 0.0
+        if not ok:
+            bad.append(b)
+    return B, near, bad
+
+
+def quantiles(t_s):
+    """p10 / median / p90 of durations in seconds, as microseconds."""
+    t = np.asarray(t_s) * 1e6
+    return {"p10": float(np.percentile(t, 10)), "median": float(np.median(t)),
+            "p90": float(np.percentile(t, 90)), "n": int(t.size)}
 
 
 def parse():
@@ -185,6 +232,9 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="time eager launches, no graph")
     ap.add_argument("--separate-kv-calls", action="store_true",
                     help="KV recipes: commit and rollback as two calls instead of one launch")
+    ap.add_argument("--debug-library", action="store_true",
+                    help="use libspecdec_debug.so, which reads the SPECDEC_* tuning switches "
+                         "from the environment (sweeps; the product library reads none)")
     ap.add_argument("--pmc-copy-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a dispatch of "
                          "known size to calibrate FETCH_SIZE / WRITE_SIZE counters)")
@@ -208,6 +258,8 @@ def main() -> int:
     from speculative_decoding_verification_05_amd import synth
 
     dev = torch.device("cuda:0")
+    if args.debug_library:
+        sd.debug_library().__enter__()  # every call of this run goes to the debug build
     sd.lib()
     if args.pmc_copy_mib:
         src = torch.ones(args.pmc_copy_mib << 18, dtype=torch.int32, device=dev)
@@ -313,7 +365,7 @@ def main() -> int:
 
     # ---- eager reference outputs, then the graphs
     eager = []
-    names = ("accept_count", "out_tokens", "p_draft", "q_draft", "residual_mass", "flags")
+    names = ("accept_count", "num_tokens", "out_tokens", "p_draft", "q_draft", "residual_mass", "flags")
     reset()
     for k in range(sets):
         step(k)
@@ -335,6 +387,20 @@ def main() -> int:
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     sec_per_step = (t1 - t0) / steps
+
+    # ---- per-step durations: each step timed alone (eager launches, events
+    # on the stream the calls use) for the median and p10 / p90
+    n_q = max(sets, (min(args.profile_steps, 400) // sets) * sets)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_q)]
+    for j in range(n_q):
+        if j % per == 0:
+            reset()  # (each slot's cache lengths once per pass, as in the graphs)
+        evs[j][0].record()
+        step(j % per)
+        evs[j][1].record()
+    torch.cuda.synchronize()
+    t_step = np.array([a.elapsed_time(b) for a, b in evs]) * 1e-3
 
     gam_sets = [h["gamma"] for h in host]
     positions = float(np.mean([g.sum() for g in gam_sets]))
@@ -403,8 +469,9 @@ def main() -> int:
     achieved = alg_k1 / k1_avg / 1e9
     trunc = bool(wl0.top_k) or wl0.top_p < 1.0
     # sampling without truncation and greedy verification run as one kernel
-    # (statistics + decision) unless SPECDEC_FUSED=0
-    fused = not trunc and os.environ.get("SPECDEC_FUSED", "1")[:1] != "0"
+    # (statistics + decision); with --debug-library, SPECDEC_FUSED=0 selects
+    # the two-kernel paths
+    fused = not trunc and not (args.debug_library and os.environ.get("SPECDEC_FUSED", "1")[:1] == "0")
     if greedy:
         kname = "k_greedy_fused" if fused else "k_stats_greedy"
     else:
@@ -426,7 +493,7 @@ def main() -> int:
         f"committed tokens/s {committed / sec_per_step:.3e}")
 
     # ---- CPU baseline: the oracle on the host copy of input set 0
-    cpu = cpu_all = None
+    cpu = cpu_all = par = None
     if not args.no_cpu_baseline:
         import oracle
         x = host[0]
@@ -453,12 +520,29 @@ def main() -> int:
         cpu = {"value": cpu_pos, "unit": "positions/s", "cores": 1, "kind": "oracle",
                "sample": f"{reps_c} pass(es) over all {n_req} requests of input set 0 "
                          f"({t_c:.1f} s, single-threaded C, double precision)"}
+        firsts = []
         rate, nt, t_a, passes = oracle_all_cores(
             lambda ix: oracle.verify(x["target"], None if greedy else x["draft"], x["draft_tokens"],
                                      x["gamma"], greedy=greedy, temperature=wl0.temperature,
                                      top_k=wl0.top_k, top_p=wl0.top_p, seed=wl0.verify_seed,
                                      requests=ix),
-            x["gamma"].astype(np.float64), args.cpu_seconds / 2)
+            x["gamma"].astype(np.float64), args.cpu_seconds / 2, firsts)
+        # every request of input set 0: the oracle's outputs (the first pass of
+        # each thread) against the GPU's
+        full = {}
+        for ix, r in firsts:
+            for k, v in r.items():
+                if k not in full:
+                    full[k] = np.zeros((B,) + v.shape[1:], v.dtype)
+                full[k][ix] = v
+        got = {k: v.cpu().numpy() for k, v in eager[0].items()}
+        n_cmp, n_near, bad = parity(full, got, x["gamma"], greedy)
+        par = {"input_set": 0, "requests": n_cmp, "near_threshold": n_near, "mismatches": len(bad),
+               "rule": "accept counts, tokens, token counts and flags bit-exact; p(d), q(d) and "
+                       "the residual mass within 1e-5 abs or 1e-4 rel; a request with a draw "
+                       "within 1e-6 of its threshold is compared up to that draw and counted"}
+        log(f"parity on input set 0: {n_cmp} requests, {len(bad)} mismatches, {n_near} near-threshold"
+            + (f"; mismatching requests {bad[:16]}" if bad else ""))
         log(f"oracle on {nt} threads: {rate:.1f} positions/s ({t_a:.1f} s, at least {passes} "
             f"pass(es) per thread)")
         cpu_all = {"value": rate, "unit": "positions/s", "cores": nt, "kind": "oracle",
@@ -499,11 +583,15 @@ def main() -> int:
                      "traffic": measured_traffic(f"{kname}__{wl0.name}"),
                      "kernel": kname,
                      "kernel_avg_us": k1_avg * 1e6, "bytes_per_launch": alg_k1},
+        "quantiles_us": {"step_eager": quantiles(t_step), "kernel": quantiles(k1)},
         "cpu_baseline": cpu,
         "cpu_baseline_all_cores": cpu_all,
+        "parity": par,
     }
     print(json.dumps(res), flush=True)
-    return 0
+    # a GPU result that differs from the oracle's outside the counted
+    # near-threshold draws fails the run
+    return 3 if par is not None and par["mismatches"] else 0
 
 
 def bench_tree(args, wl0) -> int:
@@ -621,8 +709,9 @@ def bench_tree(args, wl0) -> int:
         cbytes.append(float(((m + 1) * 2 + (depth - m)).sum() * slot))
     cb = float(np.mean(cbytes))
     depth_mean = float(np.mean([a.float().mean().item() for a, _ in eager]))
-    # the statistics and the tree decision run as one kernel unless SPECDEC_FUSED=0
-    fused = os.environ.get("SPECDEC_FUSED", "1")[:1] != "0"
+    # the statistics and the tree decision run as one kernel (with
+    # --debug-library, SPECDEC_FUSED=0 selects the two-kernel path)
+    fused = not (args.debug_library and os.environ.get("SPECDEC_FUSED", "1")[:1] == "0")
     kname = "k_tree_fused" if fused else "k_stats_greedy"
     if fused:
         log(f"step {sec_per_step * 1e6:.2f} us (graph); one-kernel tree verify avg "
@@ -634,7 +723,7 @@ def bench_tree(args, wl0) -> int:
         f"{100 * achieved / HBM_PEAK_GBPS:.1f}% of {HBM_PEAK_GBPS:.0f} GB/s; commit "
         f"{cb / kc.mean() / 1e9:.1f} GB/s; mean kept depth {depth_mean:.3f}")
 
-    cpu = cpu_all = None
+    cpu = cpu_all = par = None
     if not args.no_cpu_baseline:
         import oracle
         x = host[0]
@@ -766,7 +855,7 @@ def bench_ngram(args, wl0) -> int:
     log(f"step {sec_per_step * 1e6:.2f} us (graph); propose kernel avg {kt.mean() * 1e6:.2f} us "
         f"(events); {achieved:.1f} GB/s = {100 * achieved / HBM_PEAK_GBPS:.1f}% of "
         f"{HBM_PEAK_GBPS:.0f} GB/s; {proposed:.0f} tokens proposed per step")
-    cpu = cpu_all = None
+    cpu = cpu_all = par = None
     if not args.no_cpu_baseline:
         import oracle
         x = host[0]

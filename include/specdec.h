@@ -82,11 +82,15 @@ typedef enum specdec_mode { SPECDEC_SAMPLE = 0, SPECDEC_GREEDY = 1 } specdec_mod
 #define SPECDEC_FLAG_EOS               0x80u /* verify: the committed list ends with the EOS token */
 #define SPECDEC_FLAG_LENGTH            0x100u /* verify: the token budget ended the committed list */
 #define SPECDEC_FLAG_BAD_TREE          0x200u /* tree: a parent index outside [0, node): node rejected */
-#define SPECDEC_FLAG_WAIT_TIMEOUT      0x400u /* verify, verify_tree: a one-kernel path (sampling
-                                                 without truncation, greedy, tree) gave up waiting
-                                                 for the request's statistics or chunk masses
-                                                 (20 ms): its outputs are invalid and the
-                                                 workspace must be cleared */
+#define SPECDEC_FLAG_WAIT_TIMEOUT      0x400u /* verify, verify_tree: in a one-kernel path
+                                                 (sampling without truncation, greedy, tree)
+                                                 a decision workgroup gave up waiting (20 ms)
+                                                 for a partial of the request and computed it
+                                                 itself from the logits: the outputs are
+                                                 still valid.  The late partial is then awaited
+                                                 another 20 ms and taken; only if it never
+                                                 came may a workspace word stay set, and the
+                                                 workspace must be cleared before its next use */
 
 /* ------------------------------------------------------------------ verify */
 
@@ -176,8 +180,10 @@ size_t specdec_verify_workspace_bytes(const specdec_verify_desc_t* desc);
  *   top_p < 1), when top_k > 1024, or for top_p < 1 without an effective
  *   top_k on a vocabulary above 2048.  In each case nothing is enqueued.
  * Kernels: sampling without truncation and greedy verification run as one
- *   kernel (statistics and decision workgroups in one launch; SPECDEC_FUSED=0
- *   in the environment selects the two-kernel path, same results);
+ *   kernel (statistics and decision workgroups in one launch; the library's
+ *   debug build, libspecdec_debug.so, can select a two-kernel path with the
+ *   same results through SPECDEC_FUSED=0 in the environment; this library
+ *   reads no environment);
  *   truncation runs a selection kernel, then a decision kernel.
  * Truncation: top-k keeps every token whose raw logit is >= the k-th largest
  *   raw logit (ties kept); top-p then keeps the shortest prefix, in order of
@@ -340,7 +346,7 @@ size_t specdec_verify_tree_workspace_bytes(const specdec_tree_desc_t* desc);
  *   flags         [B] uint32 or NULL: BAD_TREE, TOKEN_RANGE, NONFINITE,
  *       EOS, LENGTH, WAIT_TIMEOUT.
  * Runs as one kernel (statistics and decision workgroups in one launch);
- * SPECDEC_FUSED=0 in the environment selects the two-kernel path.
+ * (The debug build selects a two-kernel path with SPECDEC_FUSED=0.)
  * Errors: INVALID_ARGUMENT (bad descriptor, NULL required pointer,
  *   misaligned workspace), WORKSPACE_TOO_SMALL; nothing is enqueued. */
 specdec_status_t specdec_verify_tree(const specdec_tree_desc_t* desc, const void* target_logits,

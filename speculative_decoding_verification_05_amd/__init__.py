@@ -9,11 +9,15 @@ missing or refuses a call.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libspecdec.so")
+# the same kernels built with the environment switches of the tests and
+# tuning sweeps (SPECDEC_FUSED, SPECDEC_FUSED_WAIT_TICKS, ...); see debug_library()
+DEBUG_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libspecdec_debug.so")
 
 SPECDEC_OK = 0
 SPECDEC_ERR_INVALID_ARGUMENT = 1
@@ -82,52 +86,76 @@ class SpecdecError(RuntimeError):
 
 
 _lib = None
+_loaded = {}
 
 
 def lib() -> ctypes.CDLL:
-    """The loaded libspecdec.so (build it with ``__graft_entry__.build()``)."""
+    """The loaded libspecdec.so (build it with ``__graft_entry__.build()``),
+    or the debug build inside ``debug_library()``."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"libspecdec.so is not built ({LIB_PATH}); run __graft_entry__.build()")
-        L = ctypes.CDLL(LIB_PATH)
-        P, S = ctypes.c_void_p, ctypes.c_size_t
-        L.specdec_verify_workspace_bytes.argtypes = [ctypes.POINTER(VerifyDesc)]
-        L.specdec_verify_workspace_bytes.restype = S
-        L.specdec_verify.argtypes = [ctypes.POINTER(VerifyDesc)] + [P] * 13 + [S, P]
-        L.specdec_verify.restype = ctypes.c_int
-        L.specdec_verify_profiled.argtypes = [ctypes.POINTER(VerifyDesc)] + [P] * 13 + [S, P, P]
-        L.specdec_verify_profiled.restype = ctypes.c_int
-        L.specdec_verify_noalloc.argtypes = [ctypes.POINTER(VerifyDesc)] + [P] * 12 + [P]
-        L.specdec_verify_noalloc.restype = ctypes.c_int
-        L.specdec_commit_kv_workspace_bytes.argtypes = [ctypes.POINTER(KVDesc)]
-        L.specdec_commit_kv_workspace_bytes.restype = S
-        L.specdec_commit_kv.argtypes = [ctypes.POINTER(KVDesc)] + [P] * 9 + [S, P]
-        L.specdec_commit_kv.restype = ctypes.c_int
-        L.specdec_rollback_kv.argtypes = [ctypes.POINTER(KVDesc)] + [P] * 7 + [S, P]
-        L.specdec_rollback_kv.restype = ctypes.c_int
-        L.specdec_commit_and_rollback_kv.argtypes = (
-            [ctypes.POINTER(KVDesc)] + [P] * 7 + [S] + [ctypes.POINTER(KVDesc)] + [P] * 5 + [S]
-            + [P] * 3)
-        L.specdec_commit_and_rollback_kv.restype = ctypes.c_int
-        L.specdec_verify_tree_workspace_bytes.argtypes = [ctypes.POINTER(TreeDesc)]
-        L.specdec_verify_tree_workspace_bytes.restype = S
-        L.specdec_verify_tree.argtypes = [ctypes.POINTER(TreeDesc)] + [P] * 11 + [S, P]
-        L.specdec_verify_tree.restype = ctypes.c_int
-        L.specdec_verify_tree_profiled.argtypes = [ctypes.POINTER(TreeDesc)] + [P] * 11 + [S, P, P]
-        L.specdec_verify_tree_profiled.restype = ctypes.c_int
-        L.specdec_propose_ngram.argtypes = [ctypes.POINTER(NgramDesc)] + [P] * 6 + [S, P]
-        L.specdec_propose_ngram.restype = ctypes.c_int
-        L.specdec_propose_ngram_workspace_bytes.argtypes = [ctypes.POINTER(NgramDesc)]
-        L.specdec_propose_ngram_workspace_bytes.restype = S
-        L.specdec_workspace_clear.argtypes = [P, S, P]
-        L.specdec_workspace_clear.restype = ctypes.c_int
-        L.specdec_status_string.argtypes = [ctypes.c_int]
-        L.specdec_status_string.restype = ctypes.c_char_p
-        L.specdec_abi_version.argtypes = []
-        L.specdec_abi_version.restype = ctypes.c_int32
-        _lib = L
+        _lib = _load(LIB_PATH)
     return _lib
+
+
+@contextlib.contextmanager
+def debug_library():
+    """Every call in the block goes to libspecdec_debug.so: the same kernels,
+    whose host code also reads the environment switches SPECDEC_FUSED (0: the
+    two-kernel paths), SPECDEC_FUSED_WAIT_TICKS, SPECDEC_FUSED_LAG,
+    SPECDEC_STATS_TILES and SPECDEC_SAMPLE_WPR.  For tests and sweeps only."""
+    global _lib
+    old = _lib
+    _lib = _load(DEBUG_LIB_PATH)
+    try:
+        yield _lib
+    finally:
+        _lib = old
+
+
+def _load(path: str) -> ctypes.CDLL:
+    if path in _loaded:
+        return _loaded[path]
+    if not os.path.exists(path):
+        raise ImportError(f"{os.path.basename(path)} is not built ({path}); run __graft_entry__.build()")
+    L = ctypes.CDLL(path)
+    P, S = ctypes.c_void_p, ctypes.c_size_t
+    L.specdec_verify_workspace_bytes.argtypes = [ctypes.POINTER(VerifyDesc)]
+    L.specdec_verify_workspace_bytes.restype = S
+    L.specdec_verify.argtypes = [ctypes.POINTER(VerifyDesc)] + [P] * 13 + [S, P]
+    L.specdec_verify.restype = ctypes.c_int
+    L.specdec_verify_profiled.argtypes = [ctypes.POINTER(VerifyDesc)] + [P] * 13 + [S, P, P]
+    L.specdec_verify_profiled.restype = ctypes.c_int
+    L.specdec_verify_noalloc.argtypes = [ctypes.POINTER(VerifyDesc)] + [P] * 12 + [P]
+    L.specdec_verify_noalloc.restype = ctypes.c_int
+    L.specdec_commit_kv_workspace_bytes.argtypes = [ctypes.POINTER(KVDesc)]
+    L.specdec_commit_kv_workspace_bytes.restype = S
+    L.specdec_commit_kv.argtypes = [ctypes.POINTER(KVDesc)] + [P] * 9 + [S, P]
+    L.specdec_commit_kv.restype = ctypes.c_int
+    L.specdec_rollback_kv.argtypes = [ctypes.POINTER(KVDesc)] + [P] * 7 + [S, P]
+    L.specdec_rollback_kv.restype = ctypes.c_int
+    L.specdec_commit_and_rollback_kv.argtypes = (
+        [ctypes.POINTER(KVDesc)] + [P] * 7 + [S] + [ctypes.POINTER(KVDesc)] + [P] * 5 + [S]
+        + [P] * 3)
+    L.specdec_commit_and_rollback_kv.restype = ctypes.c_int
+    L.specdec_verify_tree_workspace_bytes.argtypes = [ctypes.POINTER(TreeDesc)]
+    L.specdec_verify_tree_workspace_bytes.restype = S
+    L.specdec_verify_tree.argtypes = [ctypes.POINTER(TreeDesc)] + [P] * 11 + [S, P]
+    L.specdec_verify_tree.restype = ctypes.c_int
+    L.specdec_verify_tree_profiled.argtypes = [ctypes.POINTER(TreeDesc)] + [P] * 11 + [S, P, P]
+    L.specdec_verify_tree_profiled.restype = ctypes.c_int
+    L.specdec_propose_ngram.argtypes = [ctypes.POINTER(NgramDesc)] + [P] * 6 + [S, P]
+    L.specdec_propose_ngram.restype = ctypes.c_int
+    L.specdec_propose_ngram_workspace_bytes.argtypes = [ctypes.POINTER(NgramDesc)]
+    L.specdec_propose_ngram_workspace_bytes.restype = S
+    L.specdec_workspace_clear.argtypes = [P, S, P]
+    L.specdec_workspace_clear.restype = ctypes.c_int
+    L.specdec_status_string.argtypes = [ctypes.c_int]
+    L.specdec_status_string.restype = ctypes.c_char_p
+    L.specdec_abi_version.argtypes = []
+    L.specdec_abi_version.restype = ctypes.c_int32
+    _loaded[path] = L
+    return L
 
 
 def status_string(status: int) -> str:

@@ -66,6 +66,25 @@ __device__ __forceinline__ bool stream_row(const void* rp, int lo, int hi, F&& c
     return true;
 }
 
+// stream_row's element order with one tile in flight at a time (few
+// registers): lane l consumes the same vectors of the same tiles in the same
+// order, so a fold over it gives the same bits.  For a decision workgroup
+// that computes a missing partial itself.
+template <bool BF16, bool VEC, int U, class F>
+__device__ __forceinline__ void stream_row_lean(const void* rp, int lo, int hi, F&& consume) {
+    constexpr int N = Vec<BF16>::N;
+    constexpr int TILE = kThreads * N * U;
+    for (int t0 = lo; t0 < hi; t0 += TILE) {
+        Vec<BF16> v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            v[u] = load_vec<BF16, VEC>(rp, t0 + (u * kThreads + threadIdx.x) * N, hi, neg_inf());
+        consume(v, t0);
+    }
+}
+
+
+
 __device__ __forceinline__ MaxSum block_combine(MaxSum v, float c) {
     __shared__ float s_m[kWaves], s_s[kWaves];
     v = wave_combine(v, c);
@@ -94,7 +113,7 @@ __device__ __forceinline__ ArgMax block_argmax(ArgMax v) {
 // (max, sum of 2^((z - max) c)) of elements [lo, hi) of row rp, combined
 // over the workgroup (every lane gets the pair).  keep() as in stream_row;
 // returns false if the row was abandoned.
-template <bool BF16, bool VEC, class K>
+template <bool BF16, bool VEC, class K, bool LEAN = false>
 __device__ __forceinline__ bool chunk_maxsum(const void* rp, int lo, int hi, float c, K&& keep,
                                              MaxSum* out) {
     constexpr int N = Vec<BF16>::N;
@@ -128,9 +147,76 @@ __device__ __forceinline__ bool chunk_maxsum(const void* rp, int lo, int hi, flo
         sum = (m == neg_inf() ? 0.0f : sum * exp2f((m - mn) * c)) + part;
         m = mn;
     };
-    if (!stream_row<BF16, VEC, kUnroll>(rp, lo, hi, consume, keep)) return false;
+    if constexpr (LEAN) stream_row_lean<BF16, VEC, kUnroll>(rp, lo, hi, consume);
+    else if (!stream_row<BF16, VEC, kUnroll>(rp, lo, hi, consume, keep)) return false;
     *out = block_combine(MaxSum{m, sum}, c);
     return true;
+}
+
+// Element j of a raw 16-byte vector as fp32 (exact).
+template <bool BF16>
+__device__ __forceinline__ float raw_elem(const uint4& w, int j) {
+    if constexpr (BF16) {
+        const uint32_t x = j < 2 ? w.x : j < 4 ? w.y : j < 6 ? w.z : w.w;
+        return (j & 1) ? bf16_hi(x) : bf16_lo(x);
+    } else {
+        return __uint_as_float(j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : w.w);
+    }
+}
+
+// chunk_maxsum's (max, sum) of [lo, hi) for 16-byte aligned rows, read one
+// tile at a time and folded from the raw vectors (widened twice, in the
+// maximum pass and the sum pass) with fold_vectors' operations in its order:
+// the same bits with few registers, for a decision workgroup that computes a
+// missing partial itself.
+template <bool BF16>
+__device__ MaxSum chunk_maxsum_lean(const void* rp, int lo, int hi, float c) {
+    constexpr int N = Vec<BF16>::N;
+    constexpr int TILE = kThreads * N * kUnroll;
+    float m = neg_inf(), sum = 0.0f;
+    for (int t0 = lo; t0 < hi; t0 += TILE) {
+        uint4 r[kUnroll];
+        bool ok[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int e = t0 + (u * kThreads + threadIdx.x) * N;
+            ok[u] = e < hi;
+            r[u] = load16<BF16>(rp, min(e, hi - N));
+        }
+        float tm = neg_inf();
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+            for (int k = 0; k < N; ++k) tm = fmaxf(tm, ok[u] ? raw_elem<BF16>(r[u], k) : neg_inf());
+        // (the sum pass widens the raw vectors again)
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) __asm__ volatile("" : "+v"(r[u].x), "+v"(r[u].y), "+v"(r[u].z), "+v"(r[u].w));
+        const float mn = fmaxf(m, tm);
+        if (mn == neg_inf()) {
+            bool nan = false;
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+                for (int k = 0; k < N; ++k) {
+                    const float x = raw_elem<BF16>(r[u], k);
+                    nan |= ok[u] && x != x;
+                }
+            if (nan) m = pos_inf();
+            continue;
+        }
+        float part = 0.0f;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            float q = 0.0f;
+#pragma unroll
+            for (int k = 0; k < N; ++k)
+                q += __builtin_amdgcn_exp2f(((ok[u] ? raw_elem<BF16>(r[u], k) : neg_inf()) - mn) * c);
+            part += q;
+        }
+        sum = (m == neg_inf() ? 0.0f : sum * exp2f((m - mn) * c)) + part;
+        m = mn;
+    }
+    return block_combine(MaxSum{m, sum}, c);
 }
 
 // (max, lowest index) of elements [lo, hi) of row rp, combined over the
@@ -138,7 +224,7 @@ __device__ __forceinline__ bool chunk_maxsum(const void* rp, int lo, int hi, flo
 // lane visits its elements in ascending index order, so a strict ">" keeps
 // the lowest index among equal maxima.  keep() as in stream_row; returns
 // false if the row was abandoned.
-template <bool BF16, bool VEC, class K>
+template <bool BF16, bool VEC, class K, bool LEAN = false>
 __device__ __forceinline__ bool chunk_argmax(const void* rp, int lo, int hi, K&& keep, ArgMax* out,
                                              bool* any_nan) {
     constexpr int N = Vec<BF16>::N;
@@ -157,7 +243,8 @@ __device__ __forceinline__ bool chunk_argmax(const void* rp, int lo, int hi, K&&
             }
         }
     };
-    if (!stream_row<BF16, VEC, kUnroll>(rp, lo, hi, consume, keep)) return false;
+    if constexpr (LEAN) stream_row_lean<BF16, VEC, kUnroll>(rp, lo, hi, consume);
+    else if (!stream_row<BF16, VEC, kUnroll>(rp, lo, hi, consume, keep)) return false;
     *out = block_argmax(best);
     *any_nan = __syncthreads_or(nan);
     return true;
@@ -183,8 +270,12 @@ __device__ __forceinline__ unsigned long long greedy_word(const ArgMax& r, bool 
 // by a lane of its own with an exchange with zero (so it is cleared for the
 // next call as it is read), polled with sleeps until published, within
 // P.wait_ticks of the 100 MHz constant clock, and staged in s_part as
-// greedy_partial stores it.  Returns true (to every lane) if a wait gave up.
-template <class U>
+// greedy_partial stores it.  A word that has not come by then is computed
+// here from the row itself, with the statistics workgroup's arithmetic (so
+// the result is the same), and its late exchange is then awaited (and taken)
+// within the fixed 20 ms bound, so that no word stays set for the next call.
+// Returns true (to every lane) if a wait gave up.
+template <bool BF16, bool VEC, class U>
 __device__ bool collect_greedy(const VerifyParams& P, int b, U&& used, float4* s_part) {
     const int n = P.rows * P.nc;
     unsigned long long* w = reinterpret_cast<unsigned long long*>(P.ready) + static_cast<size_t>(b) * n;
@@ -198,9 +289,32 @@ __device__ bool collect_greedy(const VerifyParams& P, int b, U&& used, float4* s
             __builtin_amdgcn_s_sleep(16);
         }
         const uint32_t hi = static_cast<uint32_t>(v >> 32) & ~0x40000000u;
-        s_part[t] = make_float4(__uint_as_float(static_cast<uint32_t>(v)), __uint_as_float(hi), 0.0f, 0.0f);
+        // (w = 1 marks a partial that did not come)
+        s_part[t] = make_float4(__uint_as_float(static_cast<uint32_t>(v)), __uint_as_float(hi), 0.0f,
+                                v == 0ull ? 1.0f : 0.0f);
     }
-    return __syncthreads_or(late);
+    if (!__syncthreads_or(late)) return false;
+    // the missing partials, computed here
+    for (int t = 0; t < n; ++t) {
+        if (!used(t / P.nc) || s_part[t].w == 0.0f) continue;
+        const int row = t / P.nc, ci = t % P.nc;
+        const int lo = ci * P.chunk, hi = min(P.V, lo + P.chunk);
+        ArgMax r;
+        bool nan;
+        auto all = []() { return true; };
+        chunk_argmax<BF16, VEC, decltype(all)&, true>(target_row(P, b, row, BF16), lo, hi, all, &r, &nan);
+        if (threadIdx.x == 0) {
+            s_part[t] = greedy_partial(r, nan);
+            // the late word: taken when it comes, so it does not stay set
+            const uint64_t t1 = wall_clock64();
+            while (atomicExch(w + t, 0ull) == 0ull) {
+                if (wall_clock64() - t1 > kFixedWaitTicks) break;
+                __builtin_amdgcn_s_sleep(16);
+            }
+        }
+        __syncthreads();
+    }
+    return true;
 }
 
 // Statistics workgroup of a one-kernel greedy path: chunk k % nc of target

@@ -35,7 +35,7 @@ namespace {
 // Tree decision of request b.  FUSED: the partials are the words the same
 // kernel's statistics workgroups publish (collect_greedy); otherwise those
 // the statistics kernel stored.
-template <bool FUSED>
+template <bool FUSED, bool BF16 = true, bool VEC = true>
 __device__ __forceinline__ void decide_tree(const VerifyParams& P, const int b) {
     __shared__ float4 s_part[kMaxPart];
     __shared__ int s_arg[64];
@@ -56,7 +56,7 @@ __device__ __forceinline__ void decide_tree(const VerifyParams& P, const int b) 
         par = P.parents[static_cast<size_t>(b) * N + l];
     }
     bool late = false;
-    if constexpr (FUSED) late = collect_greedy(P, b, [&](int s) { return s < n; }, s_part);
+    if constexpr (FUSED) late = collect_greedy<BF16, VEC>(P, b, [&](int s) { return s < n; }, s_part);
     __syncthreads();
     // argmax of every used row: a lane per row over a few partials, else a wave
     auto part_argmax = [&](int s, int k0, int step, ArgMax& best, uint32_t& nan) {
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
         const int b = x / S;
         fused_greedy_stats<BF16, VEC>(P, b, x % S, [&](int s) { return s < tree_nodes(P, b); });
     } else {
-        decide_tree<true>(P, x - P.B * S);
+        decide_tree<true, BF16, VEC>(P, x - P.B * S);
     }
 }
 

@@ -312,9 +312,12 @@ __device__ __forceinline__ void stage_partials(const VerifyParams& P, int b, flo
 // word of the request's last used (row, chunk) in launch order, the one
 // usually published last; then every word is read (and, if still zero,
 // polled) by a lane of its own.  Polls sleep in between, and atomic reads
-// see the device-scope exchanges that published the words.  A wait longer
-// than P.wait_ticks of the 100 MHz constant clock gives up; returns true
-// (to every lane) if any wait did.
+// see the device-scope exchanges that published the words.  A word still
+// missing after P.wait_ticks of the 100 MHz constant clock is computed here
+// from its row, with the statistics workgroup's arithmetic (chunk_maxsum on
+// the same chunk), so the result does not change; returns true (to every
+// lane) if a wait gave up.
+template <bool BF16, bool VEC>
 __device__ bool wait_partials(const VerifyParams& P, int b, int g, float4* s_part) {
     const int n = P.rows * P.nc;
     unsigned long long* rdy = reinterpret_cast<unsigned long long*>(P.ready) + static_cast<size_t>(b) * n;
@@ -324,7 +327,7 @@ __device__ bool wait_partials(const VerifyParams& P, int b, int g, float4* s_par
         const int s_last = P.point ? g : (g > 0 ? P.G + g : 0);
         unsigned long long* last = rdy + s_last * P.nc + P.nc - 1;
         while (atomicOr(last, 0ull) == 0ull) {
-            if (wall_clock64() - t0 > P.wait_ticks) { late = true; break; }
+            if (wall_clock64() - t0 > P.wait_ticks) break;
             __builtin_amdgcn_s_sleep(16);
         }
     }
@@ -332,28 +335,69 @@ __device__ bool wait_partials(const VerifyParams& P, int b, int g, float4* s_par
         const int s = t / P.nc;
         const bool used = (s <= P.G) ? (s <= g) : (s - (P.G + 1) < g);
         unsigned long long v = 0;
+        bool miss = false;
         if (used) {
             while ((v = atomicOr(rdy + t, 0ull)) == 0ull) {
-                if (wall_clock64() - t0 > P.wait_ticks) { late = true; break; }
+                if (wall_clock64() - t0 > P.wait_ticks) { miss = true; break; }
                 __builtin_amdgcn_s_sleep(16);
             }
         }
+        late |= miss;
+        // (w = 1 marks a partial that did not come)
         s_part[t] = make_float4(__uint_as_float(static_cast<uint32_t>(v)),
-                                __uint_as_float(static_cast<uint32_t>(v >> 32)), 0.0f, 0.0f);
+                                __uint_as_float(static_cast<uint32_t>(v >> 32)), 0.0f, miss ? 1.0f : 0.0f);
     }
-    return __syncthreads_or(late);
+    if (!__syncthreads_or(late)) return false;
+    for (int t = 0; t < n; ++t) {
+        if (s_part[t].w == 0.0f) continue;
+        const int s = t / P.nc, ci = t % P.nc;
+        const void* rp = s <= P.G ? target_row(P, b, s, BF16) : draft_row(P, b, s - (P.G + 1), BF16);
+        const int lo = ci * P.chunk, hi = min(P.V, lo + P.chunk);
+        MaxSum r;
+        if constexpr (VEC) {
+            r = chunk_maxsum_lean<BF16>(rp, lo, hi, P.c);
+        } else {
+            auto all = []() { return true; };
+            chunk_maxsum<BF16, VEC, decltype(all)&, true>(rp, lo, hi, P.c, all, &r);
+        }
+        __syncthreads();  // every lane has read s_part[t].w
+        if (threadIdx.x == 0) s_part[t] = make_float4(r.m, r.s, 0.0f, 0.0f);
+        __syncthreads();
+    }
+    return true;
 }
 
 // Back to zero for the next call: every used word of request b (run by the
 // request's last decision workgroup, after every workgroup has read them).
-__device__ __forceinline__ void clear_partials(const VerifyParams& P, int b, int g) {
+// Without a late partial anywhere in the request every word was published
+// before it was read, and each is cleared by an exchange nobody waits for.
+// After a wait gave up (careful), a word is taken only once it has been
+// published, within the fixed 20 ms bound, since it may still land now;
+// returns true (to every lane) if one never came (it may land later and stay
+// set: the workspace must then be cleared).
+__device__ __forceinline__ bool clear_partials(const VerifyParams& P, int b, int g, bool careful) {
     const int n = P.rows * P.nc;
     unsigned long long* rdy = reinterpret_cast<unsigned long long*>(P.ready) + static_cast<size_t>(b) * n;
+    if (!careful) {
+        for (int t = threadIdx.x; t < n; t += kThreads) {
+            const int s = t / P.nc;
+            const bool used = (s <= P.G) ? (s <= g) : (s - (P.G + 1) < g);
+            if (used) atomicExch(rdy + t, 0ull);
+        }
+        return false;
+    }
+    bool lost = false;
     for (int t = threadIdx.x; t < n; t += kThreads) {
         const int s = t / P.nc;
         const bool used = (s <= P.G) ? (s <= g) : (s - (P.G + 1) < g);
-        if (used) atomicExch(rdy + t, 0ull);
+        if (!used) continue;
+        const uint64_t t0 = wall_clock64();
+        while (atomicExch(rdy + t, 0ull) == 0ull) {
+            if (wall_clock64() - t0 > kFixedWaitTicks) { lost = true; break; }
+            __builtin_amdgcn_s_sleep(16);
+        }
     }
+    return __syncthreads_or(lost);
 }
 
 // One-kernel path: the chunk masses of request b's decision workgroups
@@ -363,7 +407,11 @@ __device__ __forceinline__ void clear_partials(const VerifyParams& P, int b, int
 // workgroup (launched after all of them) reads them here, a lane per word:
 // each read is an exchange with zero, so a word is cleared for the next call
 // as it is taken.  Polls sleep in between, bounded like the statistics wait;
-// returns true (to every lane) if a wait gave up or a publisher was late.
+// a word that did not come leaves kMassMissing in s_csum (the caller
+// computes it and takes the late word).  Returns true (to every lane) if a
+// wait gave up.
+constexpr uint32_t kMassMissing = 0x7fc0deadu;  // a NaN pattern
+
 __device__ bool collect_masses(const VerifyParams& P, unsigned long long* cm, int n, float* s_csum) {
     const uint64_t t0 = wall_clock64();
     bool late = false;
@@ -374,7 +422,7 @@ __device__ bool collect_masses(const VerifyParams& P, unsigned long long* cm, in
             __builtin_amdgcn_s_sleep(16);
         }
         late |= ((v >> 33) & 1ull) != 0;
-        s_csum[k] = __uint_as_float(static_cast<uint32_t>(v));
+        s_csum[k] = v == 0ull ? __uint_as_float(kMassMissing) : __uint_as_float(static_cast<uint32_t>(v));
     }
     return __syncthreads_or(late);
 }
@@ -418,7 +466,7 @@ __device__ __forceinline__ void decide_sample(const VerifyParams& P, const int w
             zt = load_logit<BF16>(target_row(P, b, i, BF16), d);
             if (!P.point) zq = load_logit<BF16>(draft_row(P, b, i, BF16), d);
         }
-        late = wait_partials(P, b, g, s_part);
+        late = wait_partials<BF16, VEC>(P, b, g, s_part);
     } else {
         __syncthreads();
         if (w == 0 && i < g && d >= 0 && d < P.V) {
@@ -537,10 +585,34 @@ __device__ __forceinline__ void decide_sample(const VerifyParams& P, const int w
                 atomicExch(cm + k, tag | __float_as_uint(s_csum[k]));
             return;
         }
-        late = collect_masses(P, cm, k0, s_csum) || late;
+        if (collect_masses(P, cm, k0, s_csum)) {
+            late = true;
+            // a publisher that did not come in time: its chunks' masses
+            // computed here (mass_chunks gives each chunk the same value
+            // whatever the range; a real mass that happens to carry the
+            // marker's bits is only computed again), then its late words taken
+            for (int k = 0; k < k0; ++k) {
+                if (__float_as_uint(s_csum[k]) != kMassMissing) continue;
+                __syncthreads();  // every lane has read s_csum[k]
+                mass_chunks<BF16, VEC, GROUP, CACHED>(a, k, k + 1, P.chunk2, P.V, scr,
+                                                      [&](int kk, float t) -> uint32_t {
+                                                          s_csum[kk] = t;
+                                                          return 0u;
+                                                      });
+                if (threadIdx.x == 0) {
+                    const uint64_t t1 = wall_clock64();
+                    while (atomicExch(cm + k, 0ull) == 0ull) {
+                        if (wall_clock64() - t1 > kFixedWaitTicks) break;
+                        __builtin_amdgcn_s_sleep(16);
+                    }
+                }
+                __syncthreads();
+            }
+        }
         // every decision workgroup of the request has read the statistics
-        // words before publishing its masses
-        clear_partials(P, b, g);
+        // words before publishing its masses (a late one has been awaited)
+        if (late) late = clear_partials(P, b, g, true) || late;
+        else clear_partials(P, b, g, false);
     } else {
         uint32_t* csum = P.csum + static_cast<size_t>(b) * P.nc2;
         const uint32_t dep = mass_chunks<BF16, VEC, GROUP, CACHED>(
@@ -709,7 +781,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6))) v
 // Greedy decision of request b.  FUSED: the partials are the words the same
 // kernel's statistics workgroups publish (collect_greedy); otherwise those
 // the statistics kernel stored.
-template <bool FUSED>
+template <bool FUSED, bool BF16 = true, bool VEC = true>
 __device__ __forceinline__ void decide_greedy(const VerifyParams& P, const int b) {
     __shared__ float4 s_part[kMaxPart];
     __shared__ int s_arg[64];
@@ -722,7 +794,7 @@ __device__ __forceinline__ void decide_greedy(const VerifyParams& P, const int b
     const int graw = P.gamma ? P.gamma[b] : P.G;  // read once, clamped, flagged below
     const int g = min(max(graw, 0), P.G);
     bool late = false;
-    if constexpr (FUSED) late = collect_greedy(P, b, [&](int s) { return s <= g; }, s_part);
+    if constexpr (FUSED) late = collect_greedy<BF16, VEC>(P, b, [&](int s) { return s <= g; }, s_part);
     __syncthreads();
     // a lane per row over a few partials, else a wave per row
     auto part_argmax = [&](int s, int k0, int step, ArgMax& best, uint32_t& nan) {
@@ -785,7 +857,7 @@ __global__ __launch_bounds__(kThreads) void k_greedy_fused(VerifyParams P) {
         const int b = x / S;
         fused_greedy_stats<BF16, VEC>(P, b, x % S, [&](int s) { return s <= request_gamma(P, b); });
     } else {
-        decide_greedy<true>(P, x - P.B * S);
+        decide_greedy<true, BF16, VEC>(P, x - P.B * S);
     }
 }
 
@@ -807,18 +879,19 @@ bool truncation_supported(const specdec_verify_desc_t* d) {
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// a debug-build tuning switch (see debug_knob), else the default
 int env_int(const char* name, int dflt) {
-    const char* s = getenv(name);
-    if (!s || !*s) return dflt;
+    const char* s = debug_knob(name);
+    if (!s) return dflt;
     const int v = atoi(s);
     return v > 0 ? v : dflt;
 }
 
-// Decision workgroups of request j trail the statistics of request j + lag;
-// SPECDEC_FUSED_LAG overrides (0..B).
+// Decision workgroups of request j trail the statistics of request j + lag
+// (B: after all of them); the debug build's SPECDEC_FUSED_LAG overrides (0..B).
 int fused_lag(int B) {
-    const char* s = getenv("SPECDEC_FUSED_LAG");
-    const int v = (s && *s) ? atoi(s) : B;
+    const char* s = debug_knob("SPECDEC_FUSED_LAG");
+    const int v = s ? atoi(s) : B;
     return std::min(std::max(v, 0), B);
 }
 

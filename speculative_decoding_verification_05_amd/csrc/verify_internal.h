@@ -170,20 +170,39 @@ __device__ __forceinline__ float block_sum(float v) {
     return r;
 }
 
+// Tuning and test switches.  The product library reads no environment: it
+// always takes the measured defaults below.  The debug build of the same
+// sources (libspecdec_debug.so, compiled with SPECDEC_DEBUG_KNOBS) reads
+// SPECDEC_FUSED, SPECDEC_FUSED_WAIT_TICKS, SPECDEC_FUSED_LAG,
+// SPECDEC_STATS_TILES and SPECDEC_SAMPLE_WPR, for the tests that compare
+// paths or force a timeout, and for tuning sweeps.
+constexpr uint64_t kFixedWaitTicks = 2000000ull;  // 20 ms of the 100 MHz constant clock
+
+inline const char* debug_knob(const char* name) {
+#ifdef SPECDEC_DEBUG_KNOBS
+    const char* s = getenv(name);
+    return (s && *s) ? s : nullptr;
+#else
+    (void)name;
+    return nullptr;
+#endif
+}
+
 // One-kernel paths (statistics and decision workgroups in one launch) for
-// sampling without truncation, greedy chains and greedy trees;
-// SPECDEC_FUSED=0 selects the two-kernel paths.
+// sampling without truncation, greedy chains and greedy trees; the debug
+// build's SPECDEC_FUSED=0 selects the two-kernel paths.
 inline bool fused_enabled() {
-    const char* s = getenv("SPECDEC_FUSED");
+    const char* s = debug_knob("SPECDEC_FUSED");
     return !(s && s[0] == '0');
 }
 
-// Bound of a one-kernel decision workgroup's waits: 20 ms of the 100 MHz
-// constant clock; SPECDEC_FUSED_WAIT_TICKS overrides (tests force the
-// timeout path with a tiny bound).
+// First bound of a one-kernel decision workgroup's waits (20 ms; the debug
+// build's SPECDEC_FUSED_WAIT_TICKS lowers it to force the recompute path).
+// A wait that gives up computes the missing partial itself; the late word is
+// then drained under the fixed 20 ms bound so the workspace stays clean.
 inline uint64_t fused_wait_ticks() {
-    const char* s = getenv("SPECDEC_FUSED_WAIT_TICKS");
-    return (s && *s) ? strtoull(s, nullptr, 10) : 2000000ull;
+    const char* s = debug_knob("SPECDEC_FUSED_WAIT_TICKS");
+    return s ? strtoull(s, nullptr, 10) : kFixedWaitTicks;
 }
 
 // Workspace layout and chunking of one verify call (shared by the chain and

@@ -21,8 +21,9 @@ def say(msg: str) -> None:
 
 @contextlib.contextmanager
 def env(**kv):
-    """Environment variables set (value) or unset (None) for the block; the
-    library reads its tuning switches on every call."""
+    """Environment switches set (value) or unset (None) for the block, with
+    every call going to the debug build of the library, the one that reads
+    them (on every call); the product library reads no environment."""
     old = {k: os.environ.get(k) for k in kv}
     try:
         for k, v in kv.items():
@@ -30,7 +31,8 @@ def env(**kv):
                 os.environ.pop(k, None)
             else:
                 os.environ[k] = str(v)
-        yield
+        with sd.debug_library():
+            yield
     finally:
         for k, v in old.items():
             if v is None:
@@ -119,7 +121,34 @@ def compare(ref, got, gamma, greedy, requests=None, label=""):
 
 def oracle_verify(x, *, greedy=False, temperature=1.0, top_k=0, top_p=1.0, seed=0, round=0,
                   requests=None, eos_token=-1, max_tokens=None):
-    return oracle.verify(x["target"], None if greedy else x["draft"], x["draft_tokens"],
-                         x["gamma"], greedy=greedy, temperature=temperature, top_k=top_k,
-                         top_p=top_p, seed=seed, round=round, requests=requests,
-                         eos_token=eos_token, max_tokens=max_tokens)
+    """The oracle on the requests (all by default), in that order.  Large
+    batches are split over host threads (the oracle is C behind ctypes,
+    which releases the GIL); each request's result does not depend on the
+    split."""
+    B = x["target"].shape[0]
+    req = np.arange(B, dtype=np.int32) if requests is None else np.asarray(requests, np.int32)
+
+    def run(ix):
+        return oracle.verify(x["target"], None if greedy else x["draft"], x["draft_tokens"],
+                             x["gamma"], greedy=greedy, temperature=temperature, top_k=top_k,
+                             top_p=top_p, seed=seed, round=round, requests=ix,
+                             eos_token=eos_token, max_tokens=max_tokens)
+
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncpu = os.cpu_count() or 1
+    nt = max(1, min(16, ncpu, len(req) // 8))
+    if nt == 1:
+        return run(req)
+    from concurrent.futures import ThreadPoolExecutor
+    parts = np.array_split(np.arange(len(req)), nt)
+    with ThreadPoolExecutor(nt) as ex:
+        outs = list(ex.map(lambda p: run(req[p]), parts))
+    full = {}
+    for p, r in zip(parts, outs):
+        for k, v in r.items():
+            if k not in full:
+                full[k] = np.zeros((len(req),) + v.shape[1:], v.dtype)
+            full[k][p] = v
+    return full

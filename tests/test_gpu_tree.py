@@ -8,7 +8,7 @@ import pytest
 import oracle
 import speculative_decoding_verification_05_amd as sd
 from speculative_decoding_verification_05_amd import synth
-from gpu_helpers import say, to_dev
+from gpu_helpers import env, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -81,26 +81,17 @@ def test_one_kernel_tree_matches_two_kernel_path():
     """Tree verify in one launch writes the same bytes as the statistics
     kernel followed by the tree decision kernel (random trees with ties and
     ragged node counts, bf16 and fp32), on two calls in a row."""
-    import os
     rng = np.random.default_rng(77)
     for B, N, V, bf16 in ((24, 16, 20000, True), (9, 64, 3000, False), (40, 5, 151936, True)):
         x = random_trees(B, N, V, rng)
         if bf16:
             x["target"] = synth.f32_to_bf16_bits(x["target"])
         label = f"B={B} N={N} V={V} {'bf16' if bf16 else 'fp32'}"
-        old = os.environ.get("SPECDEC_FUSED")
-        try:
-            os.environ["SPECDEC_FUSED"] = "0"
-            say(f"[one-kernel tree] {label}: two-kernel path")
+        with env(SPECDEC_FUSED=0):
+            say(f"[one-kernel tree] {label}: two-kernel path (debug build)")
             ref = gpu_tree(x)
-            os.environ["SPECDEC_FUSED"] = "1"
-            say(f"[one-kernel tree] {label}: one kernel")
-            outs = [gpu_tree(x) for _ in range(2)]
-        finally:
-            if old is None:
-                os.environ.pop("SPECDEC_FUSED", None)
-            else:
-                os.environ["SPECDEC_FUSED"] = old
+        say(f"[one-kernel tree] {label}: one kernel")
+        outs = [gpu_tree(x) for _ in range(2)]
         for o in outs:
             for k in ref:
                 assert np.array_equal(o[k], ref[k]), (label, k)
