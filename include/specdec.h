@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define SPECDEC_ABI_VERSION 2
+#define SPECDEC_ABI_VERSION 3
 
 typedef enum specdec_status {
     SPECDEC_OK = 0,
@@ -105,8 +105,9 @@ typedef struct specdec_verify_desc {
     float top_p;          /* SAMPLE only: (0, 1]; 1 = off */
     uint64_t seed;        /* Philox4x32-10 key (low word, high word) */
     uint32_t round;       /* Philox counter word 2 (make it differ per round) */
-    int32_t eos_token;    /* -1: no end-of-sequence handling; else the EOS id in [0, V).
-                             NOTE: a zero-filled descriptor means EOS = token 0. */
+    int32_t eos_plus1;    /* 0: no end-of-sequence handling (so a zero-filled
+                             descriptor has none); else the EOS token id + 1,
+                             in [1, V] */
 } specdec_verify_desc_t;
 
 /* Bytes of device workspace specdec_verify needs for `desc` (0 on a bad
@@ -127,7 +128,7 @@ size_t specdec_verify_workspace_bytes(const specdec_verify_desc_t* desc);
  * right after emitting EOS; s.5.2: nothing after an EOS in the candidate
  * block may reach the cache).  The list a round commits is d_0..d_{m-1} and
  * then the correction or bonus token; it is cut after its first EOS token
- * (desc->eos_token >= 0) and after max_tokens[b] tokens.  accept_count then
+ * (desc->eos_plus1 > 0) and after max_tokens[b] tokens.  accept_count then
  * counts the drafts left in the list, so specdec_commit_kv and
  * specdec_rollback_kv keep exactly the committed tokens' K/V.
  *
@@ -280,7 +281,11 @@ size_t specdec_commit_kv_workspace_bytes(const specdec_kv_desc_t* desc);
  *   accept_count [B] int32 (m_b, e.g. specdec_verify's output), gamma [B]
  *       int32 or NULL (= G), both device-resident.
  *   seq_lens    [B] int32, in place: in t_b (valid cache entries before the
- *       round), out t_b + m_b + 1 (written after every slot of b was placed).
+ *       round), out t_b + m_b + 1.  Within the kernel the new length is
+ *       written by the request's last workgroup to start its slot, possibly
+ *       before the other workgroups' copies land; everything ordered after
+ *       the call (a later kernel or copy on the stream, or after a
+ *       synchronisation) sees both the new length and every placed slot.
  *   flags       [B] uint32 or NULL: SPECDEC_FLAG_BAD_BLOCK is OR-ed in when a
  *       block-table entry needed by the window is outside [0, num_blocks) or
  *       past the table (that slot is skipped), or when gamma_b, m_b or t_b is
@@ -305,7 +310,7 @@ typedef struct specdec_tree_desc {
     int32_t num_nodes;    /* N in [1, 64]: padded nodes per tree, node 0 = root */
     int32_t vocab;        /* V >= 1, as for specdec_verify */
     int32_t dtype;        /* specdec_dtype_t of the target logits */
-    int32_t eos_token;    /* -1: none; else the EOS id in [0, V) */
+    int32_t eos_plus1;    /* 0: none; else the EOS id + 1, in [1, V] */
     int32_t reserved;     /* must be 0 */
 } specdec_tree_desc_t;
 
@@ -451,7 +456,10 @@ specdec_status_t specdec_rollback_kv(const specdec_kv_desc_t* desc, void* kv_poo
  * gamma shared; the two descriptors must agree on batch and gamma_max.  Rows
  * that do not take 16-byte vectors are served by two launches in order.
  * Errors: as for the two calls, plus INVALID_ARGUMENT when batch or gamma_max
- * differ; nothing is enqueued in any error case. */
+ * differ, when the two workspaces overlap (the halves run side by side,
+ * each with its own arrival counters: one workspace for both would let their
+ * arrivals race; the two separate calls may share one), or when seq_lens and
+ * draft_seq_lens overlap; nothing is enqueued in any error case. */
 specdec_status_t specdec_commit_and_rollback_kv(
     const specdec_kv_desc_t* desc, const void* scratch_kv, void* kv_pool,
     const int32_t* block_table, const int32_t* slot_map, int32_t* seq_lens, uint32_t* flags,

@@ -56,7 +56,7 @@ class VerifyDesc(ctypes.Structure):
                 ("mode", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("temperature", ctypes.c_float), ("top_p", ctypes.c_float),
                 ("seed", ctypes.c_uint64), ("round", ctypes.c_uint32),
-                ("eos_token", ctypes.c_int32)]
+                ("eos_plus1", ctypes.c_int32)]
 
 
 class KVDesc(ctypes.Structure):
@@ -76,7 +76,7 @@ class NgramDesc(ctypes.Structure):
 class TreeDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_nodes", ctypes.c_int32),
                 ("vocab", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("eos_token", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("eos_plus1", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class SpecdecError(RuntimeError):
@@ -190,7 +190,7 @@ def make_verify_desc(batch, gamma_max, vocab, *, bf16=True, greedy=False, temper
                       SPECDEC_BF16 if bf16 else SPECDEC_F32,
                       SPECDEC_GREEDY if greedy else SPECDEC_SAMPLE, int(top_k),
                       float(temperature), float(top_p), int(seed) & (2 ** 64 - 1),
-                      int(round) & 0xFFFFFFFF, int(eos_token))
+                      int(round) & 0xFFFFFFFF, int(eos_token) + 1)
 
 
 def make_kv_desc(batch, gamma_max, num_layers, num_kv_heads, head_dim, block_size,
@@ -202,7 +202,7 @@ def make_kv_desc(batch, gamma_max, num_layers, num_kv_heads, head_dim, block_siz
 
 def make_tree_desc(batch, num_nodes, vocab, *, bf16=True, eos_token=-1) -> TreeDesc:
     return TreeDesc(int(batch), int(num_nodes), int(vocab), SPECDEC_BF16 if bf16 else SPECDEC_F32,
-                    int(eos_token), 0)
+                    int(eos_token) + 1, 0)
 
 
 def make_ngram_desc(batch, max_len, n_min, n_max, gamma_max) -> NgramDesc:

@@ -322,6 +322,17 @@ extern "C" specdec_status_t specdec_commit_and_rollback_kv(
     if (st != SPECDEC_OK) return st;
     if (!accept_count || d->batch != dd->batch || d->gamma_max != dd->gamma_max)
         return SPECDEC_ERR_INVALID_ARGUMENT;
+    // the two halves run side by side, each with its own arrival counters
+    // and lengths: a shared or overlapping workspace (or length array) would
+    // let their arrivals race on one counter
+    auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
+        const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+        return na > 0 && nb > 0 && x < y + nb && y < x + na;
+    };
+    if (overlap(workspace, specdec_commit_kv_workspace_bytes(d), draft_workspace,
+                specdec_commit_kv_workspace_bytes(dd)) ||
+        overlap(seq_lens, static_cast<size_t>(d->batch) * 4, draft_seq_lens, static_cast<size_t>(dd->batch) * 4))
+        return SPECDEC_ERR_INVALID_ARGUMENT;
     if (d->batch == 0) return SPECDEC_OK;
     bool va, vr;
     const CommitParams A = commit_params(d, scratch_kv, slot_map, kv_pool, block_table, accept_count,

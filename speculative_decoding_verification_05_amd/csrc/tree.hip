@@ -170,7 +170,7 @@ bool valid_tree(const specdec_tree_desc_t* d) {
         return false;
     if (d->dtype != SPECDEC_F32 && d->dtype != SPECDEC_BF16) return false;
     if (d->vocab > 1024 * kThreads * kUnroll2 * (d->dtype == SPECDEC_BF16 ? 8 : 4)) return false;
-    if (d->eos_token < -1 || d->eos_token >= d->vocab || d->reserved != 0) return false;
+    if (d->eos_plus1 < 0 || d->eos_plus1 > d->vocab || d->reserved != 0) return false;
     return true;
 }
 
@@ -184,7 +184,7 @@ specdec_verify_desc_t as_chain_desc(const specdec_tree_desc_t* d) {
     v.mode = SPECDEC_GREEDY;
     v.temperature = 1.0f;
     v.top_p = 1.0f;
-    v.eos_token = d->eos_token;
+    v.eos_plus1 = d->eos_plus1;
     return v;
 }
 
@@ -239,7 +239,7 @@ specdec_status_t tree_impl(const specdec_tree_desc_t* d, const void* target_logi
     P.nc = L.nc;
     P.chunk = L.chunk;
     P.c = 1.0f;
-    P.eos = d->eos_token;
+    P.eos = d->eos_plus1 - 1;  // -1: none
     const bool bf16 = d->dtype == SPECDEC_BF16;
     const size_t es = bf16 ? 2 : 4;
     const bool vec = (reinterpret_cast<uintptr_t>(target_logits) & 15u) == 0 &&

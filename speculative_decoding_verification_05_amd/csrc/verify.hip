@@ -903,7 +903,7 @@ bool valid_desc(const specdec_verify_desc_t* d) {
     // at most 1024 sampling chunks of 256 lanes x 2 x 16 bytes per row
     if (d->vocab > 1024 * kThreads * kUnroll2 * (d->dtype == SPECDEC_BF16 ? 8 : 4)) return false;
     if (d->mode != SPECDEC_SAMPLE && d->mode != SPECDEC_GREEDY) return false;
-    if (d->eos_token < -1 || d->eos_token >= d->vocab) return false;
+    if (d->eos_plus1 < 0 || d->eos_plus1 > d->vocab) return false;
     if (d->mode == SPECDEC_SAMPLE) {
         const float T = d->temperature;
         if (!(T > 0.0f) || !(T < 3.0e38f)) return false;
@@ -1137,7 +1137,7 @@ specdec_status_t verify_impl(const specdec_verify_desc_t* d, const void* target_
     P.key0 = static_cast<uint32_t>(d->seed & 0xffffffffu);
     P.key1 = static_cast<uint32_t>(d->seed >> 32);
     P.round = d->round;
-    P.eos = d->eos_token;
+    P.eos = d->eos_plus1 - 1;  // -1: none
     P.point = point;
 
     const bool bf16 = d->dtype == SPECDEC_BF16;

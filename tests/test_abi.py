@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert sd.specdec_abi_version() == 2
+    assert sd.specdec_abi_version() == 3
     for s in range(5):
         assert sd.status_string(s).startswith("SPECDEC_")
 
@@ -72,7 +72,7 @@ def test_bad_descriptors_are_rejected(bad):
 
 
 def test_bad_dtype_mode_eos():
-    for field, val in (("dtype", 7), ("mode", 5), ("eos_token", -2), ("eos_token", 1000)):
+    for field, val in (("dtype", 7), ("mode", 5), ("eos_plus1", -1), ("eos_plus1", 1001)):
         d = good_desc()
         setattr(d, field, val)
         assert call_verify(d, ws_bytes=1 << 30) == sd.SPECDEC_ERR_INVALID_ARGUMENT
@@ -138,7 +138,7 @@ def test_tree_descriptor_checks():
     ok = sd.make_tree_desc(4, 16, 1000)
     assert sd.specdec_verify_tree_workspace_bytes(ok) > 0
     for field, val in (("num_nodes", 0), ("num_nodes", 65), ("vocab", 0), ("dtype", 3),
-                       ("eos_token", 1000), ("eos_token", -2), ("reserved", 1), ("batch", -1)):
+                       ("eos_plus1", 1001), ("eos_plus1", -1), ("reserved", 1), ("batch", -1)):
         d = sd.make_tree_desc(4, 16, 1000)
         setattr(d, field, val)
         assert sd.specdec_verify_tree_workspace_bytes(d) == 0
@@ -228,3 +228,48 @@ def test_noalloc_refuses_oversized_descriptors_before_any_launch():
     assert st == sd.SPECDEC_ERR_WORKSPACE_TOO_SMALL
     bad = sd.make_verify_desc(4, 2, 1000, temperature=0.0)
     assert L.specdec_verify_noalloc(ctypes.byref(bad), *([16] * 12), None) == sd.SPECDEC_ERR_INVALID_ARGUMENT
+
+
+def test_commit_and_rollback_refuses_shared_workspace_and_lengths():
+    """The one-launch commit + rollback runs both halves side by side, each
+    with its own arrival counters and lengths: a shared (or overlapping)
+    workspace or length array is refused on the host, as is a batch or
+    gamma_max mismatch, before anything is enqueued (the addresses below are
+    never dereferenced)."""
+    L = sd.lib()
+    d = sd.make_kv_desc(4, 7, 28, 4, 128, 16, 300, 8)
+    dd = sd.make_kv_desc(4, 7, 24, 2, 64, 16, 300, 8)
+    nw = sd.specdec_commit_kv_workspace_bytes(d)
+    ws, dws = 1 << 24, 1 << 25
+    seq, dseq = 1 << 26, 1 << 27
+
+    def call(desc, ddesc, ws_, dws_, seq_, dseq_):
+        return L.specdec_commit_and_rollback_kv(
+            ctypes.byref(desc), 1 << 28, 1 << 29, 1 << 30, None, seq_, None, ws_, nw,
+            ctypes.byref(ddesc), 1 << 31, 1 << 30, dseq_, None, dws_, nw, 1 << 32, None, None)
+
+    bad = sd.SPECDEC_ERR_INVALID_ARGUMENT
+    assert call(d, dd, ws, ws, seq, dseq) == bad            # one workspace for both
+    assert call(d, dd, ws, ws + 4, seq, dseq) == bad        # overlapping workspaces
+    assert call(d, dd, ws, dws, seq, seq) == bad            # one length array for both
+    assert call(d, dd, ws, dws, seq, seq + 8) == bad        # overlapping length arrays
+    d2 = sd.make_kv_desc(5, 7, 28, 4, 128, 16, 300, 8)
+    assert call(d2, dd, ws, dws, seq, dseq) == bad          # batch mismatch
+    dd2 = sd.make_kv_desc(4, 6, 24, 2, 64, 16, 300, 8)
+    assert call(d, dd2, ws, dws, seq, dseq) == bad          # gamma_max mismatch
+
+
+def test_zero_filled_descriptor_has_no_eos():
+    """A C caller that zero-fills the descriptors gets no end-of-sequence
+    handling (eos_plus1 = 0), not EOS = token 0; the Python helpers take the
+    token id itself (-1: none) and store id + 1; the largest id V - 1 is
+    valid and V is not."""
+    assert sd.VerifyDesc().eos_plus1 == 0 and sd.TreeDesc().eos_plus1 == 0
+    assert sd.make_verify_desc(4, 2, 1000).eos_plus1 == 0
+    assert sd.make_verify_desc(4, 2, 1000, eos_token=0).eos_plus1 == 1
+    assert sd.make_tree_desc(4, 16, 1000, eos_token=7).eos_plus1 == 8
+    d = sd.make_verify_desc(4, 2, 1000, eos_token=999)
+    assert sd.specdec_verify_workspace_bytes(d) > 0
+    d.eos_plus1 = 1001
+    assert sd.specdec_verify_workspace_bytes(d) == 0
+    assert sd.specdec_abi_version() == 3
