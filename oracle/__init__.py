@@ -35,6 +35,18 @@ def _compile(src: str, out: str) -> None:
     os.replace(out + ".tmp", out)
 
 
+def build_sanitized(out: str) -> str:
+    """Compile a copy of liboracle.so instrumented with AddressSanitizer and
+    UndefinedBehaviorSanitizer (every report fatal), for the test that runs
+    the pins against it in a process that preloads the ASan runtime."""
+    cmd = ["gcc", "-O1", "-g", "-std=c11", "-Wall", "-Wextra", "-fPIC", "-shared",
+           "-fno-fast-math", "-ffp-contract=off", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-I", HERE, "-o", out, SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
 def build() -> str:
     """Compile liboracle.so with gcc (-O2, no fast-math: IEEE double)."""
     _compile(SRC, LIB)
