@@ -177,15 +177,21 @@ size_t specdec_verify_workspace_bytes(const specdec_verify_desc_t* desc);
  *   logits, lowest index on ties); the token at m is the argmax of row m.
  * Errors: INVALID_ARGUMENT for a bad descriptor or a NULL required pointer;
  *   WORKSPACE_TOO_SMALL if workspace_bytes < specdec_verify_workspace_bytes;
- *   UNSUPPORTED, in SAMPLE mode with truncation (0 < top_k < V, or
- *   top_p < 1), when top_k > 1024, or for top_p < 1 without an effective
- *   top_k on a vocabulary above 2048.  In each case nothing is enqueued.
+ *   UNSUPPORTED for truncation (0 < top_k < V, or top_p < 1) with
+ *   point-mass drafts (draft_logits NULL, G > 0).  In each case nothing is
+ *   enqueued.
  * Kernels: sampling without truncation and greedy verification run as one
  *   kernel (statistics and decision workgroups in one launch; the library's
  *   debug build, libspecdec_debug.so, can select a two-kernel path with the
  *   same results through SPECDEC_FUSED=0 in the environment; this library
  *   reads no environment);
- *   truncation runs a selection kernel, then a decision kernel.
+ *   truncation with top_k <= 1024, or top-p alone on V <= 2048, runs a
+ *   selection kernel that lists each row's kept tokens, then a decision
+ *   kernel over the lists; other truncation (top-p alone on larger
+ *   vocabularies, top_k > 1024) runs the statistics pass, a kernel that
+ *   finds each row's cut (the boundary logit and, among the tokens tied at
+ *   it, the last kept index) by a radix select over the logits' order
+ *   keys, and the sampling decision testing each token against the cut.
  * Truncation: top-k keeps every token whose raw logit is >= the k-th largest
  *   raw logit (ties kept); top-p then keeps the shortest prefix, in order of
  *   raw logit descending and token index ascending, whose cumulative

@@ -103,7 +103,7 @@ def debug_library():
     """Every call in the block goes to libspecdec_debug.so: the same kernels,
     whose host code also reads the environment switches SPECDEC_FUSED (0: the
     two-kernel paths), SPECDEC_FUSED_WAIT_TICKS, SPECDEC_FUSED_LAG,
-    SPECDEC_STATS_TILES and SPECDEC_SAMPLE_WPR.  For tests and sweeps only."""
+    SPECDEC_STATS_TILES, SPECDEC_SAMPLE_WPR and SPECDEC_TRUNC_CUT.  For tests and sweeps only."""
     global _lib
     old = _lib
     _lib = _load(DEBUG_LIB_PATH)

@@ -828,6 +828,359 @@ __global__ __launch_bounds__(kThreads) void k_decide_trunc(VerifyParams P) {
     }
 }
 
+// ------------------------------------------------------------------ cut records
+// Top-p without an effective top-k, or a top-k past kNucCap: the kept set can
+// hold most of the row, so it is not listed.  The kept tokens are the first
+// Nk in (logit desc, index asc) order, i.e. the set
+//   { v : z_v > tau } + { v : z_v == tau and v <= iota }
+// for the logit tau and index iota of the Nk-th (iota = INT_MAX when every
+// token at tau is kept).  k_trunc_cut finds (tau, iota) and the kept mass of
+// each used row; the sampling decision (decide_sample in its cut mode) tests
+// membership element by element as it reads the rows.
+//
+// The search is a radix select over order-preserving keys of the logits
+// (-0 taken as +0, so that equal logits have equal keys; a bf16 logit's key
+// is its 16-bit pattern's, in the top half): a 12-bit digit histogram over
+// the whole row, then histograms of the next digit over the chosen bin only,
+// down to exact values (bf16: 12 + 4 bits; fp32: 12 + 12 + 8).  top-k counts
+// elements; top-p weighs them by 2^((z - max) c) held as integers of 2^-40,
+// so every sum is exact and the same whatever order the lanes add in, and a
+// value's weight in the last digit is its count times its one element weight.
+// An element whose weight is below 2^-40 of the row's largest counts as 0: a
+// relative error below V * 2^-40 of the kept mass.  The last digit's pass
+// also counts each value per segment of the row, so the tie index iota is
+// found by reading one segment again.
+constexpr int kCutBins = 4096;  // 12-bit digits
+constexpr int kCutSegs = 8192;  // last digit: values x segments of tie counters
+constexpr float kFix = 1099511627776.0f;  // 2^40
+
+template <bool BF16>
+__device__ __forceinline__ uint32_t cut_key(float x) {
+    const uint32_t k = ordered_key(x + 0.0f);  // -0 + 0 = +0
+    return BF16 ? (k & 0xffff0000u) : k;
+}
+
+// The logit whose key is k (k from cut_key).
+template <bool BF16>
+__device__ __forceinline__ float cut_value(uint32_t k) {
+    if constexpr (BF16) {
+        const uint32_t h = k >> 16;
+        const uint32_t u = (h & 0x8000u) ? (h & 0x7fffu) : (~h & 0xffffu);
+        return __uint_as_float(u << 16);
+    } else {
+        return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+    }
+}
+
+__device__ __forceinline__ unsigned long long fixed_weight(float x, float M, float c) {
+    return static_cast<unsigned long long>(__builtin_amdgcn_exp2f((x - M) * c) * kFix);
+}
+
+// Digit d of the keys: bits [shift, shift + width).
+template <bool BF16>
+__device__ __forceinline__ int digit_shift(int d) { return d == 0 ? 20 : BF16 ? 16 : (d == 1 ? 8 : 0); }
+template <bool BF16>
+__device__ __forceinline__ int digit_width(int d) { return d == 0 ? 12 : BF16 ? 4 : (d == 1 ? 12 : 8); }
+
+struct Cross {
+    int bin;                   // -1: the bins' total is below the goal
+    unsigned long long above;  // weight of the bins past it
+    unsigned long long total;
+};
+
+// Bins [0, n) read from the top (n a power of two <= kCutBins, weights w(j)):
+// the highest bin j with above(j) < goal <= above(j) + w(j), where above(j)
+// is the weight of the bins past j, and goal = goal_abs + frac * total.
+// Thread t sums a run of consecutive bins from the top into s_run[t]
+// (kThreads entries of LDS), wave 0 scans the runs four to a lane, and the
+// crossing lane walks its runs and then bins.
+template <class W>
+__device__ Cross find_cross(int n, double goal_abs, double frac, unsigned long long* s_run, W&& w) {
+    __shared__ Cross s_res;
+    const int t = threadIdx.x, l = t % kWave;
+    const int per = n >= kThreads ? n / kThreads : 1;
+    const int nthr = n / per;
+    unsigned long long run = 0;
+    if (t < nthr)
+        for (int k = 0; k < per; ++k) run += w(n - 1 - (t * per + k));
+    s_run[t] = run;
+    __syncthreads();
+    if (t < kWave) {
+        const unsigned long long q = s_run[4 * l] + s_run[4 * l + 1] + s_run[4 * l + 2] + s_run[4 * l + 3];
+        unsigned long long incl = q;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const unsigned long long o = __shfl_up(incl, d);
+            if (l >= d) incl += o;
+        }
+        const unsigned long long total = __shfl(incl, kWave - 1);
+        const double goal = goal_abs + frac * static_cast<double>(total);
+        const uint64_t hit = __ballot(static_cast<double>(incl) >= goal);
+        if (!hit) {
+            if (l == 0) s_res = Cross{-1, total, total};
+        } else if (l == static_cast<int>(__builtin_ctzll(hit))) {
+            unsigned long long above = incl - q;
+            int j = -1;
+            for (int r = 4 * l; r < 4 * l + 4 && j < 0; ++r) {
+                if (static_cast<double>(above + s_run[r]) < goal) {
+                    above += s_run[r];
+                    continue;
+                }
+                for (int k = 0; k < per; ++k) {
+                    const int bin = n - 1 - (r * per + k);
+                    const unsigned long long x = w(bin);
+                    if (static_cast<double>(above + x) >= goal) {
+                        j = bin;
+                        break;
+                    }
+                    above += x;
+                }
+            }
+            s_res = Cross{j, above, total};
+        }
+    }
+    __syncthreads();
+    const Cross r = s_res;
+    __syncthreads();  // s_run and s_res serve the next call
+    return r;
+}
+
+// Exclusive prefix sum over the workgroup's lanes in thread order; *total
+// receives the sum (same on every lane).
+__device__ __forceinline__ int block_excl_scan(int v, int* total) {
+    __shared__ int s_w[kWaves];
+    const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+    const int incl = wave_scan(v, 0, [](int x, int y) { return x + y; });
+    __syncthreads();
+    if (l == kWave - 1) s_w[w] = incl;
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) {
+        if (k < w) off += s_w[k];
+        tot += s_w[k];
+    }
+    *total = tot;
+    return off + incl - v;
+}
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_trunc_cut(VerifyParams P) {
+    // one buffer for each pass's histogram: top-k counts (uint32), top-p
+    // weights (uint64), or the last digit's tie counters (uint32)
+    __shared__ unsigned long long s_buf[kCutBins];
+    __shared__ uint32_t s_vcnt[256];  // the last top-p digit: count per value
+    __shared__ unsigned long long s_run[kThreads];
+    __shared__ float s_ms[2];
+    __shared__ int s_tie;
+    constexpr int N = Vec<BF16>::N;
+    constexpr int TILE = kThreads * N * kUnroll;
+    constexpr int NDIG = BF16 ? 2 : 3;
+    const int s = blockIdx.x, b = blockIdx.y;
+    const bool is_target = s <= P.G;
+    const int i = is_target ? s : s - (P.G + 1);
+    const int g = request_gamma(P, b);
+    if (is_target ? (i > g) : (i >= g)) return;  // padding row
+    const void* rp = is_target ? target_row(P, b, i, BF16) : draft_row(P, b, i, BF16);
+    const int V = P.V, t = threadIdx.x;
+    const float c = P.c;
+    uint4* rec = P.cut + static_cast<size_t>(b) * P.rows + s;
+
+    // (0) the row's (max, sum) from its statistics partials
+    if (t < kWave) {
+        MaxSum acc{neg_inf(), 0.0f};
+        const float4* part = P.part + (static_cast<size_t>(b) * P.rows + s) * P.nc;
+        for (int k = t; k < P.nc; k += kWave) {
+            const float4 q = part[k];
+            acc = combine(acc, MaxSum{q.x, q.y}, c);
+        }
+        acc = wave_combine(acc, c);
+        if (t == 0) { s_ms[0] = acc.m; s_ms[1] = acc.s; }
+    }
+    __syncthreads();
+    const float M = s_ms[0];
+    if (!(M < pos_inf()) || !(M > neg_inf()) || !(s_ms[1] == s_ms[1])) {
+        // a NaN or +inf in the row, or nothing but -inf: the decision flags it
+        if (t == 0)
+            *rec = make_uint4(__float_as_uint(pos_inf()), __float_as_uint(1.0f), __float_as_uint(neg_inf()),
+                              0x7fffffffu);
+        return;
+    }
+    const bool use_k = P.top_k > 0 && P.top_k < V;
+    const bool use_p = P.top_p < 1.0f;
+
+    // one read of the row: f(x, key, e, t0) for every element e < V of the tile at t0
+    auto each = [&](auto&& f) {
+        stream_tiles<BF16, VEC>(rp, V, [&](const uint4 (&r)[kUnroll], int t0) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+                for (int q = 0; q < N; ++q) {
+                    const int e = t0 + (u * kThreads + t) * N + q;
+                    const float x = elem<BF16>(r[u], q);
+                    if (e < V) f(x, cut_key<BF16>(x), t0);
+                }
+        });
+        __syncthreads();
+    };
+    uint32_t* const s_cnt = reinterpret_cast<uint32_t*>(s_buf);
+    unsigned long long* const s_wt = s_buf;
+    auto clear = [&](int n) {  // n 64-bit entries (2n counts)
+        for (int j = t; j < n; j += kThreads) s_buf[j] = 0ull;
+        __syncthreads();
+    };
+    auto fixed_mask = [&](int d) -> uint32_t {  // the key bits above digit d
+        const int top = digit_shift<BF16>(d) + digit_width<BF16>(d);
+        return top >= 32 ? 0u : ~((1u << top) - 1u);
+    };
+
+    // (1) top-k: the key of the k-th largest logit, by counts; kept keys are >= lo
+    uint32_t lo = 0;
+    if (use_k) {
+        uint32_t prefix = 0;
+        double need = static_cast<double>(P.top_k);
+        for (int d = 0; d < NDIG; ++d) {
+            const int sh = digit_shift<BF16>(d), nb = 1 << digit_width<BF16>(d);
+            const uint32_t fm = fixed_mask(d);
+            clear(nb);
+            each([&](float, uint32_t key, int) {
+                if ((key & fm) == prefix) atomicAdd(&s_cnt[(key >> sh) & (nb - 1)], 1u);
+            });
+            const Cross cr = find_cross(nb, need, 0.0, s_run, [&](int j) { return static_cast<unsigned long long>(s_cnt[j]); });
+            // (top_k < V elements: the count always reaches it)
+            prefix |= static_cast<uint32_t>(max(cr.bin, 0)) << sh;
+            need -= static_cast<double>(cr.above);
+        }
+        lo = prefix;
+    }
+
+    // (2) the weight of keys >= lo by the top digit; without top-p that is the kept mass
+    clear(kCutBins);
+    each([&](float x, uint32_t key, int) {
+        if (key >= lo) {
+            const unsigned long long f = fixed_weight(x, M, c);
+            if (f) atomicAdd(&s_wt[key >> 20], f);
+        }
+    });
+    auto coarse = [&](int j) { return s_wt[j]; };
+    uint32_t kappa = lo;       // kept: keys > kappa, and key == kappa up to index iota
+    bool all_from_lo = true;   // ... or every key >= lo (top-k alone, or no crossing)
+    int iota = 0x7fffffff;
+    unsigned long long kept = 0;
+    if (!use_p) {
+        kept = find_cross(kCutBins, 0.0, 2.0, s_run, coarse).total;  // (a goal past the total)
+    } else {
+        // (3) top-p: the value at which the running weight, from the top,
+        // first reaches top_p of the total, digit by digit
+        Cross cr = find_cross(kCutBins, 0.0, static_cast<double>(P.top_p), s_run, coarse);
+        const unsigned long long total = cr.total;
+        const double goal_all = static_cast<double>(P.top_p) * static_cast<double>(cr.total);
+        bool found = cr.bin >= 0;
+        uint32_t prefix = static_cast<uint32_t>(max(cr.bin, 0)) << 20;
+        unsigned long long above = cr.above;
+        double goal = goal_all - static_cast<double>(above);
+        for (int d = 1; found && d < NDIG - 1; ++d) {  // fp32's middle digit
+            const int sh = digit_shift<BF16>(d), nb = 1 << digit_width<BF16>(d);
+            const uint32_t fm = fixed_mask(d);
+            clear(nb);
+            each([&](float x, uint32_t key, int) {
+                if (key >= lo && (key & fm) == prefix) {
+                    const unsigned long long f = fixed_weight(x, M, c);
+                    if (f) atomicAdd(&s_wt[(key >> sh) & (nb - 1)], f);
+                }
+            });
+            cr = find_cross(nb, goal, 0.0, s_run, coarse);
+            found = cr.bin >= 0;
+            prefix |= static_cast<uint32_t>(max(cr.bin, 0)) << sh;
+            above += cr.above;
+            goal -= static_cast<double>(cr.above);
+        }
+        // last digit: counts per value (a value's weight is count x its
+        // element weight) and per value and segment of the row
+        const int d = NDIG - 1;
+        const int sh = digit_shift<BF16>(d), nb = 1 << digit_width<BF16>(d);
+        const uint32_t fm = fixed_mask(d);
+        const int ntiles = (V + TILE - 1) / TILE;
+        const int nseg = kCutSegs / nb;
+        const int tps = (ntiles + nseg - 1) / nseg;  // tiles per segment
+        uint32_t* const seg = s_cnt;  // kCutSegs counters
+        if (found) {
+            for (int j = t; j < nb; j += kThreads) s_vcnt[j] = 0u;
+            clear(kCutSegs / 2);
+            each([&](float, uint32_t key, int t0) {
+                if (key >= lo && (key & fm) == prefix) {
+                    const int v = static_cast<int>((key >> sh) & static_cast<uint32_t>(nb - 1));
+                    atomicAdd(&s_vcnt[v], 1u);
+                    atomicAdd(&seg[v * nseg + (t0 / TILE) / tps], 1u);
+                }
+            });
+            auto value_weight = [&](int j) {
+                const uint32_t k = prefix | (static_cast<uint32_t>(j) << sh);
+                return static_cast<unsigned long long>(s_vcnt[j]) * fixed_weight(cut_value<BF16>(k), M, c);
+            };
+            cr = find_cross(nb, goal, 0.0, s_run, value_weight);
+            found = cr.bin >= 0;
+        }
+        if (!found) {
+            // (rounding only: the goal lies past the total) every key >= lo
+            kept = total;
+        } else {
+            const int v = cr.bin;
+            kappa = prefix | (static_cast<uint32_t>(v) << sh);
+            all_from_lo = false;
+            above += cr.above;
+            goal -= static_cast<double>(cr.above);
+            const unsigned long long fk = fixed_weight(cut_value<BF16>(kappa), M, c);
+            const int64_t cnt = static_cast<int64_t>(s_vcnt[v]);
+            // the fewest tokens at kappa that reach the goal, in [1, cnt]
+            int64_t n = fk ? static_cast<int64_t>(ceil(goal / static_cast<double>(fk))) : cnt;
+            n = n < 1 ? 1 : (n > cnt ? cnt : n);
+            while (n > 1 && static_cast<double>(static_cast<unsigned long long>(n - 1) * fk) >= goal) --n;
+            while (n < cnt && static_cast<double>(static_cast<unsigned long long>(n) * fk) < goal) ++n;
+            kept = above + static_cast<unsigned long long>(n) * fk;
+            if (n < cnt) {
+                // iota: the n-th token at kappa in index order.  The segment
+                // holding it from the per-segment counts (ascending order read
+                // as bins from the top), then that segment read again.
+                const Cross sc = find_cross(nseg, static_cast<double>(n), 0.0, s_run,
+                                            [&](int j) { return static_cast<unsigned long long>(seg[v * nseg + nseg - 1 - j]); });
+                const int sg = nseg - 1 - max(sc.bin, 0);
+                int r = static_cast<int>(n - static_cast<int64_t>(sc.above));  // rank inside the segment, from 1
+                if (t == 0) s_tie = 0x7fffffff;
+                __syncthreads();
+                for (int tile = sg * tps; tile < min(ntiles, (sg + 1) * tps) && r > 0; ++tile) {
+                    for (int u = 0; u < kUnroll && r > 0; ++u) {
+                        const int e = tile * TILE + (u * kThreads + t) * N;
+                        const uint4 raw = load_raw<BF16, VEC>(rp, e, V);
+                        int hits = 0;
+#pragma unroll
+                        for (int q = 0; q < N; ++q)
+                            hits += (e + q < V && cut_key<BF16>(elem<BF16>(raw, q)) == kappa) ? 1 : 0;
+                        int total;
+                        const int ex = block_excl_scan(hits, &total);
+                        if (ex < r && r <= ex + hits) {
+                            int k = r - ex;
+#pragma unroll
+                            for (int q = 0; q < N; ++q) {
+                                if (e + q < V && cut_key<BF16>(elem<BF16>(raw, q)) == kappa && --k == 0) s_tie = e + q;
+                            }
+                        }
+                        r -= total;
+                    }
+                }
+                __syncthreads();
+                iota = s_tie;
+            }
+        }
+    }
+    if (t == 0) {
+        const float kept_f = static_cast<float>(static_cast<double>(kept) * (1.0 / 1099511627776.0));
+        const float tau = (all_from_lo && !use_k) ? neg_inf() : cut_value<BF16>(kappa);
+        *rec = make_uint4(__float_as_uint(M), __float_as_uint(kept_f), __float_as_uint(tau),
+                          static_cast<uint32_t>(iota));
+    }
+}
+
 }  // namespace
 
 specdec_status_t launch_truncated(const VerifyParams& P, bool bf16, bool vec, hipStream_t stream,
@@ -851,6 +1204,21 @@ specdec_status_t launch_truncated(const VerifyParams& P, bool bf16, bool vec, hi
     }
     if (hipGetLastError() != hipSuccess) return SPECDEC_ERR_DEVICE;
     launch(k_decide_trunc, dim3(P.B), dim3(kThreads), e2, e3);
+    return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_DEVICE;
+}
+
+
+specdec_status_t launch_trunc_cut(const VerifyParams& P, bool bf16, bool vec, hipStream_t stream,
+                                  hipEvent_t start, hipEvent_t stop) {
+    const dim3 grid(P.rows, P.B);
+    auto launch = [&](auto kernel) {
+        if (start)
+            hipExtLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, start, stop, 0, P);
+        else
+            hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, P);
+    };
+    if (bf16) vec ? launch(k_trunc_cut<true, true>) : launch(k_trunc_cut<true, false>);
+    else vec ? launch(k_trunc_cut<false, true>) : launch(k_trunc_cut<false, false>);
     return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_DEVICE;
 }
 

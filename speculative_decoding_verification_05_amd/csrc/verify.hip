@@ -60,18 +60,25 @@ namespace {
 
 // The mass the draw at position m samples from: max(p - q, 0) on a
 // rejection, p itself when q is absent (bonus, or the empty-residual
-// fallback).  p = 2^((z - max) c) / sum, q likewise.
+// fallback).  p = 2^((z - max) c) / sum, q likewise.  CUT: p and q are
+// truncated to their kept sets, given by cut records (token v of logit z is
+// kept iff z > tau, or z == tau and v <= iota), sum being the kept mass.
 struct MassRows {
     const void* p;
     const void* q;
     float mp, isp, mq, isq, c;
     int point;  // point-mass draft: this token carries no residual mass (-1: none)
+    float tp, tq;  // CUT: boundary logits of p and q
+    int ip, iq;    // CUT: last kept index at the boundary logit
 };
 
-__device__ __forceinline__ float mass_at(const MassRows& a, float zp, float zq) {
-    const float pv = __builtin_amdgcn_exp2f((zp - a.mp) * a.c) * a.isp;
+template <bool CUT>
+__device__ __forceinline__ float mass_at(const MassRows& a, float zp, float zq, int v) {
+    float pv = __builtin_amdgcn_exp2f((zp - a.mp) * a.c) * a.isp;
+    if constexpr (CUT) pv = (zp > a.tp || (zp == a.tp && v <= a.ip)) ? pv : 0.0f;
     if (!a.q) return pv;
-    const float qv = __builtin_amdgcn_exp2f((zq - a.mq) * a.c) * a.isq;
+    float qv = __builtin_amdgcn_exp2f((zq - a.mq) * a.c) * a.isq;
+    if constexpr (CUT) qv = (zq > a.tq || (zq == a.tq && v <= a.iq)) ? qv : 0.0f;
     return fmaxf(pv - qv, 0.0f);
 }
 
@@ -103,7 +110,7 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<BF16, VEC>& r, const MassRo
 }
 
 // Lane's share of the chunk's mass (VEC layout).
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, bool CUT = false>
 __device__ __forceinline__ float lane_mass(const ChunkRegs<BF16, VEC>& r, const MassRows& a, int lo, int hi) {
     constexpr int N = Vec<BF16>::N;
     float acc = 0.0f;
@@ -116,7 +123,7 @@ __device__ __forceinline__ float lane_mass(const ChunkRegs<BF16, VEC>& r, const 
         float s = 0.0f;
 #pragma unroll
         for (int k = 0; k < N; ++k) {
-            const float r = mass_at(a, vp.x[k], a.q ? vq.x[k] : 0.0f);
+            const float r = mass_at<CUT>(a, vp.x[k], a.q ? vq.x[k] : 0.0f, e + k);
             s += (e + k == a.point) ? 0.0f : r;
         }
         acc += (e < hi) ? s : 0.0f;
@@ -126,7 +133,7 @@ __device__ __forceinline__ float lane_mass(const ChunkRegs<BF16, VEC>& r, const 
 
 // Lane's share of the chunk's mass with element loads (rows not 16-byte
 // aligned): a slow path kept simple.
-template <bool BF16>
+template <bool BF16, bool CUT = false>
 __device__ float lane_mass_elements(const MassRows& a, int lo, int hi) {
     constexpr int N = Vec<BF16>::N;
     float acc = 0.0f;
@@ -136,7 +143,7 @@ __device__ float lane_mass_elements(const MassRows& a, int lo, int hi) {
             if (e + k >= hi) break;
             const float zp = load_logit<BF16>(a.p, e + k);
             const float zq = a.q ? load_logit<BF16>(a.q, e + k) : 0.0f;
-            if (e + k != a.point) acc += mass_at(a, zp, zq);
+            if (e + k != a.point) acc += mass_at<CUT>(a, zp, zq, e + k);
         }
     }
     return acc;
@@ -150,7 +157,7 @@ __device__ float lane_mass_elements(const MassRows& a, int lo, int hi) {
 // chunk), and after one barrier thread 0 adds them in wave order and emits
 // the whole batch at once (batches of 1024 / kWaves chunks).  Returns the OR
 // of emit's results (a dependency for arrive_last when emit publishes).
-template <bool BF16, bool VEC, int GROUP, bool CACHED, class Emit>
+template <bool BF16, bool VEC, int GROUP, bool CACHED, bool CUT = false, class Emit>
 __device__ uint32_t mass_chunks(const MassRows& a, int k0, int k1, int chunk2, int V, float* scr,
                                 Emit&& emit) {
     uint32_t dep = 0;
@@ -172,7 +179,7 @@ __device__ uint32_t mass_chunks(const MassRows& a, int k0, int k1, int chunk2, i
                 for (int j = 0; j < GROUP; ++j) {
                     if (kb + j >= b1) break;
                     const int lo = (kb + j) * chunk2, hi = min(V, lo + chunk2);
-                    const float s = wave_sum(lane_mass<BF16, VEC>(r[j], a, lo, hi));
+                    const float s = wave_sum(lane_mass<BF16, VEC, CUT>(r[j], a, lo, hi));
                     if (l == 0) scr[(kb + j - b0) * kWaves + w] = s;
                 }
             };
@@ -200,7 +207,7 @@ __device__ uint32_t mass_chunks(const MassRows& a, int k0, int k1, int chunk2, i
     } else {
         for (int k = k0; k < k1; ++k) {
             const int lo = k * chunk2, hi = min(V, lo + chunk2);
-            const float t = block_sum(lane_mass_elements<BF16>(a, lo, hi));
+            const float t = block_sum(lane_mass_elements<BF16, CUT>(a, lo, hi));
             if (threadIdx.x == 0) dep |= emit(k, t);
         }
     }
@@ -208,14 +215,14 @@ __device__ uint32_t mass_chunks(const MassRows& a, int k0, int k1, int chunk2, i
 }
 
 // Mass of one chunk (the empty-residual fallback path).
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, bool CUT = false>
 __device__ float chunk_mass(const MassRows& a, int lo, int hi) {
     if constexpr (VEC) {
         ChunkRegs<BF16, VEC> r;
         load_chunk<BF16, VEC, false>(r, a, lo, hi);
-        return block_sum(lane_mass<BF16, VEC>(r, a, lo, hi));
+        return block_sum(lane_mass<BF16, VEC, CUT>(r, a, lo, hi));
     } else {
-        return block_sum(lane_mass_elements<BF16>(a, lo, hi));
+        return block_sum(lane_mass_elements<BF16, CUT>(a, lo, hi));
     }
 }
 
@@ -225,7 +232,7 @@ __device__ float chunk_mass(const MassRows& a, int lo, int hi) {
 // block-wide exclusive scan of the lane totals gives each lane its offset.
 // Returns 0x7fffffff if none; *last_pos receives the chunk's largest v with
 // mass > 0.
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, bool CUT = false>
 __device__ int search_chunk(const MassRows& a, int lo, int hi, float base, float target,
                             int* last_pos) {
     constexpr int N = Vec<BF16>::N;
@@ -256,7 +263,7 @@ __device__ int search_chunk(const MassRows& a, int lo, int hi, float base, float
 #pragma unroll
         for (int k = 0; k < N; ++k) {
             const int v = e0 + u * N + k;
-            const float x = (v < hi && v != a.point) ? mass_at(a, vp[u].x[k], a.q ? vq[u].x[k] : 0.0f) : 0.0f;
+            const float x = (v < hi && v != a.point) ? mass_at<CUT>(a, vp[u].x[k], a.q ? vq[u].x[k] : 0.0f, v) : 0.0f;
             if (x > 0.0f) lastp = v;
             r[u * N + k] = x;
             run += x;
@@ -430,11 +437,14 @@ __device__ bool collect_masses(const VerifyParams& P, unsigned long long* cm, in
 // Decision workgroup wg of request b.  FUSED: the statistics come from the
 // same kernel's statistics workgroups (wait_partials), and the drafted
 // tokens' logits are read from the rows directly; otherwise from the
-// partials the statistics kernel stored.
-template <bool BF16, bool VEC, int GROUP, bool FUSED, bool CACHED>
+// partials the statistics kernel stored.  CUT: p and q are truncated, each
+// row's (max, kept mass) and kept set coming from its cut record
+// (k_trunc_cut); everything else as without truncation.
+template <bool BF16, bool VEC, int GROUP, bool FUSED, bool CACHED, bool CUT = false>
 __device__ __forceinline__ void decide_sample(const VerifyParams& P, const int wg, const int b) {
     __shared__ float4 s_part[kMaxPart];
     __shared__ float2 s_stat[127];
+    __shared__ float2 s_cut[CUT ? 127 : 1];  // (boundary logit, last kept index at it as bits)
     __shared__ float s_csum[1024];
     __shared__ int s_m, s_dm;
     __shared__ uint32_t s_fl;
@@ -477,8 +487,17 @@ __device__ __forceinline__ void decide_sample(const VerifyParams& P, const int w
     }
 
     // (1) (max, sum) of every used row from its chunk partials: a lane per
-    // row over a few partials, else a wave per row
-    if (P.nc <= kSerialParts) {
+    // row over a few partials, else a wave per row (CUT: (max, kept mass)
+    // and the kept set from the row's cut record)
+    if constexpr (CUT) {
+        for (int s = threadIdx.x; s < P.rows; s += kThreads) {
+            const bool used = (s <= P.G) ? (s <= g) : (s - (P.G + 1) < g);
+            if (!used) continue;
+            const uint4 r = P.cut[static_cast<size_t>(b) * P.rows + s];
+            s_stat[s] = make_float2(__uint_as_float(r.x), __uint_as_float(r.y));
+            s_cut[s] = make_float2(__uint_as_float(r.z), __uint_as_float(r.w));
+        }
+    } else if (P.nc <= kSerialParts) {
         for (int s = threadIdx.x; s < P.rows; s += kThreads) {
             const bool used = (s <= P.G) ? (s <= g) : (s - (P.G + 1) < g);
             if (!used) continue;
@@ -528,6 +547,12 @@ __device__ __forceinline__ void decide_sample(const VerifyParams& P, const int w
                 } else {
                     qd = exp2f((zq - q.x) * c) / q.y;
                 }
+                if constexpr (CUT) {
+                    // a token outside a kept set has probability 0 there
+                    const float2 kt = s_cut[i], kq = s_cut[P.G + 1 + i];
+                    if (!(zt > kt.x || (zt == kt.x && d <= __float_as_int(kt.y)))) pd = 0.0f;
+                    if (!P.point && !(zq > kq.x || (zq == kq.x && d <= __float_as_int(kq.y)))) qd = 0.0f;
+                }
                 if (qd > 0.0f) a = fminf(1.0f, pd / qd);
                 else a = pd > 0.0f ? 1.0f : 0.0f;
             } else {
@@ -559,6 +584,12 @@ __device__ __forceinline__ void decide_sample(const VerifyParams& P, const int w
     a.mq = 0.0f;
     a.isq = 0.0f;
     a.point = -1;
+    a.tp = a.tq = neg_inf();
+    a.ip = a.iq = 0x7fffffff;
+    if constexpr (CUT) {
+        a.tp = s_cut[m].x;
+        a.ip = __float_as_int(s_cut[m].y);
+    }
     if (resid && P.point) {
         // max(p - delta_d, 0): p itself without the rejected token
         a.point = s_dm;
@@ -567,6 +598,10 @@ __device__ __forceinline__ void decide_sample(const VerifyParams& P, const int w
         a.q = draft_row(P, b, m, BF16);
         a.mq = tq.x;
         a.isq = 1.0f / tq.y;
+        if constexpr (CUT) {
+            a.tq = s_cut[P.G + 1 + m].x;
+            a.iq = __float_as_int(s_cut[P.G + 1 + m].y);
+        }
     }
     const int k0 = wg * P.cpw, k1 = min(P.nc2, k0 + P.cpw);
     float* scr = reinterpret_cast<float*>(s_part);  // the partials are combined: free
@@ -615,7 +650,7 @@ __device__ __forceinline__ void decide_sample(const VerifyParams& P, const int w
         else clear_partials(P, b, g, false);
     } else {
         uint32_t* csum = P.csum + static_cast<size_t>(b) * P.nc2;
-        const uint32_t dep = mass_chunks<BF16, VEC, GROUP, CACHED>(
+        const uint32_t dep = mass_chunks<BF16, VEC, GROUP, CACHED, CUT>(
             a, k0, k1, P.chunk2, P.V, scr, [&](int k, float t) { return publish(csum + k, __float_as_uint(t)); });
         if (!arrive_last(P.cnt + b, static_cast<uint32_t>(P.wpr), dep)) return;
         for (int k = threadIdx.x; k < P.nc2; k += kThreads) s_csum[k] = __uint_as_float(fetch(csum + k));
@@ -678,7 +713,7 @@ __device__ __forceinline__ void decide_sample(const VerifyParams& P, const int w
             a.q = nullptr;
             a.point = -1;
             for (int k = 0; k < P.nc2; ++k) {
-                const float v = chunk_mass<BF16, VEC>(a, k * P.chunk2, min(P.V, (k + 1) * P.chunk2));
+                const float v = chunk_mass<BF16, VEC, CUT>(a, k * P.chunk2, min(P.V, (k + 1) * P.chunk2));
                 if (threadIdx.x == 0) s_csum[k] = v;
             }
             __syncthreads();
@@ -688,7 +723,7 @@ __device__ __forceinline__ void decide_sample(const VerifyParams& P, const int w
     const float target = s_um * s_R;
     int lastp;
     const int l2 = s_chunk * P.chunk2, h2 = min(P.V, l2 + P.chunk2);
-    int token = search_chunk<BF16, VEC>(a, l2, h2, s_before, target, &lastp);
+    int token = search_chunk<BF16, VEC, CUT>(a, l2, h2, s_before, target, &lastp);
     // The chunk sums and the in-chunk prefixes associate the additions
     // differently; if that rounding leaves no element above u*R in the chosen
     // chunk, the crossing is its last token with mass.
@@ -710,6 +745,12 @@ __device__ __forceinline__ void decide_sample(const VerifyParams& P, const int w
 template <bool BF16, bool VEC, int GROUP>
 __global__ __launch_bounds__(kThreads) void k_decide_sample(VerifyParams P) {
     decide_sample<BF16, VEC, GROUP, false, false>(P, blockIdx.x, blockIdx.y);
+}
+
+// The sampling decision over truncated rows given by cut records.
+template <bool BF16, bool VEC, int GROUP>
+__global__ __launch_bounds__(kThreads) void k_decide_cut(VerifyParams P) {
+    decide_sample<BF16, VEC, GROUP, false, false, true>(P, blockIdx.x, blockIdx.y);
 }
 
 // ------------------------------------------------------------------ one-kernel sampling verify
@@ -869,12 +910,16 @@ bool truncation_mode(const specdec_verify_desc_t* d) {
            ((d->top_k > 0 && d->top_k < d->vocab) || d->top_p < 1.0f);
 }
 
-// Truncation requests the kernels do not serve (see specdec.h).
-bool truncation_supported(const specdec_verify_desc_t* d) {
+// Truncation whose kept sets may be too long to list (top-p alone over more
+// than kTruncCap tokens, or a top-k past kNucCap): cut records instead of
+// kept-token records.  The debug build can force this path for any
+// truncation (SPECDEC_TRUNC_CUT=1), for the tests that compare the two.
+bool truncation_cut(const specdec_verify_desc_t* d) {
+    if (!truncation_mode(d)) return false;
     const bool use_k = d->top_k > 0 && d->top_k < d->vocab;
-    if (use_k && d->top_k > kNucCap) return false;
-    if (!use_k && d->vocab > kTruncCap) return false;
-    return true;
+    if (use_k ? d->top_k > kNucCap : d->vocab > kTruncCap) return true;
+    const char* s = debug_knob("SPECDEC_TRUNC_CUT");
+    return s && s[0] == '1';
 }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -972,8 +1017,13 @@ Layout make_layout(const specdec_verify_desc_t* d, bool point) {
     L.off_part = off; off = align256(off + B * L.rows * L.nc * sizeof(float4));
     L.off_csum = off; off = align256(off + B * L.nc2 * sizeof(uint32_t));
     L.trunc = truncation_mode(d);
-    L.off_nuc = off;
-    if (L.trunc) off = align256(off + B * L.rows * (1 + kNucCap) * sizeof(uint2));
+    L.cut = truncation_cut(d);
+    // the cut decision's membership tests take registers: groups of at most
+    // two chunks (larger ones spill)
+    if (L.cut && L.group > kMassGroupChunks) L.group = kMassGroupChunks;
+    L.off_nuc = off;  // kept-token records, or cut records
+    if (L.cut) off = align256(off + B * L.rows * sizeof(uint4));
+    else if (L.trunc) off = align256(off + B * L.rows * (1 + kNucCap) * sizeof(uint2));
     L.total = off;
     return L;
 }
@@ -1066,6 +1116,29 @@ specdec_status_t launch_all(const specdec_verify_desc_t* d, const VerifyParams& 
     return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_DEVICE;
 }
 
+// Truncation by cut records: the statistics pass, the cut records, then the
+// sampling decision over the truncated rows.  ev (may be null): start/stop
+// of the cut kernel (the pass that dominates) and of the decision.
+template <bool BF16, bool VEC>
+specdec_status_t launch_cut(const specdec_verify_desc_t* d, const VerifyParams& P, const Layout& L,
+                            hipStream_t stream, hipEvent_t* ev) {
+    hipEvent_t e0 = ev ? ev[0] : nullptr, e1 = ev ? ev[1] : nullptr;
+    hipEvent_t e2 = ev ? ev[2] : nullptr, e3 = ev ? ev[3] : nullptr;
+    if (launch_stats(P, BF16, VEC, false, dim3(L.nc, L.rows, d->batch), stream, nullptr, nullptr) != SPECDEC_OK)
+        return SPECDEC_ERR_DEVICE;
+    if (launch_trunc_cut(P, BF16, VEC, stream, e0, e1) != SPECDEC_OK) return SPECDEC_ERR_DEVICE;
+    const dim3 grid(L.wpr, d->batch), block(kThreads);
+    auto launch = [&](auto kernel) {
+        if (ev)
+            hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, e2, e3, 0, P);
+        else
+            hipLaunchKernelGGL(kernel, grid, block, 0, stream, P);
+    };
+    if (L.group == 1) launch(k_decide_cut<BF16, VEC, 1>);
+    else launch(k_decide_cut<BF16, VEC, 2>);
+    return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_DEVICE;
+}
+
 specdec_status_t verify_impl(const specdec_verify_desc_t* d, const void* target_logits,
                              const void* draft_logits, const int32_t* draft_tokens,
                              const int32_t* gamma, const int32_t* max_tokens,
@@ -1081,7 +1154,7 @@ specdec_status_t verify_impl(const specdec_verify_desc_t* d, const void* target_
     // sampling without draft rows: point-mass drafts of a deterministic proposer
     // (with gamma_max = 0 there is no draft row either way)
     const bool point = sample && !draft_logits && d->gamma_max > 0;
-    if (truncation_mode(d) && (point || !truncation_supported(d))) return SPECDEC_ERR_UNSUPPORTED;
+    if (truncation_mode(d) && point) return SPECDEC_ERR_UNSUPPORTED;
     const Layout L = make_layout(d, point);
     if (workspace_bytes < L.total) return SPECDEC_ERR_WORKSPACE_TOO_SMALL;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return SPECDEC_ERR_INVALID_ARGUMENT;
@@ -1116,6 +1189,7 @@ specdec_status_t verify_impl(const specdec_verify_desc_t* d, const void* target_
     P.part = reinterpret_cast<float4*>(ws + L.off_part);
     P.csum = reinterpret_cast<uint32_t*>(ws + L.off_csum);
     P.nuc = reinterpret_cast<uint2*>(ws + L.off_nuc);
+    P.cut = reinterpret_cast<uint4*>(ws + L.off_nuc);
     P.top_k = d->top_k;
     P.top_p = d->top_p;
     P.B = d->batch;
@@ -1153,6 +1227,8 @@ specdec_status_t verify_impl(const specdec_verify_desc_t* d, const void* target_
                      kResidCachedBytes;
     const bool vec = aligned16(target_logits) && (!sample || aligned16(draft_logits)) &&
                      (static_cast<size_t>(d->vocab) * es) % 16 == 0;
+    if (L.cut) return bf16 ? (vec ? launch_cut<true, true>(d, P, L, stream, ev) : launch_cut<true, false>(d, P, L, stream, ev))
+                           : (vec ? launch_cut<false, true>(d, P, L, stream, ev) : launch_cut<false, false>(d, P, L, stream, ev));
     if (L.trunc) return launch_truncated(P, bf16, vec, stream, ev);
     if (bf16)
         return vec ? launch_all<true, true>(d, P, L, fused, stream, ev)

@@ -62,6 +62,7 @@ struct VerifyParams {
     int top_k;          // 0 or >= V: no top-k
     float top_p;        // 1: no top-p
     uint2* nuc;         // [B][R][1 + kNucCap] kept-token records
+    uint4* cut;         // [B][R] cut records: (max, kept mass, boundary logit, last kept index at it)
 };
 
 // gamma_b clamped into [0, G] (an out-of-range value is flagged by the
@@ -174,7 +175,7 @@ __device__ __forceinline__ float block_sum(float v) {
 // always takes the measured defaults below.  The debug build of the same
 // sources (libspecdec_debug.so, compiled with SPECDEC_DEBUG_KNOBS) reads
 // SPECDEC_FUSED, SPECDEC_FUSED_WAIT_TICKS, SPECDEC_FUSED_LAG,
-// SPECDEC_STATS_TILES and SPECDEC_SAMPLE_WPR, for the tests that compare
+// SPECDEC_STATS_TILES, SPECDEC_SAMPLE_WPR and SPECDEC_TRUNC_CUT, for the tests that compare
 // paths or force a timeout, and for tuning sweeps.
 constexpr uint64_t kFixedWaitTicks = 2000000ull;  // 20 ms of the 100 MHz constant clock
 
@@ -212,6 +213,7 @@ struct Layout {
     int group;          // sampling-pass chunks loaded together (1..kMassGroupWide)
     int fwpr, fcpw;     // one-kernel path: decision workgroups per request, chunks each
     bool trunc;
+    bool cut;           // truncation by cut records (kept sets not listed)
     size_t off_cnt, off_ready, off_cmass, off_part, off_csum, off_nuc, total;
 };
 // point: sampling with point-mass drafts (no draft rows)
@@ -226,5 +228,12 @@ specdec_status_t launch_stats(const VerifyParams& P, bool bf16, bool vec, bool g
 // every used row's kept tokens, then the per-request decision over them.
 specdec_status_t launch_truncated(const VerifyParams& P, bool bf16, bool vec, hipStream_t stream,
                                   hipEvent_t* ev);
+
+// Truncation whose kept set is not listed (top-p without an effective top-k,
+// or top-k past kNucCap): the cut record of every used row, from the row and
+// its statistics partials (run the statistics pass first).  start/stop
+// events (both null, or both set) bracket the kernel.
+specdec_status_t launch_trunc_cut(const VerifyParams& P, bool bf16, bool vec, hipStream_t stream,
+                                  hipEvent_t start, hipEvent_t stop);
 
 }  // namespace specdec

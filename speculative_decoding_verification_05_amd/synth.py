@@ -23,6 +23,9 @@ pages; sizes are the full-scale cases used for parity and timing):
                               top-k 50 then top-p 0.9.
 * ``b512_ragged_v262144_kv`` B=512, gamma_i in U{1..8}, V=262144, bf16, T=1.0,
                               paged KV commit (32 layers x 8 heads x 128).
+* ``b64_g4_v128256_topp09``  the b64_g4_v128256_bf16 recipe with top-p 0.9 and
+                              no top-k (kept sets of hundreds to thousands of
+                              tokens, too many to list).
 
 * ``tree_b64_n16_v151936_greedy_kv``  B=64 draft trees of 16 nodes (depth 5,
                               the fixed topology TREE16 below), V=151936, bf16,
@@ -146,6 +149,9 @@ WORKLOADS: Dict[str, Workload] = {w.name: w for w in [
              kv=KVShape(28, 4, 128, 16, 512, 4096), data_seed=1006, verify_seed=48),
     Workload("ngram_b512_ctx1k8k_g8", 512, 8, 262144, "bf16", "greedy", 1.0, 0.0,
              "history", zipf_s=1.1, ngram=(2, 4, 1024, 8192), data_seed=1007, verify_seed=49),
+    Workload("b64_g4_v128256_topp09", 64, 4, 128256, "bf16", "sample", 0.8, 3.0,
+             "noise_per_request", sigma_lo=0.2, sigma_hi=1.5, top_p=0.9,
+             data_seed=1008, verify_seed=50),
     Workload("b512_ragged_v262144_kv", 512, 8, 262144, "bf16", "sample", 1.0, 3.0,
              "noise_fixed", draft_sigma=0.6, ragged=True,
              kv=KVShape(32, 8, 128, 16, 1024, 8192), draft_kv=KVShape(18, 1, 256, 16, 1024, 8192),

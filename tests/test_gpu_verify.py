@@ -477,18 +477,9 @@ def test_truncation_ties_at_the_kth_value():
     check_sample(wl, x, label="ties at the k-th value")
 
 
-def test_truncation_unsupported_shapes_are_rejected():
-    import torch
-    B, G = 2, 2
+def test_truncation_past_the_listed_limits_matches_the_oracle():
+    """top_k above 1024, and top-p alone above 2048 tokens, run through the
+    cut records (no longer rejected)."""
     for vocab, top_k, top_p in ((50000, 2000, 1.0), (5000, 0, 0.9)):
-        desc = sd.make_verify_desc(B, G, vocab, temperature=1.0, top_k=top_k, top_p=top_p)
-        ws = torch.zeros(sd.specdec_verify_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
-        t = torch.zeros(B, G + 1, vocab, dtype=torch.int16, device="cuda")
-        d = torch.zeros(B, G, vocab, dtype=torch.int16, device="cuda")
-        tok = torch.zeros(B, G, dtype=torch.int32, device="cuda")
-        acc = torch.zeros(B, dtype=torch.int32, device="cuda")
-        out = torch.zeros(B, G + 1, dtype=torch.int32, device="cuda")
-        with pytest.raises(sd.SpecdecError) as e:
-            sd.specdec_verify(desc, t, d, tok, None, None, acc, None, out, None, None, None, None,
-                              ws)
-        assert e.value.status == sd.SPECDEC_ERR_UNSUPPORTED
+        wl = W["b128_g4_v128256_topk50_topp09"].scaled(3, vocab, top_k=top_k, top_p=top_p)
+        check_sample(wl, label=f"V={vocab} k={top_k} p={top_p}")
