@@ -34,3 +34,41 @@ def test_runner_enqueues_exactly_n_steps(per, n):
     assert sum(calls) == n
     assert calls == [per] * (n // per) + ([n % per] if n % per else [])
     assert not runner.graphed
+
+
+@pytest.mark.parametrize("graph_s,eager_s,want", [(0.002, 0.0, "eager"), (0.0, 0.002, "hipgraph")])
+def test_runner_picks_the_faster_launch_mode(monkeypatch, graph_s, eager_s, want):
+    """pick_faster times untimed windows both ways and keeps the faster
+    mode; the timed run then launches only that way."""
+    import time
+    import torch
+    monkeypatch.setattr(torch.cuda, "synchronize", lambda: None)
+
+    class FakeGraph:
+        replays = 0
+
+        def replay(self):
+            FakeGraph.replays += 1
+            time.sleep(graph_s)
+
+    calls = []
+
+    def enqueue(k):
+        calls.append(k)
+        time.sleep(eager_s)
+
+    runner = bench.GraphSteps(enqueue, 4, lambda i: True)
+    runner.graphs = {4: FakeGraph()}
+    assert runner.pick_faster(8, rounds=3) == want
+    assert runner.graphed == (want == "hipgraph")
+    calls.clear()
+    FakeGraph.replays = 0
+    runner.run(8)
+    assert (FakeGraph.replays, sum(calls)) == ((2, 0) if want == "hipgraph" else (0, 8))
+
+
+def test_runner_without_graphs_stays_eager():
+    calls = []
+    runner = bench.GraphSteps(lambda k: calls.append(k), 4, lambda i: True, use_graphs=False)
+    assert runner.pick_faster(8) == "eager"
+    assert calls == []  # nothing run: there is no choice to make
