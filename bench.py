@@ -105,7 +105,7 @@ class GraphSteps:
                         "timing eager launches")
                     self.graphed = False
 
-    def pick_faster(self, n: int, rounds: int = 3) -> str:
+    def pick_faster(self, n: int, rounds: int = 5) -> str:
         """Untimed windows of n steps, launched from the graphs and eagerly
         in turn; the faster by median becomes the launch mode of the timed
         run (a graph replay's start-up is paid once per window, which a short

@@ -883,19 +883,21 @@ template <bool BF16>
 __device__ __forceinline__ int digit_width(int d) { return d == 0 ? 12 : BF16 ? 4 : (d == 1 ? 12 : 8); }
 
 struct Cross {
-    int bin;                   // -1: the bins' total is below the goal
-    unsigned long long above;  // weight of the bins past it
-    unsigned long long total;
+    int bin;                   // -1: base plus the bins' total stays below the goal
+    unsigned long long above;  // base plus the weight of the bins past it
+    unsigned long long total;  // base plus the weight of all the bins
 };
 
-// Bins [0, n) read from the top (n a power of two <= kCutBins, weights w(j)):
-// the highest bin j with above(j) < goal <= above(j) + w(j), where above(j)
-// is the weight of the bins past j, and goal = goal_abs + frac * total.
+// Bins [0, n) read from the top (n a power of two <= kCutBins, weights w(j)),
+// after `base` (the weight already above them): the highest bin j with
+// base + above(j) < goal <= base + above(j) + w(j), above(j) being the
+// weight of the bins past j.  Every test compares an exact integer sum with
+// the goal the same way, so successive searches agree at their edges.
 // Thread t sums a run of consecutive bins from the top into s_run[t]
 // (kThreads entries of LDS), wave 0 scans the runs four to a lane, and the
 // crossing lane walks its runs and then bins.
 template <class W>
-__device__ Cross find_cross(int n, double goal_abs, double frac, unsigned long long* s_run, W&& w) {
+__device__ Cross find_cross(int n, double goal, unsigned long long base, unsigned long long* s_run, W&& w) {
     __shared__ Cross s_res;
     const int t = threadIdx.x, l = t % kWave;
     const int per = n >= kThreads ? n / kThreads : 1;
@@ -913,13 +915,12 @@ __device__ Cross find_cross(int n, double goal_abs, double frac, unsigned long l
             const unsigned long long o = __shfl_up(incl, d);
             if (l >= d) incl += o;
         }
-        const unsigned long long total = __shfl(incl, kWave - 1);
-        const double goal = goal_abs + frac * static_cast<double>(total);
-        const uint64_t hit = __ballot(static_cast<double>(incl) >= goal);
+        const unsigned long long total = base + __shfl(incl, kWave - 1);
+        const uint64_t hit = __ballot(static_cast<double>(base + incl) >= goal);
         if (!hit) {
             if (l == 0) s_res = Cross{-1, total, total};
         } else if (l == static_cast<int>(__builtin_ctzll(hit))) {
-            unsigned long long above = incl - q;
+            unsigned long long above = base + incl - q;
             int j = -1;
             for (int r = 4 * l; r < 4 * l + 4 && j < 0; ++r) {
                 if (static_cast<double>(above + s_run[r]) < goal) {
@@ -1038,7 +1039,7 @@ __global__ __launch_bounds__(kThreads) void k_trunc_cut(VerifyParams P) {
     uint32_t lo = 0;
     if (use_k) {
         uint32_t prefix = 0;
-        double need = static_cast<double>(P.top_k);
+        unsigned long long above = 0;  // elements with keys past the prefix's range
         for (int d = 0; d < NDIG; ++d) {
             const int sh = digit_shift<BF16>(d), nb = 1 << digit_width<BF16>(d);
             const uint32_t fm = fixed_mask(d);
@@ -1046,15 +1047,22 @@ __global__ __launch_bounds__(kThreads) void k_trunc_cut(VerifyParams P) {
             each([&](float, uint32_t key, int) {
                 if ((key & fm) == prefix) atomicAdd(&s_cnt[(key >> sh) & (nb - 1)], 1u);
             });
-            const Cross cr = find_cross(nb, need, 0.0, s_run, [&](int j) { return static_cast<unsigned long long>(s_cnt[j]); });
+            const Cross cr = find_cross(nb, static_cast<double>(P.top_k), above, s_run,
+                                        [&](int j) { return static_cast<unsigned long long>(s_cnt[j]); });
             // (top_k < V elements: the count always reaches it)
             prefix |= static_cast<uint32_t>(max(cr.bin, 0)) << sh;
-            need -= static_cast<double>(cr.above);
+            above = cr.above;
         }
         lo = prefix;
     }
 
-    // (2) the weight of keys >= lo by the top digit; without top-p that is the kept mass
+    // (2) the weight of keys >= lo by the top digit (without top-p, their
+    // total is the kept mass)
+    auto coarse = [&](int j) { return s_wt[j]; };
+    uint32_t kappa = lo;       // kept: keys > kappa, and key == kappa up to index iota
+    bool all_from_lo = true;   // ... or every key >= lo (top-k alone, or no crossing)
+    int iota = 0x7fffffff;
+    unsigned long long kept = 0;
     clear(kCutBins);
     each([&](float x, uint32_t key, int) {
         if (key >= lo) {
@@ -1062,23 +1070,20 @@ __global__ __launch_bounds__(kThreads) void k_trunc_cut(VerifyParams P) {
             if (f) atomicAdd(&s_wt[key >> 20], f);
         }
     });
-    auto coarse = [&](int j) { return s_wt[j]; };
-    uint32_t kappa = lo;       // kept: keys > kappa, and key == kappa up to index iota
-    bool all_from_lo = true;   // ... or every key >= lo (top-k alone, or no crossing)
-    int iota = 0x7fffffff;
-    unsigned long long kept = 0;
+    const double goal_frac = static_cast<double>(P.top_p);
+    // (a goal past any total: the bins' total alone)
+    const unsigned long long total = find_cross(kCutBins, 1e300, 0ull, s_run, coarse).total;
+    Cross cr{-1, 0, 0};
+    if (use_p) cr = find_cross(kCutBins, goal_frac * static_cast<double>(total), 0ull, s_run, coarse);
     if (!use_p) {
-        kept = find_cross(kCutBins, 0.0, 2.0, s_run, coarse).total;  // (a goal past the total)
+        kept = total;
     } else {
         // (3) top-p: the value at which the running weight, from the top,
         // first reaches top_p of the total, digit by digit
-        Cross cr = find_cross(kCutBins, 0.0, static_cast<double>(P.top_p), s_run, coarse);
-        const unsigned long long total = cr.total;
-        const double goal_all = static_cast<double>(P.top_p) * static_cast<double>(cr.total);
+        const double goal = goal_frac * static_cast<double>(total);
         bool found = cr.bin >= 0;
         uint32_t prefix = static_cast<uint32_t>(max(cr.bin, 0)) << 20;
         unsigned long long above = cr.above;
-        double goal = goal_all - static_cast<double>(above);
         for (int d = 1; found && d < NDIG - 1; ++d) {  // fp32's middle digit
             const int sh = digit_shift<BF16>(d), nb = 1 << digit_width<BF16>(d);
             const uint32_t fm = fixed_mask(d);
@@ -1089,11 +1094,10 @@ __global__ __launch_bounds__(kThreads) void k_trunc_cut(VerifyParams P) {
                     if (f) atomicAdd(&s_wt[(key >> sh) & (nb - 1)], f);
                 }
             });
-            cr = find_cross(nb, goal, 0.0, s_run, coarse);
+            cr = find_cross(nb, goal, above, s_run, coarse);
             found = cr.bin >= 0;
             prefix |= static_cast<uint32_t>(max(cr.bin, 0)) << sh;
-            above += cr.above;
-            goal -= static_cast<double>(cr.above);
+            above = cr.above;
         }
         // last digit: counts per value (a value's weight is count x its
         // element weight) and per value and segment of the row
@@ -1118,31 +1122,31 @@ __global__ __launch_bounds__(kThreads) void k_trunc_cut(VerifyParams P) {
                 const uint32_t k = prefix | (static_cast<uint32_t>(j) << sh);
                 return static_cast<unsigned long long>(s_vcnt[j]) * fixed_weight(cut_value<BF16>(k), M, c);
             };
-            cr = find_cross(nb, goal, 0.0, s_run, value_weight);
+            cr = find_cross(nb, goal, above, s_run, value_weight);
             found = cr.bin >= 0;
         }
         if (!found) {
-            // (rounding only: the goal lies past the total) every key >= lo
+            // (not reached: the goal lies past the total) every key >= lo
             kept = total;
         } else {
             const int v = cr.bin;
             kappa = prefix | (static_cast<uint32_t>(v) << sh);
             all_from_lo = false;
-            above += cr.above;
-            goal -= static_cast<double>(cr.above);
+            above = cr.above;
             const unsigned long long fk = fixed_weight(cut_value<BF16>(kappa), M, c);
+            auto reach = [&](unsigned long long x) { return static_cast<double>(x) >= goal; };
             const int64_t cnt = static_cast<int64_t>(s_vcnt[v]);
             // the fewest tokens at kappa that reach the goal, in [1, cnt]
-            int64_t n = fk ? static_cast<int64_t>(ceil(goal / static_cast<double>(fk))) : cnt;
+            int64_t n = fk ? static_cast<int64_t>(ceil((goal - static_cast<double>(above)) / static_cast<double>(fk))) : cnt;
             n = n < 1 ? 1 : (n > cnt ? cnt : n);
-            while (n > 1 && static_cast<double>(static_cast<unsigned long long>(n - 1) * fk) >= goal) --n;
-            while (n < cnt && static_cast<double>(static_cast<unsigned long long>(n) * fk) < goal) ++n;
+            while (n > 1 && reach(above + static_cast<unsigned long long>(n - 1) * fk)) --n;
+            while (n < cnt && !reach(above + static_cast<unsigned long long>(n) * fk)) ++n;
             kept = above + static_cast<unsigned long long>(n) * fk;
             if (n < cnt) {
                 // iota: the n-th token at kappa in index order.  The segment
                 // holding it from the per-segment counts (ascending order read
                 // as bins from the top), then that segment read again.
-                const Cross sc = find_cross(nseg, static_cast<double>(n), 0.0, s_run,
+                const Cross sc = find_cross(nseg, static_cast<double>(n), 0ull, s_run,
                                             [&](int j) { return static_cast<unsigned long long>(seg[v * nseg + nseg - 1 - j]); });
                 const int sg = nseg - 1 - max(sc.bin, 0);
                 int r = static_cast<int>(n - static_cast<int64_t>(sc.above));  // rank inside the segment, from 1
@@ -1156,8 +1160,8 @@ __global__ __launch_bounds__(kThreads) void k_trunc_cut(VerifyParams P) {
 #pragma unroll
                         for (int q = 0; q < N; ++q)
                             hits += (e + q < V && cut_key<BF16>(elem<BF16>(raw, q)) == kappa) ? 1 : 0;
-                        int total;
-                        const int ex = block_excl_scan(hits, &total);
+                        int tot;
+                        const int ex = block_excl_scan(hits, &tot);
                         if (ex < r && r <= ex + hits) {
                             int k = r - ex;
 #pragma unroll
@@ -1165,7 +1169,7 @@ __global__ __launch_bounds__(kThreads) void k_trunc_cut(VerifyParams P) {
                                 if (e + q < V && cut_key<BF16>(elem<BF16>(raw, q)) == kappa && --k == 0) s_tie = e + q;
                             }
                         }
-                        r -= total;
+                        r -= tot;
                     }
                 }
                 __syncthreads();
