@@ -496,10 +496,15 @@ def main() -> int:
     # (statistics + decision); with --debug-library, SPECDEC_FUSED=0 selects
     # the two-kernel paths
     fused = not trunc and not (args.debug_library and os.environ.get("SPECDEC_FUSED", "1")[:1] == "0")
+    # truncation lists each row's kept tokens (top_k <= 1024, or top-p alone
+    # on V <= 2048) or finds each row's cut (k_trunc_cut) otherwise
+    use_k = 0 < wl0.top_k < wl0.vocab
+    cut = trunc and (wl0.top_k > 1024 if use_k else wl0.vocab > 2048)
     if greedy:
         kname = "k_greedy_fused" if fused else "k_stats_greedy"
     else:
-        kname = "k_trunc_select" if trunc else "k_verify_fused" if fused else "k_stats_sample"
+        kname = ("k_trunc_cut" if cut else "k_trunc_select") if trunc else \
+            "k_verify_fused" if fused else "k_stats_sample"
     if fused:
         log(f"step {sec_per_step * 1e6:.2f} us ({'graph' if runner.graphed else 'eager'}); "
             f"one-kernel verify avg {k1_avg * 1e6:.2f} us (p10 {np.percentile(k1, 10) * 1e6:.2f}, "
@@ -508,9 +513,9 @@ def main() -> int:
             f"{HBM_PEAK_GBPS:.0f} GB/s; whole step {alg_k1 / sec_per_step / 1e9:.1f} GB/s")
     else:
         log(f"step {sec_per_step * 1e6:.2f} us ({'graph' if runner.graphed else 'eager'}); "
-            f"stats kernel avg {k1_avg * 1e6:.2f} us (p10 {np.percentile(k1, 10) * 1e6:.2f}, "
+            f"{kname} avg {k1_avg * 1e6:.2f} us (p10 {np.percentile(k1, 10) * 1e6:.2f}, "
             f"p90 {np.percentile(k1, 90) * 1e6:.2f}); decision kernel avg {k2.mean() * 1e6:.2f} us")
-        log(f"stats kernel {achieved:.1f} GB/s = {100 * achieved / HBM_PEAK_GBPS:.1f}% of "
+        log(f"{kname} {achieved:.1f} GB/s = {100 * achieved / HBM_PEAK_GBPS:.1f}% of "
             f"{HBM_PEAK_GBPS:.0f} GB/s; whole step {alg_k1 / sec_per_step / 1e9:.1f} GB/s")
     log(f"mean accepted {np.mean([a.mean() for a in acc]):.3f} of {G}; histogram of m: "
         f"{np.bincount(np.concatenate(acc), minlength=G + 1).tolist()}; "
@@ -599,8 +604,8 @@ def main() -> int:
         "kernels": dict(({kname[2:]: {"avg_us": k1_avg * 1e6, "bytes_per_launch": alg_k1,
                                       "GBps": achieved, "frac": achieved / HBM_PEAK_GBPS}}
                           if fused else
-                          {"stats": {"avg_us": k1_avg * 1e6, "bytes_per_launch": alg_k1,
-                                     "GBps": achieved, "frac": achieved / HBM_PEAK_GBPS},
+                          {kname[2:]: {"avg_us": k1_avg * 1e6, "bytes_per_launch": alg_k1,
+                                       "GBps": achieved, "frac": achieved / HBM_PEAK_GBPS},
                            "decision": {"avg_us": float(k2.mean()) * 1e6}}), **kernels),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
