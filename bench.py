@@ -281,9 +281,15 @@ def main() -> int:
     from speculative_decoding_verification_05_amd import synth
 
     dev = torch.device("cuda:0")
-    if args.debug_library:
-        sd.debug_library().__enter__()  # every call of this run goes to the debug build
-    sd.lib()
+    # every call of this run goes to the debug build (the context object is
+    # kept for the whole run: dropping it would close the context and bring
+    # the product library back)
+    debug_ctx = sd.debug_library() if args.debug_library else None
+    if debug_ctx is not None:
+        debug_ctx.__enter__()
+    lib = sd.lib()
+    if args.debug_library and getattr(lib, "_name", "") != sd.DEBUG_LIB_PATH:
+        raise RuntimeError("--debug-library: the debug build is not the library in use")
     if args.pmc_copy_mib:
         src = torch.ones(args.pmc_copy_mib << 18, dtype=torch.int32, device=dev)
         dst = torch.empty_like(src)
