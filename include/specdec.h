@@ -143,9 +143,10 @@ size_t specdec_verify_workspace_bytes(const specdec_verify_desc_t* desc);
  *       q_i is the point mass on d_i, so draft i is accepted with probability
  *       p_i(d_i) and a rejection draws from p_i with d_i removed (AI-infra KB
  *       M013 s.08 asks for the candidates' probability representation; the
- *       rule of s.04 then applies unchanged).  Not combined with truncation
- *       (UNSUPPORTED) when G > 0; with G = 0 there are no draft rows and
- *       NULL is simply the absent array.
+ *       rule of s.04 then applies unchanged).  With truncation, p_i is the
+ *       truncated target distribution (s.04) and q_i stays the point mass.
+ *       With G = 0 there are no draft rows and NULL is simply the absent
+ *       array.
  *   draft_tokens  [B][G] int32: the proposed tokens d_0..d_{gamma_b - 1}.
  *   gamma         [B] int32 in [0, G], or NULL (every request uses G).  Rows
  *       and tokens past gamma_b are never read.  A value outside [0, G] is
@@ -176,10 +177,8 @@ size_t specdec_verify_workspace_bytes(const specdec_verify_desc_t* desc);
  * Greedy: draft i is kept iff it equals the argmax of target row i (raw
  *   logits, lowest index on ties); the token at m is the argmax of row m.
  * Errors: INVALID_ARGUMENT for a bad descriptor or a NULL required pointer;
- *   WORKSPACE_TOO_SMALL if workspace_bytes < specdec_verify_workspace_bytes;
- *   UNSUPPORTED for truncation (0 < top_k < V, or top_p < 1) with
- *   point-mass drafts (draft_logits NULL, G > 0).  In each case nothing is
- *   enqueued.
+ *   WORKSPACE_TOO_SMALL if workspace_bytes < specdec_verify_workspace_bytes.
+ *   In each case nothing is enqueued.
  * Kernels: sampling without truncation and greedy verification run as one
  *   kernel (statistics and decision workgroups in one launch; the library's
  *   debug build, libspecdec_debug.so, can select a two-kernel path with the
@@ -188,7 +187,8 @@ size_t specdec_verify_workspace_bytes(const specdec_verify_desc_t* desc);
  *   truncation with top_k <= 1024, or top-p alone on V <= 2048, runs a
  *   selection kernel that lists each row's kept tokens, then a decision
  *   kernel over the lists; other truncation (top-p alone on larger
- *   vocabularies, top_k > 1024) runs the statistics pass, a kernel that
+ *   vocabularies, top_k > 1024, any truncation with point-mass drafts)
+ *   runs the statistics pass, a kernel that
  *   finds each row's cut (the boundary logit and, among the tokens tied at
  *   it, the last kept index) by a radix select over the logits' order
  *   keys, and the sampling decision testing each token against the cut.

@@ -1017,7 +1017,9 @@ Layout make_layout(const specdec_verify_desc_t* d, bool point) {
     L.off_part = off; off = align256(off + B * L.rows * L.nc * sizeof(float4));
     L.off_csum = off; off = align256(off + B * L.nc2 * sizeof(uint32_t));
     L.trunc = truncation_mode(d);
-    L.cut = truncation_cut(d);
+    // point-mass drafts under truncation: the cut path (its decision serves
+    // point masses; the listed path's does not)
+    L.cut = truncation_cut(d) || (point && L.trunc);
     // the cut decision's membership tests take registers: groups of at most
     // two chunks (larger ones spill)
     if (L.cut && L.group > kMassGroupChunks) L.group = kMassGroupChunks;
@@ -1154,7 +1156,6 @@ specdec_status_t verify_impl(const specdec_verify_desc_t* d, const void* target_
     // sampling without draft rows: point-mass drafts of a deterministic proposer
     // (with gamma_max = 0 there is no draft row either way)
     const bool point = sample && !draft_logits && d->gamma_max > 0;
-    if (truncation_mode(d) && point) return SPECDEC_ERR_UNSUPPORTED;
     const Layout L = make_layout(d, point);
     if (workspace_bytes < L.total) return SPECDEC_ERR_WORKSPACE_TOO_SMALL;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return SPECDEC_ERR_INVALID_ARGUMENT;

@@ -539,6 +539,44 @@ def pin_point_mass_acceptance(orc, B=200_000):
             errs.append(f"d={d0}: a rejection committed the rejected token itself")
     return errs
 
+def pin_point_mass_truncated(orc, B=200_000):
+    """Point-mass drafts under truncation: q stays the point mass on d, and p
+    is the truncated, renormalised target ([KB] s.04: the probabilities after
+    truncation; s.08: a deterministic proposer's candidates as point masses).
+    With p = [0.1, 0.45, 0.3, 0.15], worked by hand: top-k 2 keeps tokens 1
+    and 2, so p~ = [0, 0.6, 0.4, 0]; top-p 0.8 keeps 1, 2, 3 (running sums
+    0.45, 0.75, 0.9), so p~ = [0, 1/2, 1/3, 1/6].  The first draft is kept
+    with probability p~(d) (never when d lies outside the kept set), the first
+    committed token follows p~, and a rejection never commits d itself."""
+    p = np.array([0.1, 0.45, 0.3, 0.15])
+    cases = [  # (top_k, top_p, d0, p~ by hand)
+        (2, 1.0, 1, np.array([0.0, 0.6, 0.4, 0.0])),
+        (2, 1.0, 3, np.array([0.0, 0.6, 0.4, 0.0])),
+        (0, 0.8, 3, np.array([0.0, 1 / 2, 1 / 3, 1 / 6])),
+    ]
+    errs = []
+    for top_k, top_p, d0, pt in cases:
+        tgt = np.empty((B, 2, 4), np.float32)
+        tgt[:] = _ln_f32(p)
+        d = np.full((B, 1), d0, np.int32)
+        r = orc.verify(tgt, None, d, temperature=1.0, top_k=top_k, top_p=top_p, seed=11 + d0 + top_k)
+        acc = r["accept_count"].astype(np.float64)
+        se = math.sqrt(max(pt[d0] * (1 - pt[d0]), 1e-12) / B)
+        if abs(acc.mean() - pt[d0]) > 4 * se:
+            errs.append(f"k={top_k} p={top_p} d={d0}: acceptance {acc.mean():.5f} vs p~(d) {pt[d0]:.5f}")
+        first = r["out_tokens"][:, 0]
+        cnt = np.bincount(first, minlength=4)
+        if np.any(cnt[pt == 0] != 0):
+            errs.append(f"k={top_k} p={top_p} d={d0}: tokens outside the kept set committed: {cnt}")
+        keep = pt > 0  # (tokens outside the kept set are reported above)
+        if stats.chisquare(cnt[keep], pt[keep] * cnt[keep].sum()).pvalue < P_MIN:
+            errs.append(f"k={top_k} p={top_p} d={d0}: first committed token {cnt} not distributed as p~")
+        rejected = r["accept_count"] == 0
+        if np.any(first[rejected] == d0):
+            errs.append(f"k={top_k} p={top_p} d={d0}: a rejection committed the rejected token itself")
+    return errs
+
+
 # ------------------------------------------------- closed form at fixed alpha
 
 def _fixed_alpha_batch(alpha, gamma, B):
@@ -883,4 +921,5 @@ ALL_PINS = {
     "ngram_worked_cases": pin_ngram_worked_cases,
     "ngram_brute_force": pin_ngram_brute_force,
     "point_mass_acceptance": pin_point_mass_acceptance,
+    "point_mass_truncated": pin_point_mass_truncated,
 }

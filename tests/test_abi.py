@@ -166,9 +166,13 @@ def test_commit_slot_count_must_cover_the_window():
     assert st == sd.SPECDEC_ERR_INVALID_ARGUMENT     # rollback takes no scratch
 
 
-def test_point_mass_drafts_with_truncation_are_unsupported():
-    d = good_desc(top_k=50)
-    assert call_verify(d, draft=None, ws_bytes=1 << 30) == sd.SPECDEC_ERR_UNSUPPORTED
+def test_point_mass_drafts_with_truncation_pass_the_host_checks():
+    """Truncation with point-mass drafts is served (by the cut path): the
+    host checks go on to the workspace size instead of refusing the request
+    (a too-small workspace stops the call before any launch)."""
+    for kw in (dict(top_k=50), dict(top_p=0.9), dict(top_k=5000, top_p=0.5)):
+        d = good_desc(**kw)
+        assert call_verify(d, draft=None, ws_bytes=256) == sd.SPECDEC_ERR_WORKSPACE_TOO_SMALL
 
 
 def test_workspace_covers_point_mass_layout():

@@ -1,5 +1,6 @@
 """GPU parity of truncation by cut records (top-p without an effective top-k
-on large vocabularies, top-k past 1024) against the CPU oracle.
+on large vocabularies, top-k past 1024, truncation with point-mass drafts)
+against the CPU oracle.
 
 p and q are softmax(z/T) restricted to their kept sets and renormalised
 (AI-infra KB M013 s.04; the nxmr.cn note on lossless acceleration: top-p and
@@ -165,3 +166,16 @@ def test_cut_nonfinite_rows_are_flagged():
     got = gpu_verify(x, bf16=True, temperature=wl.temperature, top_p=wl.top_p, seed=wl.verify_seed)
     assert got["flags"][1] & sd.FLAG_NONFINITE
     assert not np.any(got["flags"][[0, 2, 3]] & sd.FLAG_NONFINITE)
+
+
+@pytest.mark.parametrize("vocab,top_k,top_p", [(128256, 50, 0.9), (128256, 0, 0.9), (32000, 2000, 1.0),
+                                                (3000, 0, 0.5), (5000, 7, 1.0)])
+def test_point_mass_drafts_with_truncation(vocab, top_k, top_p):
+    """Point-mass drafts (no draft rows, as from an n-gram proposer) under
+    truncation: p is the truncated target, q the point mass on the drafted
+    token, so a draft is kept with probability p~(d) and a rejection draws
+    from p~ without d (AI-infra KB M013 s.04 and s.08)."""
+    wl = W["b128_g4_v128256_topk50_topp09"].scaled(16, vocab, top_k=top_k, top_p=top_p)
+    x = synth.make_verify_inputs(wl)
+    x["draft"] = None
+    check(wl, x, label=f"point-mass drafts V={vocab} k={top_k} p={top_p}")

@@ -1,7 +1,7 @@
 """specdec_verify against the CPU oracle on seeded random small shapes in
 every mode: sampling (draft rows or point-mass drafts), greedy, and
-truncated sampling (top-k, top-p, both, and top-k past the 1024 listed
-tokens), with ragged gamma, EOS tokens and token budgets.  The comparison is element by element as in the other parity
+truncated sampling (top-k, top-p, both, top-k past the 1024 listed
+tokens, and truncation with point-mass drafts), with ragged gamma, EOS tokens and token budgets.  The comparison is element by element as in the other parity
 tests (near-threshold decisions excluded and counted)."""
 import dataclasses
 import os
@@ -19,7 +19,7 @@ def _cases(n, seed):
     rng = np.random.default_rng(seed)
     out = []
     while len(out) < n:
-        mode = str(rng.choice(["sample", "point", "greedy", "topk", "topp", "topkp", "topkw"]))
+        mode = str(rng.choice(["sample", "point", "greedy", "topk", "topp", "topkp", "topkw", "pointtr"]))
         B = int(rng.choice([1, 3, 8, 21]))
         G = int(rng.integers(0, 9))
         V = int(rng.choice([2, 17, 300, 2048, 5000, 32000]))
@@ -28,9 +28,9 @@ def _cases(n, seed):
         if mode == "topkw" and V <= 1025:
             continue
         # topkw: top-k past the 1024 listed tokens, with or without top-p
-        top_k = (int(rng.integers(1, min(V, 200) + 1)) if mode in ("topk", "topkp") else
+        top_k = (int(rng.integers(1, min(V, 200) + 1)) if mode in ("topk", "topkp", "pointtr") else
                  int(rng.integers(1025, V)) if mode == "topkw" else 0)
-        top_p = (float(rng.uniform(0.3, 0.99)) if mode in ("topp", "topkp") else
+        top_p = (float(rng.uniform(0.3, 0.99)) if mode in ("topp", "topkp", "pointtr") else
                  float(rng.choice([1.0, 0.9])) if mode == "topkw" else 1.0)
         out.append(dict(mode=mode, batch=B, gamma_max=G, vocab=V, top_k=top_k, top_p=top_p,
                         dtype=str(rng.choice(["bf16", "f32"])),
@@ -58,7 +58,7 @@ def test_random_against_oracle(case):
                              data_seed=case["data_seed"], verify_seed=case["verify_seed"])
     say(f"[random vs oracle] {case}")
     x = synth.make_verify_inputs(wl, need_draft_logits=not greedy)
-    if case["mode"] == "point":
+    if case["mode"] in ("point", "pointtr"):
         x["draft"] = None
     if greedy:
         x["draft"] = None

@@ -100,6 +100,12 @@ MUTANTS = [
     ("point_mass_misplaced", "if (d[i] >= 0 && d[i] < V) Q[(size_t)i * V + d[i]] = 1.0;",
      "if (d[i] >= 0 && d[i] < V) Q[(size_t)i * V + (d[i] + 1) % V] = 1.0;",
      ["point_mass_acceptance"]),
+    ("point_mass_untruncated_target",
+     "a->is_bf16, V, a->temperature, a->top_k, a->top_p,\n"
+     "                                        P + (size_t)i * V, &nc);",
+     "a->is_bf16, V, a->temperature, draft ? a->top_k : 0, draft ? a->top_p : 1.0,\n"
+     "                                        P + (size_t)i * V, &nc);",
+     ["point_mass_truncated"]),
 ]
 
 
