@@ -39,6 +39,8 @@
 
 #include <hip/hip_ext.h>
 
+#include <type_traits>
+
 
 namespace specdec {
 namespace {
@@ -1010,20 +1012,24 @@ __global__ __launch_bounds__(kThreads) void k_trunc_cut(VerifyParams P) {
     const bool use_k = P.top_k > 0 && P.top_k < V;
     const bool use_p = P.top_p < 1.0f;
 
-    // one read of the row: f(x, key, e, t0) for every element e < V of the tile at t0
-    auto each = [&](auto&& f) {
+    // one read of the row: f(x, key, t0) for every element e < V of the tile
+    // at t0 (each_w: also for the -inf filling past V, which weighs nothing,
+    // for the passes that only add weights)
+    auto each_impl = [&](auto&& f, auto check) {
         stream_tiles<BF16, VEC>(rp, V, [&](const uint4 (&r)[kUnroll], int t0) {
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
                 for (int q = 0; q < N; ++q) {
-                    const int e = t0 + (u * kThreads + t) * N + q;
                     const float x = elem<BF16>(r[u], q);
-                    if (e < V) f(x, cut_key<BF16>(x), t0);
+                    if (!decltype(check)::value || t0 + (u * kThreads + t) * N + q < V)
+                        f(x, cut_key<BF16>(x), t0);
                 }
         });
         __syncthreads();
     };
+    auto each = [&](auto&& f) { each_impl(f, std::true_type{}); };
+    auto each_w = [&](auto&& f) { each_impl(f, std::false_type{}); };
     uint32_t* const s_cnt = reinterpret_cast<uint32_t*>(s_buf);
     unsigned long long* const s_wt = s_buf;
     auto clear = [&](int n) {  // n 64-bit entries (2n counts)
@@ -1064,7 +1070,7 @@ __global__ __launch_bounds__(kThreads) void k_trunc_cut(VerifyParams P) {
     int iota = 0x7fffffff;
     unsigned long long kept = 0;
     clear(kCutBins);
-    each([&](float x, uint32_t key, int) {
+    each_w([&](float x, uint32_t key, int) {
         if (key >= lo) {
             const unsigned long long f = fixed_weight(x, M, c);
             if (f) atomicAdd(&s_wt[key >> 20], f);
@@ -1088,7 +1094,7 @@ __global__ __launch_bounds__(kThreads) void k_trunc_cut(VerifyParams P) {
             const int sh = digit_shift<BF16>(d), nb = 1 << digit_width<BF16>(d);
             const uint32_t fm = fixed_mask(d);
             clear(nb);
-            each([&](float x, uint32_t key, int) {
+            each_w([&](float x, uint32_t key, int) {
                 if (key >= lo && (key & fm) == prefix) {
                     const unsigned long long f = fixed_weight(x, M, c);
                     if (f) atomicAdd(&s_wt[(key >> sh) & (nb - 1)], f);
@@ -1111,7 +1117,9 @@ __global__ __launch_bounds__(kThreads) void k_trunc_cut(VerifyParams P) {
         if (found) {
             for (int j = t; j < nb; j += kThreads) s_vcnt[j] = 0u;
             clear(kCutSegs / 2);
-            each([&](float, uint32_t key, int t0) {
+            // (the -inf filling past V never shares the crossing value's
+            // prefix: it weighs nothing, and the crossing value weighs more)
+            each_w([&](float, uint32_t key, int t0) {
                 if (key >= lo && (key & fm) == prefix) {
                     const int v = static_cast<int>((key >> sh) & static_cast<uint32_t>(nb - 1));
                     atomicAdd(&s_vcnt[v], 1u);

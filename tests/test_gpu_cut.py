@@ -179,3 +179,48 @@ def test_point_mass_drafts_with_truncation(vocab, top_k, top_p):
     x = synth.make_verify_inputs(wl)
     x["draft"] = None
     check(wl, x, label=f"point-mass drafts V={vocab} k={top_k} p={top_p}")
+
+
+def test_cut_path_in_hip_graph_replays():
+    """The cut path's three launches (statistics, cut records, decision; no
+    fills) captured once and replayed three times, with eager calls on other
+    inputs in between: every replay equals the eager call byte for byte, and
+    the eager call the oracle."""
+    import dataclasses
+    import torch
+    from gpu_helpers import to_dev
+    wl = W["b64_g4_v128256_topp09"].scaled(16, 50000)
+    x = synth.make_verify_inputs(wl)
+    x2 = synth.make_verify_inputs(dataclasses.replace(wl, data_seed=wl.data_seed + 1))
+    dev = "cuda"
+    desc = sd.make_verify_desc(wl.batch, wl.gamma_max, wl.vocab, temperature=wl.temperature,
+                               top_p=wl.top_p, seed=wl.verify_seed)
+    ver = sd.Verifier(desc, dev)
+    args = [to_dev(x[k], dev) for k in ("target", "draft", "draft_tokens", "gamma")]
+    args2 = [to_dev(x2[k], dev) for k in ("target", "draft", "draft_tokens", "gamma")]
+    names = ("accept_count", "num_tokens", "out_tokens", "p_draft", "q_draft", "residual_mass", "flags")
+
+    def state():
+        torch.cuda.synchronize()
+        return {n: getattr(ver, n).cpu().numpy().copy() for n in names}
+
+    say("[cut graph] eager call")
+    ver(*args)
+    want = state()
+    ref = oracle_verify(x, temperature=wl.temperature, top_p=wl.top_p, seed=wl.verify_seed)
+    errs, _ = compare(ref, want, x["gamma"], False, None, "cut graph")
+    assert not errs, "\n".join(errs[:20])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=s):
+        ver(*args)
+    for k in range(3):
+        ver(*args2)                      # eager work on other inputs between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        now = state()
+        for n in names:
+            assert np.array_equal(now[n], want[n]), (k, n)
+        say(f"[cut graph] replay {k} matches the eager call")

@@ -55,6 +55,9 @@ CASES = [
     # small ragged batch
     ("top-k/top-p B=128", lambda: W["b128_g4_v128256_topk50_topp09"]),
     ("ragged B=40 V=3001", lambda: W["b512_ragged_v262144_kv"].scaled(40, 3001)),
+    # truncation by cut records (top-p alone), then a smaller fp32 one
+    ("top-p alone B=64 V=128256", lambda: W["b64_g4_v128256_topp09"]),
+    ("fp32 top-p alone B=8 V=32000", lambda: W["b8_g4_v32000_f32"].scaled(8, top_p=0.9)),
 ]
 
 
