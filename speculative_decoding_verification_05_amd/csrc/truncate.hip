@@ -186,17 +186,17 @@ __device__ __forceinline__ uint4 load_raw(const void* rp, int e, int V) {
 // clamped into the row, so each byte of the row is fetched once; the last
 // tile's vectors past V (wholly past it: V is a multiple of N) become -inf
 // before its visit.
-template <bool BF16, bool VEC, class F>
+template <bool BF16, bool VEC, int NT = kThreads, class F>
 __device__ __forceinline__ void stream_tiles(const void* rp, int V, F&& f) {
     constexpr int N = Vec<BF16>::N;
-    constexpr int TILE = kThreads * N * kUnroll;
+    constexpr int TILE = NT * N * kUnroll;
     const int t = threadIdx.x;
     if constexpr (VEC) {
         const int ntiles = (V + TILE - 1) / TILE;
         auto load_tile = [&](uint4 (&r)[kUnroll], int t0) {
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u)
-                r[u] = load16_stream<BF16>(rp, min(t0 + (u * kThreads + t) * N, V - N));
+                r[u] = load16_stream<BF16>(rp, min(t0 + (u * NT + t) * N, V - N));
         };
         uint4 cur[kUnroll];
         load_tile(cur, 0);
@@ -208,7 +208,7 @@ __device__ __forceinline__ void stream_tiles(const void* rp, int V, F&& f) {
                 const uint32_t ninf = BF16 ? 0xff80ff80u : 0xff800000u;
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u)
-                    if (t0 + (u * kThreads + t) * N >= V) cur[u] = make_uint4(ninf, ninf, ninf, ninf);
+                    if (t0 + (u * NT + t) * N >= V) cur[u] = make_uint4(ninf, ninf, ninf, ninf);
             }
             f(cur, t0);
             if (k + 1 < ntiles) {
@@ -221,7 +221,7 @@ __device__ __forceinline__ void stream_tiles(const void* rp, int V, F&& f) {
             uint4 r[kUnroll];
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u)
-                r[u] = narrow<BF16>(load_vec<BF16, false>(rp, t0 + (u * kThreads + t) * N, V, neg_inf()));
+                r[u] = narrow<BF16>(load_vec<BF16, false>(rp, t0 + (u * NT + t) * N, V, neg_inf()));
             f(r, t0);
         }
     }
@@ -895,9 +895,10 @@ struct Cross {
 // base + above(j) < goal <= base + above(j) + w(j), above(j) being the
 // weight of the bins past j.  Every test compares an exact integer sum with
 // the goal the same way, so successive searches agree at their edges.
-// Thread t sums a run of consecutive bins from the top into s_run[t]
-// (kThreads entries of LDS), wave 0 scans the runs four to a lane, and the
-// crossing lane walks its runs and then bins.
+// Thread t < kThreads sums a run of consecutive bins from the top into
+// s_run[t] (kThreads entries of LDS; larger workgroups leave their other
+// lanes out), wave 0 scans the runs four to a lane, and the crossing lane
+// walks its runs and then bins.
 template <class W>
 __device__ Cross find_cross(int n, double goal, unsigned long long base, unsigned long long* s_run, W&& w) {
     __shared__ Cross s_res;
@@ -907,7 +908,7 @@ __device__ Cross find_cross(int n, double goal, unsigned long long base, unsigne
     unsigned long long run = 0;
     if (t < nthr)
         for (int k = 0; k < per; ++k) run += w(n - 1 - (t * per + k));
-    s_run[t] = run;
+    if (t < kThreads) s_run[t] = run;
     __syncthreads();
     if (t < kWave) {
         const unsigned long long q = s_run[4 * l] + s_run[4 * l + 1] + s_run[4 * l + 2] + s_run[4 * l + 3];
@@ -948,10 +949,11 @@ __device__ Cross find_cross(int n, double goal, unsigned long long base, unsigne
     return r;
 }
 
-// Exclusive prefix sum over the workgroup's lanes in thread order; *total
-// receives the sum (same on every lane).
+// Exclusive prefix sum over the workgroup's lanes (NW waves) in thread
+// order; *total receives the sum (same on every lane).
+template <int NW = kWaves>
 __device__ __forceinline__ int block_excl_scan(int v, int* total) {
-    __shared__ int s_w[kWaves];
+    __shared__ int s_w[NW];
     const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
     const int incl = wave_scan(v, 0, [](int x, int y) { return x + y; });
     __syncthreads();
@@ -959,7 +961,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* total) {
     __syncthreads();
     int off = 0, tot = 0;
 #pragma unroll
-    for (int k = 0; k < kWaves; ++k) {
+    for (int k = 0; k < NW; ++k) {
         if (k < w) off += s_w[k];
         tot += s_w[k];
     }
@@ -967,8 +969,15 @@ __device__ __forceinline__ int block_excl_scan(int v, int* total) {
     return off + incl - v;
 }
 
+// 512 lanes per row: one workgroup per row leaves about two rows per CU on
+// the tested batches, and with 256 lanes the passes were bound by latency
+// (too few loads in flight and waves to hide the arithmetic): 130 us against
+// 113 us at 512 lanes and 146 us at 1024 (B=64 x V=128256, top-p 0.9).
+constexpr int kCutThreads = 512;
+
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_trunc_cut(VerifyParams P) {
+__global__ __launch_bounds__(kCutThreads) void k_trunc_cut(VerifyParams P) {
+    constexpr int NT = kCutThreads;
     // one buffer for each pass's histogram: top-k counts (uint32), top-p
     // weights (uint64), or the last digit's tie counters (uint32)
     __shared__ unsigned long long s_buf[kCutBins];
@@ -977,7 +986,7 @@ __global__ __launch_bounds__(kThreads) void k_trunc_cut(VerifyParams P) {
     __shared__ float s_ms[2];
     __shared__ int s_tie;
     constexpr int N = Vec<BF16>::N;
-    constexpr int TILE = kThreads * N * kUnroll;
+    constexpr int TILE = NT * N * kUnroll;
     constexpr int NDIG = BF16 ? 2 : 3;
     const int s = blockIdx.x, b = blockIdx.y;
     const bool is_target = s <= P.G;
@@ -1016,13 +1025,13 @@ __global__ __launch_bounds__(kThreads) void k_trunc_cut(VerifyParams P) {
     // at t0 (each_w: also for the -inf filling past V, which weighs nothing,
     // for the passes that only add weights)
     auto each_impl = [&](auto&& f, auto check) {
-        stream_tiles<BF16, VEC>(rp, V, [&](const uint4 (&r)[kUnroll], int t0) {
+        stream_tiles<BF16, VEC, NT>(rp, V, [&](const uint4 (&r)[kUnroll], int t0) {
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
                 for (int q = 0; q < N; ++q) {
                     const float x = elem<BF16>(r[u], q);
-                    if (!decltype(check)::value || t0 + (u * kThreads + t) * N + q < V)
+                    if (!decltype(check)::value || t0 + (u * NT + t) * N + q < V)
                         f(x, cut_key<BF16>(x), t0);
                 }
         });
@@ -1033,7 +1042,7 @@ __global__ __launch_bounds__(kThreads) void k_trunc_cut(VerifyParams P) {
     uint32_t* const s_cnt = reinterpret_cast<uint32_t*>(s_buf);
     unsigned long long* const s_wt = s_buf;
     auto clear = [&](int n) {  // n 64-bit entries (2n counts)
-        for (int j = t; j < n; j += kThreads) s_buf[j] = 0ull;
+        for (int j = t; j < n; j += NT) s_buf[j] = 0ull;
         __syncthreads();
     };
     auto fixed_mask = [&](int d) -> uint32_t {  // the key bits above digit d
@@ -1115,7 +1124,7 @@ __global__ __launch_bounds__(kThreads) void k_trunc_cut(VerifyParams P) {
         const int tps = (ntiles + nseg - 1) / nseg;  // tiles per segment
         uint32_t* const seg = s_cnt;  // kCutSegs counters
         if (found) {
-            for (int j = t; j < nb; j += kThreads) s_vcnt[j] = 0u;
+            for (int j = t; j < nb; j += NT) s_vcnt[j] = 0u;
             clear(kCutSegs / 2);
             // (the -inf filling past V never shares the crossing value's
             // prefix: it weighs nothing, and the crossing value weighs more)
@@ -1162,14 +1171,14 @@ __global__ __launch_bounds__(kThreads) void k_trunc_cut(VerifyParams P) {
                 __syncthreads();
                 for (int tile = sg * tps; tile < min(ntiles, (sg + 1) * tps) && r > 0; ++tile) {
                     for (int u = 0; u < kUnroll && r > 0; ++u) {
-                        const int e = tile * TILE + (u * kThreads + t) * N;
+                        const int e = tile * TILE + (u * NT + t) * N;
                         const uint4 raw = load_raw<BF16, VEC>(rp, e, V);
                         int hits = 0;
 #pragma unroll
                         for (int q = 0; q < N; ++q)
                             hits += (e + q < V && cut_key<BF16>(elem<BF16>(raw, q)) == kappa) ? 1 : 0;
                         int tot;
-                        const int ex = block_excl_scan(hits, &tot);
+                        const int ex = block_excl_scan<NT / kWave>(hits, &tot);
                         if (ex < r && r <= ex + hits) {
                             int k = r - ex;
 #pragma unroll
@@ -1225,9 +1234,9 @@ specdec_status_t launch_trunc_cut(const VerifyParams& P, bool bf16, bool vec, hi
     const dim3 grid(P.rows, P.B);
     auto launch = [&](auto kernel) {
         if (start)
-            hipExtLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, start, stop, 0, P);
+            hipExtLaunchKernelGGL(kernel, grid, dim3(kCutThreads), 0, stream, start, stop, 0, P);
         else
-            hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, P);
+            hipLaunchKernelGGL(kernel, grid, dim3(kCutThreads), 0, stream, P);
     };
     if (bf16) vec ? launch(k_trunc_cut<true, true>) : launch(k_trunc_cut<true, false>);
     else vec ? launch(k_trunc_cut<false, true>) : launch(k_trunc_cut<false, false>);
