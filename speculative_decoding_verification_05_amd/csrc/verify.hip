@@ -1021,7 +1021,17 @@ Layout make_layout(const specdec_verify_desc_t* d, bool point) {
     // point masses; the listed path's does not)
     L.cut = truncation_cut(d) || (point && L.trunc);
     // the cut decision's membership tests take registers: groups of at most
-    // two chunks (larger ones spill)
+    // two chunks (larger ones spill).  Where shares of two chunks still keep
+    // the decision's workgroups within about one resident round (2048), take
+    // twice the workgroups, each loading its whole share at once.
+    if (L.cut && L.cpw > kMassGroupChunks) {
+        const int wpr2 = (L.nc2 + kMassGroupChunks - 1) / kMassGroupChunks;
+        if (static_cast<long>(bb) * wpr2 <= 2048) {
+            L.cpw = kMassGroupChunks;
+            L.wpr = (L.nc2 + L.cpw - 1) / L.cpw;
+            L.group = L.cpw;
+        }
+    }
     if (L.cut && L.group > kMassGroupChunks) L.group = kMassGroupChunks;
     L.off_nuc = off;  // kept-token records, or cut records
     if (L.cut) off = align256(off + B * L.rows * sizeof(uint4));
