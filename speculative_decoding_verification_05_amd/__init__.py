@@ -113,12 +113,41 @@ def debug_library():
         _lib = old
 
 
+def _hip_runtimes() -> set:
+    """Files of the HIP runtime (libamdhip64) mapped into this process."""
+    found = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                p = line.split(None, 5)[-1].strip()
+                if os.path.basename(p).startswith("libamdhip64.so"):
+                    found.add(os.path.realpath(p))
+    except OSError:
+        pass
+    return found
+
+
 def _load(path: str) -> ctypes.CDLL:
     if path in _loaded:
         return _loaded[path]
     if not os.path.exists(path):
         raise ImportError(f"{os.path.basename(path)} is not built ({path}); run __graft_entry__.build()")
+    # One HIP runtime per process.  torch ships its own libamdhip64 (soname
+    # libamdhip64.so.7) and asks for it by the unversioned name; the library
+    # asks for libamdhip64.so.7.  Loaded after torch, the library binds to
+    # torch's copy by its soname.  Loaded first, it would bind the system
+    # copy, and torch would then load its own beside it: the runtime that
+    # initialises second finds no device it can open, and the process's
+    # pinned host allocations fail from then on.
+    try:
+        import torch  # noqa: F401  (for its HIP runtime, loaded with it)
+    except ImportError:
+        pass
     L = ctypes.CDLL(path)
+    runtimes = _hip_runtimes()
+    if len(runtimes) > 1:
+        raise ImportError("two HIP runtimes are loaded in this process (" + ", ".join(sorted(runtimes))
+                          + "); import torch before anything that loads a HIP runtime")
     P, S = ctypes.c_void_p, ctypes.c_size_t
     L.specdec_verify_workspace_bytes.argtypes = [ctypes.POINTER(VerifyDesc)]
     L.specdec_verify_workspace_bytes.restype = S

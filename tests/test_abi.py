@@ -277,3 +277,47 @@ def test_zero_filled_descriptor_has_no_eos():
     d.eos_plus1 = 1001
     assert sd.specdec_verify_workspace_bytes(d) == 0
     assert sd.specdec_abi_version() == 3
+
+
+def _fresh_python(code):
+    import subprocess
+    import sys
+    return subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                          timeout=300)
+
+
+def test_loading_first_keeps_a_single_hip_runtime():
+    """A process that loads the library before it imports torch still maps
+    one HIP runtime, torch's: two (the system copy and torch's) leave the
+    one that initialises second without a device, and pinned host
+    allocations failing.  The debug build is loaded the way the tests'
+    environment switches load it."""
+    r = _fresh_python(
+        "import speculative_decoding_verification_05_amd as sd\n"
+        "sd._load(sd.DEBUG_LIB_PATH); sd.lib()\n"
+        "rt = sd._hip_runtimes()\n"
+        "print(len(rt), *sorted(rt))\n")
+    assert r.returncode == 0, r.stderr
+    n, *paths = r.stdout.split()
+    assert n == "1", r.stdout
+    assert "torch" in paths[0], paths
+
+
+def test_a_second_hip_runtime_is_refused():
+    """With the system's HIP runtime already loaded when torch brings its
+    own, the loader refuses instead of handing out calls that would fail
+    later with unrelated-looking errors."""
+    r = _fresh_python(
+        "import ctypes, glob\n"
+        "cands = sorted(glob.glob('/opt/rocm*/lib/libamdhip64.so.*'))\n"
+        "if not cands: raise SystemExit(3)\n"
+        "ctypes.CDLL(cands[0])\n"
+        "import speculative_decoding_verification_05_amd as sd\n"
+        "try:\n"
+        "    sd.lib()\n"
+        "except ImportError as e:\n"
+        "    print('refused', e)\n")
+    if r.returncode == 3:
+        pytest.skip("no system HIP runtime here")
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.startswith("refused two HIP runtimes"), r.stdout
