@@ -65,7 +65,8 @@ typedef enum specdec_status {
     SPECDEC_OK = 0,
     SPECDEC_ERR_INVALID_ARGUMENT = 1,   /* bad descriptor, NULL or misaligned pointer */
     SPECDEC_ERR_WORKSPACE_TOO_SMALL = 2,
-    SPECDEC_ERR_UNSUPPORTED = 3,        /* valid request the library does not implement */
+    SPECDEC_ERR_UNSUPPORTED = 3,        /* valid request the library does not implement
+                                           (no entry point of this version returns it) */
     SPECDEC_ERR_DEVICE = 4              /* the HIP runtime refused a launch */
 } specdec_status_t;
 
@@ -216,7 +217,11 @@ specdec_status_t specdec_verify(const specdec_verify_desc_t* desc,
  * correction/bonus draw).  The events bracket the kernels' execution
  * (hipExtLaunchKernel), not the enqueue.  Sampling without truncation and
  * greedy verification run both passes in one kernel: [0]/[1] bracket that
- * kernel and [2]/[3] are recorded right after it.
+ * kernel and [2]/[3] are recorded right after it.  With truncation, [0]/[1]
+ * bracket the pass that dominates instead: the selection kernel that lists
+ * the kept tokens, or the kernel that finds the cut records (the statistics
+ * kernel launched before it is then not bracketed); [2]/[3] bracket the
+ * decision kernel as above.
  * Everything else, including every error, is as for specdec_verify. */
 specdec_status_t specdec_verify_profiled(const specdec_verify_desc_t* desc,
                                          const void* target_logits, const void* draft_logits,

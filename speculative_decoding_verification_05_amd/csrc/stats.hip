@@ -58,7 +58,7 @@ __global__ __launch_bounds__(kThreads) void k_stats(VerifyParams P) {
 specdec_status_t launch_stats(const VerifyParams& P, bool bf16, bool vec, bool greedy, dim3 grid,
                               hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     auto launch = [&](auto kernel) {
-        if (start)
+        if (start || stop)
             hipExtLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, start, stop, 0, P);
         else
             hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, stream, P);

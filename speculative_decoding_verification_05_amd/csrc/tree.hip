@@ -255,8 +255,9 @@ specdec_status_t tree_impl(const specdec_tree_desc_t* d, const void* target_logi
         };
         if (bf16) vec ? launch(k_tree_fused<true, true>) : launch(k_tree_fused<true, false>);
         else vec ? launch(k_tree_fused<false, true>) : launch(k_tree_fused<false, false>);
-        if (ev && (hipEventRecord(ev[2], stream) != hipSuccess || hipEventRecord(ev[3], stream) != hipSuccess))
-            return SPECDEC_ERR_DEVICE;
+        // (any entry may be NULL)
+        if (ev && ev[2] && hipEventRecord(ev[2], stream) != hipSuccess) return SPECDEC_ERR_DEVICE;
+        if (ev && ev[3] && hipEventRecord(ev[3], stream) != hipSuccess) return SPECDEC_ERR_DEVICE;
         return hipGetLastError() == hipSuccess ? SPECDEC_OK : SPECDEC_ERR_DEVICE;
     }
     if (launch_stats(P, bf16, vec, true, dim3(L.nc, L.rows, d->batch), stream,

@@ -1233,7 +1233,7 @@ specdec_status_t launch_trunc_cut(const VerifyParams& P, bool bf16, bool vec, hi
                                   hipEvent_t start, hipEvent_t stop) {
     const dim3 grid(P.rows, P.B);
     auto launch = [&](auto kernel) {
-        if (start)
+        if (start || stop)
             hipExtLaunchKernelGGL(kernel, grid, dim3(kCutThreads), 0, stream, start, stop, 0, P);
         else
             hipLaunchKernelGGL(kernel, grid, dim3(kCutThreads), 0, stream, P);
