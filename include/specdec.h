@@ -96,13 +96,13 @@ typedef enum specdec_mode { SPECDEC_SAMPLE = 0, SPECDEC_GREEDY = 1 } specdec_mod
 /* ------------------------------------------------------------------ verify */
 
 typedef struct specdec_verify_desc {
-    int32_t batch;        /* B >= 0 requests */
+    int32_t batch;        /* B in [0, 65535] requests */
     int32_t gamma_max;    /* G in [0, 63]: padded draft length */
     int32_t vocab;        /* V >= 1; at most 4194304 (bf16) / 2097152 (fp32) */
     int32_t dtype;        /* specdec_dtype_t of both logits tensors */
     int32_t mode;         /* specdec_mode_t */
     int32_t top_k;        /* SAMPLE only: 0 = off, else keep logits >= k-th largest */
-    float temperature;    /* SAMPLE only: > 0 */
+    float temperature;    /* SAMPLE only: > 0 and finite */
     float top_p;          /* SAMPLE only: (0, 1]; 1 = off */
     uint64_t seed;        /* Philox4x32-10 key (low word, high word) */
     uint32_t round;       /* Philox counter word 2 (make it differ per round) */
@@ -260,7 +260,7 @@ specdec_status_t specdec_verify_noalloc(const specdec_verify_desc_t* desc,
 /* ------------------------------------------------------------- commit K/V */
 
 typedef struct specdec_kv_desc {
-    int32_t batch;              /* B */
+    int32_t batch;              /* B in [0, 65535] */
     int32_t gamma_max;          /* G in [0, 63] */
     int32_t num_layers;         /* L >= 1 */
     int32_t num_kv_heads;       /* H >= 1 */
@@ -271,6 +271,9 @@ typedef struct specdec_kv_desc {
                                    (specdec_commit_kv only; must be 0 for rollback) */
     int64_t num_blocks;         /* physical blocks in the pool */
 } specdec_kv_desc_t;
+/* Descriptor limits checked on the host (INVALID_ARGUMENT otherwise):
+ * max_blocks_per_req >= 1, num_blocks >= 1, scratch_slots >= 0, H*D <= 2^24
+ * and L*2*H*D < 2^31 (element offsets inside one slot stay 32-bit). */
 
 /* Bytes of device workspace specdec_commit_kv needs (per-request arrival
  * counters; same zero-at-first-use rule as the verify workspace). */
@@ -317,7 +320,7 @@ specdec_status_t specdec_commit_kv(const specdec_kv_desc_t* desc,
 /* ------------------------------------------------------------ tree verify */
 
 typedef struct specdec_tree_desc {
-    int32_t batch;        /* B >= 0 requests */
+    int32_t batch;        /* B in [0, 65535] requests */
     int32_t num_nodes;    /* N in [1, 64]: padded nodes per tree, node 0 = root */
     int32_t vocab;        /* V >= 1, as for specdec_verify */
     int32_t dtype;        /* specdec_dtype_t of the target logits */
@@ -388,7 +391,7 @@ specdec_status_t specdec_verify_tree_profiled(const specdec_tree_desc_t* desc,
 /* ------------------------------------------------------------ n-gram drafts */
 
 typedef struct specdec_ngram_desc {
-    int32_t batch;        /* B >= 0 requests */
+    int32_t batch;        /* B in [0, 65535] requests */
     int32_t max_len;      /* row stride of the history, in [1, 2^24) */
     int32_t n_min;        /* shortest n-gram matched, >= 1 */
     int32_t n_max;        /* longest n-gram matched, in [n_min, 32] */
