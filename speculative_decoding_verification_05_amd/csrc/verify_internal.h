@@ -220,7 +220,7 @@ struct Layout {
 Layout make_layout(const specdec_verify_desc_t* d, bool point = false);
 
 // The statistics pass (one partial per chunk of every used row); start/stop
-// events (both null, or both set) bracket the kernel.
+// events (either may be null) bracket the kernel.
 specdec_status_t launch_stats(const VerifyParams& P, bool bf16, bool vec, bool greedy, dim3 grid,
                               hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 
