@@ -85,16 +85,22 @@ __device__ __forceinline__ void stream_row_lean(const void* rp, int lo, int hi, 
 
 
 
+// The workgroup's pair (every lane gets it): the waves' pairs meet in LDS,
+// then the same as wave_combine over them (the maximum, then each wave's
+// sum rescaled to it, added in wave order).
 __device__ __forceinline__ MaxSum block_combine(MaxSum v, float c) {
     __shared__ float s_m[kWaves], s_s[kWaves];
     v = wave_combine(v, c);
     const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
     if (l == 0) { s_m[w] = v.m; s_s[w] = v.s; }
     __syncthreads();
-    MaxSum r{s_m[0], s_s[0]};
+    float m = s_m[0];
 #pragma unroll
-    for (int k = 1; k < kWaves; ++k) r = combine(r, MaxSum{s_m[k], s_s[k]}, c);
-    return r;
+    for (int k = 1; k < kWaves; ++k) m = fmaxf(m, s_m[k]);
+    float s = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) s += s_m[k] == neg_inf() ? 0.0f : s_s[k] * exp2f((s_m[k] - m) * c);
+    return {m, s};
 }
 
 __device__ __forceinline__ ArgMax block_argmax(ArgMax v) {
