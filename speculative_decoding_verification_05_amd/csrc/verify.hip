@@ -501,24 +501,32 @@ __device__ __forceinline__ void decide_sample(const VerifyParams& P, const int w
         for (int s = threadIdx.x; s < P.rows; s += kThreads) {
             const bool used = (s <= P.G) ? (s <= g) : (s - (P.G + 1) < g);
             if (!used) continue;
-            MaxSum acc{neg_inf(), 0.0f};
+            // the maximum first, then each partial's sum rescaled to it and
+            // added in chunk order (no chain of dependent exponentials)
+            float m = neg_inf();
+            for (int k = 0; k < P.nc; ++k) m = fmaxf(m, s_part[s * P.nc + k].x);
+            float sum = 0.0f;
             for (int k = 0; k < P.nc; ++k) {
                 const float4 q = s_part[s * P.nc + k];
-                acc = combine(acc, MaxSum{q.x, q.y}, c);
+                sum += q.x == neg_inf() ? 0.0f : q.y * exp2f((q.x - m) * c);
             }
-            s_stat[s] = make_float2(acc.m, acc.s);
+            s_stat[s] = make_float2(m, sum);
         }
     } else {
         for (int s = w; s < P.rows; s += kWaves) {
             const bool used = (s <= P.G) ? (s <= g) : (s - (P.G + 1) < g);
             if (!used) continue;
-            MaxSum acc{neg_inf(), 0.0f};
+            // as above, a lane per partial
+            float ml = neg_inf();
+            for (int k = l; k < P.nc; k += kWave) ml = fmaxf(ml, s_part[s * P.nc + k].x);
+            const float m = wave_max(ml);
+            float sl = 0.0f;
             for (int k = l; k < P.nc; k += kWave) {
                 const float4 q = s_part[s * P.nc + k];
-                acc = combine(acc, MaxSum{q.x, q.y}, c);
+                sl += q.x == neg_inf() ? 0.0f : q.y * exp2f((q.x - m) * c);
             }
-            acc = wave_combine(acc, c);
-            if (l == 0) s_stat[s] = make_float2(acc.m, acc.s);
+            const float sum = wave_sum(sl);
+            if (l == 0) s_stat[s] = make_float2(m, sum);
         }
     }
     __syncthreads();
