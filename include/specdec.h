@@ -40,7 +40,10 @@
  *     reached that point.  Nothing is copied back to the host.
  *   - A non-OK status means that NOTHING was enqueued (argument errors are
  *     found on the host before any launch), except SPECDEC_ERR_DEVICE, which
- *     reports a launch failure from the HIP runtime.
+ *     reports a launch failure from the HIP runtime.  Launches are checked
+ *     with hipGetLastError, which also returns (and clears) an error that an
+ *     earlier HIP call on the calling thread left pending: check and clear
+ *     your own calls' errors before calling in.
  *   - Data anomalies (a draft token outside [0,V), a non-finite logit, an
  *     empty residual, an unusable block-table entry) never change the status;
  *     they are reported per request in the optional `flags` output.
