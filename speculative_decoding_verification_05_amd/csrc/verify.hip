@@ -52,6 +52,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 namespace specdec {
 namespace {
@@ -80,6 +81,37 @@ __device__ __forceinline__ float mass_at(const MassRows& a, float zp, float zq, 
     float qv = __builtin_amdgcn_exp2f((zq - a.mq) * a.c) * a.isq;
     if constexpr (CUT) qv = (zq > a.tq || (zq == a.tq && v <= a.iq)) ? qv : 0.0f;
     return fmaxf(pv - qv, 0.0f);
+}
+
+// The three kinds of sampling mass, told apart once per call (a uniform
+// branch) so that the per-element loops carry neither the test for a draft
+// row nor the point-mass token's: a residual max(p - q, 0) with draft rows,
+// p itself (bonus, or the empty-residual fallback), p without one token
+// (point-mass drafts).  Same operations per element as mass_at, so the same
+// bits; three fewer vector operations per element of about fifteen.
+enum class MassKind { kResidual, kTarget, kTargetButOne };
+
+template <MassKind K, bool CUT>
+__device__ __forceinline__ float mass_of(const MassRows& a, float zp, float zq, int v) {
+    float pv = __builtin_amdgcn_exp2f((zp - a.mp) * a.c) * a.isp;
+    if constexpr (CUT) pv = (zp > a.tp || (zp == a.tp && v <= a.ip)) ? pv : 0.0f;
+    if constexpr (K == MassKind::kResidual) {
+        float qv = __builtin_amdgcn_exp2f((zq - a.mq) * a.c) * a.isq;
+        if constexpr (CUT) qv = (zq > a.tq || (zq == a.tq && v <= a.iq)) ? qv : 0.0f;
+        return fmaxf(pv - qv, 0.0f);
+    } else if constexpr (K == MassKind::kTargetButOne) {
+        return v == a.point ? 0.0f : pv;
+    } else {
+        return pv;
+    }
+}
+
+// Calls f.template operator()<K>() with the kind of mass a describes.
+template <class F>
+__device__ __forceinline__ auto with_mass_kind(const MassRows& a, F&& f) {
+    if (a.q) return f(std::integral_constant<MassKind, MassKind::kResidual>{});
+    if (a.point >= 0) return f(std::integral_constant<MassKind, MassKind::kTargetButOne>{});
+    return f(std::integral_constant<MassKind, MassKind::kTarget>{});
 }
 
 // One chunk of the sampling pass is one tile: lane l holds the 16-byte
@@ -113,22 +145,23 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<BF16, VEC>& r, const MassRo
 template <bool BF16, bool VEC, bool CUT = false>
 __device__ __forceinline__ float lane_mass(const ChunkRegs<BF16, VEC>& r, const MassRows& a, int lo, int hi) {
     constexpr int N = Vec<BF16>::N;
-    float acc = 0.0f;
+    return with_mass_kind(a, [&](auto kind) {
+        constexpr MassKind K = decltype(kind)::value;
+        float acc = 0.0f;
 #pragma unroll
-    for (int u = 0; u < kUnroll2; ++u) {
-        const Vec<BF16> vp = widen<BF16>(r.p[u]);
-        Vec<BF16> vq;
-        if (a.q) vq = widen<BF16>(r.q[u]);
-        const int e = lo + (u * kThreads + threadIdx.x) * N;
-        float s = 0.0f;
+        for (int u = 0; u < kUnroll2; ++u) {
+            const Vec<BF16> vp = widen<BF16>(r.p[u]);
+            Vec<BF16> vq;
+            if constexpr (K == MassKind::kResidual) vq = widen<BF16>(r.q[u]);
+            const int e = lo + (u * kThreads + threadIdx.x) * N;
+            float s = 0.0f;
 #pragma unroll
-        for (int k = 0; k < N; ++k) {
-            const float r = mass_at<CUT>(a, vp.x[k], a.q ? vq.x[k] : 0.0f, e + k);
-            s += (e + k == a.point) ? 0.0f : r;
+            for (int k = 0; k < N; ++k)
+                s += mass_of<K, CUT>(a, vp.x[k], K == MassKind::kResidual ? vq.x[k] : 0.0f, e + k);
+            acc += (e < hi) ? s : 0.0f;
         }
-        acc += (e < hi) ? s : 0.0f;
-    }
-    return acc;
+        return acc;
+    });
 }
 
 // Lane's share of the chunk's mass with element loads (rows not 16-byte
@@ -258,16 +291,21 @@ __device__ int search_chunk(const MassRows& a, int lo, int hi, float base, float
     float r[PER];
     float run = 0.0f;
     int lastp = -1;
+    with_mass_kind(a, [&](auto kind) {
+        constexpr MassKind K = decltype(kind)::value;
 #pragma unroll
-    for (int u = 0; u < kUnroll2; ++u)
+        for (int u = 0; u < kUnroll2; ++u)
 #pragma unroll
-        for (int k = 0; k < N; ++k) {
-            const int v = e0 + u * N + k;
-            const float x = (v < hi && v != a.point) ? mass_at<CUT>(a, vp[u].x[k], a.q ? vq[u].x[k] : 0.0f, v) : 0.0f;
-            if (x > 0.0f) lastp = v;
-            r[u * N + k] = x;
-            run += x;
-        }
+            for (int k = 0; k < N; ++k) {
+                const int v = e0 + u * N + k;
+                const float x =
+                    v < hi ? mass_of<K, CUT>(a, vp[u].x[k], K == MassKind::kResidual ? vq[u].x[k] : 0.0f, v) : 0.0f;
+                if (x > 0.0f) lastp = v;
+                r[u * N + k] = x;
+                run += x;
+            }
+        return 0;
+    });
     // exclusive scan of the lane totals: inclusive within the wave, shifted,
     // plus the totals of the waves before
     const float incl = wave_prefix_sum(run);
