@@ -141,13 +141,21 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<BF16, VEC>& r, const MassRo
     }
 }
 
-// Lane's share of the chunk's mass (VEC layout).
+// A chunk of the sampling pass is kUnroll2 = 2 halves in token order: half u
+// is the kThreads vectors u*kThreads .. u*kThreads + kThreads - 1, lane l
+// holding vector u*kThreads + l of each.  The pass keeps the two halves'
+// masses apart, so that the final search reads and weighs only the half
+// where the running mass crosses u*R (half the vector work of searching the
+// whole chunk, on the decision's critical path).
+static_assert(kUnroll2 == 2, "a sampling chunk is two halves, one vector per lane each");
+
+// Lane's share of each half's mass (VEC layout).
 template <bool BF16, bool VEC, bool CUT = false>
-__device__ __forceinline__ float lane_mass(const ChunkRegs<BF16, VEC>& r, const MassRows& a, int lo, int hi) {
+__device__ __forceinline__ float2 lane_mass(const ChunkRegs<BF16, VEC>& r, const MassRows& a, int lo, int hi) {
     constexpr int N = Vec<BF16>::N;
     return with_mass_kind(a, [&](auto kind) {
         constexpr MassKind K = decltype(kind)::value;
-        float acc = 0.0f;
+        float h[kUnroll2];
 #pragma unroll
         for (int u = 0; u < kUnroll2; ++u) {
             const Vec<BF16> vp = widen<BF16>(r.p[u]);
@@ -158,38 +166,40 @@ __device__ __forceinline__ float lane_mass(const ChunkRegs<BF16, VEC>& r, const 
 #pragma unroll
             for (int k = 0; k < N; ++k)
                 s += mass_of<K, CUT>(a, vp.x[k], K == MassKind::kResidual ? vq.x[k] : 0.0f, e + k);
-            acc += (e < hi) ? s : 0.0f;
+            h[u] = (e < hi) ? s : 0.0f;
         }
-        return acc;
+        return make_float2(h[0], h[1]);
     });
 }
 
 // Lane's share of the chunk's mass with element loads (rows not 16-byte
 // aligned): a slow path kept simple.
 template <bool BF16, bool CUT = false>
-__device__ float lane_mass_elements(const MassRows& a, int lo, int hi) {
+__device__ float2 lane_mass_elements(const MassRows& a, int lo, int hi) {
     constexpr int N = Vec<BF16>::N;
-    float acc = 0.0f;
+    float h[kUnroll2] = {0.0f, 0.0f};
     for (int u = 0; u < kUnroll2; ++u) {
         const int e = lo + (u * kThreads + threadIdx.x) * N;
         for (int k = 0; k < N; ++k) {
             if (e + k >= hi) break;
             const float zp = load_logit<BF16>(a.p, e + k);
             const float zq = a.q ? load_logit<BF16>(a.q, e + k) : 0.0f;
-            if (e + k != a.point) acc += mass_at<CUT>(a, zp, zq, e + k);
+            if (e + k != a.point) h[u] += mass_at<CUT>(a, zp, zq, e + k);
         }
     }
-    return acc;
+    return make_float2(h[0], h[1]);
 }
 
-// Masses of chunks [k0, k1), handed to emit(k, mass) by thread 0.  Loads go
-// in groups of GROUP chunks, into two register sets in turn (no copies
-// between them), so the next group's loads are in flight while the current
-// group is reduced.  Nothing inside the walk waits on other waves or on
-// memory writes: each chunk's wave sums go to LDS (scr: kWaves floats per
-// chunk), and after one barrier thread 0 adds them in wave order and emits
-// the whole batch at once (batches of 1024 / kWaves chunks).  Returns the OR
-// of emit's results (a dependency for arrive_last when emit publishes).
+// Masses of chunks [k0, k1), handed to emit(k, h0, h1) by thread 0, h0 and
+// h1 the masses of the chunk's two halves (the chunk's mass is their sum,
+// chunk_total).  Loads go in groups of GROUP chunks, into two register sets
+// in turn (no copies between them), so the next group's loads are in flight
+// while the current group is reduced.  Nothing inside the walk waits on other
+// waves or on memory writes: each half's wave sums go to LDS (scr: 2 kWaves
+// floats per chunk), and after one barrier thread 0 adds them in wave order
+// and emits the whole batch at once (batches of 1024 / (2 kWaves) chunks).
+// Returns the OR of emit's results (a dependency for arrive_last when emit
+// publishes).
 template <bool BF16, bool VEC, int GROUP, bool CACHED, bool CUT = false, class Emit>
 __device__ uint32_t mass_chunks(const MassRows& a, int k0, int k1, int chunk2, int V, float* scr,
                                 Emit&& emit) {
@@ -197,7 +207,7 @@ __device__ uint32_t mass_chunks(const MassRows& a, int k0, int k1, int chunk2, i
     if (k0 >= k1) return dep;
     if constexpr (VEC) {
         const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
-        constexpr int kBatch = 1024 / kWaves;
+        constexpr int kBatch = 1024 / (kUnroll2 * kWaves);
         for (int b0 = k0; b0 < k1; b0 += kBatch) {
             const int b1 = min(k1, b0 + kBatch);
             auto load_group = [&](ChunkRegs<BF16, VEC>(&r)[GROUP], int kb) {
@@ -212,8 +222,12 @@ __device__ uint32_t mass_chunks(const MassRows& a, int k0, int k1, int chunk2, i
                 for (int j = 0; j < GROUP; ++j) {
                     if (kb + j >= b1) break;
                     const int lo = (kb + j) * chunk2, hi = min(V, lo + chunk2);
-                    const float s = wave_sum(lane_mass<BF16, VEC, CUT>(r[j], a, lo, hi));
-                    if (l == 0) scr[(kb + j - b0) * kWaves + w] = s;
+                    const float2 h = lane_mass<BF16, VEC, CUT>(r[j], a, lo, hi);
+                    const float s0 = wave_sum(h.x), s1 = wave_sum(h.y);
+                    if (l == 0) {
+                        scr[((kb + j - b0) * kUnroll2 + 0) * kWaves + w] = s0;
+                        scr[((kb + j - b0) * kUnroll2 + 1) * kWaves + w] = s1;
+                    }
                 }
             };
             ChunkRegs<BF16, VEC> ra[GROUP], rb[GROUP];
@@ -228,11 +242,14 @@ __device__ uint32_t mass_chunks(const MassRows& a, int k0, int k1, int chunk2, i
             __syncthreads();
             if (threadIdx.x == 0) {
                 for (int k = b0; k < b1; ++k) {
-                    const float* s = scr + (k - b0) * kWaves;
-                    float t = s[0];
+                    const float* s = scr + (k - b0) * kUnroll2 * kWaves;
+                    float h0 = s[0], h1 = s[kWaves];
 #pragma unroll
-                    for (int q = 1; q < kWaves; ++q) t += s[q];
-                    dep |= emit(k, t);
+                    for (int q = 1; q < kWaves; ++q) {
+                        h0 += s[q];
+                        h1 += s[kWaves + q];
+                    }
+                    dep |= emit(k, h0, h1);
                 }
             }
             __syncthreads();  // scr is reused by the next batch and by the caller
@@ -240,53 +257,57 @@ __device__ uint32_t mass_chunks(const MassRows& a, int k0, int k1, int chunk2, i
     } else {
         for (int k = k0; k < k1; ++k) {
             const int lo = k * chunk2, hi = min(V, lo + chunk2);
-            const float t = block_sum(lane_mass_elements<BF16, CUT>(a, lo, hi));
-            if (threadIdx.x == 0) dep |= emit(k, t);
+            const float2 h = lane_mass_elements<BF16, CUT>(a, lo, hi);
+            const float h0 = block_sum(h.x), h1 = block_sum(h.y);
+            if (threadIdx.x == 0) dep |= emit(k, h0, h1);
         }
     }
     return dep;
 }
 
-// Mass of one chunk (the empty-residual fallback path).
+// A chunk's mass from its halves' (every path adds them the same way).
+__device__ __forceinline__ float chunk_total(float h0, float h1) { return h0 + h1; }
+
+// Masses of one chunk's halves (the empty-residual fallback path).
 template <bool BF16, bool VEC, bool CUT = false>
-__device__ float chunk_mass(const MassRows& a, int lo, int hi) {
+__device__ float2 chunk_mass(const MassRows& a, int lo, int hi) {
+    float2 h;
     if constexpr (VEC) {
         ChunkRegs<BF16, VEC> r;
         load_chunk<BF16, VEC, false>(r, a, lo, hi);
-        return block_sum(lane_mass<BF16, VEC, CUT>(r, a, lo, hi));
+        h = lane_mass<BF16, VEC, CUT>(r, a, lo, hi);
     } else {
-        return block_sum(lane_mass_elements<BF16, CUT>(a, lo, hi));
+        h = lane_mass_elements<BF16, CUT>(a, lo, hi);
     }
+    const float h0 = block_sum(h.x);
+    const float h1 = block_sum(h.y);
+    return make_float2(h0, h1);
 }
 
-// First v of the chunk [lo, hi) with base + prefix(v) > target, scanning the
-// mass in ascending token order.  Lane l holds the kUnroll2*N consecutive
-// elements starting at lo + l*kUnroll2*N (every load issued at once), so one
-// block-wide exclusive scan of the lane totals gives each lane its offset.
-// Returns 0x7fffffff if none; *last_pos receives the chunk's largest v with
-// mass > 0.
+// First v of one half [lo, hi) of a chunk (at most kThreads*N elements, hi
+// >= N) with base + prefix(v) > target, scanning the mass in ascending token
+// order.  Lane l holds the N consecutive elements starting at lo + l*N (one
+// vector), so one block-wide exclusive scan of the lane totals gives each
+// lane its offset.  Returns 0x7fffffff if none; *last_pos receives the half's
+// largest v with mass > 0.
 template <bool BF16, bool VEC, bool CUT = false>
-__device__ int search_chunk(const MassRows& a, int lo, int hi, float base, float target,
-                            int* last_pos) {
+__device__ int search_half(const MassRows& a, int lo, int hi, float base, float target,
+                           int* last_pos) {
     constexpr int N = Vec<BF16>::N;
-    constexpr int PER = kUnroll2 * N;  // elements per lane
+    constexpr int PER = N;  // elements per lane
     __shared__ float s_wtot[kWaves];
     __shared__ int s_found[kWaves], s_last[kWaves];
     const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
     const int e0 = lo + threadIdx.x * PER;
-    Vec<BF16> vp[kUnroll2], vq[kUnroll2];
-#pragma unroll
-    for (int u = 0; u < kUnroll2; ++u) {
-        const int e = e0 + u * N;
-        if constexpr (VEC) {
-            // clamped into the row: a vector lies wholly inside [lo, hi) or past it
-            const int ec = min(e, hi - N);
-            vp[u] = widen<BF16>(load16<BF16>(a.p, ec));
-            if (a.q) vq[u] = widen<BF16>(load16<BF16>(a.q, ec));
-        } else {
-            vp[u] = load_vec<BF16, VEC>(a.p, e, hi, neg_inf());
-            if (a.q) vq[u] = load_vec<BF16, VEC>(a.q, e, hi, neg_inf());
-        }
+    Vec<BF16> vp, vq;
+    if constexpr (VEC) {
+        // clamped into the row: a vector lies wholly inside [lo, hi) or past it
+        const int ec = min(e0, hi - N);
+        vp = widen<BF16>(load16<BF16>(a.p, ec));
+        if (a.q) vq = widen<BF16>(load16<BF16>(a.q, ec));
+    } else {
+        vp = load_vec<BF16, VEC>(a.p, e0, hi, neg_inf());
+        if (a.q) vq = load_vec<BF16, VEC>(a.q, e0, hi, neg_inf());
     }
     float r[PER];
     float run = 0.0f;
@@ -294,16 +315,13 @@ __device__ int search_chunk(const MassRows& a, int lo, int hi, float base, float
     with_mass_kind(a, [&](auto kind) {
         constexpr MassKind K = decltype(kind)::value;
 #pragma unroll
-        for (int u = 0; u < kUnroll2; ++u)
-#pragma unroll
-            for (int k = 0; k < N; ++k) {
-                const int v = e0 + u * N + k;
-                const float x =
-                    v < hi ? mass_of<K, CUT>(a, vp[u].x[k], K == MassKind::kResidual ? vq[u].x[k] : 0.0f, v) : 0.0f;
-                if (x > 0.0f) lastp = v;
-                r[u * N + k] = x;
-                run += x;
-            }
+        for (int k = 0; k < N; ++k) {
+            const int v = e0 + k;
+            const float x = v < hi ? mass_of<K, CUT>(a, vp.x[k], K == MassKind::kResidual ? vq.x[k] : 0.0f, v) : 0.0f;
+            if (x > 0.0f) lastp = v;
+            r[k] = x;
+            run += x;
+        }
         return 0;
     });
     // exclusive scan of the lane totals: inclusive within the wave, shifted,
@@ -447,8 +465,8 @@ __device__ __forceinline__ bool clear_partials(const VerifyParams& P, int b, int
 
 // One-kernel path: the chunk masses of request b's decision workgroups
 // other than the last, words [0, n) of cm.  Each publisher writes its word
-// once, (1 << 32) | mass bits, with bit 33 set if its own statistics wait
-// gave up, by an atomic exchange it does not wait for.  The last decision
+// once, the chunk's two half masses packed by pack_halves, by an atomic
+// exchange it does not wait for.  The last decision
 // workgroup (launched after all of them) reads them here, a lane per word:
 // each read is an exchange with zero, so a word is cleared for the next call
 // as it is taken.  Polls sleep in between, bounded like the statistics wait;
@@ -457,7 +475,22 @@ __device__ __forceinline__ bool clear_partials(const VerifyParams& P, int b, int
 // wait gave up.
 constexpr uint32_t kMassMissing = 0x7fc0deadu;  // a NaN pattern
 
-__device__ bool collect_masses(const VerifyParams& P, unsigned long long* cm, int n, float* s_csum) {
+// A published chunk-mass word: bit 63 set (never all zero), bit 62 if the
+// publisher's own statistics wait gave up, then the two halves' masses as
+// 31-bit floats without their sign bit (masses are >= 0; a NaN stays a NaN).
+__device__ __forceinline__ unsigned long long pack_halves(float h0, float h1, bool late) {
+    return (1ull << 63) | (late ? (1ull << 62) : 0ull) |
+           (static_cast<unsigned long long>(__float_as_uint(h0) & 0x7fffffffu) << 31) |
+           static_cast<unsigned long long>(__float_as_uint(h1) & 0x7fffffffu);
+}
+
+__device__ __forceinline__ float2 unpack_halves(unsigned long long v) {
+    return make_float2(__uint_as_float(static_cast<uint32_t>(v >> 31) & 0x7fffffffu),
+                       __uint_as_float(static_cast<uint32_t>(v) & 0x7fffffffu));
+}
+
+__device__ bool collect_masses(const VerifyParams& P, unsigned long long* cm, int n, float* s_csum,
+                               float2* s_half) {
     const uint64_t t0 = wall_clock64();
     bool late = false;
     for (int k = threadIdx.x; k < n; k += kThreads) {
@@ -466,8 +499,10 @@ __device__ bool collect_masses(const VerifyParams& P, unsigned long long* cm, in
             if (wall_clock64() - t0 > P.wait_ticks) { late = true; break; }
             __builtin_amdgcn_s_sleep(16);
         }
-        late |= ((v >> 33) & 1ull) != 0;
-        s_csum[k] = v == 0ull ? __uint_as_float(kMassMissing) : __uint_as_float(static_cast<uint32_t>(v));
+        late |= ((v >> 62) & 1ull) != 0;
+        const float2 h = unpack_halves(v);
+        s_half[k] = h;
+        s_csum[k] = v == 0ull ? __uint_as_float(kMassMissing) : chunk_total(h.x, h.y);
     }
     return __syncthreads_or(late);
 }
@@ -484,6 +519,7 @@ __device__ __forceinline__ void decide_sample(const VerifyParams& P, const int w
     __shared__ float2 s_stat[127];
     __shared__ float2 s_cut[CUT ? 127 : 1];  // (boundary logit, last kept index at it as bits)
     __shared__ float s_csum[1024];
+    __shared__ float2 s_half[1024];  // each chunk's half masses
     __shared__ int s_m, s_dm;
     __shared__ uint32_t s_fl;
     __shared__ float s_R, s_um;
@@ -655,18 +691,19 @@ __device__ __forceinline__ void decide_sample(const VerifyParams& P, const int w
         // the request's last decision workgroup (chunks [k0, nc2)) keeps its
         // masses in LDS and collects the others' published words
         unsigned long long* cm = reinterpret_cast<unsigned long long*>(P.cmass) + static_cast<size_t>(b) * P.nc2;
-        mass_chunks<BF16, VEC, GROUP, CACHED>(a, k0, k1, P.chunk2, P.V, scr, [&](int k, float t) -> uint32_t {
-            s_csum[k] = t;
-            return 0u;
-        });
+        mass_chunks<BF16, VEC, GROUP, CACHED>(a, k0, k1, P.chunk2, P.V, scr,
+                                              [&](int k, float h0, float h1) -> uint32_t {
+                                                  s_half[k] = make_float2(h0, h1);
+                                                  s_csum[k] = chunk_total(h0, h1);
+                                                  return 0u;
+                                              });
         // (mass_chunks ends with a barrier: s_csum[k0, k1) is visible)
         if (wg != P.wpr - 1) {
-            const unsigned long long tag = (1ull << 32) | (late ? (1ull << 33) : 0ull);
             for (int k = k0 + threadIdx.x; k < k1; k += kThreads)
-                atomicExch(cm + k, tag | __float_as_uint(s_csum[k]));
+                atomicExch(cm + k, pack_halves(s_half[k].x, s_half[k].y, late));
             return;
         }
-        if (collect_masses(P, cm, k0, s_csum)) {
+        if (collect_masses(P, cm, k0, s_csum, s_half)) {
             late = true;
             // a publisher that did not come in time: its chunks' masses
             // computed here (mass_chunks gives each chunk the same value
@@ -676,8 +713,9 @@ __device__ __forceinline__ void decide_sample(const VerifyParams& P, const int w
                 if (__float_as_uint(s_csum[k]) != kMassMissing) continue;
                 __syncthreads();  // every lane has read s_csum[k]
                 mass_chunks<BF16, VEC, GROUP, CACHED>(a, k, k + 1, P.chunk2, P.V, scr,
-                                                      [&](int kk, float t) -> uint32_t {
-                                                          s_csum[kk] = t;
+                                                      [&](int kk, float h0, float h1) -> uint32_t {
+                                                          s_half[kk] = make_float2(h0, h1);
+                                                          s_csum[kk] = chunk_total(h0, h1);
                                                           return 0u;
                                                       });
                 if (threadIdx.x == 0) {
@@ -695,11 +733,17 @@ __device__ __forceinline__ void decide_sample(const VerifyParams& P, const int w
         if (late) late = clear_partials(P, b, g, true) || late;
         else clear_partials(P, b, g, false);
     } else {
-        uint32_t* csum = P.csum + static_cast<size_t>(b) * P.nc2;
+        uint32_t* csum = P.csum + static_cast<size_t>(b) * P.nc2 * 2;  // (h0, h1) per chunk
         const uint32_t dep = mass_chunks<BF16, VEC, GROUP, CACHED, CUT>(
-            a, k0, k1, P.chunk2, P.V, scr, [&](int k, float t) { return publish(csum + k, __float_as_uint(t)); });
+            a, k0, k1, P.chunk2, P.V, scr, [&](int k, float h0, float h1) {
+                return publish(csum + 2 * k, __float_as_uint(h0)) | publish(csum + 2 * k + 1, __float_as_uint(h1));
+            });
         if (!arrive_last(P.cnt + b, static_cast<uint32_t>(P.wpr), dep)) return;
-        for (int k = threadIdx.x; k < P.nc2; k += kThreads) s_csum[k] = __uint_as_float(fetch(csum + k));
+        for (int k = threadIdx.x; k < P.nc2; k += kThreads) {
+            const float2 h = make_float2(__uint_as_float(fetch(csum + 2 * k)), __uint_as_float(fetch(csum + 2 * k + 1)));
+            s_half[k] = h;
+            s_csum[k] = chunk_total(h.x, h.y);
+        }
         __syncthreads();
     }
 
@@ -759,8 +803,11 @@ __device__ __forceinline__ void decide_sample(const VerifyParams& P, const int w
             a.q = nullptr;
             a.point = -1;
             for (int k = 0; k < P.nc2; ++k) {
-                const float v = chunk_mass<BF16, VEC, CUT>(a, k * P.chunk2, min(P.V, (k + 1) * P.chunk2));
-                if (threadIdx.x == 0) s_csum[k] = v;
+                const float2 h = chunk_mass<BF16, VEC, CUT>(a, k * P.chunk2, min(P.V, (k + 1) * P.chunk2));
+                if (threadIdx.x == 0) {
+                    s_half[k] = h;
+                    s_csum[k] = chunk_total(h.x, h.y);
+                }
             }
             __syncthreads();
             scan();
@@ -768,12 +815,22 @@ __device__ __forceinline__ void decide_sample(const VerifyParams& P, const int w
     }
     const float target = s_um * s_R;
     int lastp;
-    const int l2 = s_chunk * P.chunk2, h2 = min(P.V, l2 + P.chunk2);
-    int token = search_chunk<BF16, VEC, CUT>(a, l2, h2, s_before, target, &lastp);
-    // The chunk sums and the in-chunk prefixes associate the additions
+    // The chosen chunk's half: the first if the mass before the chunk plus
+    // the first half's passes u*R, else the second, after the first's mass.
+    // Without a crossing (s_before = +inf: rounding left u*R at or above the
+    // total), the last token with mass is taken, in the chunk's last half
+    // with mass.  A half of the last chunk may be empty (past V): never chosen.
+    constexpr int kHalf = kThreads * Vec<BF16>::N;
+    const int l2 = s_chunk * P.chunk2, h2 = min(P.V, l2 + P.chunk2), lm = min(h2, l2 + kHalf);
+    const float2 hc = s_half[s_chunk];
+    const bool none = !(s_before < pos_inf());
+    const bool second = lm < h2 && (none ? hc.y > 0.0f : !(s_before + hc.x > target));
+    const float base = second ? s_before + hc.x : s_before;
+    int token = search_half<BF16, VEC, CUT>(a, second ? lm : l2, second ? h2 : lm, base, target, &lastp);
+    // The chunk sums and the in-half prefixes associate the additions
     // differently; if that rounding leaves no element above u*R in the chosen
-    // chunk, the crossing is its last token with mass.
-    if (token == 0x7fffffff) token = lastp;
+    // half, the crossing is its last token with mass.
+    if (none || token == 0x7fffffff) token = lastp;
 
     if (w == 0) {
         fl2 |= write_round(P, b, m, i < m ? d : token);
@@ -1075,7 +1132,7 @@ Layout make_layout(const specdec_verify_desc_t* d, bool point) {
     L.off_ready = off; off = align256(off + B * L.rows * L.nc * sizeof(uint64_t));
     L.off_cmass = off; off = align256(off + B * L.nc2 * sizeof(uint64_t));
     L.off_part = off; off = align256(off + B * L.rows * L.nc * sizeof(float4));
-    L.off_csum = off; off = align256(off + B * L.nc2 * sizeof(uint32_t));
+    L.off_csum = off; off = align256(off + B * L.nc2 * 2 * sizeof(uint32_t));
     L.trunc = truncation_mode(d);
     // point-mass drafts under truncation: the cut path (its decision serves
     // point masses; the listed path's does not)
