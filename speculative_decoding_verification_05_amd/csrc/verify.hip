@@ -88,11 +88,18 @@ __device__ __forceinline__ float mass_at(const MassRows& a, float zp, float zq, 
 // row nor the point-mass token's: a residual max(p - q, 0) with draft rows,
 // p itself (bonus, or the empty-residual fallback), p without one token
 // (point-mass drafts).  Same operations per element as mass_at, so the same
-// bits; three fewer vector operations per element of about fifteen.
-enum class MassKind { kResidual, kTarget, kTargetButOne };
+// bits; three fewer vector operations per element of about fifteen.  The
+// decision over cut records (CUT) keeps one generic loop (kAny, mass_at's
+// tests per element): its membership tests leave it the tightest on
+// registers, and three copies of its walk cost it more than they saved.
+enum class MassKind { kResidual, kTarget, kTargetButOne, kAny };
 
 template <MassKind K, bool CUT>
 __device__ __forceinline__ float mass_of(const MassRows& a, float zp, float zq, int v) {
+    if constexpr (K == MassKind::kAny) {
+        const float r = mass_at<CUT>(a, zp, zq, v);
+        return v == a.point ? 0.0f : r;
+    }
     float pv = __builtin_amdgcn_exp2f((zp - a.mp) * a.c) * a.isp;
     if constexpr (CUT) pv = (zp > a.tp || (zp == a.tp && v <= a.ip)) ? pv : 0.0f;
     if constexpr (K == MassKind::kResidual) {
@@ -106,9 +113,10 @@ __device__ __forceinline__ float mass_of(const MassRows& a, float zp, float zq, 
     }
 }
 
-// Calls f.template operator()<K>() with the kind of mass a describes.
-template <class F>
+// Calls f with the kind of mass a describes (kAny for the cut decision).
+template <bool CUT, class F>
 __device__ __forceinline__ auto with_mass_kind(const MassRows& a, F&& f) {
+    if constexpr (CUT) return f(std::integral_constant<MassKind, MassKind::kAny>{});
     if (a.q) return f(std::integral_constant<MassKind, MassKind::kResidual>{});
     if (a.point >= 0) return f(std::integral_constant<MassKind, MassKind::kTargetButOne>{});
     return f(std::integral_constant<MassKind, MassKind::kTarget>{});
@@ -149,27 +157,27 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<BF16, VEC>& r, const MassRo
 // whole chunk, on the decision's critical path).
 static_assert(kUnroll2 == 2, "a sampling chunk is two halves, one vector per lane each");
 
-// Lane's share of each half's mass (VEC layout).
-template <bool BF16, bool VEC, bool CUT = false>
+// Lane's share of each half's mass (VEC layout), for mass kind K.
+template <MassKind K, bool BF16, bool VEC, bool CUT = false>
 __device__ __forceinline__ float2 lane_mass(const ChunkRegs<BF16, VEC>& r, const MassRows& a, int lo, int hi) {
     constexpr int N = Vec<BF16>::N;
-    return with_mass_kind(a, [&](auto kind) {
-        constexpr MassKind K = decltype(kind)::value;
-        float h[kUnroll2];
+    float h[kUnroll2];
 #pragma unroll
-        for (int u = 0; u < kUnroll2; ++u) {
-            const Vec<BF16> vp = widen<BF16>(r.p[u]);
-            Vec<BF16> vq;
-            if constexpr (K == MassKind::kResidual) vq = widen<BF16>(r.q[u]);
-            const int e = lo + (u * kThreads + threadIdx.x) * N;
-            float s = 0.0f;
-#pragma unroll
-            for (int k = 0; k < N; ++k)
-                s += mass_of<K, CUT>(a, vp.x[k], K == MassKind::kResidual ? vq.x[k] : 0.0f, e + k);
-            h[u] = (e < hi) ? s : 0.0f;
+    for (int u = 0; u < kUnroll2; ++u) {
+        const Vec<BF16> vp = widen<BF16>(r.p[u]);
+        Vec<BF16> vq;
+        if constexpr (K == MassKind::kResidual) vq = widen<BF16>(r.q[u]);
+        if constexpr (K == MassKind::kAny) {
+            if (a.q) vq = widen<BF16>(r.q[u]);
         }
-        return make_float2(h[0], h[1]);
-    });
+        const int e = lo + (u * kThreads + threadIdx.x) * N;
+        float s = 0.0f;
+#pragma unroll
+        for (int k = 0; k < N; ++k)
+            s += mass_of<K, CUT>(a, vp.x[k], K != MassKind::kTarget && K != MassKind::kTargetButOne && a.q ? vq.x[k] : 0.0f, e + k);
+        h[u] = (e < hi) ? s : 0.0f;
+    }
+    return make_float2(h[0], h[1]);
 }
 
 // Lane's share of the chunk's mass with element loads (rows not 16-byte
@@ -200,9 +208,9 @@ __device__ float2 lane_mass_elements(const MassRows& a, int lo, int hi) {
 // and emits the whole batch at once (batches of 1024 / (2 kWaves) chunks).
 // Returns the OR of emit's results (a dependency for arrive_last when emit
 // publishes).
-template <bool BF16, bool VEC, int GROUP, bool CACHED, bool CUT = false, class Emit>
-__device__ uint32_t mass_chunks(const MassRows& a, int k0, int k1, int chunk2, int V, float* scr,
-                                Emit&& emit) {
+template <MassKind K, bool BF16, bool VEC, int GROUP, bool CACHED, bool CUT, class Emit>
+__device__ __forceinline__ uint32_t mass_chunks_of(const MassRows& a, int k0, int k1, int chunk2, int V, float* scr,
+                                   Emit&& emit) {
     uint32_t dep = 0;
     if (k0 >= k1) return dep;
     if constexpr (VEC) {
@@ -222,7 +230,7 @@ __device__ uint32_t mass_chunks(const MassRows& a, int k0, int k1, int chunk2, i
                 for (int j = 0; j < GROUP; ++j) {
                     if (kb + j >= b1) break;
                     const int lo = (kb + j) * chunk2, hi = min(V, lo + chunk2);
-                    const float2 h = lane_mass<BF16, VEC, CUT>(r[j], a, lo, hi);
+                    const float2 h = lane_mass<K, BF16, VEC, CUT>(r[j], a, lo, hi);
                     const float s0 = wave_sum(h.x), s1 = wave_sum(h.y);
                     if (l == 0) {
                         scr[((kb + j - b0) * kUnroll2 + 0) * kWaves + w] = s0;
@@ -265,6 +273,20 @@ __device__ uint32_t mass_chunks(const MassRows& a, int k0, int k1, int chunk2, i
     return dep;
 }
 
+// mass_chunks_of for the kind of mass a describes, chosen once for the whole
+// walk, with no branch on the kind between one group's loads and their
+// reduction.  Each copy of the walk is inlined: a walk left as a call takes
+// its register sets by reference, which puts them in scratch memory (the cut
+// decision with two-chunk groups went from 22.3 to 33.1 us that way).
+template <bool BF16, bool VEC, int GROUP, bool CACHED, bool CUT = false, class Emit>
+__device__ uint32_t mass_chunks(const MassRows& a, int k0, int k1, int chunk2, int V, float* scr,
+                                Emit&& emit) {
+    return with_mass_kind<CUT>(a, [&](auto kind) {
+        return mass_chunks_of<decltype(kind)::value, BF16, VEC, GROUP, CACHED, CUT>(a, k0, k1, chunk2, V, scr,
+                                                                                     emit);
+    });
+}
+
 // A chunk's mass from its halves' (every path adds them the same way).
 __device__ __forceinline__ float chunk_total(float h0, float h1) { return h0 + h1; }
 
@@ -275,7 +297,9 @@ __device__ float2 chunk_mass(const MassRows& a, int lo, int hi) {
     if constexpr (VEC) {
         ChunkRegs<BF16, VEC> r;
         load_chunk<BF16, VEC, false>(r, a, lo, hi);
-        h = lane_mass<BF16, VEC, CUT>(r, a, lo, hi);
+        h = with_mass_kind<CUT>(a, [&](auto kind) {
+            return lane_mass<decltype(kind)::value, BF16, VEC, CUT>(r, a, lo, hi);
+        });
     } else {
         h = lane_mass_elements<BF16, CUT>(a, lo, hi);
     }
@@ -312,12 +336,14 @@ __device__ int search_half(const MassRows& a, int lo, int hi, float base, float 
     float r[PER];
     float run = 0.0f;
     int lastp = -1;
-    with_mass_kind(a, [&](auto kind) {
+    with_mass_kind<CUT>(a, [&](auto kind) {
         constexpr MassKind K = decltype(kind)::value;
 #pragma unroll
         for (int k = 0; k < N; ++k) {
             const int v = e0 + k;
-            const float x = v < hi ? mass_of<K, CUT>(a, vp.x[k], K == MassKind::kResidual ? vq.x[k] : 0.0f, v) : 0.0f;
+            const float x =
+                v < hi ? mass_of<K, CUT>(a, vp.x[k], K != MassKind::kTarget && K != MassKind::kTargetButOne && a.q ? vq.x[k] : 0.0f, v)
+                       : 0.0f;
             if (x > 0.0f) lastp = v;
             r[k] = x;
             run += x;
