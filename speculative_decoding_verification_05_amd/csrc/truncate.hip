@@ -15,18 +15,19 @@
 //   is kept.  Target and draft rows are filtered independently.
 //
 // k_trunc_select  one 256-lane workgroup per used row, one streaming read of
-//                 the row.  Each lane keeps the four largest of its per-tile
-//                 maxima (the maximum of its 32 elements of a tile) with
-//                 their tiles: distinct elements of the row, so the k-th
-//                 largest of these 1024 values bounds the row's k-th largest
-//                 logit from below, and every element at or above that bound
-//                 lies in one of its lane's top-three tiles (or the lane's
-//                 fourth maximum reaches the bound too, and its whole share
-//                 is read again).  Those tiles (a few percent of the row) are
-//                 read again and their elements at or above the bound go to
-//                 per-wave LDS regions: a few dozen of 128K tokens for the
-//                 tested shapes.  One wave then ranks them by (logit desc,
-//                 index asc), keeps the exact top-k set (ties kept) and the
+//                 the row.  Each lane keeps the four largest of its
+//                 per-vector maxima (the maximum of one 16-byte vector), each
+//                 packed with its vector's number into one word: distinct
+//                 elements of the row, so the k-th largest of these 1024
+//                 values bounds the row's k-th largest logit from below, and
+//                 every element at or above that bound lies in one of its
+//                 lane's four tracked vectors (or the lane's fourth maximum
+//                 reaches the bound while the lane has more vectors, and its
+//                 whole share is read again).  Those vectors (one cache line
+//                 each) are read again and their elements at or above the
+//                 bound go to per-wave LDS regions: a few dozen of 128K
+//                 tokens for the tested shapes.  One wave then ranks them by
+//                 (logit desc, index asc), keeps the exact top-k set (ties kept) and the
 //                 top-p prefix, and records the kept tokens sorted by index
 //                 with their weights 2^((z - max) c) and the kept total
 //                 (longer lists go through LDS bitonic sorts; lists past the
@@ -178,6 +179,25 @@ __device__ __forceinline__ uint4 load_raw(const void* rp, int e, int V) {
     }
 }
 
+// mag with the magnitude bits of a raw 16-byte vector folded in: per 16-bit
+// half with a packed maximum (bf16), per word (fp32).  A half (word) above
+// 0x7f80 (0x7f800000) afterwards means a NaN was seen.
+template <bool BF16>
+__device__ __forceinline__ uint32_t nan_mag(uint32_t mag, const uint4& r) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+    if constexpr (BF16) {
+        typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+        u16x2 a = __builtin_bit_cast(u16x2, mag);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a = __builtin_elementwise_max(a, __builtin_bit_cast(u16x2, w[j] & 0x7fff7fffu));
+        return __builtin_bit_cast(uint32_t, a);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mag = max(mag, w[j] & 0x7fffffffu);
+        return mag;
+    }
+}
+
 // One pass over a whole row in tiles of 256 lanes x kUnroll 16-byte vectors;
 // f(r, t0) sees a lane's kUnroll raw vectors of the tile at t0 (vector u
 // holds tokens t0 + (u * 256 + lane) * N ...), -inf past V.  VEC: every
@@ -185,8 +205,13 @@ __device__ __forceinline__ uint4 load_raw(const void* rp, int e, int V) {
 // tile's loads in flight while the current one is visited) with addresses
 // clamped into the row, so each byte of the row is fetched once; the last
 // tile's vectors past V (wholly past it: V is a multiple of N) become -inf
-// before its visit.
-template <bool BF16, bool VEC, int NT = kThreads, class F>
+// before its visit.  PEEL: every tile but the last is whole, so the loop
+// issues the next tile's loads unconditionally and the last tile is visited
+// after it (a load under a branch makes the compiler wait for every load in
+// flight, the next tile's included, before each visit); the visit's code is
+// then there twice, which costs registers.  Without PEEL one loop covers
+// every tile, the next tile's loads under a branch.
+template <bool BF16, bool VEC, bool PEEL, int NT = kThreads, class F>
 __device__ __forceinline__ void stream_tiles(const void* rp, int V, F&& f) {
     constexpr int N = Vec<BF16>::N;
     constexpr int TILE = NT * N * kUnroll;
@@ -198,22 +223,39 @@ __device__ __forceinline__ void stream_tiles(const void* rp, int V, F&& f) {
             for (int u = 0; u < kUnroll; ++u)
                 r[u] = load16_stream<BF16>(rp, min(t0 + (u * NT + t) * N, V - N));
         };
+        const uint32_t ninf = BF16 ? 0xff80ff80u : 0xff800000u;
         uint4 cur[kUnroll];
         load_tile(cur, 0);
-        for (int k = 0; k < ntiles; ++k) {
-            const int t0 = k * TILE;
-            uint4 nxt[kUnroll];
-            if (k + 1 < ntiles) load_tile(nxt, t0 + TILE);
+        if constexpr (PEEL) {
+            int t0 = 0;
+            for (int k = 0; k + 1 < ntiles; ++k, t0 += TILE) {
+                uint4 nxt[kUnroll];
+                load_tile(nxt, t0 + TILE);
+                f(cur, t0);
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) cur[u] = nxt[u];
+            }
             if (t0 + TILE > V) {
-                const uint32_t ninf = BF16 ? 0xff80ff80u : 0xff800000u;
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u)
                     if (t0 + (u * NT + t) * N >= V) cur[u] = make_uint4(ninf, ninf, ninf, ninf);
             }
             f(cur, t0);
-            if (k + 1 < ntiles) {
+        } else {
+            for (int k = 0; k < ntiles; ++k) {
+                const int t0 = k * TILE;
+                uint4 nxt[kUnroll];
+                if (k + 1 < ntiles) load_tile(nxt, t0 + TILE);
+                if (t0 + TILE > V) {
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u) cur[u] = nxt[u];
+                    for (int u = 0; u < kUnroll; ++u)
+                        if (t0 + (u * NT + t) * N >= V) cur[u] = make_uint4(ninf, ninf, ninf, ninf);
+                }
+                f(cur, t0);
+                if (k + 1 < ntiles) {
+#pragma unroll
+                    for (int u = 0; u < kUnroll; ++u) cur[u] = nxt[u];
+                }
             }
         }
     } else {
@@ -319,8 +361,6 @@ __global__ __launch_bounds__(kThreads) void k_trunc_select(VerifyParams P) {
     __shared__ int s_sel[3];
     constexpr int N = Vec<BF16>::N;
     constexpr int TILE = kThreads * N * kUnroll;
-    // widened bf16 values share the low 16 key bits: searching the top 16 is exact
-    constexpr int LO = BF16 ? 16 : 0;
     const int s = blockIdx.x, b = blockIdx.y;
     const bool is_target = s <= P.G;
     const int i = is_target ? s : s - (P.G + 1);
@@ -332,52 +372,51 @@ __global__ __launch_bounds__(kThreads) void k_trunc_select(VerifyParams P) {
     const uint64_t below = (1ull << l) - 1ull;
     const bool use_k = P.top_k > 0 && P.top_k < V;
 
-    // (1) the one read.  Per lane, the four largest of its per-tile maxima
-    // (the maximum of the lane's kUnroll vectors of a tile) with the tiles
-    // they come from; they are distinct elements of the row.
-    float v1 = neg_inf(), v2 = neg_inf(), v3 = neg_inf(), v4 = neg_inf();
-    int t1 = -1, t2 = -1, t3 = -1, t4 = -1;
-    uint64_t bad = 0;  // wave-uniform: a NaN was seen
+    // (1) the one read.  Per lane, the four largest of its per-vector maxima,
+    // each packed with its vector's unit number (tile * kUnroll + u) into one
+    // word: the top 16 bits of the maximum's order-preserving key (-0 taken
+    // as +0), then the unit.  Cutting a key's low bits only lowers the value
+    // it stands for (a widened bf16 loses nothing when positive).  The units
+    // hold distinct elements of the row.  0: no unit.
+    uint32_t k1 = 0u, k2 = 0u, k3 = 0u, k4 = 0u;
+    // NaNs: the lane's largest magnitude bits per 16-bit half (bf16) or per
+    // word (fp32); a NaN's exceed +inf's.  The tail's -inf does not.
+    uint32_t mag = 0;
     auto visit = [&](const uint4 (&r)[kUnroll], int t0) {
-        float m = neg_inf();  // the tail is filled with -inf; NaNs are skipped
+        const uint32_t unit0 = static_cast<uint32_t>(t0 / TILE) * kUnroll;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
+        for (int u = 0; u < kUnroll; ++u) {
+            float m = neg_inf();  // the tail is filled with -inf; NaNs are skipped
 #pragma unroll
-            for (int q = 0; q < N; ++q) {
-                const float x = elem<BF16>(r[u], q);
-                m = fmaxf(m, x);
-                bad |= __ballot(__builtin_isnan(x));
-            }
-        const int tile = t0 / TILE;
-        const bool c1 = m > v1, c2 = m > v2, c3 = m > v3, c4 = m > v4;
-        t4 = c3 ? t3 : (c4 ? tile : t4);
-        t3 = c2 ? t2 : (c3 ? tile : t3);
-        t2 = c1 ? t1 : (c2 ? tile : t2);
-        t1 = c1 ? tile : t1;
-        v4 = fmaxf(v4, fminf(m, v3));
-        v3 = fmaxf(v3, fminf(m, v2));
-        v2 = fmaxf(v2, fminf(m, v1));
-        v1 = fmaxf(v1, m);
+            for (int q = 0; q < N; ++q) m = fmaxf(m, elem<BF16>(r[u], q));
+            mag = nan_mag<BF16>(mag, r[u]);
+            const uint32_t key = (ordered_key(m + 0.0f) & 0xffff0000u) | (unit0 + u);
+            k4 = max(k4, min(key, k3));
+            k3 = max(k3, min(key, k2));
+            k2 = max(k2, min(key, k1));
+            k1 = max(k1, key);
+        }
     };
-    stream_tiles<BF16, VEC>(rp, V, visit);
-    bad |= __ballot(v1 == pos_inf());
+    stream_tiles<BF16, VEC, true>(rp, V, visit);
+    const bool lane_nan = BF16 ? ((mag & 0xffffu) > 0x7f80u || (mag >> 16) > 0x7f80u) : mag > 0x7f800000u;
+    // wave-uniform: a NaN or a +inf (key 0xff80....) was seen
+    const uint64_t bad = __ballot(lane_nan || (k1 >> 16) >= 0xff80u);
 
-    // (2) the bound: the k-th largest of the 4 x 256 tracked maxima, a lower
-    // bound on the row's k-th largest logit.  Radix select over the order-
-    // preserving keys, 8 bits a round from the top (the top 16 bits decide a
-    // widened bf16 exactly): an LDS histogram of the digit among the keys
-    // that share the digits chosen so far, then one wave scans the bins from
-    // the top for the one where the running count reaches k.
-    float bound = neg_inf();
+    // (2) the bound: the k-th largest of the 4 x 256 tracked keys, a lower
+    // bound on the row's k-th largest logit.  Radix select over the keys'
+    // top 16 bits, 8 a round from the top: an LDS histogram of the digit
+    // among the keys that share the digits chosen so far, then one wave
+    // scans the bins from the top for the one where the running count
+    // reaches k.
+    uint32_t bkey = 0u;  // no bound: every unit reaches
     if (t == 0) s_count = 0;
     if (use_k) {
-        constexpr int ROUNDS = (32 - LO) / 8;
-        const uint32_t kk[4] = {ordered_key(v1), ordered_key(v2), ordered_key(v3), ordered_key(v4)};
+        const uint32_t kk[4] = {k1 & 0xffff0000u, k2 & 0xffff0000u, k3 & 0xffff0000u, k4 & 0xffff0000u};
         uint32_t prefix = 0;
         int need = P.top_k;
         bool found = true;
 #pragma unroll
-        for (int r = 0; r < ROUNDS; ++r) {
+        for (int r = 0; r < 2; ++r) {
             const int shift = 24 - 8 * r;
             s_hist[t] = 0u;  // kThreads == 256 bins
             __syncthreads();
@@ -419,15 +458,18 @@ __global__ __launch_bounds__(kThreads) void k_trunc_select(VerifyParams P) {
             prefix |= static_cast<uint32_t>(s_sel[0]) << shift;
             need = s_sel[1];
         }
-        bound = found ? key_value(prefix) : neg_inf();
+        bkey = found ? prefix : 0u;
     }
+    const float bound = key_value(bkey);  // -inf when there is no bound
     __syncthreads();
 
-    // (3) every element at or above the bound lies in a tile whose lane
-    // maximum reaches it: read those tiles again (at most three per lane,
-    // one batch of loads) and append their elements >= bound to the wave's
-    // own LDS region (a wave-uniform count, no atomics).  A lane with a
-    // fourth such tile has its whole share re-read by its wave instead.
+    // (3) every element at or above the bound lies in a vector whose maximum
+    // reaches it, so in one of the lane's four tracked vectors unless the
+    // fourth reaches it too and the lane has other vectors (more than one
+    // tile): then its whole share is read again by its wave.  Otherwise the
+    // reaching tracked vectors are read again (one batch of loads) and their
+    // elements >= bound appended to the wave's own LDS region (a
+    // wave-uniform count, no atomics).
     float* zw = s_z + w * kWaveCap;
     int* iw = s_i + w * kWaveCap;
     int c = 0;
@@ -441,42 +483,41 @@ __global__ __launch_bounds__(kThreads) void k_trunc_select(VerifyParams P) {
         }
         c += __popcll(mask);
     };
-    const bool all = t4 >= 0 && v4 >= bound;
-    const int tl[3] = {t1 >= 0 && v1 >= bound && !all ? t1 : -1, t2 >= 0 && v2 >= bound && !all ? t2 : -1,
-                       t3 >= 0 && v3 >= bound && !all ? t3 : -1};
-    const bool any1 = __ballot(tl[0] >= 0) != 0, any2 = __ballot(tl[1] >= 0) != 0,
-               any3 = __ballot(tl[2] >= 0) != 0;
-    const int nt = any3 ? 3 : any2 ? 2 : any1 ? 1 : 0;
+    const int ntiles = (V + TILE - 1) / TILE;
+    auto reach = [&](uint32_t k) { return k != 0u && k >= bkey; };
+    const bool all = ntiles > 1 && reach(k4);
+    const uint32_t kt[4] = {k1, k2, k3, k4};
+    int ue[4];  // first element of each vector to read again, or -1
+    int nt = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int unit = static_cast<int>(kt[j] & 0xffffu);
+        ue[j] = reach(kt[j]) && !all ? (unit / kUnroll) * TILE + ((unit % kUnroll) * kThreads + t) * N : -1;
+        if (__ballot(ue[j] >= 0)) nt = j + 1;
+    }
     if (nt > 0) {
-        uint4 rv[3][kUnroll];
+        uint4 rv[4];
 #pragma unroll
-        for (int j = 0; j < 3; ++j) {
+        for (int j = 0; j < 4; ++j) {
             if (j >= nt) break;
-            // only lanes with a tile to re-read load (the others' loads are
+            // only lanes with a vector to read load (the others' loads are
             // masked off; their address stays inside the row all the same)
-            const int base = max(tl[j], 0) * TILE;
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
-                rv[j][u] = tl[j] >= 0 ? load_raw<BF16, VEC>(rp, base + (u * kThreads + t) * N, V)
-                                      : make_uint4(0u, 0u, 0u, 0u);
+            rv[j] = ue[j] >= 0 ? load_raw<BF16, VEC>(rp, max(ue[j], 0), V) : make_uint4(0u, 0u, 0u, 0u);
         }
 #pragma unroll
-        for (int j = 0; j < 3; ++j) {
+        for (int j = 0; j < 4; ++j) {
             if (j >= nt) break;
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-                for (int q = 0; q < N; ++q) {
-                    const int e = tl[j] * TILE + (u * kThreads + t) * N + q;
-                    const float x = elem<BF16>(rv[j][u], q);
-                    append(tl[j] >= 0 && e < V && x >= bound, x, e);
-                }
+            for (int q = 0; q < N; ++q) {
+                const int e = ue[j] + q;
+                const float x = elem<BF16>(rv[j], q);
+                append(ue[j] >= 0 && e < V && x >= bound, x, e);
+            }
         }
     }
     {
         // whole-share re-reads, one lane at a time: lane l reads tiles l, l + 64, ...
         uint64_t heavy = __ballot(all);
-        const int ntiles = (V + TILE - 1) / TILE;
         while (heavy) {
             const int L = __builtin_ctzll(heavy);
             heavy &= heavy - 1ull;
@@ -1025,7 +1066,7 @@ __global__ __launch_bounds__(kCutThreads) void k_trunc_cut(VerifyParams P) {
     // at t0 (each_w: also for the -inf filling past V, which weighs nothing,
     // for the passes that only add weights)
     auto each_impl = [&](auto&& f, auto check) {
-        stream_tiles<BF16, VEC, NT>(rp, V, [&](const uint4 (&r)[kUnroll], int t0) {
+        stream_tiles<BF16, VEC, false, NT>(rp, V, [&](const uint4 (&r)[kUnroll], int t0) {
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
