@@ -477,6 +477,49 @@ def test_truncation_ties_at_the_kth_value():
     check_sample(wl, x, label="ties at the k-th value")
 
 
+def test_truncation_fp32_values_sharing_their_top_key_bits():
+    """fp32 rows whose 200 largest logits differ only in their low mantissa
+    bits (one 16-bit key bucket): the selection's bound, taken from the keys'
+    top 16 bits, keeps all of them as candidates and the exact top-k is
+    found among them."""
+    wl = W["b8_g4_v32000_f32"].scaled(6, 20000, top_k=50, top_p=0.9)
+    x = synth.make_verify_inputs(wl)
+    rng = np.random.default_rng(11)
+    for arr in (x["target"], x["draft"]):
+        for b in range(arr.shape[0]):
+            for i in range(arr.shape[1]):
+                row = arr[b, i]
+                if np.isnan(row[0]):
+                    continue
+                np.minimum(row, np.float32(2.0), out=row)
+                pos = rng.choice(row.shape[0], 200, replace=False)
+                row[pos] = (np.uint32(0x40400000) + rng.permutation(200).astype(np.uint32)).view(np.float32)
+    check_sample(wl, x, label="fp32 candidates within one key bucket")
+
+
+def test_truncation_signed_zeros_and_negative_rows():
+    """bf16 rows with every logit negative, and rows whose k-th largest value
+    is zero with +0 and -0 both present (equal logits: all of them kept)."""
+    wl = W["b128_g4_v128256_topk50_topp09"].scaled(6, 30000, top_p=1.0)
+    x = synth.make_verify_inputs(wl)
+    rng = np.random.default_rng(12)
+    for arr in (x["target"], x["draft"]):
+        for b in range(arr.shape[0]):
+            for i in range(arr.shape[1]):
+                row = arr[b, i]
+                if row[0] == synth.BF16_QNAN:
+                    continue
+                v = synth.bf16_bits_to_f32(row)
+                if (b + i) % 2 == 0:
+                    row[:] = synth.f32_to_bf16_bits(v - np.float32(100.0))
+                else:
+                    row[:] = synth.f32_to_bf16_bits(v - np.float32(v.max() + 1.0))
+                    pos = rng.choice(row.shape[0], 70, replace=False)
+                    row[pos[:30]] = np.uint16(0x0000)
+                    row[pos[30:]] = np.uint16(0x8000)
+    check_sample(wl, x, label="negative rows and signed zeros at the k-th value")
+
+
 def test_truncation_past_the_listed_limits_matches_the_oracle():
     """top_k above 1024, and top-p alone above 2048 tokens, run through the
     cut records (no longer rejected)."""
