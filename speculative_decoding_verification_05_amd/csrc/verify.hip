@@ -240,12 +240,35 @@ __device__ __forceinline__ uint32_t mass_chunks_of(const MassRows& a, int k0, in
             };
             ChunkRegs<BF16, VEC> ra[GROUP], rb[GROUP];
             load_group(ra, b0);
-            for (int kb = b0; kb < b1; kb += 2 * GROUP) {
-                if (kb + GROUP < b1) load_group(rb, kb + GROUP);
-                reduce_group(ra, kb);
-                if (kb + GROUP >= b1) break;
-                if (kb + 2 * GROUP < b1) load_group(ra, kb + 2 * GROUP);
-                reduce_group(rb, kb + GROUP);
+            if constexpr (!CUT) {
+                // no load under a branch between a group's loads and their
+                // reduction (the compiler would wait there for every load in
+                // flight, the next group's included): the last one or two
+                // groups after the loop, ra holding [kb, kb + GROUP)
+                int kb = b0;
+                for (; kb + 2 * GROUP < b1; kb += 2 * GROUP) {
+                    load_group(rb, kb + GROUP);
+                    reduce_group(ra, kb);
+                    load_group(ra, kb + 2 * GROUP);
+                    reduce_group(rb, kb + GROUP);
+                }
+                if (kb + GROUP < b1) {
+                    load_group(rb, kb + GROUP);
+                    reduce_group(ra, kb);
+                    reduce_group(rb, kb + GROUP);
+                } else {
+                    reduce_group(ra, kb);
+                }
+            } else {
+                // one copy of the (generic, membership-testing) reduction:
+                // the cut decision's registers do not hold a second
+                for (int kb = b0; kb < b1; kb += 2 * GROUP) {
+                    if (kb + GROUP < b1) load_group(rb, kb + GROUP);
+                    reduce_group(ra, kb);
+                    if (kb + GROUP >= b1) break;
+                    if (kb + 2 * GROUP < b1) load_group(ra, kb + 2 * GROUP);
+                    reduce_group(rb, kb + GROUP);
+                }
             }
             __syncthreads();
             if (threadIdx.x == 0) {
